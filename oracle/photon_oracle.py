@@ -1,0 +1,444 @@
+"""CPU oracle for PHOTON recursive generation (RecGen) and hierarchical
+generation (HierGen).  TEST INFRASTRUCTURE ONLY: the product never imports,
+calls or links this module; only the tests, the smoke check and the CPU
+baseline leg of the benchmark do.
+
+Plain, slow and meant to be read against the pages:
+  [abstract]  PHOTON paper record (ACL 2026 long paper "PHOTON: Hierarchical
+              Autoregressive Modeling for Lightspeed and Memory-Efficient
+              Language Generation"), abstract.
+  [modules]   PHOTON explainer (mokumoku.ipfde.com, Fujitsu PHOTON vertical
+              scan), module table: Context Chunker / Encoder / Converter /
+              Decoder rows, and the hierarchy-shape paragraph under it.
+  [recgen]    same explainer, recursive-generation section: HierGen's three
+              steps, RecGen's feedback of the bottleneck reconstruction,
+              Theorem A.6 (paper appendix A), the cache-drop paragraph.
+  [tpm]       same explainer, 1.2B decode-heavy table and the paragraph on
+              why both factors come from the hierarchy (decoder span).
+
+Every float is float64.  For bf16 models a rounding contract (round to the
+nearest bf16, ties to even) is applied at fixed points; for fp32 models the
+rounding is the identity and the oracle is plain fp64.  Contract:
+  * weights are bf16 (they arrive bf16-exact from the input generator);
+  * every activation operand of a matrix product is rounded: RMSNorm outputs,
+    attention outputs, GELU outputs, stack outputs (A, A-hat, h, z) and the
+    concatenated chunker inputs;
+  * K and V are rounded when they enter a cache (K after RoPE); q is not;
+  * accumulation, residual stream, norms, softmax, GELU and logits are not
+    rounded.
+Block internals are not given by the pages (they only say encoder and decoder
+are Transformers inside); the reading taken is a pre-norm block with RMSNorm
+(eps 1e-5), bias-free linears, multi-head attention with rotary position
+embedding (theta 1e4, rotate-half) and a d -> 4d -> d GELU MLP.
+
+Parity status: attention, RMSNorm, GELU, RoPE, chunker, converter, rounding
+and the cache/equivalence invariants are pinned by the CPU tests.  The
+overall model outputs are parity unpinned against the pages, which print no
+model output: the block internals above are a reading, not a checked fact.
+"""
+import math
+import numpy as np
+from scipy.special import erf
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# rounding
+# --------------------------------------------------------------------------
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bf16 has an 8-bit significand and fp32's exponent range.  For |x| in
+    [2^e, 2^(e+1)) the spacing is 2^(e-7); below 2^-126 (subnormal) it is the
+    fixed 2^-133.  numpy's rint rounds half to even.  Values beyond the
+    largest finite bf16 overflow to +-inf.
+    """
+    x = np.asarray(x, dtype=F64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    ax = np.abs(x[nz])
+    e = np.floor(np.log2(ax))
+    # guard floor(log2) at exact powers of two and rounding of log2
+    e = np.where(2.0 ** e > ax, e - 1, e)
+    e = np.where(2.0 ** (e + 1) <= ax, e + 1, e)
+    q = 2.0 ** np.maximum(e - 7, -133)
+    r = np.rint(x[nz] / q) * q
+    big = np.abs(r) > 3.3895313892515355e38
+    r[big] = np.copysign(np.inf, r[big])
+    out[nz] = r
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
+class Precision:
+    """Applies the rounding contract: ``r`` is round_bf16 for bf16 models and
+    the identity for fp32 models."""
+
+    def __init__(self, dtype):
+        assert dtype in ("f32", "bf16")
+        self.bf16 = dtype == "bf16"
+
+    def r(self, x):
+        return round_bf16(x) if self.bf16 else np.asarray(x, dtype=F64)
+
+
+# --------------------------------------------------------------------------
+# primitives
+# --------------------------------------------------------------------------
+def rmsnorm(x, g, eps):
+    """g * x / sqrt(mean(x^2) + eps) over the last axis."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return g * (x / np.sqrt(ms + eps))
+
+
+def gelu(z):
+    """Exact GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt 2))."""
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def rope_angles(pos, hd, theta):
+    """phi[p, i] = pos[p] * theta^(-2i/hd), i < hd/2."""
+    i = np.arange(hd // 2, dtype=F64)
+    inv = theta ** (-2.0 * i / hd)
+    return np.asarray(pos, dtype=F64)[:, None] * inv[None, :]
+
+
+def rope(x, pos, theta):
+    """Rotate-half rotary embedding over the full head dim.
+
+    x: [..., T, H, hd]; pos: [T].  Pair (x_i, x_{i+hd/2}) is rotated by
+    phi = pos * theta^(-2i/hd).
+    """
+    hd = x.shape[-1]
+    h = hd // 2
+    phi = rope_angles(pos, hd, theta)[:, None, :]       # [T, 1, h]
+    c, s = np.cos(phi), np.sin(phi)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def attention(q, k, v, n_prev):
+    """Causal multi-head attention with a cache prefix.
+
+    q: [B, Tq, H, hd] queries at absolute key indices n_prev .. n_prev+Tq-1;
+    k, v: [B, n_prev+Tq, H, hd] (cache followed by the new keys).
+    Query t sees keys 0 .. n_prev + t.  softmax(q k^T / sqrt(hd)) v.
+    """
+    B, Tq, H, hd = q.shape
+    Tk = k.shape[1]
+    s = np.einsum("bthe,bshe->bhts", q, k) / math.sqrt(hd)
+    allowed = np.arange(Tk)[None, :] <= (n_prev + np.arange(Tq))[:, None]
+    s = np.where(allowed[None, None], s, -np.inf)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return np.einsum("bhts,bshe->bthe", p, v)
+
+
+def linear(x, W):
+    """y = x W^T, W[out, in]."""
+    return x @ W.T
+
+
+# --------------------------------------------------------------------------
+# model pieces
+# --------------------------------------------------------------------------
+class Model:
+    """Weights (float64) plus the precision contract for one configuration."""
+
+    def __init__(self, cfg, weights):
+        self.cfg = cfg
+        self.pr = Precision(cfg.dtype)
+        self.w = {k: np.asarray(v, dtype=F64) for k, v in weights.items()}
+
+    def layers(self, prefix, n):
+        return [{p: self.w[f"{prefix}.{l}.{p}"] for p in
+                 ("g1", "Wq", "Wk", "Wv", "Wo", "g2", "W1", "W2")}
+                for l in range(n)]
+
+    # ---- a Transformer stack with optional per-layer KV cache ----
+    def stack(self, prefix, n_layers, x, pos, cache=None):
+        """Run a stack of pre-norm blocks then its final RMSNorm.
+
+        x: [B, T, d] residual input (float); pos: [T] rotary positions of the
+        new rows.  cache: None (no history, nothing kept) or a list with one
+        entry per layer, each a dict {"k": [B, n, H, hd], "v": ...} holding
+        the rounded K/V of earlier positions; the new K/V are appended in
+        place.  Returns the rounded stack output r(RMSNorm(x; gf)).
+        """
+        cfg, r = self.cfg, self.pr.r
+        B, T, d = x.shape
+        H, hd = cfg.n_heads, cfg.head_dim
+        x = np.array(x, dtype=F64)
+        for l, L in enumerate(self.layers(prefix, n_layers)):
+            a = r(rmsnorm(x, L["g1"], cfg.norm_eps))
+            q = linear(a, L["Wq"]).reshape(B, T, H, hd)
+            k = linear(a, L["Wk"]).reshape(B, T, H, hd)
+            v = linear(a, L["Wv"]).reshape(B, T, H, hd)
+            q = rope(q, pos, cfg.rope_theta)
+            k = r(rope(k, pos, cfg.rope_theta))
+            v = r(v)
+            if cache is not None:
+                ent = cache[l]
+                n_prev = ent["k"].shape[1]
+                ent["k"] = np.concatenate([ent["k"], k], axis=1)
+                ent["v"] = np.concatenate([ent["v"], v], axis=1)
+                kk, vv = ent["k"], ent["v"]
+            else:
+                n_prev, kk, vv = 0, k, v
+            o = r(attention(q, kk, vv, n_prev).reshape(B, T, d))
+            x = x + linear(o, L["Wo"])
+            a = r(rmsnorm(x, L["g2"], cfg.norm_eps))
+            hmid = r(gelu(linear(a, L["W1"])))
+            x = x + linear(hmid, L["W2"])
+        return r(rmsnorm(x, self.w[prefix + ".gf"], cfg.norm_eps))
+
+    def empty_cache(self, n_layers, B):
+        H, hd = self.cfg.n_heads, self.cfg.head_dim
+        return [{"k": np.zeros((B, 0, H, hd)), "v": np.zeros((B, 0, H, hd))}
+                for _ in range(n_layers)]
+
+    # ---- chunker and converter [modules] ----
+    def chunker(self, name, z):
+        """Context Chunker: concatenate C consecutive vectors in time order,
+        then one bias-free linear C*d -> d.  z: [B, T, d], T % C == 0."""
+        B, T, d = z.shape
+        W = self.w[name]
+        C = W.shape[1] // d
+        cat = self.pr.r(z).reshape(B, T // C, C * d)
+        return linear(cat, W)
+
+    def converter(self, name, h):
+        """Context Converter: transposed 1-D convolution with kernel = stride
+        = C on a length-1 input, i.e. output j = W[j*d:(j+1)*d, :] h.
+        h: [..., d] -> [..., C, d]."""
+        W = self.w[name]
+        d = h.shape[-1]
+        C = W.shape[0] // d
+        y = linear(self.pr.r(h), W)
+        return y.reshape(h.shape[:-1] + (C, d))
+
+    def embed(self, ids):
+        return self.w["E"][np.asarray(ids)]
+
+    def logits(self, z):
+        return linear(self.pr.r(z), self.w["W_out"])
+
+
+# --------------------------------------------------------------------------
+# generation
+# --------------------------------------------------------------------------
+class State:
+    """Decode state kept after prefill: the top-level K/V of every top layer,
+    the latest top output h, the number of top states, and (HierGen only)
+    the level-1 encoder K/V."""
+
+    def __init__(self, top_cache, h_last, n_top_states, lvl1_cache=None):
+        self.top = top_cache
+        self.h = h_last
+        self.top_len = n_top_states
+        self.lvl1 = lvl1_cache
+
+    def copy(self):
+        cp = lambda c: None if c is None else [
+            {"k": e["k"].copy(), "v": e["v"].copy()} for e in c]
+        return State(cp(self.top), self.h.copy(), self.top_len, cp(self.lvl1))
+
+
+def prefill(model, prompt, mode="recgen"):
+    """Bottom-up pass over the prompt [modules], [recgen].
+
+    tokens -> embedding -> Chunker^1 (C1 tokens -> 1) -> level-1 encoder
+    (causal, pos = level-1 index) -> Chunker^2 (C2 states -> 1) -> top
+    encoder (causal, pos = top index).  RecGen keeps only the top K/V and the
+    last top output; HierGen also keeps the level-1 K/V (the lower cache
+    that RecGen drops after prefill).
+    """
+    cfg = model.cfg
+    prompt = np.asarray(prompt)
+    B, P = prompt.shape
+    S = cfg.S
+    if P < S or P % S:
+        raise ValueError("prompt length must be a positive multiple of C1*C2")
+    e = model.embed(prompt)
+    u1 = model.chunker("W_ch1", e)
+    n1 = P // cfg.C1
+    c1 = model.empty_cache(cfg.n_enc1, B)
+    A1 = model.stack("enc1", cfg.n_enc1, u1, np.arange(n1), c1)
+    u2 = model.chunker("W_ch2", A1)
+    n = P // S
+    ct = model.empty_cache(cfg.n_top, B)
+    h = model.stack("top", cfg.n_top, u2, np.arange(n), ct)
+    return State(ct, h[:, -1], n, c1 if mode == "hiergen" else None)
+
+
+def _decode_tokens(model, A_hat, forced_tokens=None):
+    """Top-down token generation for one chunk [modules], [recgen].
+
+    A_hat: [B, C2, d] level-1 decoder outputs.  Each of the B*C2 level-1
+    positions is expanded independently: Converter^1 gives C1 conditioning
+    vectors c_0..c_{C1-1}; the token decoder runs C1 steps with attention
+    confined to the sub-chunk (in-chunk KV, positions 0..j); step j's input
+    is c_j plus the embedding of the previous token of the same sub-chunk
+    (c_0 alone at j = 0); greedy argmax with the lowest index on ties.
+    Returns (tokens [B, C2*C1], logits [B, C2*C1, V]) in k-major order,
+    token index k*C1 + j.  forced_tokens [B, C2*C1] replaces the fed-back
+    token (teacher forcing); the argmax is still reported.
+    """
+    cfg = model.cfg
+    B, C2, d = A_hat.shape
+    C1 = cfg.C1
+    c0 = model.converter("W_cv1", A_hat)              # [B, C2, C1, d]
+    rows = c0.reshape(B * C2, C1, d)
+    cache = model.empty_cache(cfg.n_dec0, B * C2)
+    toks = np.zeros((B * C2, C1), dtype=np.int64)
+    logits = np.zeros((B * C2, C1, cfg.vocab))
+    forced = None if forced_tokens is None else \
+        np.asarray(forced_tokens).reshape(B * C2, C1)
+    prev = None
+    for j in range(C1):
+        x = rows[:, j, :].copy()
+        if j > 0:
+            x = x + model.embed(prev)
+        z = model.stack("dec0", cfg.n_dec0, x[:, None, :], np.array([j]), cache)
+        lg = model.logits(z[:, 0, :])
+        logits[:, j] = lg
+        toks[:, j] = np.argmax(lg, axis=-1)           # first maximum
+        prev = toks[:, j] if forced is None else forced[:, j]
+    return toks.reshape(B, C2 * C1), logits.reshape(B, C2 * C1, cfg.vocab)
+
+
+def _top_step(model, state, u):
+    """One top-encoder step at position state.top_len: append the new K/V to
+    the global cache, attend over all top states, return h."""
+    h = model.stack("top", model.cfg.n_top, u[:, None, :],
+                    np.array([state.top_len]), state.top)
+    state.top_len += 1
+    state.h = h[:, 0]
+    return state.h
+
+
+def decode_chunk(model, state, mode="recgen", forced_tokens=None,
+                 forced_u=None):
+    """Generate the next chunk of S = C1*C2 tokens; updates ``state``.
+
+    Converter^2 expands h_{i-1} into C2 conditioning vectors; the level-1
+    decoder (causal inside the chunk, pos 0..C2-1, no cache kept) gives the
+    bottleneck reconstruction A-hat_i; tokens are written top-down.
+      RecGen  [recgen]: u_i = Chunker^2(A-hat_i), fed straight to the top.
+      HierGen [recgen]: the chunk's tokens are re-encoded bottom-up:
+              embedding -> Chunker^1 -> one level-1 encoder step over the
+              C2 new level-1 positions with the kept level-1 cache ->
+              A_i -> u_i = Chunker^2(A_i).
+    forced_u replaces u_i (used to force the premise of Theorem A.6).
+    Returns a dict with tokens, logits, A_hat, u (and A for HierGen).
+    """
+    cfg = model.cfg
+    B = state.h.shape[0]
+    C1, C2, d = cfg.C1, cfg.C2, cfg.d_model
+    c1 = model.converter("W_cv2", state.h)            # [B, C2, d]
+    A_hat = model.stack("dec1", cfg.n_dec1, c1, np.arange(C2), None)
+    toks, logits = _decode_tokens(model, A_hat, forced_tokens)
+    out = {"tokens": toks, "logits": logits, "A_hat": A_hat}
+    if mode == "recgen":
+        u = model.chunker("W_ch2", A_hat)[:, 0]
+    else:
+        fed = toks if forced_tokens is None else np.asarray(forced_tokens)
+        e = model.embed(fed)                           # [B, S, d]
+        u1 = model.chunker("W_ch1", e)                # [B, C2, d]
+        base = state.top_len * C2
+        A = model.stack("enc1", cfg.n_enc1, u1, base + np.arange(C2),
+                        state.lvl1)
+        out["A"] = A
+        u = model.chunker("W_ch2", A)[:, 0]
+    if forced_u is not None:
+        u = np.asarray(forced_u, dtype=F64)
+    out["u"] = u
+    out["h"] = _top_step(model, state, u)
+    return out
+
+
+def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None):
+    """Prefill then new_tokens / S decode chunks.  Returns (tokens [B, N],
+    logits [B, N, V], final state, per-chunk records)."""
+    S = model.cfg.S
+    if new_tokens % S:
+        raise ValueError("new_tokens must be a multiple of C1*C2")
+    st = prefill(model, prompt, mode)
+    toks, lg, recs = [], [], []
+    for c in range(new_tokens // S):
+        ft = None if forced_tokens is None else \
+            np.asarray(forced_tokens)[:, c * S:(c + 1) * S]
+        o = decode_chunk(model, st, mode, ft)
+        toks.append(o["tokens"])
+        lg.append(o["logits"])
+        recs.append(o)
+    return np.concatenate(toks, 1), np.concatenate(lg, 1), st, recs
+
+
+# --------------------------------------------------------------------------
+# full recompute (no caches), for the incremental == full checks
+# --------------------------------------------------------------------------
+def top_full(model, u_all):
+    """Causal top-encoder forward over all inputs u_all [B, n, d] at once."""
+    n = u_all.shape[1]
+    return model.stack("top", model.cfg.n_top, u_all, np.arange(n), None)
+
+
+def hier_full_logits(model, tokens, n_prompt_states):
+    """Teacher-forced HierGen forward over a whole token sequence [B, T]:
+    bottom-up over all tokens, then for every chunk i >= n_prompt_states the
+    top-down pass conditioned on h_{i-1}, with the true previous tokens fed
+    to the token decoder.  Returns logits [B, T - P, V]."""
+    cfg = model.cfg
+    tokens = np.asarray(tokens)
+    B, T = tokens.shape
+    S, C1, C2 = cfg.S, cfg.C1, cfg.C2
+    e = model.embed(tokens)
+    A1 = model.stack("enc1", cfg.n_enc1, model.chunker("W_ch1", e),
+                     np.arange(T // C1), None)
+    h = top_full(model, model.chunker("W_ch2", A1))     # [B, T/S, d]
+    out = []
+    for i in range(n_prompt_states, T // S):
+        c1 = model.converter("W_cv2", h[:, i - 1])
+        A_hat = model.stack("dec1", cfg.n_dec1, c1, np.arange(C2), None)
+        c0 = model.converter("W_cv1", A_hat).reshape(B * C2, C1, -1)
+        y = tokens[:, i * S:(i + 1) * S].reshape(B * C2, C1)
+        x = c0.copy()
+        x[:, 1:] += model.embed(y[:, :-1])
+        z = model.stack("dec0", cfg.n_dec0, x, np.arange(C1), None)
+        out.append(model.logits(z).reshape(B, S, cfg.vocab))
+    return np.concatenate(out, 1)
+
+
+# --------------------------------------------------------------------------
+# memory accounting (the TPM denominator) [tpm], [recgen]
+# --------------------------------------------------------------------------
+def top_states(cfg, tokens):
+    """Top-level KV length after ``tokens`` tokens: ceil(T / (C1*C2))."""
+    return -(-tokens // cfg.S)
+
+
+def kv_bytes(cfg, batch, tokens, mode="recgen"):
+    """Resident cache bytes after ``tokens`` tokens.
+
+    top: n_top layers x K,V x B x ceil(T/S) states x d, the only O(T) state.
+    dec: the token decoder's in-chunk K/V, n_dec0 x K,V x B*C2 sub-chunks x
+         C1 positions x d -- independent of T (the decoder's span is the
+         chunk).
+    lower: HierGen's level-1 K/V, n_enc1 x K,V x B x ceil(T/C1) x d; RecGen
+         drops it after prefill (0).
+    """
+    b = 2 if cfg.dtype == "bf16" else 4
+    d = cfg.d_model
+    top = cfg.n_top * 2 * batch * top_states(cfg, tokens) * d * b
+    dec = cfg.n_dec0 * 2 * batch * cfg.C2 * cfg.C1 * d * b
+    lower = 0 if mode == "recgen" else \
+        cfg.n_enc1 * 2 * batch * (-(-tokens // cfg.C1)) * d * b
+    return {"top": top, "dec": dec, "lower": lower}
+
+
+def tpm(ktok_per_s, gib):
+    """Throughput per unit memory: K tok/s divided by GiB."""
+    return ktok_per_s / gib

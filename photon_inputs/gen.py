@@ -1,0 +1,88 @@
+"""Seeded weight and prompt generators.
+
+Weights: every matrix is drawn in a fixed canonical order from one stream,
+``numpy.random.default_rng([seed, 0])``, as ``standard_normal(float32) * 0.02``
+(N(0, 0.02^2)). Norm gains are 1 and there are no biases. For bf16 models the
+drawn matrices are stored as bf16 (round to nearest, ties to even), so both
+the oracle and the GPU receive bit-identical values.
+
+Prompts: ``default_rng([seed, 1]).integers(0, V, (B, P), dtype=int32)``.
+
+Matrices are W[out, in]; a linear layer computes y = x W^T.
+"""
+from collections import OrderedDict
+import numpy as np
+
+MATRIX_STD = np.float32(0.02)
+LAYER_PARTS = ("g1", "Wq", "Wk", "Wv", "Wo", "g2", "W1", "W2")
+
+
+def _layer_shapes(prefix, n, d, dff):
+    out = []
+    for l in range(n):
+        p = f"{prefix}.{l}."
+        out += [(p + "g1", (d,)), (p + "Wq", (d, d)), (p + "Wk", (d, d)),
+                (p + "Wv", (d, d)), (p + "Wo", (d, d)), (p + "g2", (d,)),
+                (p + "W1", (dff, d)), (p + "W2", (d, dff))]
+    out.append((prefix + ".gf", (d,)))
+    return out
+
+
+def weight_shapes(cfg):
+    """Canonical (name, shape) list, in generation order."""
+    d, dff, V, C1, C2 = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.C1, cfg.C2
+    s = [("E", (V, d)), ("W_ch1", (d, C1 * d))]
+    s += _layer_shapes("enc1", cfg.n_enc1, d, dff)
+    s += [("W_ch2", (d, C2 * d))]
+    s += _layer_shapes("top", cfg.n_top, d, dff)
+    s += [("W_cv2", (C2 * d, d))]
+    s += _layer_shapes("dec1", cfg.n_dec1, d, dff)
+    s += [("W_cv1", (C1 * d, d))]
+    s += _layer_shapes("dec0", cfg.n_dec0, d, dff)
+    s += [("W_out", (V, d))]
+    return s
+
+
+def weight_names(cfg):
+    return [n for n, _ in weight_shapes(cfg)]
+
+
+def bf16_bits(x):
+    """float32 array -> uint16 bf16 bit patterns, round to nearest even.
+
+    Input values here are finite (weights), so no NaN handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite inputs: u + 0x8000 cannot wrap a uint32
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _bf16_values(x):
+    return (bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
+
+
+def gen_weights(cfg, seed, zero=()):
+    """Seeded weights as float32 arrays (bf16-exact when cfg.dtype == 'bf16').
+
+    ``zero`` names tensors to replace by zeros after drawing (the stream is
+    unchanged, so every other tensor keeps its value).
+    """
+    rng = np.random.default_rng([seed, 0])
+    out = OrderedDict()
+    for name, shape in weight_shapes(cfg):
+        if len(shape) == 1:
+            w = np.ones(shape, dtype=np.float32)
+        else:
+            w = rng.standard_normal(shape, dtype=np.float32) * MATRIX_STD
+            if cfg.dtype == "bf16":
+                w = _bf16_values(w)
+        if name in zero:
+            w = np.zeros_like(w)
+        out[name] = w
+    return out
+
+
+def gen_prompts(cfg, batch, prompt, seed):
+    rng = np.random.default_rng([seed, 1])
+    return rng.integers(0, cfg.vocab, size=(batch, prompt), dtype=np.int32)
