@@ -1,0 +1,178 @@
+#!/usr/bin/env python
+"""Decode benchmark of PHOTON recursive generation (RecGen) on one MI355X.
+
+A step is one decode chunk: the whole hot path (Converter^2, level-1
+decoder, C1 token-decoder steps with the greedy head, Chunker^2 feedback and
+the top-encoder step over the global K/V) for every sequence of the batch,
+B * C1 * C2 tokens.  The workload is prefilled once (untimed); the timed
+steps decode chunk after chunk from the prompt end, rewinding to the prompt
+end (restore h, reset the position) whenever the workload's new_tokens are
+used up, so every step runs at the workload's real cache lengths.
+
+Prints one JSON line: decode tok/s (value), TPM = tok/s per GiB of resident
+decode weights + top K/V + decoder K/V + state, the whole path's fraction of
+the HBM roofline (algorithmic bytes per chunk at 8 TB/s), the dominant
+kernel's achieved bandwidth measured with HIP events over the timed region,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+METRIC = "decode tok/s and TPM (tok/s/GiB) at 1 MI355X; % HBM roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, W, prompt, seqs, threads):
+    """The oracle as it stands, RecGen decode phase only (perf_counter),
+    on `seqs` sequences of the workload; prefill and weight setup untimed."""
+    from threadpoolctl import threadpool_limits
+    from oracle import photon_oracle as O
+    with threadpool_limits(limits=threads):
+        m = O.Model(wl.cfg, W)
+        st = O.prefill(m, prompt[:seqs])
+        t0 = time.perf_counter()
+        for _ in range(wl.chunks):
+            O.decode_chunk(m, st)
+        dt = time.perf_counter() - t0
+    return seqs * wl.new_tokens / dt, dt
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode chunks (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed decode chunks (default: the workload's)")
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: photon-150m B32 P1024 N256)")
+    ap.add_argument("--mode", default="recgen", choices=["recgen", "hiergen"])
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path shards by batch "
+              "with no collective, so N GPUs give N x the one-GPU figure; nothing here uses a second GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import photon_inputs as pi
+    from hierarchical_autoregressive_lm_amd.photon import Photon
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = pi.get(args.workload)
+    cfg = wl.cfg
+    K = args.steps if args.steps is not None else wl.chunks
+    Wm = args.warmup if args.warmup is not None else wl.chunks
+    B, S = wl.batch, cfg.S
+    log(f"workload {wl.name}: generating weights")
+    W = pi.gen_weights(cfg, wl.seed)
+    prompt = pi.gen_prompts(cfg, B, wl.prompt, wl.seed)
+    model = Photon(cfg, W)
+    model.prefill(torch.from_numpy(prompt).cuda(), wl.max_tokens, args.mode)
+    if args.mode == "recgen":
+        model.release_prefill_weights()
+    snap = model.state_snapshot()
+    tok = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    pos = [0]
+
+    def step():
+        if pos[0] == wl.chunks:
+            model.state_restore(snap, wl.prompt)
+            pos[0] = 0
+        model.decode_chunk(tok)
+        pos[0] += 1
+
+    # one traced pass over the workload's chunks: per-kernel bytes and times
+    model.trace_enable(None)
+    for _ in range(wl.chunks):
+        step()
+    torch.cuda.synchronize()
+    per_class = model.trace_read()
+    chunk_bytes = sum(v["bytes"] for v in per_class.values()) / wl.chunks
+    dominant = max(per_class, key=lambda k: per_class[k]["ms"])
+    log(f"dominant kernel class: {dominant}")
+
+    # warmup, then the timed steps with only the dominant class traced
+    model.trace_enable([])
+    for _ in range(Wm):
+        step()
+    model.state_restore(snap, wl.prompt)
+    pos[0] = 0
+    model.trace_enable([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dom = model.trace_read()[dominant]
+    model.trace_enable([])
+
+    tok_s = B * S * K / dt
+    rep = model.report(B, wl.max_tokens, args.mode)
+    resident = rep["weights_decode"] + rep["top_kv"] + rep["dec_kv"] + rep["state"]
+    if args.mode == "hiergen":
+        resident += rep["weights_prefill_only"] + rep["lower_kv"]
+    gib = resident / 2 ** 30
+    kv_gib = (rep["top_kv"] + rep["dec_kv"] + rep["lower_kv"]) / 2 ** 30
+    ideal_s = chunk_bytes / (HBM_PEAK_GBS * 1e9)
+    roof_tok_s = B * S / ideal_s
+    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_seqs > 0:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        log(f"oracle baseline on {args.cpu_seqs} sequences, {threads} threads")
+        cv, cdt = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads)
+        cpu = {"value": round(cv, 2), "unit": "tok/s", "cores": threads, "kind": "oracle",
+               "sample": f"RecGen decode phase of {args.cpu_seqs} of {B} sequences, all {wl.chunks} chunks "
+                         f"({args.cpu_seqs * wl.new_tokens} tokens, {cdt:.1f} s), numpy float64"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(dt / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "mode": args.mode, "batch": B, "prompt": wl.prompt,
+                   "new_tokens": wl.new_tokens, "d_model": cfg.d_model, "heads": cfg.n_heads,
+                   "chunk": list(cfg.chunk), "layers_top_enc1_dec1_dec0": [cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0],
+                   "vocab": cfg.vocab, "tokens_per_step": B * S},
+        "tpm": round(tok_s / gib, 1),
+        "tpm_unit": "tok/s/GiB (decode weights + top K/V + decoder K/V + state)",
+        "resident_gib": round(gib, 4),
+        "tpm_kv_only": round(tok_s / kv_gib, 1),
+        "path_roofline": {"algorithmic_bytes_per_step": round(chunk_bytes), "ideal_us_per_step": round(ideal_s * 1e6, 2),
+                          "roofline_tok_s": round(roof_tok_s, 1), "frac": round(tok_s / roof_tok_s, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": dominant, "launches": dom["launches"],
+                     "avg_us": round(dom["ms"] * 1e3 / dom["launches"], 2),
+                     "bytes_per_launch": round(dom["bytes"] / dom["launches"])},
+        "kernels": {k: {"launches_per_step": v["launches"] // wl.chunks,
+                        "us_per_step": round(v["ms"] * 1e3 / wl.chunks, 2),
+                        "GB_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+                    for k, v in sorted(per_class.items(), key=lambda kv: -kv[1]["ms"])},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

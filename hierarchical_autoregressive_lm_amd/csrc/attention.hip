@@ -1,0 +1,420 @@
+// Attention kernels for the PHOTON decode and prefill paths.
+//
+//  * attn_decode: the top encoder's step over the global coarse K/V cache
+//    (and HierGen's level-1 step).  Memory-bound: every byte of K and V is
+//    streamed once.  One workgroup per (sequence, head, key split); the 256
+//    threads form 16 row slots x 16 lanes, each lane owning hd/16 contiguous
+//    elements, so a wave reads 4 consecutive cache rows per instruction
+//    (contiguous bytes).  Each row slot keeps its own online-softmax state
+//    (max, sum, partial output) over the keys it visits; the 16 slots are
+//    merged through LDS at the end, and the splits by a combine kernel.
+//  * attn_chunk: the decoders' attention confined to the chunk (at most a
+//    few keys per query); one wave per (sequence, head).
+//  * attn_prefill: causal attention over a whole prompt, fp32 FMA, 64
+//    queries per workgroup with K/V tiles of 64 keys staged in LDS.
+// q is fp32 everywhere; K and V are read in the storage dtype; softmax and
+// accumulation are fp32; the output is rounded to the storage dtype.
+#include "common.h"
+#include "kernels.h"
+
+namespace photon {
+namespace {
+
+template <typename T, int CE> struct Chunk;
+template <int CE> struct Chunk<bf16_t, CE> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[CE]) {
+    if constexpr (CE == 2) {
+      uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = __uint_as_float(w << 16); v[1] = __uint_as_float(w & 0xffff0000u);
+    } else if constexpr (CE == 4) {
+      uint2 w = *reinterpret_cast<const uint2*>(p);
+      v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+      v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else if constexpr (CE == 6) {
+      uint32_t w0 = reinterpret_cast<const uint32_t*>(p)[0];
+      uint32_t w1 = reinterpret_cast<const uint32_t*>(p)[1];
+      uint32_t w2 = reinterpret_cast<const uint32_t*>(p)[2];
+      v[0] = __uint_as_float(w0 << 16); v[1] = __uint_as_float(w0 & 0xffff0000u);
+      v[2] = __uint_as_float(w1 << 16); v[3] = __uint_as_float(w1 & 0xffff0000u);
+      v[4] = __uint_as_float(w2 << 16); v[5] = __uint_as_float(w2 & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < CE; ++e) v[e] = bf2f(p[e]);
+    }
+  }
+};
+template <int CE> struct Chunk<float, CE> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[CE]) {
+#pragma unroll
+    for (int e = 0; e < CE; ++e) v[e] = p[e];
+  }
+};
+
+__device__ __forceinline__ int resolve_len(int L_host, const int* L_dev, int L_mul, int L_add) {
+  return L_dev ? (*L_dev) * L_mul + L_add : L_host;
+}
+
+// ---------------------------------------------------------------- decode
+template <typename T, int HD, int Q, int U>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnCall a, float scale) {
+  constexpr int CE = HD / 16;
+  const int tid = threadIdx.x;
+  const int c = tid & 15, r = tid >> 4;
+  const int nsplit = a.nsplit;
+  const int split = blockIdx.x % nsplit;
+  const int gh = blockIdx.x / nsplit;
+  const int h = gh % a.H, g = gh / a.H;
+  const int L = resolve_len(a.L_host, a.L_dev, a.L_mul, a.L_add);
+  int kps = (L + nsplit - 1) / nsplit;
+  kps = (kps + 15) & ~15;
+  const int k0 = split * kps;
+  const int k1 = min(L, k0 + kps);
+
+  float qv[Q][CE];
+#pragma unroll
+  for (int t = 0; t < Q; ++t)
+#pragma unroll
+    for (int e = 0; e < CE; ++e)
+      qv[t][e] = a.q[(int64_t)(g * Q + t) * a.q_ld + h * HD + c * CE + e] * scale;
+
+  const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
+  const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
+
+  float m[Q], l[Q], o[Q][CE];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {
+    m[t] = -INFINITY; l[t] = 0.f;
+#pragma unroll
+    for (int e = 0; e < CE; ++e) o[t][e] = 0.f;
+  }
+
+  for (int kb = k0; kb < k1; kb += 16 * U) {
+    float kv[U][CE], vv[U][CE];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int key = kb + r + 16 * u;
+      key = key < k1 ? key : k1 - 1;       // in-bounds; masked below
+      Chunk<T, CE>::load(Kb + (int64_t)key * HD, kv[u]);
+      Chunk<T, CE>::load(Vb + (int64_t)key * HD, vv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = kb + r + 16 * u;
+#pragma unroll
+      for (int t = 0; t < Q; ++t) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) s = fmaf(qv[t][e], kv[u][e], s);
+        s += __shfl_xor(s, 8, 64);
+        s += __shfl_xor(s, 4, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 1, 64);
+        const bool ok = key < k1 && key <= L - Q + t;
+        if (ok) {
+          const float mn = fmaxf(m[t], s);
+          const float corr = expf(m[t] - mn);
+          const float pr = expf(s - mn);
+          l[t] = l[t] * corr + pr;
+#pragma unroll
+          for (int e = 0; e < CE; ++e) o[t][e] = fmaf(pr, vv[u][e], o[t][e] * corr);
+          m[t] = mn;
+        }
+      }
+    }
+  }
+
+  // merge the 16 row slots
+  __shared__ float sm[16][Q], sl[16][Q];
+  __shared__ float so[16][Q][HD];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {
+    if (c == 0) { sm[r][t] = m[t]; sl[r][t] = l[t]; }
+#pragma unroll
+    for (int e = 0; e < CE; ++e) so[r][t][c * CE + e] = o[t][e];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < Q * HD; idx += 256) {
+    const int t = idx / HD, e = idx % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) M = fmaxf(M, sm[s][t]);
+    float den = 0.f, num = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const float w = expf(sm[s][t] - M);
+        den = fmaf(sl[s][t], w, den);
+        num = fmaf(so[s][t][e], w, num);
+      }
+    }
+    if (nsplit == 1) {
+      T* out = reinterpret_cast<T*>(a.out);
+      out[(int64_t)(g * Q + t) * a.out_ld + h * HD + e] = St<T>::st(num / den);
+    } else {
+      float* pp = a.part + ((((int64_t)g * a.H + h) * Q + t) * nsplit + split) * (HD + 2);
+      pp[e] = num;
+      if (e == 0) { pp[HD] = M; pp[HD + 1] = den; }
+    }
+  }
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnCall a) {
+  // one wave per (g, h, t)
+  const int idx = blockIdx.x;
+  const int t = idx % a.Q;
+  const int h = (idx / a.Q) % a.H;
+  const int g = idx / (a.Q * a.H);
+  const float* pp = a.part + (((int64_t)g * a.H + h) * a.Q + t) * a.nsplit * (HD + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pp[s * (HD + 2) + HD]);
+  T* out = reinterpret_cast<T*>(a.out);
+  for (int e = threadIdx.x; e < HD; e += 64) {
+    float den = 0.f, num = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = pp[s * (HD + 2) + HD];
+      if (ms == -INFINITY) continue;
+      const float w = expf(ms - M);
+      den = fmaf(pp[s * (HD + 2) + HD + 1], w, den);
+      num = fmaf(pp[s * (HD + 2) + e], w, num);
+    }
+    out[(int64_t)(g * a.Q + t) * a.out_ld + h * HD + e] = St<T>::st(num / den);
+  }
+}
+
+// ----------------------------------------------------------------- chunk
+template <typename T, int HD, int MAXL>
+__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnCall a, float scale) {
+  constexpr int EP = (HD + 63) / 64;       // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.G * a.H) return;            // whole wave exits together
+  const int h = pair % a.H, g = pair / a.H;
+  const int L = resolve_len(a.L_host, a.L_dev, a.L_mul, a.L_add);
+  const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
+  const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
+  float kv[MAXL][EP], vv[MAXL][EP];
+#pragma unroll
+  for (int j = 0; j < MAXL; ++j)
+#pragma unroll
+    for (int x = 0; x < EP; ++x) {
+      const int e = lane + 64 * x;
+      const bool ok = j < L && e < HD;
+      kv[j][x] = ok ? St<T>::ld(Kb[j * HD + e]) : 0.f;
+      vv[j][x] = ok ? St<T>::ld(Vb[j * HD + e]) : 0.f;
+    }
+  T* out = reinterpret_cast<T*>(a.out);
+  for (int t = 0; t < a.Q; ++t) {
+    float q[EP];
+#pragma unroll
+    for (int x = 0; x < EP; ++x) {
+      const int e = lane + 64 * x;
+      q[x] = e < HD ? a.q[(int64_t)(g * a.Q + t) * a.q_ld + h * HD + e] * scale : 0.f;
+    }
+    const int last = L - a.Q + t;           // last visible key
+    float s[MAXL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+      float d = 0.f;
+#pragma unroll
+      for (int x = 0; x < EP; ++x) d = fmaf(q[x], kv[j][x], d);
+      d = wave_sum(d);
+      s[j] = d;
+      if (j <= last) mx = fmaxf(mx, d);
+    }
+    float den = 0.f, num[EP];
+#pragma unroll
+    for (int x = 0; x < EP; ++x) num[x] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+      if (j <= last) {
+        const float pr = expf(s[j] - mx);
+        den += pr;
+#pragma unroll
+        for (int x = 0; x < EP; ++x) num[x] = fmaf(pr, vv[j][x], num[x]);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < EP; ++x) {
+      const int e = lane + 64 * x;
+      if (e < HD) out[(int64_t)(g * a.Q + t) * a.out_ld + h * HD + e] = St<T>::st(num[x] / den);
+    }
+  }
+}
+
+// --------------------------------------------------------------- prefill
+// 64 queries per workgroup, 4 threads per query.  Thread part pp computes
+// the scores of keys pp, pp+4, ... of each 64-key tile and accumulates
+// output elements [pp*HD/4, (pp+1)*HD/4).
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnCall a, float scale) {
+  constexpr int TK = 64, QB = 64, OE = HD / 4;
+  __shared__ float Ks[TK][HD + 1];
+  __shared__ float Vs[TK][HD];
+  const int tid = threadIdx.x;
+  const int qi = tid >> 2, pp = tid & 3;
+  const int nqb = (a.Q + QB - 1) / QB;
+  const int qb = blockIdx.x % nqb;
+  const int gh = blockIdx.x / nqb;
+  const int h = gh % a.H, g = gh / a.H;
+  const int t = qb * QB + qi;                  // query index in sequence
+  const bool qok = t < a.Q;
+  float q[HD];
+#pragma unroll
+  for (int e = 0; e < HD; ++e)
+    q[e] = qok ? a.q[(int64_t)(g * a.Q + t) * a.q_ld + h * HD + e] * scale : 0.f;
+  float o[OE];
+#pragma unroll
+  for (int e = 0; e < OE; ++e) o[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
+  const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
+  const int kend = min(a.Q, (qb + 1) * QB);    // keys 0..kend-1 may be visible
+  for (int k0 = 0; k0 < kend; k0 += TK) {
+    __syncthreads();
+    for (int idx = tid; idx < TK * HD; idx += 256) {
+      const int j = idx / HD, e = idx % HD;
+      const bool ok = k0 + j < kend;
+      Ks[j][e] = ok ? St<T>::ld(Kb[(int64_t)(k0 + j) * HD + e]) : 0.f;
+      Vs[j][e] = ok ? St<T>::ld(Vb[(int64_t)(k0 + j) * HD + e]) : 0.f;
+    }
+    __syncthreads();
+    float s[TK / 4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < TK / 4; ++jj) {
+      const int j = jj * 4 + pp;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < HD; ++e) d = fmaf(q[e], Ks[j][e], d);
+      const bool vis = (k0 + j) <= t && (k0 + j) < kend;
+      s[jj] = vis ? d : -INFINITY;
+      tmax = fmaxf(tmax, s[jj]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
+    const float mn = fmaxf(m, tmax);
+    if (mn == -INFINITY) continue;             // nothing visible yet (uniform per query)
+    const float corr = expf(m - mn);
+    float psum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < TK / 4; ++jj) {
+      s[jj] = expf(s[jj] - mn);
+      psum += s[jj];
+    }
+    psum += __shfl_xor(psum, 1, 64);
+    psum += __shfl_xor(psum, 2, 64);
+    l = l * corr + psum;
+#pragma unroll
+    for (int e = 0; e < OE; ++e) o[e] *= corr;
+    const int base = (threadIdx.x & 63) & ~3;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      const float pj = __shfl(s[j / 4], base + (j & 3), 64);
+#pragma unroll
+      for (int e = 0; e < OE; ++e) o[e] = fmaf(pj, Vs[j][pp * OE + e], o[e]);
+    }
+    m = mn;
+  }
+  if (qok) {
+    T* out = reinterpret_cast<T*>(a.out);
+#pragma unroll
+    for (int e = 0; e < OE; ++e)
+      out[(int64_t)(g * a.Q + t) * a.out_ld + h * HD + pp * OE + e] = St<T>::st(o[e] / l);
+  }
+}
+
+template <typename T, int HD>
+hipError_t decode_hd(const AttnCall& a, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)HD);
+  dim3 grid(a.G * a.H * a.nsplit), block(256);
+  switch (a.Q) {
+    case 1: attn_decode_kernel<T, HD, 1, 4><<<grid, block, 0, st>>>(a, scale); break;
+    case 2: attn_decode_kernel<T, HD, 2, 4><<<grid, block, 0, st>>>(a, scale); break;
+    case 4: attn_decode_kernel<T, HD, 4, 2><<<grid, block, 0, st>>>(a, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  attn_combine_kernel<T, HD><<<a.G * a.H * a.Q, 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int HD>
+hipError_t chunk_hd(const AttnCall& a, hipStream_t st, int maxl) {
+  const float scale = 1.0f / sqrtf((float)HD);
+  dim3 grid((a.G * a.H + 3) / 4), block(256);
+  if (maxl <= 2) attn_chunk_kernel<T, HD, 2><<<grid, block, 0, st>>>(a, scale);
+  else if (maxl <= 4) attn_chunk_kernel<T, HD, 4><<<grid, block, 0, st>>>(a, scale);
+  else if (maxl <= 8) attn_chunk_kernel<T, HD, 8><<<grid, block, 0, st>>>(a, scale);
+  else if (maxl <= 16) attn_chunk_kernel<T, HD, 16><<<grid, block, 0, st>>>(a, scale);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T, int HD>
+hipError_t prefill_hd(const AttnCall& a, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)HD);
+  const int nqb = (a.Q + 63) / 64;
+  attn_prefill_kernel<T, HD><<<a.G * a.H * nqb, 256, 0, st>>>(a, scale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_decode(const AttnCall& a, hipStream_t st) {
+  switch (a.hd) {
+    case 32: return decode_hd<T, 32>(a, st);
+    case 64: return decode_hd<T, 64>(a, st);
+    case 96: return decode_hd<T, 96>(a, st);
+    case 128: return decode_hd<T, 128>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <typename T>
+hipError_t dispatch_chunk(const AttnCall& a, hipStream_t st, int maxl) {
+  switch (a.hd) {
+    case 32: return chunk_hd<T, 32>(a, st, maxl);
+    case 64: return chunk_hd<T, 64>(a, st, maxl);
+    case 96: return chunk_hd<T, 96>(a, st, maxl);
+    case 128: return chunk_hd<T, 128>(a, st, maxl);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <typename T>
+hipError_t dispatch_prefill(const AttnCall& a, hipStream_t st) {
+  switch (a.hd) {
+    case 32: return prefill_hd<T, 32>(a, st);
+    case 64: return prefill_hd<T, 64>(a, st);
+    case 96: return prefill_hd<T, 96>(a, st);
+    case 128: return prefill_hd<T, 128>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int attn_decode_splits(int G, int H, int cap) {
+  // aim for ~2048 workgroups, at least 64 keys per split
+  const int pairs = G * H;
+  int ns = (2048 + pairs - 1) / pairs;
+  const int max_ns = (cap + 63) / 64;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  return ns;
+}
+
+hipError_t launch_attn_decode(const AttnCall& a, hipStream_t st) {
+  return a.dtype ? dispatch_decode<bf16_t>(a, st) : dispatch_decode<float>(a, st);
+}
+
+hipError_t launch_attn_chunk(const AttnCall& a, hipStream_t st) {
+  const int maxl = a.L_dev ? a.cap : a.L_host;
+  return a.dtype ? dispatch_chunk<bf16_t>(a, st, maxl) : dispatch_chunk<float>(a, st, maxl);
+}
+
+hipError_t launch_attn_prefill(const AttnCall& a, hipStream_t st) {
+  return a.dtype ? dispatch_prefill<bf16_t>(a, st) : dispatch_prefill<float>(a, st);
+}
+
+}  // namespace photon

@@ -1,0 +1,388 @@
+// Weight-streaming GEMMs for the PHOTON decode and prefill paths.
+//
+// C[M,N] = A[M,K] W[N,K]^T.  In decode, M is small (B or B*C2 rows) and the
+// whole cost is streaming W from HBM once, so the kernel is organised around
+// W: each workgroup owns a slab of W rows (output features) and keeps every
+// activation row of its M tile in LDS, k-block by k-block.  bf16 operands go
+// through v_mfma_f32_16x16x32_bf16 with W as the MFMA A operand (16 features
+// x 32 k) and the activations as the B operand (32 k x 16 rows), so each
+// lane ends with 4 consecutive features of one row and stores 16 bytes.
+//
+// Workgroup = 4 waves arranged WN (along N) x WK (along K).  Small M tiles
+// use WK = 4 (each wave streams a quarter of every k-block, partial sums
+// reduced through LDS at the end) so that narrow GEMMs still spread over
+// many CUs; the largest M tile uses WK = 1.
+#include "common.h"
+#include "kernels.h"
+
+namespace photon {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmP {
+  const bf16_t* A; int64_t lda;
+  const bf16_t* W;
+  int M, N, K;
+  float* C; int64_t ldc;
+  bf16_t* Cb;
+  float* av; int* ai;
+  int m_tiles, n_tiles;
+};
+
+template <int MB, int NI, int WK, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
+  constexpr int WN = 4 / WK;
+  constexpr int BM = 16 * MB;
+  constexpr int BN = 16 * NI * WN;
+  constexpr int KT = 64 * WK;             // k per iteration; 64 per wave
+  constexpr int ROW = KT + 8;             // padded LDS row, bf16 elements
+  constexpr int A_ELEMS = BM * ROW;
+  constexpr int CHUNKS = BM * KT / 8;     // 16-byte A chunks per k-block
+  constexpr int CH = (CHUNKS + 255) / 256;
+  constexpr int RED = (WK > 1) ? (WK - 1) * WN * MB * NI * 4 * 64 : 0;
+  constexpr int BYTES_A = 2 * A_ELEMS * 2;
+  constexpr int BYTES = BYTES_A > RED * 4 ? BYTES_A : RED * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[BYTES];
+  bf16_t* As = reinterpret_cast<bf16_t*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % WN, wk = wave / WN;
+
+  // XCD-aware tile order: consecutive workgroups land on different XCDs, so
+  // give each XCD a contiguous run of tiles (M tiles of one W slab share L2).
+  const int total = p.m_tiles * p.n_tiles;
+  const int bid = blockIdx.x;
+  const int tile = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  const int mt = tile % p.m_tiles, nt = tile / p.m_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+
+  const int K = p.K, N = p.N, M = p.M;
+  const int kl = (lane >> 4) * 8;
+  const bf16_t* wp[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    int row = n0 + wn * NI * 16 + ni * 16 + (lane & 15);
+    row = row < N ? row : N - 1;          // clamp: columns >= N never stored
+    wp[ni] = p.W + (int64_t)row * K + wk * 64 + kl;
+  }
+
+  f32x4 acc[MB][NI];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  uint4 areg[CH];
+  auto load_a = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / (KT / 8), c8 = c % (KT / 8);
+      const int gm = m0 + r;
+      if (c < CHUNKS && gm < M)
+        areg[i] = *reinterpret_cast<const uint4*>(p.A + (int64_t)gm * p.lda + (int64_t)kb * KT + c8 * 8);
+      else
+        areg[i] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / (KT / 8), c8 = c % (KT / 8);
+      if (c < CHUNKS) *reinterpret_cast<uint4*>(As + buf * A_ELEMS + r * ROW + c8 * 8) = areg[i];
+    }
+  };
+  bf16x8 wcur[2][NI], wnxt[2][NI];
+  auto load_w = [&](int kb, bf16x8 (&w)[2][NI]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        w[u][ni] = *reinterpret_cast<const bf16x8*>(wp[ni] + (int64_t)kb * KT + u * 32);
+  };
+
+  const int nkb = K / KT;
+  load_a(0);
+  load_w(0, wcur);
+  store_a(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      load_a(kb + 1);
+      load_w(kb + 1, wnxt);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kk = wk * 64 + u * 32 + kl;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            As + buf * A_ELEMS + (mb * 16 + (lane & 15)) * ROW + kk);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mb][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[u][ni], a, acc[mb][ni], 0, 0, 0);
+      }
+    }
+    if (more) store_a(buf ^ 1);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) wcur[u][ni] = wnxt[u][ni];
+    }
+  }
+
+  // reduce the WK partial sums (fixed order: wk = 0, 1, 2, 3)
+  if constexpr (WK > 1) {
+    float* red = reinterpret_cast<float*>(smem);
+    if (wk > 0) {
+      float* dst = red + ((wk - 1) * WN + wn) * (MB * NI * 4 * 64);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[((mb * NI + ni) * 4 + r) * 64 + lane] = acc[mb][ni][r];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 1; w < WK; ++w) {
+        const float* src = red + ((w - 1) * WN + wn) * (MB * NI * 4 * 64);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mb][ni][r] += src[((mb * NI + ni) * 4 + r) * 64 + lane];
+      }
+    }
+  }
+
+  // epilogue (waves with wk == 0 own the final sums)
+  const int fl = (lane >> 4) * 4;
+  if constexpr (EPI != EPI_ARGMAX) {
+    if (wk == 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = m0 + mb * 16 + (lane & 15);
+        if (row >= M) continue;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int f = n0 + wn * NI * 16 + ni * 16 + fl;
+          if (f >= N) continue;
+          const f32x4 v = acc[mb][ni];
+          if constexpr (EPI == EPI_STORE) {
+            *reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f) = make_float4(v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EPI_ADD) {
+            float4* o = reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f);
+            float4 c = *o;
+            c.x += v[0]; c.y += v[1]; c.z += v[2]; c.w += v[3];
+            *o = c;
+          } else {  // GELU, rounded to bf16
+            uint2 pk;
+            pk.x = (uint32_t)f2bf(gelu_f(v[0])) | ((uint32_t)f2bf(gelu_f(v[1])) << 16);
+            pk.y = (uint32_t)f2bf(gelu_f(v[2])) | ((uint32_t)f2bf(gelu_f(v[3])) << 16);
+            *reinterpret_cast<uint2*>(p.Cb + (int64_t)row * p.ldc + f) = pk;
+          }
+        }
+      }
+    }
+  } else {
+    // greedy head: optional logits, then the per-row first maximum
+    __shared__ float bv[WN][BM];
+    __shared__ int bi[WN][BM];
+    if (wk == 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = m0 + mb * 16 + (lane & 15);
+        float best = -INFINITY;
+        int bidx = 0x7fffffff;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int f = n0 + wn * NI * 16 + ni * 16 + fl;
+          if (f >= N) continue;
+          const f32x4 v = acc[mb][ni];
+          if (p.C && row < M)
+            *reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (v[r] > best) { best = v[r]; bidx = f + r; }
+        }
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+          const float ov = __shfl_xor(best, o, 64);
+          const int oi = __shfl_xor(bidx, o, 64);
+          if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+        }
+        if ((lane >> 4) == 0) { bv[wn][mb * 16 + lane] = best; bi[wn][mb * 16 + lane] = bidx; }
+      }
+    }
+    __syncthreads();
+    if (tid < BM) {
+      const int row = m0 + tid;
+      if (row < M) {
+        float best = bv[0][tid];
+        int bidx = bi[0][tid];
+#pragma unroll
+        for (int w = 1; w < WN; ++w)
+          if (bv[w][tid] > best) { best = bv[w][tid]; bidx = bi[w][tid]; }
+        p.av[(int64_t)nt * M + row] = best;
+        p.ai[(int64_t)nt * M + row] = bidx;
+      }
+    }
+  }
+}
+
+// ---- fp32 models: plain FMA kernel, one thread per output ----
+struct GemmPF {
+  const float* A; int64_t lda;
+  const float* W;
+  int M, N, K;
+  float* C; int64_t ldc;
+  float* Cf;
+  float* av; int* ai;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(64) void gemm_f32_kernel(GemmPF p) {
+  const int n = blockIdx.x * 64 + threadIdx.x;
+  const int m = blockIdx.y;
+  float acc = 0.f;
+  if (n < p.N) {
+    const float* a = p.A + (int64_t)m * p.lda;
+    const float* w = p.W + (int64_t)n * p.K;
+    for (int k = 0; k < p.K; ++k) acc = fmaf(a[k], w[k], acc);
+  }
+  if constexpr (EPI == EPI_STORE) {
+    if (n < p.N) p.C[(int64_t)m * p.ldc + n] = acc;
+  } else if constexpr (EPI == EPI_ADD) {
+    if (n < p.N) p.C[(int64_t)m * p.ldc + n] += acc;
+  } else if constexpr (EPI == EPI_GELU) {
+    if (n < p.N) p.Cf[(int64_t)m * p.ldc + n] = gelu_f(acc);
+  } else {
+    if (n < p.N && p.C) p.C[(int64_t)m * p.ldc + n] = acc;
+    float best = n < p.N ? acc : -INFINITY;
+    int bidx = n < p.N ? n : 0x7fffffff;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bidx, o, 64);
+      if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+    }
+    if (threadIdx.x == 0) {
+      p.av[(int64_t)blockIdx.x * p.M + m] = best;
+      p.ai[(int64_t)blockIdx.x * p.M + m] = bidx;
+    }
+  }
+}
+
+struct Plan {
+  int MB, NI, WK, m_tiles, n_tiles;
+};
+
+// Waves along K: as many as the LDS budget of the M tile allows (4 for
+// M tiles up to 64 rows, 2 for 128, 1 for 256) and K divides into.
+int wk_of(int MB, int K) {
+  int wk = MB >= 16 ? 1 : (MB >= 8 ? 2 : 4);
+  while (wk > 1 && K % (64 * wk)) wk >>= 1;
+  return wk;
+}
+
+Plan plan_bf16(int M, int N, int K) {
+  Plan pl;
+  pl.MB = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 128 ? 8 : 16;
+  pl.m_tiles = (M + 16 * pl.MB - 1) / (16 * pl.MB);
+  pl.WK = wk_of(pl.MB, K);
+  const int WN = 4 / pl.WK;
+  const int ni_max = pl.MB >= 16 ? 2 : 4;
+  pl.NI = 1;
+  for (int ni = ni_max; ni >= 1; ni >>= 1) {
+    const int bn = 16 * ni * WN;
+    const int tiles = (N + bn - 1) / bn * pl.m_tiles;
+    if (tiles >= 240 || ni == 1) { pl.NI = ni; break; }
+  }
+  pl.n_tiles = (N + 16 * pl.NI * WN - 1) / (16 * pl.NI * WN);
+  return pl;
+}
+
+template <int MB, int NI, int WK>
+hipError_t run_bf16(const GemmP& p, int epi, hipStream_t st) {
+  dim3 grid(p.m_tiles * p.n_tiles), block(256);
+  switch (epi) {
+    case EPI_STORE: gemm_bf16_kernel<MB, NI, WK, EPI_STORE><<<grid, block, 0, st>>>(p); break;
+    case EPI_ADD: gemm_bf16_kernel<MB, NI, WK, EPI_ADD><<<grid, block, 0, st>>>(p); break;
+    case EPI_GELU: gemm_bf16_kernel<MB, NI, WK, EPI_GELU><<<grid, block, 0, st>>>(p); break;
+    default: gemm_bf16_kernel<MB, NI, WK, EPI_ARGMAX><<<grid, block, 0, st>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+template <int MB, int WK>
+hipError_t run_bf16_ni(const GemmP& p, int NI, int epi, hipStream_t st) {
+  if constexpr (MB >= 16) {
+    if (NI == 2) return run_bf16<MB, 2, WK>(p, epi, st);
+    return run_bf16<MB, 1, WK>(p, epi, st);
+  } else {
+    if (NI == 4) return run_bf16<MB, 4, WK>(p, epi, st);
+    if (NI == 2) return run_bf16<MB, 2, WK>(p, epi, st);
+    return run_bf16<MB, 1, WK>(p, epi, st);
+  }
+}
+
+template <int MB>
+hipError_t run_bf16_wk(const GemmP& p, int NI, int WK, int epi, hipStream_t st) {
+  if constexpr (MB <= 4) {
+    if (WK == 4) return run_bf16_ni<MB, 4>(p, NI, epi, st);
+  }
+  if constexpr (MB <= 8) {
+    if (WK == 2) return run_bf16_ni<MB, 2>(p, NI, epi, st);
+  }
+  return run_bf16_ni<MB, 1>(p, NI, epi, st);
+}
+
+}  // namespace
+
+int gemm_supported(int dtype, int M, int N, int K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  if (dtype == 0) return 1;
+  return N % 16 == 0 && K % 64 == 0;
+}
+
+int gemm_argmax_tiles(int dtype, int M, int N, int K) {
+  if (dtype == 0) return (N + 63) / 64;
+  return plan_bf16(M, N, K).n_tiles;
+}
+
+hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
+  if (g.dtype == 0) {
+    GemmPF p{(const float*)g.A, g.lda, (const float*)g.W, g.M, g.N, g.K,
+             g.C, g.ldc, (float*)g.Cb, g.amax_val, g.amax_idx};
+    dim3 grid((g.N + 63) / 64, g.M), block(64);
+    switch (g.epi) {
+      case EPI_STORE: gemm_f32_kernel<EPI_STORE><<<grid, block, 0, st>>>(p); break;
+      case EPI_ADD: gemm_f32_kernel<EPI_ADD><<<grid, block, 0, st>>>(p); break;
+      case EPI_GELU: gemm_f32_kernel<EPI_GELU><<<grid, block, 0, st>>>(p); break;
+      default: gemm_f32_kernel<EPI_ARGMAX><<<grid, block, 0, st>>>(p); break;
+    }
+    return hipGetLastError();
+  }
+  const Plan pl = plan_bf16(g.M, g.N, g.K);
+  GemmP p{(const bf16_t*)g.A, g.lda, (const bf16_t*)g.W, g.M, g.N, g.K,
+          g.C, g.ldc, (bf16_t*)g.Cb, g.amax_val, g.amax_idx, pl.m_tiles, pl.n_tiles};
+  switch (pl.MB) {
+    case 1: return run_bf16_wk<1>(p, pl.NI, pl.WK, g.epi, st);
+    case 2: return run_bf16_wk<2>(p, pl.NI, pl.WK, g.epi, st);
+    case 4: return run_bf16_wk<4>(p, pl.NI, pl.WK, g.epi, st);
+    case 8: return run_bf16_wk<8>(p, pl.NI, pl.WK, g.epi, st);
+    default: return run_bf16_wk<16>(p, pl.NI, pl.WK, g.epi, st);
+  }
+}
+
+}  // namespace photon

@@ -1,0 +1,97 @@
+// Launchers for the HIP kernels of the PHOTON decode path (gfx950).
+// Every launcher enqueues on `st`, never synchronises and returns the
+// launch status.  dtype: 0 = fp32 storage, 1 = bf16 storage.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace photon {
+
+enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_GELU = 2, EPI_ARGMAX = 3 };
+
+// C[M,N] = A[M,K] W[N,K]^T with a fused epilogue:
+//   STORE : C (fp32, row stride ldc) = acc
+//   ADD   : C += acc                     (residual stream update)
+//   GELU  : Cb (storage dtype, stride ldc) = round(gelu(acc))
+//   ARGMAX: per-row (max, first index) over each column tile written to
+//           amax_val/amax_idx [n_tiles][M]; logits stored to C if non-null.
+struct GemmCall {
+  int dtype;
+  const void* A; int64_t lda;
+  const void* W;           // [N][K] row-major, storage dtype
+  int M, N, K;
+  int epi;
+  float* C; int64_t ldc;
+  void* Cb;
+  float* amax_val; int* amax_idx;
+};
+hipError_t launch_gemm(const GemmCall& g, hipStream_t st);
+// Column tiles the ARGMAX epilogue produces for a GEMM of this shape.
+int gemm_argmax_tiles(int dtype, int M, int N, int K);
+// Host-side shape check: 0 when the GEMM kernels support (M, N, K).
+int gemm_supported(int dtype, int M, int N, int K);
+
+// out[r] = round(g * x[r*stride + off] / sqrt(mean(x^2) + eps)), r < rows
+hipError_t launch_rmsnorm(int dtype, const float* x, int64_t in_stride,
+                          int64_t in_off, const float* g, void* out, int rows,
+                          int d, float eps, hipStream_t st);
+
+// Positions: pos(t) = pos_add + (pos_dev ? *pos_dev * pos_mul : 0) + t for
+// the t-th new row of a sequence; the K/V of that row go to cache slot pos.
+struct RopeKvCall {
+  int dtype;
+  const float* qkv;        // [M][3d] fp32: q | k | v
+  int M, d, H, hd;
+  float* q_out;            // [M][d] fp32 rotated q
+  void* Kc; void* Vc;      // cache planes [seq][H][cap][hd], storage dtype
+  int64_t seq_stride;      // elements between sequences (H*cap*hd)
+  int cap, rows_per_seq, seq0;
+  int pos_add; const int* pos_dev; int pos_mul;
+  const float* rope;       // [max_pos][hd/2][2] (cos, sin)
+};
+hipError_t launch_rope_kv(const RopeKvCall& c, hipStream_t st);
+
+// Attention of Q new queries per sequence over a K/V cache.  Query t of
+// sequence g sees keys 0 .. L - Q + t, L = L_host or *L_dev*L_mul + L_add.
+struct AttnCall {
+  int dtype;
+  int G, Q, H, hd;
+  const float* q; int64_t q_ld;   // row g*Q + t, head h at column h*hd
+  const void* Kc; const void* Vc; int64_t seq_stride; int cap; int seq0;
+  int L_host; const int* L_dev; int L_mul; int L_add;
+  void* out; int64_t out_ld;      // storage dtype, same row/col map as q
+  float* part; int nsplit;        // decode split-K partials
+};
+// Long caches: split over keys, then combine.  part holds
+// G*H*Q*nsplit*(hd+2) floats when nsplit > 1.
+hipError_t launch_attn_decode(const AttnCall& a, hipStream_t st);
+// Short in-chunk caches (L <= 64).
+hipError_t launch_attn_chunk(const AttnCall& a, hipStream_t st);
+// Causal self-attention over a whole prompt (L = Q = rows per sequence).
+hipError_t launch_attn_prefill(const AttnCall& a, hipStream_t st);
+
+// out[i] = E[ids[i]] for i < n (storage dtype rows of length d); ids are
+// clamped to [0, V)
+hipError_t launch_embed_gather(int dtype, const int* ids, int64_t n,
+                               const void* E, int d, int V, void* out,
+                               hipStream_t st);
+// x[m] = c0[m*c0_ld + j*d ..] + (j > 0 ? E[prev[m]] : 0), fp32
+hipError_t launch_embed_add(int dtype, const float* c0, int64_t c0_ld, int j,
+                            const int* prev, const void* E, int M, int d,
+                            float* x, hipStream_t st);
+// Reduce the ARGMAX tiles of row m (m = b*C2 + k) to the greedy token:
+// tokens[b*S + k*C1 + j] and prev[m].
+hipError_t launch_argmax_finalize(const float* val, const int* idx,
+                                  int n_tiles, int M, int C1, int C2, int j,
+                                  int* tokens, int* prev, hipStream_t st);
+// tab[p][i] = (cos, sin)(p * theta^(-2i/hd)), angles in double precision.
+hipError_t launch_rope_table(float* tab, int max_pos, int hd, float theta,
+                             hipStream_t st);
+hipError_t launch_set_int(int* p, int v, hipStream_t st);
+hipError_t launch_add_int(int* p, int v, hipStream_t st);
+
+// Number of key splits the decode attention uses for G*H pairs over a cache
+// of `cap` slots (plan-time, so one plan serves every length <= cap).
+int attn_decode_splits(int G, int H, int cap);
+
+}  // namespace photon

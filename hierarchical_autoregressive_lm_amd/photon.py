@@ -1,0 +1,306 @@
+"""ctypes binding of the PHOTON C ABI (include/photon.h).
+
+Argument marshalling only: every step of prefill and decoding runs in the
+HIP kernels of libphoton.so.  PyTorch supplies device memory and the stream.
+The library must have been built (``__graft_entry__.build()``); importing
+this module without it raises, there is no fallback path.
+"""
+import ctypes
+import os
+
+import numpy as np
+# torch first: it loads its own HIP runtime (SONAME libamdhip64.so.7), and
+# libphoton.so must bind to that same runtime instance, not a second copy
+import torch  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libphoton.so")
+
+OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+RECGEN, HIERGEN = 0, 1
+_MODES = {"recgen": RECGEN, "hiergen": HIERGEN}
+
+
+class PhotonError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"photon status {status}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("n_levels", ctypes.c_int32), ("chunk", ctypes.c_int32 * 2),
+                ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("mlp_mult", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_top", ctypes.c_int32), ("n_enc1", ctypes.c_int32),
+                ("n_dec1", ctypes.c_int32), ("n_dec0", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float)]
+
+
+class KvReport(ctypes.Structure):
+    _fields_ = [("top_len", ctypes.c_int64), ("lower_len", ctypes.c_int64),
+                ("top_kv", ctypes.c_uint64), ("lower_kv", ctypes.c_uint64),
+                ("dec_kv", ctypes.c_uint64), ("state", ctypes.c_uint64),
+                ("decode_scratch", ctypes.c_uint64),
+                ("workspace_total", ctypes.c_uint64),
+                ("weights_decode", ctypes.c_uint64),
+                ("weights_prefill_only", ctypes.c_uint64),
+                ("off_top_kv", ctypes.c_uint64), ("off_lower_kv", ctypes.c_uint64),
+                ("off_dec_kv", ctypes.c_uint64), ("off_state", ctypes.c_uint64),
+                ("off_scratch", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class TensorInfo(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("blob", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("offset", ctypes.c_uint64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class TraceStat(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("ms", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("flops", ctypes.c_double)]
+
+
+# kernel classes of photon_trace_enable, in photon_kernel_class order
+KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_up", "gemm_down", "gemm_head",
+                  "gemm_conv", "gemm_chunk", "attn_top", "attn_chunk",
+                  "attn_prefill", "norm", "rope_kv", "embed", "argmax"]
+
+EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
+           "photon_weight_layout", "photon_weight_tensor", "photon_open",
+           "photon_release_prefill_weights", "photon_close",
+           "photon_last_error", "photon_prefill", "photon_decode_chunk",
+           "photon_position", "photon_set_position", "photon_trace_enable",
+           "photon_trace_read"]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, V = ctypes.POINTER, ctypes.c_void_p
+    i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    sig = {
+        "photon_kv_bytes": [P(Config), i32, i64, i32, P(KvReport)],
+        "photon_prefill_scratch_bytes": [P(Config), i32, i32, i32, P(u64)],
+        "photon_weight_layout": [P(Config), P(u64), P(u64), P(i32)],
+        "photon_weight_tensor": [P(Config), i32, P(TensorInfo)],
+        "photon_open": [P(Config), V, V, P(V)],
+        "photon_release_prefill_weights": [V],
+        "photon_close": [V],
+        "photon_last_error": [],
+        "photon_prefill": [V, i32, V, u64, V, u64, V, i32, i32, i64, V],
+        "photon_decode_chunk": [V, V, V, V],
+        "photon_position": [V, P(i64), P(i64)],
+        "photon_set_position": [V, i64, V],
+        "photon_trace_enable": [V, ctypes.c_uint32],
+        "photon_trace_read": [V, P(TraceStat)],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "photon_last_error" else ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status):
+    if status != OK:
+        raise PhotonError(status, _lib.photon_last_error().decode())
+
+
+def make_config(cfg):
+    """photon_config from a photon_inputs.PhotonConfig."""
+    c = Config()
+    c.n_levels = 2
+    c.chunk[0], c.chunk[1] = cfg.chunk
+    c.d_model, c.n_heads, c.mlp_mult, c.vocab = cfg.d_model, cfg.n_heads, cfg.mlp_mult, cfg.vocab
+    c.n_top, c.n_enc1, c.n_dec1, c.n_dec0 = cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0
+    c.dtype = BF16 if cfg.dtype == "bf16" else F32
+    c.norm_eps, c.rope_theta = cfg.norm_eps, cfg.rope_theta
+    return c
+
+
+def kv_bytes(cfg, batch, tokens, mode="recgen"):
+    rep = KvReport()
+    _check(_lib.photon_kv_bytes(ctypes.byref(make_config(cfg)), batch, tokens,
+                                _MODES[mode], ctypes.byref(rep)))
+    return rep.as_dict()
+
+
+def prefill_scratch_bytes(cfg, batch, prompt_len, mode="recgen"):
+    out = ctypes.c_uint64()
+    _check(_lib.photon_prefill_scratch_bytes(ctypes.byref(make_config(cfg)), batch,
+                                             prompt_len, _MODES[mode], ctypes.byref(out)))
+    return out.value
+
+
+def weight_layout(cfg):
+    c = make_config(cfg)
+    dec, pre, n = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_int32()
+    _check(_lib.photon_weight_layout(ctypes.byref(c), ctypes.byref(dec), ctypes.byref(pre), ctypes.byref(n)))
+    tensors = []
+    for i in range(n.value):
+        t = TensorInfo()
+        _check(_lib.photon_weight_tensor(ctypes.byref(c), i, ctypes.byref(t)))
+        tensors.append({"name": t.name.decode(), "blob": t.blob, "dtype": t.dtype,
+                        "offset": t.offset, "rows": t.rows, "cols": t.cols})
+    return dec.value, pre.value, tensors
+
+
+def _stream_handle(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Photon:
+    """One model on the current GPU: packed weight blobs plus a context.
+
+    weights: mapping name -> float32 numpy array (bf16-exact for bf16
+    models), as produced by photon_inputs.gen_weights.
+    """
+
+    def __init__(self, cfg, weights, device="cuda"):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.c = make_config(cfg)
+        dec, pre, tensors = weight_layout(cfg)
+        blobs = [torch.zeros(dec, dtype=torch.uint8, device=self.device),
+                 torch.zeros(max(pre, 256), dtype=torch.uint8, device=self.device)]
+        for t in tensors:
+            w = np.ascontiguousarray(weights[t["name"]], dtype=np.float32)
+            assert w.size == t["rows"] * t["cols"], t["name"]
+            src = torch.from_numpy(w.reshape(-1)).to(self.device)
+            if t["dtype"] == BF16:
+                src = src.to(torch.bfloat16)
+            raw = src.view(torch.uint8)
+            blobs[t["blob"]][t["offset"]:t["offset"] + raw.numel()].copy_(raw)
+        self.w_decode, self.w_prefill = blobs
+        self.weight_bytes = {"decode": dec, "prefill_only": pre}
+        ctx = ctypes.c_void_p()
+        _check(_lib.photon_open(ctypes.byref(self.c), ctypes.c_void_p(self.w_decode.data_ptr()),
+                                ctypes.c_void_p(self.w_prefill.data_ptr()), ctypes.byref(ctx)))
+        self.ctx = ctx
+        self.workspace = None
+        self.mode = None
+        self.batch = None
+
+    def close(self):
+        if self.ctx:
+            _lib.photon_close(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def release_prefill_weights(self):
+        """Drop the Chunker^1 / level-1 encoder blob (RecGen never uses it
+        after prefill)."""
+        _check(_lib.photon_release_prefill_weights(self.ctx))
+        self.w_prefill = None
+
+    def report(self, batch, tokens, mode="recgen"):
+        return kv_bytes(self.cfg, batch, tokens, mode)
+
+    def prefill(self, prompt, max_tokens, mode="recgen"):
+        """prompt: int32 CUDA tensor [B, P]."""
+        torch = self.torch
+        B, P = prompt.shape
+        rep = kv_bytes(self.cfg, B, max_tokens, mode)
+        if self.workspace is None or self.workspace.numel() < rep["workspace_total"]:
+            self.workspace = torch.empty(rep["workspace_total"], dtype=torch.uint8, device=self.device)
+        scratch_n = prefill_scratch_bytes(self.cfg, B, P, mode)
+        scratch = torch.empty(scratch_n, dtype=torch.uint8, device=self.device)
+        prompt = prompt.to(device=self.device, dtype=torch.int32).contiguous()
+        _check(_lib.photon_prefill(self.ctx, _MODES[mode], ctypes.c_void_p(self.workspace.data_ptr()),
+                                   self.workspace.numel(), ctypes.c_void_p(scratch.data_ptr()), scratch_n,
+                                   ctypes.c_void_p(prompt.data_ptr()), B, P, max_tokens,
+                                   _stream_handle(torch)))
+        self._scratch_hold = (scratch, prompt)   # freed at the next prefill
+        self.report_ = rep
+        self.mode = mode
+        self.batch = B
+
+    def decode_chunk(self, tokens_out, logits_out=None):
+        """tokens_out: int32 CUDA [B, S]; logits_out: float32 [B, S, V] or None."""
+        lp = ctypes.c_void_p(logits_out.data_ptr()) if logits_out is not None else None
+        _check(_lib.photon_decode_chunk(self.ctx, ctypes.c_void_p(tokens_out.data_ptr()), lp,
+                                        _stream_handle(self.torch)))
+
+    def position(self):
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        _check(_lib.photon_position(self.ctx, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def set_position(self, tokens):
+        _check(_lib.photon_set_position(self.ctx, tokens, _stream_handle(self.torch)))
+
+    def state_snapshot(self):
+        """Copy of the h region (enough, with set_position, to rewind)."""
+        return self.h_state().clone()
+
+    def state_restore(self, snap, tokens):
+        self.h_state().copy_(snap)
+        self.set_position(tokens)
+
+    def trace_enable(self, classes=None):
+        """classes: iterable of KERNEL_CLASSES names (None = all, [] = off)."""
+        names = KERNEL_CLASSES if classes is None else list(classes)
+        mask = 0
+        for n in names:
+            mask |= 1 << KERNEL_CLASSES.index(n)
+        _check(_lib.photon_trace_enable(self.ctx, mask))
+
+    def trace_read(self):
+        out = (TraceStat * len(KERNEL_CLASSES))()
+        _check(_lib.photon_trace_read(self.ctx, out))
+        return {n: {"launches": out[i].launches, "ms": out[i].ms, "bytes": out[i].bytes,
+                    "flops": out[i].flops} for i, n in enumerate(KERNEL_CLASSES) if out[i].launches}
+
+    def generate(self, prompt, new_tokens, mode="recgen", logits=False, max_tokens=None):
+        torch = self.torch
+        B, P = prompt.shape
+        S = self.cfg.S
+        if new_tokens % S:
+            raise ValueError("new_tokens must be a multiple of C1*C2")
+        self.prefill(prompt, max_tokens or P + new_tokens, mode)
+        toks = torch.empty((new_tokens // S, B, S), dtype=torch.int32, device=self.device)
+        lg = torch.empty((new_tokens // S, B, S, self.cfg.vocab), dtype=torch.float32,
+                         device=self.device) if logits else None
+        for c in range(new_tokens // S):
+            self.decode_chunk(toks[c], lg[c] if logits else None)
+        toks = toks.permute(1, 0, 2).reshape(B, new_tokens)
+        if logits:
+            lg = lg.permute(1, 0, 2, 3).reshape(B, new_tokens, self.cfg.vocab)
+        return toks, lg
+
+    # ---- views into the workspace (tests read the caches directly) ----
+    def top_kv(self):
+        """Top-level K/V as a tensor [n_top, 2, B, H, top_cap, hd] (storage dtype)."""
+        torch = self.torch
+        rep = self.report_
+        cfg = self.cfg
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        eb = 2 if cfg.dtype == "bf16" else 4
+        n = rep["top_kv"] // eb
+        raw = self.workspace[rep["off_top_kv"]:rep["off_top_kv"] + rep["top_kv"]]
+        return raw.view(dt)[:n].view(cfg.n_top, 2, self.batch, cfg.n_heads, rep["top_len"], cfg.head_dim)
+
+    def h_state(self):
+        torch = self.torch
+        cfg = self.cfg
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        eb = 2 if cfg.dtype == "bf16" else 4
+        off = self.report_["off_state"]
+        return self.workspace[off:off + self.batch * cfg.d_model * eb].view(dt).view(self.batch, cfg.d_model)

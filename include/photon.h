@@ -1,0 +1,255 @@
+/*
+ * photon.h -- C ABI of the PHOTON recursive-generation (RecGen) decode path
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The method: PHOTON paper record (ACL 2026 long paper "PHOTON: Hierarchical
+ * Autoregressive Modeling for Lightspeed and Memory-Efficient Language
+ * Generation"), abstract; PHOTON explainer (mokumoku.ipfde.com, Fujitsu
+ * PHOTON vertical scan): module table (Context Chunker, Context Encoder,
+ * Context Converter, Context Decoder), the recursive-generation section
+ * (HierGen's three steps, RecGen's feedback of the bottleneck
+ * reconstruction, Theorem A.6, dropping the lower encoder caches after
+ * prefill, keeping only the decoders resident), and the decode-heavy table
+ * (throughput per unit memory, TPM).
+ *
+ * Conventions shared by every entry point:
+ *   - Every call returns a photon_status; no C++ exception crosses the ABI.
+ *     photon_last_error() gives a thread-local detail string for the most
+ *     recent failing call on this thread.
+ *   - Every shape, capacity and state check happens on the host before any
+ *     HIP call; a call that fails a check has no side effect.
+ *   - Device pointers ("d_" prefix) are allocated and owned by the caller.
+ *     The library owns only the small host-side photon_ctx (and the HIP
+ *     graphs it may instantiate for it).
+ *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
+ *     NULL is the null stream) and is asynchronous: no call synchronises.
+ *     A launch failure returns PHOTON_EHIP; device faults surface at the
+ *     caller's next synchronisation.
+ *   - A photon_ctx is not thread safe; separate contexts are independent.
+ *   - Token ids are int32 in [0, vocab).
+ *
+ * Shapes: L = 2 levels; chunk = {C1, C2}: C1 tokens form one level-1 state,
+ * C2 level-1 states form one top state, so one top state covers S = C1*C2
+ * tokens.  d = d_model, H = n_heads, hd = d / H, F = mlp_mult * d.
+ */
+#ifndef PHOTON_H
+#define PHOTON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PHOTON_OK = 0,
+  PHOTON_EINVAL = -1,      /* null pointer, bad enum, misaligned buffer */
+  PHOTON_ESHAPE = -2,      /* P % S != 0, P < S, batch < 1, d % H != 0 ... */
+  PHOTON_ECAPACITY = -3,   /* workspace too small or max_tokens exceeded */
+  PHOTON_ESTATE = -4,      /* decode before prefill, HierGen without the
+                              prefill-only weights, ... */
+  PHOTON_EUNSUPPORTED = -5,/* a shape this build does not handle */
+  PHOTON_EHIP = -6         /* a HIP runtime call or launch failed */
+} photon_status;
+
+typedef enum { PHOTON_F32 = 0, PHOTON_BF16 = 1 } photon_dtype;
+
+/* RecGen feeds the level-1 decoder's reconstruction A-hat straight to the
+ * top encoder; HierGen re-encodes the emitted tokens bottom-up (explainer,
+ * recursive-generation section). */
+typedef enum { PHOTON_RECGEN = 0, PHOTON_HIERGEN = 1 } photon_mode;
+
+typedef struct {
+  int32_t n_levels;     /* must be 2 */
+  int32_t chunk[2];     /* C1, C2 */
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t mlp_mult;     /* MLP width F = mlp_mult * d_model */
+  int32_t vocab;
+  int32_t n_top;        /* top (level-2) encoder layers */
+  int32_t n_enc1;       /* level-1 encoder layers (prefill / HierGen only) */
+  int32_t n_dec1;       /* level-1 decoder layers */
+  int32_t n_dec0;       /* token decoder layers */
+  int32_t dtype;        /* photon_dtype: storage of weights, K/V, operands */
+  float norm_eps;       /* RMSNorm epsilon */
+  float rope_theta;     /* rotary base */
+} photon_config;
+
+/* ------------------------------------------------------------------------
+ * Memory accounting (pure host, no device call).
+ *
+ * photon_kv_bytes: byte counts for `batch` sequences holding `tokens` tokens
+ * in `mode` (explainer, decode-heavy table: TPM = throughput / memory; the
+ * RecGen section: only the top-level global KV is kept, the level-1 encoder
+ * cache is dropped after prefill; the module table: the decoder's cache is
+ * confined to the chunk and does not grow with the context).
+ *
+ * The workspace that photon_prefill/photon_decode_chunk use is laid out for
+ * a capacity of `tokens` tokens: call with tokens = max_tokens to size it.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t top_len;            /* ceil(tokens / S) top states per sequence */
+  int64_t lower_len;          /* ceil(tokens / C1) level-1 states (HierGen) */
+  uint64_t top_kv;            /* n_top*2*batch*top_len*d*elem bytes */
+  uint64_t lower_kv;          /* HierGen: n_enc1*2*batch*lower_len*d*elem; RecGen 0 */
+  uint64_t dec_kv;            /* n_dec0*2*batch*C2*C1*d*elem, independent of tokens */
+  uint64_t state;             /* h_{i-1}, positions, argmax keys, counters */
+  uint64_t decode_scratch;    /* activations of one decode chunk */
+  uint64_t workspace_total;   /* bytes the workspace must hold (256-aligned) */
+  uint64_t weights_decode;    /* decode-resident weight blob */
+  uint64_t weights_prefill_only; /* Chunker^1 + level-1 encoder blob */
+  /* byte offsets of the regions inside the workspace; the top K/V region
+   * is [n_top][2 (K,V)][batch][H][top_len][hd], the level-1 region
+   * [n_enc1][2][batch][H][lower_len][hd], the decoder region
+   * [n_dec0][2][batch*C2][H][C1][hd]; h is [batch][d] at off_state. */
+  uint64_t off_top_kv, off_lower_kv, off_dec_kv, off_state, off_scratch;
+} photon_kv_report;
+
+photon_status photon_kv_bytes(const photon_config* cfg, int32_t batch,
+                              int64_t tokens, int32_t mode,
+                              photon_kv_report* out);
+
+/* Transient device bytes photon_prefill needs for a prompt of `prompt_len`
+ * tokens per sequence (activations, and RecGen's level-1 K/V, which is not
+ * kept).  The buffer may be freed once photon_prefill's work has completed. */
+photon_status photon_prefill_scratch_bytes(const photon_config* cfg,
+                                           int32_t batch, int32_t prompt_len,
+                                           int32_t mode, uint64_t* out);
+
+/* ------------------------------------------------------------------------
+ * Weight blobs (pure host).  Two device blobs: the decode blob (embedding,
+ * Chunker^2, top encoder, Converter^2, level-1 decoder, Converter^1, token
+ * decoder, output head) and the prefill-only blob (Chunker^1, level-1
+ * encoder), which RecGen never touches after prefill (explainer, recursive-
+ * generation section: only the decoder side must stay on the GPU).
+ *
+ * Tensors are the canonical ones: matrices W[out][in] (y = x W^T) stored in
+ * the config dtype, row-major; norm gains float32.  Within a layer Wq, Wk, Wv
+ * are adjacent so that [Wq;Wk;Wv] is one [3d][d] matrix.
+ * Tensor names: "E", "W_ch1", "W_ch2", "W_cv2", "W_cv1", "W_out",
+ * "<stack>.<l>.{g1,Wq,Wk,Wv,Wo,g2,W1,W2}", "<stack>.gf" for stack in
+ * enc1, top, dec1, dec0.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  char name[32];
+  int32_t blob;       /* 0 = decode blob, 1 = prefill-only blob */
+  int32_t dtype;      /* photon_dtype of the stored elements */
+  uint64_t offset;    /* byte offset inside its blob (256-aligned) */
+  int64_t rows;       /* out features (vector: length) */
+  int64_t cols;       /* in features (vector: 1) */
+} photon_tensor_info;
+
+photon_status photon_weight_layout(const photon_config* cfg,
+                                   uint64_t* decode_bytes,
+                                   uint64_t* prefill_only_bytes,
+                                   int32_t* n_tensors);
+photon_status photon_weight_tensor(const photon_config* cfg, int32_t index,
+                                   photon_tensor_info* out);
+
+/* ------------------------------------------------------------------------
+ * Context.  d_w_decode must stay valid until photon_close.  d_w_prefill_only
+ * may be NULL, or released later with photon_release_prefill_weights, after
+ * which prefill and HierGen decoding return PHOTON_ESTATE.
+ * ---------------------------------------------------------------------- */
+typedef struct photon_ctx photon_ctx;
+
+photon_status photon_open(const photon_config* cfg, const void* d_w_decode,
+                          const void* d_w_prefill_only, photon_ctx** out);
+photon_status photon_release_prefill_weights(photon_ctx* ctx);
+photon_status photon_close(photon_ctx* ctx);
+const char* photon_last_error(void);
+
+/* Prefill (explainer, module table and recursive-generation section):
+ * embedding -> Chunker^1 -> level-1 encoder (causal) -> Chunker^2 -> top
+ * encoder (causal), writing top K/V slots 0 .. P/S - 1 and the last top
+ * output h into the workspace.  RecGen keeps no level-1 K/V; HierGen writes
+ * it into the workspace's level-1 region.
+ *   d_prompt   [batch][prompt_len] int32 device ids.
+ *   prompt_len positive multiple of S (else PHOTON_ESHAPE).
+ *   max_tokens the capacity the workspace was sized for; prompt_len plus
+ *              every later decoded chunk must fit (else PHOTON_ECAPACITY).
+ *   d_workspace >= photon_kv_bytes(cfg, batch, max_tokens, mode)
+ *              .workspace_total bytes, 256-byte aligned; it holds the whole
+ *              decode state and must stay valid while decoding.
+ *   d_scratch  >= photon_prefill_scratch_bytes(...) bytes, 256-aligned.
+ * Resets the context's position to the end of the prompt. */
+photon_status photon_prefill(photon_ctx* ctx, int32_t mode, void* d_workspace,
+                             uint64_t ws_bytes, void* d_scratch,
+                             uint64_t scratch_bytes, const int32_t* d_prompt,
+                             int32_t batch, int32_t prompt_len,
+                             int64_t max_tokens, void* stream);
+
+/* One decode chunk of S tokens per sequence (explainer, recursive-generation
+ * section).  Converter^2 expands h_{i-1} into C2 conditioning vectors; the
+ * level-1 decoder (attention confined to the chunk) gives A-hat_i; every
+ * level-1 position is expanded by Converter^1 and the token decoder (in-chunk
+ * K/V of C1 slots) into C1 greedy tokens; RecGen then feeds Chunker^2(A-hat_i)
+ * to the top encoder, which appends slot i to the global K/V and attends
+ * over slots 0..i to give h_i.  HierGen instead re-encodes the tokens through
+ * Chunker^1 and one level-1 encoder step before the top step.
+ *   d_tokens  [batch][S] int32 out; token k*C1 + j is position j of level-1
+ *             sub-chunk k; greedy argmax, lowest index on ties.
+ *   d_logits  NULL, or [batch][S][vocab] float32 out (the logits behind
+ *             every token).
+ * PHOTON_ESTATE before a prefill; PHOTON_ECAPACITY when the chunk would pass
+ * max_tokens. */
+photon_status photon_decode_chunk(photon_ctx* ctx, int32_t* d_tokens,
+                                  float* d_logits, void* stream);
+
+/* Position bookkeeping: top states held and tokens (prompt + generated). */
+photon_status photon_position(const photon_ctx* ctx, int64_t* top_len,
+                              int64_t* tokens);
+
+/* Move the decode position back to `tokens` (a multiple of S between the
+ * prompt length and the current position), enqueued on `stream`.  The top
+ * K/V slots from tokens/S on become free and are rewritten by the next
+ * chunks.  The caller must first restore the workspace's h region (the
+ * photon_kv_report state region, [batch][d] at off_state) to the value it
+ * held at that position, e.g. from a copy taken then: this is the resume
+ * half of a snapshot (copy the workspace) / restore (copy back + this call)
+ * pair.  PHOTON_ESTATE before a prefill, PHOTON_ESHAPE for a bad position. */
+photon_status photon_set_position(photon_ctx* ctx, int64_t tokens,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * Tracing: per kernel class, HIP events around every launch of the enabled
+ * classes, with the algorithmic bytes and flops of each launch (weights,
+ * activations and caches read or written once; nothing for cache hits).
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  PHOTON_K_GEMM_QKV = 0,   /* [Wq;Wk;Wv] projection */
+  PHOTON_K_GEMM_O,         /* attention output projection (+ residual) */
+  PHOTON_K_GEMM_UP,        /* MLP up projection + GELU */
+  PHOTON_K_GEMM_DOWN,      /* MLP down projection (+ residual) */
+  PHOTON_K_GEMM_HEAD,      /* output head + greedy argmax */
+  PHOTON_K_GEMM_CONV,      /* Context Converter (both levels) */
+  PHOTON_K_GEMM_CHUNK,     /* Context Chunker (both levels) */
+  PHOTON_K_ATTN_TOP,       /* top-level / level-1 decode attention (split) */
+  PHOTON_K_ATTN_CHUNK,     /* decoder attention confined to the chunk */
+  PHOTON_K_ATTN_PREFILL,   /* causal prompt attention */
+  PHOTON_K_NORM,           /* RMSNorm */
+  PHOTON_K_ROPE_KV,        /* rotary embedding + K/V cache append */
+  PHOTON_K_EMBED,          /* embedding gather / conditioning add */
+  PHOTON_K_ARGMAX,         /* argmax reduction across column tiles */
+  PHOTON_K_COUNT
+} photon_kernel_class;
+
+typedef struct {
+  int64_t launches;
+  double ms;               /* summed event time of the launches */
+  double bytes;            /* summed algorithmic HBM bytes */
+  double flops;            /* summed algorithmic flops */
+} photon_trace_stat;
+
+/* Enable tracing for the classes whose bit (1 << class) is set; 0 turns it
+ * off.  Clears previous records. */
+photon_status photon_trace_enable(photon_ctx* ctx, uint32_t class_mask);
+/* Wait for the recorded events, sum them per class into out[PHOTON_K_COUNT]
+ * and clear the records (tracing stays enabled). */
+photon_status photon_trace_read(photon_ctx* ctx, photon_trace_stat* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PHOTON_H */

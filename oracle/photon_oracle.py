@@ -16,9 +16,14 @@ Plain, slow and meant to be read against the pages:
   [tpm]       same explainer, 1.2B decode-heavy table and the paragraph on
               why both factors come from the hierarchy (decoder span).
 
-Every float is float64.  For bf16 models a rounding contract (round to the
-nearest bf16, ties to even) is applied at fixed points; for fp32 models the
-rounding is the identity and the oracle is plain fp64.  Contract:
+Every float is float64 (``compute="f64"``, the reference).  The same code
+can run its arithmetic in float32 (``compute="f32"``): that is not a
+reference but a second, equally valid implementation of the rounding
+contract, used to measure how far two implementations that differ only in
+accumulation precision drift apart (the contract's intrinsic noise).  For
+bf16 models a rounding contract (round to the nearest bf16, ties to even) is
+applied at fixed points; for fp32 models the rounding is the identity and
+the oracle is plain fp64.  Contract:
   * weights are bf16 (they arrive bf16-exact from the input generator);
   * every activation operand of a matrix product is rounded: RMSNorm outputs,
     attention outputs, GELU outputs, stack outputs (A, A-hat, h, z) and the
@@ -73,14 +78,17 @@ def round_bf16(x):
 
 class Precision:
     """Applies the rounding contract: ``r`` is round_bf16 for bf16 models and
-    the identity for fp32 models."""
+    the identity for fp32 models; values are held in the compute dtype."""
 
-    def __init__(self, dtype):
-        assert dtype in ("f32", "bf16")
+    def __init__(self, dtype, compute="f64"):
+        assert dtype in ("f32", "bf16") and compute in ("f64", "f32")
         self.bf16 = dtype == "bf16"
+        self.dt = np.float64 if compute == "f64" else np.float32
 
     def r(self, x):
-        return round_bf16(x) if self.bf16 else np.asarray(x, dtype=F64)
+        if self.bf16:
+            return round_bf16(x).astype(self.dt)
+        return np.asarray(x, dtype=self.dt)
 
 
 # --------------------------------------------------------------------------
@@ -94,7 +102,7 @@ def rmsnorm(x, g, eps):
 
 def gelu(z):
     """Exact GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt 2))."""
-    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+    return 0.5 * z * (1.0 + erf(z / z.dtype.type(math.sqrt(2.0))))
 
 
 def rope_angles(pos, hd, theta):
@@ -108,12 +116,12 @@ def rope(x, pos, theta):
     """Rotate-half rotary embedding over the full head dim.
 
     x: [..., T, H, hd]; pos: [T].  Pair (x_i, x_{i+hd/2}) is rotated by
-    phi = pos * theta^(-2i/hd).
+    phi = pos * theta^(-2i/hd) (angles in float64, then the compute dtype).
     """
     hd = x.shape[-1]
     h = hd // 2
     phi = rope_angles(pos, hd, theta)[:, None, :]       # [T, 1, h]
-    c, s = np.cos(phi), np.sin(phi)
+    c, s = np.cos(phi).astype(x.dtype), np.sin(phi).astype(x.dtype)
     a, b = x[..., :h], x[..., h:]
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
@@ -127,7 +135,7 @@ def attention(q, k, v, n_prev):
     """
     B, Tq, H, hd = q.shape
     Tk = k.shape[1]
-    s = np.einsum("bthe,bshe->bhts", q, k) / math.sqrt(hd)
+    s = np.einsum("bthe,bshe->bhts", q, k) / q.dtype.type(math.sqrt(hd))
     allowed = np.arange(Tk)[None, :] <= (n_prev + np.arange(Tq))[:, None]
     s = np.where(allowed[None, None], s, -np.inf)
     s = s - s.max(axis=-1, keepdims=True)
@@ -147,10 +155,11 @@ def linear(x, W):
 class Model:
     """Weights (float64) plus the precision contract for one configuration."""
 
-    def __init__(self, cfg, weights):
+    def __init__(self, cfg, weights, compute="f64"):
         self.cfg = cfg
-        self.pr = Precision(cfg.dtype)
-        self.w = {k: np.asarray(v, dtype=F64) for k, v in weights.items()}
+        self.pr = Precision(cfg.dtype, compute)
+        self.dt = self.pr.dt
+        self.w = {k: np.asarray(v, dtype=self.dt) for k, v in weights.items()}
 
     def layers(self, prefix, n):
         return [{p: self.w[f"{prefix}.{l}.{p}"] for p in
@@ -170,9 +179,10 @@ class Model:
         cfg, r = self.cfg, self.pr.r
         B, T, d = x.shape
         H, hd = cfg.n_heads, cfg.head_dim
-        x = np.array(x, dtype=F64)
+        x = np.array(x, dtype=self.dt)
+        eps = self.dt(cfg.norm_eps)
         for l, L in enumerate(self.layers(prefix, n_layers)):
-            a = r(rmsnorm(x, L["g1"], cfg.norm_eps))
+            a = r(rmsnorm(x, L["g1"], eps))
             q = linear(a, L["Wq"]).reshape(B, T, H, hd)
             k = linear(a, L["Wk"]).reshape(B, T, H, hd)
             v = linear(a, L["Wv"]).reshape(B, T, H, hd)
@@ -189,14 +199,15 @@ class Model:
                 n_prev, kk, vv = 0, k, v
             o = r(attention(q, kk, vv, n_prev).reshape(B, T, d))
             x = x + linear(o, L["Wo"])
-            a = r(rmsnorm(x, L["g2"], cfg.norm_eps))
+            a = r(rmsnorm(x, L["g2"], eps))
             hmid = r(gelu(linear(a, L["W1"])))
             x = x + linear(hmid, L["W2"])
-        return r(rmsnorm(x, self.w[prefix + ".gf"], cfg.norm_eps))
+        return r(rmsnorm(x, self.w[prefix + ".gf"], eps))
 
     def empty_cache(self, n_layers, B):
         H, hd = self.cfg.n_heads, self.cfg.head_dim
-        return [{"k": np.zeros((B, 0, H, hd)), "v": np.zeros((B, 0, H, hd))}
+        return [{"k": np.zeros((B, 0, H, hd), self.dt),
+                 "v": np.zeros((B, 0, H, hd), self.dt)}
                 for _ in range(n_layers)]
 
     # ---- chunker and converter [modules] ----
@@ -293,7 +304,7 @@ def _decode_tokens(model, A_hat, forced_tokens=None):
     rows = c0.reshape(B * C2, C1, d)
     cache = model.empty_cache(cfg.n_dec0, B * C2)
     toks = np.zeros((B * C2, C1), dtype=np.int64)
-    logits = np.zeros((B * C2, C1, cfg.vocab))
+    logits = np.zeros((B * C2, C1, cfg.vocab), dtype=model.dt)
     forced = None if forced_tokens is None else \
         np.asarray(forced_tokens).reshape(B * C2, C1)
     prev = None
@@ -353,7 +364,7 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
         out["A"] = A
         u = model.chunker("W_ch2", A)[:, 0]
     if forced_u is not None:
-        u = np.asarray(forced_u, dtype=F64)
+        u = np.asarray(forced_u, dtype=model.dt)
     out["u"] = u
     out["h"] = _top_step(model, state, u)
     return out

@@ -1,0 +1,187 @@
+"""Host-side checks of the C ABI (CPU only; no call reaches the GPU).
+
+The library must load and export every entry point include/photon.h
+declares; memory accounting must follow the closed forms (top K/V of
+ceil(T/S) states, decoder K/V independent of T, no level-1 K/V for RecGen);
+every shape/state/capacity error must be reported before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import photon_inputs as pi
+from oracle import photon_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = pytest.importorskip("hierarchical_autoregressive_lm_amd.photon")
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "photon.h")).read()
+    decl = r"^(?:photon_status|const char\*)\s+(photon_[a-z_]+)\s*\("
+    return sorted(set(re.findall(decl, src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(P.EXPORTS) == names
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("mode", ["recgen", "hiergen"])
+def test_kv_bytes_closed_forms(idx, mode):
+    w = pi.get(idx)
+    for T in (w.prompt, w.max_tokens, w.max_tokens + 7):
+        r = P.kv_bytes(w.cfg, w.batch, T, mode)
+        o = O.kv_bytes(w.cfg, w.batch, T, mode)
+        assert r["top_len"] == -(-T // w.cfg.S)
+        assert r["top_kv"] == o["top"]
+        assert r["dec_kv"] == o["dec"]
+        assert r["lower_kv"] == o["lower"]
+        assert r["workspace_total"] % 256 == 0
+        for k in ("off_top_kv", "off_lower_kv", "off_dec_kv", "off_state", "off_scratch"):
+            assert r[k] % 256 == 0 and r[k] < r["workspace_total"]
+
+
+def test_decoder_cache_does_not_grow_with_context():
+    cfg = pi.CONFIGS["m600"]
+    a, b = P.kv_bytes(cfg, 8, 4096), P.kv_bytes(cfg, 8, 65536)
+    assert a["dec_kv"] == b["dec_kv"] > 0
+    assert b["top_kv"] == 16 * a["top_kv"]
+
+
+def test_weight_layout_matches_canonical_tensors():
+    for cfg in (pi.CONFIGS["tiny"], pi.CONFIGS["m150"], pi.CONFIGS["m600_2x2"]):
+        dec, pre, tensors = P.weight_layout(cfg)
+        shapes = dict(pi.weight_shapes(cfg))
+        assert sorted(t["name"] for t in tensors) == sorted(shapes)
+        eb = 2 if cfg.dtype == "bf16" else 4
+        end = {0: 0, 1: 0}
+        by = {t["name"]: t for t in tensors}
+        for t in tensors:
+            shp = shapes[t["name"]]
+            assert t["rows"] * t["cols"] == int(np.prod(shp))
+            assert t["offset"] % 256 == 0
+            nbytes = t["rows"] * t["cols"] * (4 if len(shp) == 1 else eb)
+            assert t["offset"] >= end[t["blob"]]
+            end[t["blob"]] = t["offset"] + nbytes
+        assert end[0] <= dec and end[1] <= pre
+        # prefill-only blob: Chunker^1 and the level-1 encoder, nothing else
+        pre_names = {t["name"] for t in tensors if t["blob"] == 1}
+        assert pre_names == {"W_ch1"} | {n for n in shapes if n.startswith("enc1.")}
+        # [Wq; Wk; Wv] forms one [3d][d] matrix
+        dd = cfg.d_model * cfg.d_model * eb
+        for l in range(cfg.n_top):
+            q, k, v = (by[f"top.{l}.W{x}"]["offset"] for x in "qkv")
+            assert k == q + dd and v == k + dd
+
+
+def _cfg(**kw):
+    return P.make_config(pi.CONFIGS["tiny"].with_(**kw))
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_config_errors_are_reported():
+    rep = P.KvReport()
+    lib = P._lib
+    c = _cfg(n_heads=3)                   # 64 % 3 != 0
+    assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.ESHAPE
+    c = _cfg(d_model=96, n_heads=2)       # head_dim 48
+    assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.EUNSUPPORTED
+    assert "head_dim" in lib.photon_last_error().decode()
+    c = _cfg()
+    assert lib.photon_kv_bytes(ctypes.byref(c), 0, 16, 0, ctypes.byref(rep)) == P.ESHAPE
+    assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 7, ctypes.byref(rep)) == P.EINVAL
+    assert lib.photon_kv_bytes(None, 1, 16, 0, ctypes.byref(rep)) == P.EINVAL
+    c.n_levels = 3
+    assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.EUNSUPPORTED
+
+
+def test_prompt_shape_errors():
+    out = ctypes.c_uint64()
+    c = _cfg()
+    lib = P._lib
+    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 24, 0, ctypes.byref(out)) == P.ESHAPE
+    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 8, 0, ctypes.byref(out)) == P.ESHAPE
+    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 32, 0, ctypes.byref(out)) == P.OK
+
+
+class FakeCtx:
+    """A context opened on fake (never dereferenced) device addresses: every
+    call below must fail its host-side checks before touching the GPU."""
+
+    def __init__(self, cfg=None):
+        self.c = P.make_config(cfg or pi.CONFIGS["tiny"])
+        self.ctx = ctypes.c_void_p()
+        assert P._lib.photon_open(ctypes.byref(self.c), ctypes.c_void_p(1 << 20),
+                                  ctypes.c_void_p(2 << 20), ctypes.byref(self.ctx)) == P.OK
+
+    def close(self):
+        P._lib.photon_close(self.ctx)
+
+
+def test_state_and_capacity_errors_before_any_device_call():
+    lib = P._lib
+    f = FakeCtx()
+    V = ctypes.c_void_p
+    tok = V(3 << 20)
+    assert lib.photon_decode_chunk(f.ctx, tok, None, None) == P.ESTATE
+    assert "before prefill" in lib.photon_last_error().decode()
+    assert lib.photon_decode_chunk(f.ctx, None, None, None) == P.EINVAL
+    ws, sc, pr = V(4 << 20), V(8 << 20), V(12 << 20)
+    # workspace too small
+    assert lib.photon_prefill(f.ctx, 0, ws, 1024, sc, 1 << 30, pr, 2, 64, 96, None) == P.ECAPACITY
+    need = P.kv_bytes(pi.CONFIGS["tiny"], 2, 96)["workspace_total"]
+    # prefill scratch too small
+    assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 16, pr, 2, 64, 96, None) == P.ECAPACITY
+    # ragged prompt, max_tokens below the prompt, misaligned workspace
+    assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 1 << 30, pr, 2, 60, 96, None) == P.ESHAPE
+    assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 1 << 30, pr, 2, 64, 32, None) == P.ECAPACITY
+    assert lib.photon_prefill(f.ctx, 0, V((4 << 20) + 8), need, sc, 1 << 30, pr, 2, 64, 96, None) == P.EINVAL
+    assert lib.photon_prefill(f.ctx, 5, ws, need, sc, 1 << 30, pr, 2, 64, 96, None) == P.EINVAL
+    # prefill after releasing the prefill-only weights
+    assert lib.photon_release_prefill_weights(f.ctx) == P.OK
+    assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 1 << 30, pr, 2, 64, 96, None) == P.ESTATE
+    top, toks = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    assert lib.photon_position(f.ctx, ctypes.byref(top), ctypes.byref(toks)) == P.OK
+    assert top.value == 0 and toks.value == 0
+    f.close()
+
+
+def test_open_rejects_bad_blobs():
+    c = P.make_config(pi.CONFIGS["tiny"])
+    ctx = ctypes.c_void_p()
+    lib = P._lib
+    assert lib.photon_open(ctypes.byref(c), None, None, ctypes.byref(ctx)) == P.EINVAL
+    assert lib.photon_open(ctypes.byref(c), ctypes.c_void_p(4096 + 4), None, ctypes.byref(ctx)) == P.EINVAL
+
+
+def test_tpm_denominator_recgen_below_hiergen():
+    # RecGen keeps only the top K/V and the decode weights resident
+    w = pi.get(4)
+    r = P.kv_bytes(w.cfg, w.batch, w.max_tokens, "recgen")
+    h = P.kv_bytes(w.cfg, w.batch, w.max_tokens, "hiergen")
+    rec = r["weights_decode"] + r["top_kv"] + r["dec_kv"] + r["state"]
+    hier = h["weights_decode"] + h["weights_prefill_only"] + h["top_kv"] + h["lower_kv"] + h["dec_kv"] + h["state"]
+    assert hier / rec > 1.5
+
+
+def test_set_position_and_trace_need_state():
+    lib = P._lib
+    f = FakeCtx()
+    assert lib.photon_set_position(f.ctx, 16, None) == P.ESTATE
+    assert lib.photon_trace_enable(f.ctx, 0xffffffff) == P.OK
+    out = (P.TraceStat * len(P.KERNEL_CLASSES))()
+    assert lib.photon_trace_read(f.ctx, out) == P.OK
+    assert all(out[i].launches == 0 for i in range(len(P.KERNEL_CLASSES)))
+    f.close()

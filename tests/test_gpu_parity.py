@@ -1,0 +1,137 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on
+seeded synthetic inputs.  See tests/parity.py for the tolerance rules."""
+import numpy as np
+import pytest
+
+import photon_inputs as pi
+from parity import gpu_generate, check_against_oracle, small_cfg
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg, B, P, seed, zero=()):
+    return pi.gen_weights(cfg, seed, zero=zero), pi.gen_prompts(cfg, B, P, seed)
+
+
+def _report(name, r):
+    print(f"[parity] {name}: max_err={r['max_err']:.3g} noise_max={r['noise_max']:.3g} "
+          f"near_ties={r['near_ties']}/{r['tokens']}", flush=True)
+
+
+@pytest.mark.parametrize("mode", ["recgen", "hiergen"])
+def test_tiny_f32_exact_ids(mode):
+    wl = pi.get(1)
+    W, pr = _inputs(wl.cfg, wl.batch, wl.prompt, wl.seed)
+    model, toks, lg = gpu_generate(wl.cfg, W, pr, wl.new_tokens, mode)
+    r = check_against_oracle(wl.cfg, W, pr, toks, lg, mode)
+    _report(f"tiny-f32 {mode}", r)
+
+
+def test_tiny_f32_long_prompt_split_attention():
+    # 300 top states: the top step's attention runs over several key splits
+    # with a ragged last split
+    cfg = pi.CONFIGS["tiny"]
+    W, pr = _inputs(cfg, 2, 16 * 300, 21)
+    model, toks, lg = gpu_generate(cfg, W, pr, 48)
+    r = check_against_oracle(cfg, W, pr, toks, lg)
+    _report("tiny-f32 P=4800", r)
+
+
+@pytest.mark.parametrize("mode", ["recgen", "hiergen"])
+def test_small_bf16_ragged_batch(mode):
+    cfg = small_cfg()
+    W, pr = _inputs(cfg, 3, 64, 5)
+    model, toks, lg = gpu_generate(cfg, W, pr, 48, mode)
+    r = check_against_oracle(cfg, W, pr, toks, lg, mode)
+    _report(f"small-bf16 B=3 {mode}", r)
+
+
+@pytest.mark.parametrize("mode", ["recgen", "hiergen"])
+def test_small_bf16_hd96_chunk2x2(mode):
+    cfg = small_cfg(d_model=384, n_heads=4, chunk=(2, 2), vocab=2000, n_top=2)
+    W, pr = _inputs(cfg, 5, 40, 6)
+    model, toks, lg = gpu_generate(cfg, W, pr, 24, mode)
+    r = check_against_oracle(cfg, W, pr, toks, lg, mode)
+    _report(f"bf16 hd96 2x2 {mode}", r)
+
+
+def test_thm_a6_zero_chunker_gpu_recgen_equals_hiergen():
+    cfg = small_cfg()
+    W, pr = _inputs(cfg, 2, 32, 7, zero=("W_ch2",))
+    m1, t1, l1 = gpu_generate(cfg, W, pr, 32, "recgen")
+    kv1 = m1.top_kv().float().cpu().numpy()
+    m2, t2, l2 = gpu_generate(cfg, W, pr, 32, "hiergen")
+    kv2 = m2.top_kv().float().cpu().numpy()
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(kv1, kv2)
+
+
+def test_deterministic_and_top_kv_matches_oracle():
+    cfg = small_cfg()
+    W, pr = _inputs(cfg, 2, 32, 8)
+    m1, t1, l1 = gpu_generate(cfg, W, pr, 32)
+    kv1 = m1.top_kv().float().cpu().numpy()
+    m2, t2, l2 = gpu_generate(cfg, W, pr, 32)
+    kv2 = m2.top_kv().float().cpu().numpy()
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(kv1, kv2)
+    r = check_against_oracle(cfg, W, pr, t1, l1)
+    st = r["state"]
+    assert m1.position() == (st.top_len, 32 + 32)
+    for l, e in enumerate(st.top):
+        np.testing.assert_allclose(kv1[l, 0].transpose(0, 2, 1, 3), e["k"], atol=3e-2)
+        np.testing.assert_allclose(kv1[l, 1].transpose(0, 2, 1, 3), e["v"], atol=3e-2)
+
+
+def test_recgen_after_releasing_prefill_weights():
+    import torch
+    from hierarchical_autoregressive_lm_amd.photon import Photon, PhotonError
+    cfg = small_cfg()
+    W, pr = _inputs(cfg, 2, 32, 9)
+    ref_model, ref_t, _ = gpu_generate(cfg, W, pr, 32, logits=False)
+    model = Photon(cfg, W)
+    model.prefill(torch.from_numpy(pr).cuda(), 64)
+    model.release_prefill_weights()
+    out = torch.empty((2, 2, cfg.S), dtype=torch.int32, device="cuda")
+    model.decode_chunk(out[0])
+    model.decode_chunk(out[1])
+    torch.cuda.synchronize()
+    got = out.permute(1, 0, 2).reshape(2, 32).cpu().numpy()
+    np.testing.assert_array_equal(got, ref_t)
+    with pytest.raises(PhotonError):
+        model.decode_chunk(out[0])          # capacity: 64 tokens reached
+    with pytest.raises(PhotonError):
+        model.prefill(torch.from_numpy(pr).cuda(), 64)
+
+
+def test_full_size_150m_sampled_sequences():
+    # the benchmarked workload, full batch on the GPU; the oracle recomputes
+    # sequences 0 and B-1 teacher-forced with the GPU's tokens
+    wl = pi.get(2)
+    W, pr = _inputs(wl.cfg, wl.batch, wl.prompt, wl.seed)
+    rows = [0, wl.batch - 1]
+    model, toks, lg = gpu_generate(wl.cfg, W, pr, wl.new_tokens, rows=rows)
+    r = check_against_oracle(wl.cfg, W, pr[rows], toks, lg)
+    _report("photon-150m B32 rows {0,31}", r)
+
+
+def test_rewind_replays_identical_chunks():
+    import torch
+    from hierarchical_autoregressive_lm_amd.photon import Photon
+    cfg = small_cfg()
+    W, pr = _inputs(cfg, 2, 32, 10)
+    model = Photon(cfg, W)
+    model.prefill(torch.from_numpy(pr).cuda(), 32 + 48)
+    snap = model.state_snapshot()
+    a = torch.empty((3, 2, cfg.S), dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    for c in range(3):
+        model.decode_chunk(a[c])
+    model.state_restore(snap, 32)
+    assert model.position() == (2, 32)
+    for c in range(3):
+        model.decode_chunk(b[c])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
