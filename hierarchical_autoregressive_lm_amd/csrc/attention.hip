@@ -395,10 +395,11 @@ hipError_t dispatch_prefill(const AttnCall& a, hipStream_t st) {
 }  // namespace
 
 int attn_decode_splits(int G, int H, int cap) {
-  // aim for ~2048 workgroups, at least 64 keys per split
+  // aim for ~2048 workgroups with at least 256 keys per split (a short cache
+  // is one split: no combine launch)
   const int pairs = G * H;
   int ns = (2048 + pairs - 1) / pairs;
-  const int max_ns = (cap + 63) / 64;
+  const int max_ns = (cap + 255) / 256;
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
   return ns;

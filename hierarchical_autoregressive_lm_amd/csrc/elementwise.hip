@@ -1,36 +1,75 @@
 // Row-wise and gather kernels of the PHOTON path: RMSNorm, rotary embedding
 // with K/V cache append, embedding gather / conditioning add, the greedy
 // argmax reduction and small state updates.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace photon {
 namespace {
 
-// one wave per row; fp32 sum of squares; output rounded to the storage type
+// Block-wide sum for the row kernels (blockDim.x a multiple of 64, <= 1024).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();                      // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// Row epilogue, one workgroup per output row i (input row r = i*row_stride
+// + row_off), one float4 column group per thread:
+//   x = resid[r] + sum_s P[s][r] + E[ids[r]]  (each term optional; slabs
+//   summed in order), x_out[r] = x, a_out[i] = round(g * x / rms(x)).
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int64_t in_stride, int64_t in_off,
-                                                      const float* g, T* out, int rows, int d, float eps) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float* xr = x + (row * in_stride + in_off) * (int64_t)d;
-  float ss = 0.f;
-  for (int e = lane * 4; e < d; e += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + e);
-    ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss);
-    ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+__global__ __launch_bounds__(1024) void rows_epilogue_kernel(RowsEpi e) {
+  __shared__ float red[16];
+  const int i = blockIdx.x;
+  const int64_t r = (int64_t)i * e.row_stride + e.row_off;
+  const int d = e.d;
+  const int c = threadIdx.x * 4;
+  const bool act = c < d;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (act) {
+    if (e.resid) acc = *reinterpret_cast<const float4*>(e.resid + r * d + c);
+    const float* pp = e.P + r * e.ldp + c;
+    int s = 0;
+    for (; s + 4 <= e.ksplit; s += 4) {   // four slabs in flight, added in order
+      const float4 p0 = *reinterpret_cast<const float4*>(pp + (s + 0) * e.pstride);
+      const float4 p1 = *reinterpret_cast<const float4*>(pp + (s + 1) * e.pstride);
+      const float4 p2 = *reinterpret_cast<const float4*>(pp + (s + 2) * e.pstride);
+      const float4 p3 = *reinterpret_cast<const float4*>(pp + (s + 3) * e.pstride);
+      acc.x += p0.x; acc.y += p0.y; acc.z += p0.z; acc.w += p0.w;
+      acc.x += p1.x; acc.y += p1.y; acc.z += p1.z; acc.w += p1.w;
+      acc.x += p2.x; acc.y += p2.y; acc.z += p2.z; acc.w += p2.w;
+      acc.x += p3.x; acc.y += p3.y; acc.z += p3.z; acc.w += p3.w;
+    }
+    for (; s < e.ksplit; ++s) {
+      const float4 p0 = *reinterpret_cast<const float4*>(pp + s * e.pstride);
+      acc.x += p0.x; acc.y += p0.y; acc.z += p0.z; acc.w += p0.w;
+    }
+    if (e.ids) {
+      const T* erow = reinterpret_cast<const T*>(e.E) + (int64_t)e.ids[r] * d;
+      acc.x += St<T>::ld(erow[c]); acc.y += St<T>::ld(erow[c + 1]);
+      acc.z += St<T>::ld(erow[c + 2]); acc.w += St<T>::ld(erow[c + 3]);
+    }
+    if (e.x_out) *reinterpret_cast<float4*>(e.x_out + r * d + c) = acc;
   }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  T* orow = out + (int64_t)row * d;
-  for (int e = lane * 4; e < d; e += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + e);
-    const float4 gg = *reinterpret_cast<const float4*>(g + e);
-    orow[e + 0] = St<T>::st(gg.x * (v.x * inv));
-    orow[e + 1] = St<T>::st(gg.y * (v.y * inv));
-    orow[e + 2] = St<T>::st(gg.z * (v.z * inv));
-    orow[e + 3] = St<T>::st(gg.w * (v.w * inv));
+  if (!e.a_out) return;                   // uniform across the block
+  float ss = act ? acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w : 0.f;
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)d + e.eps);
+  if (act) {
+    T* orow = reinterpret_cast<T*>(e.a_out) + (int64_t)i * e.a_ld;
+    const float4 gg = *reinterpret_cast<const float4*>(e.g + c);
+    orow[c + 0] = St<T>::st(gg.x * (acc.x * inv));
+    orow[c + 1] = St<T>::st(gg.y * (acc.y * inv));
+    orow[c + 2] = St<T>::st(gg.z * (acc.z * inv));
+    orow[c + 3] = St<T>::st(gg.w * (acc.w * inv));
   }
 }
 
@@ -48,11 +87,14 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvCall c) {
   const int pos = c.pos_add + (c.pos_dev ? (*c.pos_dev) * c.pos_mul : 0) + t;
   const float cs = c.rope[((int64_t)pos * half + i) * 2];
   const float sn = c.rope[((int64_t)pos * half + i) * 2 + 1];
-  const float* row = c.qkv + (int64_t)m * 3 * c.d;
   const int ca = h * c.hd + i, cb = ca + half;
-  const float qa = row[ca], qb = row[cb];
-  const float ka = row[c.d + ca], kb = row[c.d + cb];
-  const float va = row[2 * c.d + ca], vb = row[2 * c.d + cb];
+  float qa = 0.f, qb = 0.f, ka = 0.f, kb = 0.f, va = 0.f, vb = 0.f;
+  for (int sl = 0; sl < c.ksplit; ++sl) {      // K slabs of the QKV GEMM, in order
+    const float* row = c.qkv + sl * c.pstride + (int64_t)m * 3 * c.d;
+    qa += row[ca]; qb += row[cb];
+    ka += row[c.d + ca]; kb += row[c.d + cb];
+    va += row[2 * c.d + ca]; vb += row[2 * c.d + cb];
+  }
   c.q_out[(int64_t)m * c.d + ca] = qa * cs - qb * sn;
   c.q_out[(int64_t)m * c.d + cb] = qb * cs + qa * sn;
   const int64_t off = (int64_t)(c.seq0 + s) * c.seq_stride + ((int64_t)h * c.cap + pos) * c.hd;
@@ -76,31 +118,62 @@ __global__ __launch_bounds__(256) void embed_gather_kernel(const int* ids, int64
   out[idx] = E[clamp_id(ids[r], V) * d + e];
 }
 
+// Greedy head, step j: one workgroup per row m = b*C2 + k reduces the
+// column tiles to the first maximum (lowest id on ties), writes the token
+// and, when a next step exists, that step's decoder input
+// x = c0[m][j+1] + E[token] and its first norm a = round(g * x / rms(x)).
 template <typename T>
-__global__ __launch_bounds__(256) void embed_add_kernel(const float* c0, int64_t c0_ld, int j, const int* prev,
-                                                        const T* E, int M, int d, float* x) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)M * d) return;
-  const int m = (int)(idx / d), e = (int)(idx % d);
-  float v = c0[(int64_t)m * c0_ld + (int64_t)j * d + e];
-  if (j > 0) v += St<T>::ld(E[(int64_t)prev[m] * d + e]);
-  x[idx] = v;
-}
-
-__global__ void argmax_finalize_kernel(const float* val, const int* idx, int n_tiles, int M, int C1, int C2, int j,
-                                       int* tokens, int* prev) {
-  const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= M) return;
-  float best = val[m];
-  int bi = idx[m];
-  for (int t = 1; t < n_tiles; ++t) {
-    const float v = val[(int64_t)t * M + m];
-    const int i = idx[(int64_t)t * M + m];
-    if (v > best || (v == best && i < bi)) { best = v; bi = i; }
+__global__ __launch_bounds__(1024) void argmax_next_kernel(ArgmaxNext c) {
+  __shared__ float red[16];
+  __shared__ float bvs[16];
+  __shared__ int bis[16];
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int t = threadIdx.x; t < c.n_tiles; t += blockDim.x) {
+    const float v = c.val[(int64_t)t * c.M + m];
+    const int ix = c.idx[(int64_t)t * c.M + m];
+    if (v > best || (v == best && ix < bi)) { best = v; bi = ix; }
   }
-  const int b = m / C2, k = m % C2;
-  tokens[(int64_t)b * C1 * C2 + k * C1 + j] = bi;
-  prev[m] = bi;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+  }
+  if (lane == 0) { bvs[w] = best; bis[w] = bi; }
+  __syncthreads();
+  best = bvs[0]; bi = bis[0];
+  for (int i = 1; i < nw; ++i)
+    if (bvs[i] > best || (bvs[i] == best && bis[i] < bi)) { best = bvs[i]; bi = bis[i]; }
+  if (threadIdx.x == 0) {
+    const int b = m / c.C2, k = m % c.C2;
+    c.tokens[(int64_t)b * c.C1 * c.C2 + k * c.C1 + c.j] = bi;
+  }
+  if (!c.x) return;                      // uniform across the block
+  const int d = c.d;
+  const int col = threadIdx.x * 4;
+  const bool act = col < d;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (act) {
+    acc = *reinterpret_cast<const float4*>(c.c0 + (int64_t)m * c.c0_ld + (int64_t)(c.j + 1) * d + col);
+    const T* erow = reinterpret_cast<const T*>(c.E) + (int64_t)bi * d;
+    acc.x += St<T>::ld(erow[col]); acc.y += St<T>::ld(erow[col + 1]);
+    acc.z += St<T>::ld(erow[col + 2]); acc.w += St<T>::ld(erow[col + 3]);
+    *reinterpret_cast<float4*>(c.x + (int64_t)m * d + col) = acc;
+  }
+  float ss = act ? acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w : 0.f;
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)d + c.eps);
+  if (act) {
+    T* orow = reinterpret_cast<T*>(c.a) + (int64_t)m * d;
+    const float4 gg = *reinterpret_cast<const float4*>(c.g + col);
+    orow[col + 0] = St<T>::st(gg.x * (acc.x * inv));
+    orow[col + 1] = St<T>::st(gg.y * (acc.y * inv));
+    orow[col + 2] = St<T>::st(gg.z * (acc.z * inv));
+    orow[col + 3] = St<T>::st(gg.w * (acc.w * inv));
+  }
 }
 
 __global__ void rope_table_kernel(float* tab, int max_pos, int hd, double theta) {
@@ -120,11 +193,14 @@ inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
 
-hipError_t launch_rmsnorm(int dtype, const float* x, int64_t in_stride, int64_t in_off, const float* g, void* out,
-                          int rows, int d, float eps, hipStream_t st) {
-  dim3 grid((rows + 3) / 4), block(256);
-  if (dtype) rmsnorm_kernel<bf16_t><<<grid, block, 0, st>>>(x, in_stride, in_off, g, (bf16_t*)out, rows, d, eps);
-  else rmsnorm_kernel<float><<<grid, block, 0, st>>>(x, in_stride, in_off, g, (float*)out, rows, d, eps);
+// threads for one row of d elements, one float4 each, whole waves
+inline unsigned row_threads(int d) { return (unsigned)(((d / 4) + 63) / 64 * 64); }
+
+hipError_t launch_rows_epilogue(int dtype, const RowsEpi& e, hipStream_t st) {
+  if (e.d > 4096 || e.d % 4) return hipErrorInvalidValue;
+  dim3 grid(e.R), block(row_threads(e.d));
+  if (dtype) rows_epilogue_kernel<bf16_t><<<grid, block, 0, st>>>(e);
+  else rows_epilogue_kernel<float><<<grid, block, 0, st>>>(e);
   return hipGetLastError();
 }
 
@@ -142,17 +218,11 @@ hipError_t launch_embed_gather(int dtype, const int* ids, int64_t n, const void*
   return hipGetLastError();
 }
 
-hipError_t launch_embed_add(int dtype, const float* c0, int64_t c0_ld, int j, const int* prev, const void* E, int M,
-                            int d, float* x, hipStream_t st) {
-  const int64_t n = (int64_t)M * d;
-  if (dtype) embed_add_kernel<bf16_t><<<blocks(n), 256, 0, st>>>(c0, c0_ld, j, prev, (const bf16_t*)E, M, d, x);
-  else embed_add_kernel<float><<<blocks(n), 256, 0, st>>>(c0, c0_ld, j, prev, (const float*)E, M, d, x);
-  return hipGetLastError();
-}
-
-hipError_t launch_argmax_finalize(const float* val, const int* idx, int n_tiles, int M, int C1, int C2, int j,
-                                  int* tokens, int* prev, hipStream_t st) {
-  argmax_finalize_kernel<<<(M + 255) / 256, 256, 0, st>>>(val, idx, n_tiles, M, C1, C2, j, tokens, prev);
+hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st) {
+  if (c.d > 4096 || c.d % 4) return hipErrorInvalidValue;
+  dim3 grid(c.M), block(std::max(256u, row_threads(c.d)));
+  if (dtype) argmax_next_kernel<bf16_t><<<grid, block, 0, st>>>(c);
+  else argmax_next_kernel<float><<<grid, block, 0, st>>>(c);
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ struct GemmP {
   bf16_t* Cb;
   float* av; int* ai;
   int m_tiles, n_tiles;
+  int ksplit; int64_t pstride;   // k slabs; elements between RAW slabs
 };
 
 template <int MB, int NI, int WK, int EPI>
@@ -53,7 +54,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
   // XCD-aware tile order: consecutive workgroups land on different XCDs, so
   // give each XCD a contiguous run of tiles (M tiles of one W slab share L2).
   const int total = p.m_tiles * p.n_tiles;
-  const int bid = blockIdx.x;
+  const int ks = blockIdx.x % p.ksplit;
+  const int bid = blockIdx.x / p.ksplit;
   const int tile = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
   const int mt = tile % p.m_tiles, nt = tile / p.m_tiles;
   const int m0 = mt * BM, n0 = nt * BN;
@@ -104,17 +106,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
         w[u][ni] = *reinterpret_cast<const bf16x8*>(wp[ni] + (int64_t)kb * KT + u * 32);
   };
 
-  const int nkb = K / KT;
-  load_a(0);
-  load_w(0, wcur);
+  // this workgroup's k slab: k-blocks [kb0, kb0 + nkb)
+  const int nkb = K / KT / p.ksplit;
+  const int kb0 = ks * nkb;
+  load_a(kb0);
+  load_w(kb0, wcur);
   store_a(0);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
     const bool more = kb + 1 < nkb;
     if (more) {
-      load_a(kb + 1);
-      load_w(kb + 1, wnxt);
+      load_a(kb0 + kb + 1);
+      load_w(kb0 + kb + 1, wnxt);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -179,7 +183,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
           if (f >= N) continue;
           const f32x4 v = acc[mb][ni];
           if constexpr (EPI == EPI_STORE) {
-            *reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(p.C + ks * p.pstride + (int64_t)row * p.ldc + f) =
+                make_float4(v[0], v[1], v[2], v[3]);
           } else if constexpr (EPI == EPI_ADD) {
             float4* o = reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f);
             float4 c = *o;
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(64) void gemm_f32_kernel(GemmPF p) {
 }
 
 struct Plan {
-  int MB, NI, WK, m_tiles, n_tiles;
+  int MB, NI, WK, m_tiles, n_tiles, ksplit;
 };
 
 // Waves along K: as many as the LDS budget of the M tile allows (4 for
@@ -295,26 +300,52 @@ int wk_of(int MB, int K) {
   return wk;
 }
 
-Plan plan_bf16(int M, int N, int K) {
-  Plan pl;
-  pl.MB = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 128 ? 8 : 16;
-  pl.m_tiles = (M + 16 * pl.MB - 1) / (16 * pl.MB);
-  pl.WK = wk_of(pl.MB, K);
-  const int WN = 4 / pl.WK;
-  const int ni_max = pl.MB >= 16 ? 2 : 4;
-  pl.NI = 1;
-  for (int ni = ni_max; ni >= 1; ni >>= 1) {
-    const int bn = 16 * ni * WN;
-    const int tiles = (N + bn - 1) / bn * pl.m_tiles;
-    if (tiles >= 240 || ni == 1) { pl.NI = ni; break; }
+// Tile plan.  Decode GEMMs are skinny (M = B or B*C2 rows) and their cost is
+// streaming W once, so the plan looks for enough workgroups to keep every CU
+// streaming: the widest column tile that still gives >= 256 workgroups, and
+// otherwise a split of K into slabs (RAW partials, summed by the consumer).
+Plan plan_bf16(int M, int N, int K, bool allow_split) {
+  Plan best{};
+  const int MB0 = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 128 ? 8 : 16;
+  const int target = 256;
+  long best_score = -1;
+  // candidate M tiles: the one covering M (up to 256 rows) and, for tall
+  // skinny GEMMs, half of it (two M tiles of one W slab are adjacent and land
+  // on the same XCD, so the second read of the slab hits L2)
+  for (int MB = MB0; MB >= 1 && MB >= MB0 / 2; MB >>= 1) {
+    if (MB < MB0 && MB0 < 8) break;
+    const int m_tiles = (M + 16 * MB - 1) / (16 * MB);
+    const int wk_max = wk_of(MB, K);
+    const int ni_max = MB >= 16 ? 2 : 4;
+    for (int wk = wk_max; wk >= 1; wk >>= 1) {
+      if (K % (64 * wk)) continue;
+      const int WN = 4 / wk;
+      const int nkb = K / (64 * wk);
+      for (int ni = ni_max; ni >= 1; ni >>= 1) {
+        const int n_tiles = (N + 16 * ni * WN - 1) / (16 * ni * WN);
+        for (int ks = 1; ks <= (allow_split ? nkb : 1); ++ks) {
+          if (nkb % ks) continue;
+          const long wgs = (long)n_tiles * m_tiles * ks;
+          // reach the target first; then fewest slabs, fewest M tiles, the
+          // widest tile and the most waves along K
+          const long score = wgs >= target
+                                 ? (1L << 40) - (long)ks * (1L << 24) - (long)m_tiles * (1L << 18) + ni * WN * 16 * 8 + wk
+                                 : wgs * 64 + ni;
+          if (score > best_score) {
+            best_score = score;
+            best = Plan{MB, ni, wk, m_tiles, n_tiles, ks};
+          }
+          if (wgs >= target) break;   // more slabs only add partial traffic
+        }
+      }
+    }
   }
-  pl.n_tiles = (N + 16 * pl.NI * WN - 1) / (16 * pl.NI * WN);
-  return pl;
+  return best;
 }
 
 template <int MB, int NI, int WK>
 hipError_t run_bf16(const GemmP& p, int epi, hipStream_t st) {
-  dim3 grid(p.m_tiles * p.n_tiles), block(256);
+  dim3 grid(p.m_tiles * p.n_tiles * p.ksplit), block(256);
   switch (epi) {
     case EPI_STORE: gemm_bf16_kernel<MB, NI, WK, EPI_STORE><<<grid, block, 0, st>>>(p); break;
     case EPI_ADD: gemm_bf16_kernel<MB, NI, WK, EPI_ADD><<<grid, block, 0, st>>>(p); break;
@@ -357,7 +388,12 @@ int gemm_supported(int dtype, int M, int N, int K) {
 
 int gemm_argmax_tiles(int dtype, int M, int N, int K) {
   if (dtype == 0) return (N + 63) / 64;
-  return plan_bf16(M, N, K).n_tiles;
+  return plan_bf16(M, N, K, false).n_tiles;
+}
+
+int gemm_splits(int dtype, int M, int N, int K) {
+  if (dtype == 0) return 1;
+  return plan_bf16(M, N, K, true).ksplit;
 }
 
 hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
@@ -373,9 +409,10 @@ hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  const Plan pl = plan_bf16(g.M, g.N, g.K);
+  const Plan pl = plan_bf16(g.M, g.N, g.K, g.epi == EPI_STORE && g.allow_split);
   GemmP p{(const bf16_t*)g.A, g.lda, (const bf16_t*)g.W, g.M, g.N, g.K,
-          g.C, g.ldc, (bf16_t*)g.Cb, g.amax_val, g.amax_idx, pl.m_tiles, pl.n_tiles};
+          g.C, g.ldc, (bf16_t*)g.Cb, g.amax_val, g.amax_idx, pl.m_tiles, pl.n_tiles,
+          pl.ksplit, (int64_t)g.M * g.ldc};
   switch (pl.MB) {
     case 1: return run_bf16_wk<1>(p, pl.NI, pl.WK, g.epi, st);
     case 2: return run_bf16_wk<2>(p, pl.NI, pl.WK, g.epi, st);

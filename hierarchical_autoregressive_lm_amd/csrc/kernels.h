@@ -15,6 +15,9 @@ enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_GELU = 2, EPI_ARGMAX = 3 };
 //   GELU  : Cb (storage dtype, stride ldc) = round(gelu(acc))
 //   ARGMAX: per-row (max, first index) over each column tile written to
 //           amax_val/amax_idx [n_tiles][M]; logits stored to C if non-null.
+//   With allow_split (STORE only) K may be cut into gemm_splits() slabs; slab
+//   s then writes its raw partial sums to C + s*M*ldc and the consumer adds
+//   the slabs in order (deterministic).
 struct GemmCall {
   int dtype;
   const void* A; int64_t lda;
@@ -24,23 +27,39 @@ struct GemmCall {
   float* C; int64_t ldc;
   void* Cb;
   float* amax_val; int* amax_idx;
+  int allow_split;
 };
 hipError_t launch_gemm(const GemmCall& g, hipStream_t st);
+// K slabs launch_gemm uses for a STORE GEMM with allow_split set.
+int gemm_splits(int dtype, int M, int N, int K);
 // Column tiles the ARGMAX epilogue produces for a GEMM of this shape.
 int gemm_argmax_tiles(int dtype, int M, int N, int K);
 // Host-side shape check: 0 when the GEMM kernels support (M, N, K).
 int gemm_supported(int dtype, int M, int N, int K);
 
-// out[r] = round(g * x[r*stride + off] / sqrt(mean(x^2) + eps)), r < rows
-hipError_t launch_rmsnorm(int dtype, const float* x, int64_t in_stride,
-                          int64_t in_off, const float* g, void* out, int rows,
-                          int d, float eps, hipStream_t st);
+// Row epilogue of the GEMMs that feed a residual stream: for output row i
+// (input row r = i*row_stride + row_off, i < R):
+//   x = resid[r] + sum_{s<ksplit} P[s*pstride + r*ldp ..] + E[ids[r]]
+// (resid, P, ids optional), x_out[r] = x (optional), and, if a_out is set,
+// a_out[i*a_ld ..] = round(g * x / sqrt(mean(x^2) + eps)).  Rows have d
+// (<= 4096, multiple of 4) fp32 elements.
+struct RowsEpi {
+  const float* P; int ksplit; int64_t pstride; int64_t ldp;
+  const float* resid;
+  const int* ids; const void* E;
+  float* x_out;
+  const float* g; void* a_out; int64_t a_ld;
+  int R, d; int64_t row_stride, row_off;
+  float eps;
+};
+hipError_t launch_rows_epilogue(int dtype, const RowsEpi& e, hipStream_t st);
 
 // Positions: pos(t) = pos_add + (pos_dev ? *pos_dev * pos_mul : 0) + t for
 // the t-th new row of a sequence; the K/V of that row go to cache slot pos.
 struct RopeKvCall {
   int dtype;
-  const float* qkv;        // [M][3d] fp32: q | k | v
+  const float* qkv;        // ksplit slabs of [M][3d] fp32: q | k | v
+  int ksplit; int64_t pstride;
   int M, d, H, hd;
   float* q_out;            // [M][d] fp32 rotated q
   void* Kc; void* Vc;      // cache planes [seq][H][cap][hd], storage dtype
@@ -75,15 +94,16 @@ hipError_t launch_attn_prefill(const AttnCall& a, hipStream_t st);
 hipError_t launch_embed_gather(int dtype, const int* ids, int64_t n,
                                const void* E, int d, int V, void* out,
                                hipStream_t st);
-// x[m] = c0[m*c0_ld + j*d ..] + (j > 0 ? E[prev[m]] : 0), fp32
-hipError_t launch_embed_add(int dtype, const float* c0, int64_t c0_ld, int j,
-                            const int* prev, const void* E, int M, int d,
-                            float* x, hipStream_t st);
-// Reduce the ARGMAX tiles of row m (m = b*C2 + k) to the greedy token:
-// tokens[b*S + k*C1 + j] and prev[m].
-hipError_t launch_argmax_finalize(const float* val, const int* idx,
-                                  int n_tiles, int M, int C1, int C2, int j,
-                                  int* tokens, int* prev, hipStream_t st);
+// Greedy head of token step j: reduce the ARGMAX tiles of row m = b*C2 + k
+// to its token (tokens[b*S + k*C1 + j]); if x is set, also write the next
+// step's input x[m] = c0[m*c0_ld + (j+1)*d ..] + E[token] and its norm a[m].
+struct ArgmaxNext {
+  const float* val; const int* idx; int n_tiles, M, C1, C2, j;
+  int* tokens;
+  const float* c0; int64_t c0_ld; const void* E;
+  float* x; void* a; const float* g; int d; float eps;
+};
+hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st);
 // tab[p][i] = (cos, sin)(p * theta^(-2i/hd)), angles in double precision.
 hipError_t launch_rope_table(float* tab, int max_pos, int hd, float theta,
                              hipStream_t st);

@@ -135,10 +135,10 @@ struct WsPlan {
   int nsplit_top = 1, nsplit_low = 1;
   int head_tiles = 1;
   // persistent
-  Region top_kv, low_kv, dec_kv, h, counter, rope, prev, tok;
-  // decode scratch, set A (top branch) and set B (token branch)
-  Region xA, aA, qkvA, qA, oA, hidA, partA, eA, AA;
-  Region xB, aB, qkvB, qB, oB, hidB, c0, Ahat, zB, kv1tmp, amv, ami;
+  Region top_kv, low_kv, dec_kv, h, counter, rope, tok;
+  // decode scratch, set A (top branch) and set B (level-1 decoder + tokens)
+  Region xA, aA, partA, qA, oA, hidA, apartA, eA, AA;
+  Region xB, aB, partB, qB, oB, hidB, c0, Ahat, zB, kv1tmp, amv, ami;
   uint64_t state_bytes = 0, scratch_bytes = 0, total = 0;
   uint64_t off_state = 0, off_scratch = 0;
 };
@@ -154,8 +154,21 @@ struct Cursor {
   }
 };
 
+// bytes of the K-slab partials a STORE GEMM of this shape writes
+uint64_t part_bytes(int dt, int64_t M, int64_t N, int64_t K) {
+  return (uint64_t)gemm_splits(dt, (int)M, (int)N, (int)K) * M * N * 4;
+}
+
+// largest slab buffer any layer of a stack with M rows needs
+uint64_t layer_part_bytes(const photon_config* c, int64_t M) {
+  const int dt = c->dtype;
+  const int64_t d = c->d_model, F = (int64_t)c->mlp_mult * d;
+  return std::max({part_bytes(dt, M, 3 * d, d), part_bytes(dt, M, d, d), part_bytes(dt, M, d, F)});
+}
+
 WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mode) {
   WsPlan p;
+  const int dt = c->dtype;
   const int64_t d = c->d_model, H = c->n_heads, hd = d / H, F = (int64_t)c->mlp_mult * d, V = c->vocab;
   const int64_t C1 = c->chunk[0], C2 = c->chunk[1], S = C1 * C2;
   const uint64_t eb = elem_bytes(c);
@@ -165,7 +178,7 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.rope_pos = std::max<int64_t>({p.top_cap, p.low_cap, C1, C2});
   p.nsplit_top = attn_decode_splits((int)B, (int)H, (int)p.top_cap);
   p.nsplit_low = hier ? attn_decode_splits((int)B, (int)H, (int)p.low_cap) : 1;
-  p.head_tiles = gemm_argmax_tiles(c->dtype, (int)(B * C2), (int)V, (int)d);
+  p.head_tiles = gemm_argmax_tiles(dt, (int)(B * C2), (int)V, (int)d);
   Cursor cur;
   p.top_kv = cur.take((uint64_t)c->n_top * 2 * B * H * p.top_cap * hd * eb);
   p.low_kv = cur.take((uint64_t)c->n_enc1 * 2 * B * H * p.low_cap * hd * eb);
@@ -174,24 +187,26 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.h = cur.take((uint64_t)B * d * eb);
   p.counter = cur.take(sizeof(int));
   p.rope = cur.take((uint64_t)p.rope_pos * (hd / 2) * 2 * sizeof(float));
-  p.prev = cur.take((uint64_t)B * C2 * sizeof(int));
   p.tok = cur.take((uint64_t)B * S * sizeof(int));
   p.off_scratch = align_up(cur.pos);
   p.state_bytes = p.off_scratch - p.off_state;
   const int64_t MA = hier ? B * C2 : B, MB = B * C2;
+  uint64_t partA = std::max(layer_part_bytes(c, B), part_bytes(dt, B, d, C2 * d));
+  if (hier) partA = std::max({partA, layer_part_bytes(c, MB), part_bytes(dt, MB, d, C1 * d)});
   p.xA = cur.take((uint64_t)MA * d * 4);
   p.aA = cur.take((uint64_t)MA * d * eb);
-  p.qkvA = cur.take((uint64_t)MA * 3 * d * 4);
+  p.partA = cur.take(partA);
   p.qA = cur.take((uint64_t)MA * d * 4);
   p.oA = cur.take((uint64_t)MA * d * eb);
   p.hidA = cur.take((uint64_t)MA * F * eb);
   const int64_t parts = std::max<int64_t>((int64_t)B * H * p.nsplit_top, hier ? (int64_t)B * H * C2 * p.nsplit_low : 0);
-  p.partA = cur.take((uint64_t)parts * (hd + 2) * 4);
+  p.apartA = cur.take((uint64_t)parts * (hd + 2) * 4);
   p.eA = cur.take(hier ? (uint64_t)B * S * d * eb : 0);
   p.AA = cur.take(hier ? (uint64_t)B * C2 * d * eb : 0);
+  const uint64_t partB = std::max(layer_part_bytes(c, MB), part_bytes(dt, B, C2 * d, d));
   p.xB = cur.take((uint64_t)MB * d * 4);
   p.aB = cur.take((uint64_t)MB * d * eb);
-  p.qkvB = cur.take((uint64_t)MB * 3 * d * 4);
+  p.partB = cur.take(partB);
   p.qB = cur.take((uint64_t)MB * d * 4);
   p.oB = cur.take((uint64_t)MB * d * eb);
   p.hidB = cur.take((uint64_t)MB * F * eb);
@@ -211,24 +226,33 @@ constexpr int64_t kPrefillRows = 65536;
 
 struct PrePlan {
   int64_t bs = 1, n1 = 0, n = 0;
-  Region e, x, a, qkv, q, o, hid, A1, kv1, rope1;
+  Region e, x, a, part, q, o, hid, A1, kv1, rope1;
   uint64_t total = 0;
 };
 
 PrePlan plan_prefill(const photon_config* c, int64_t B, int64_t P, int mode) {
   PrePlan p;
+  const int dt = c->dtype;
   const int64_t d = c->d_model, H = c->n_heads, hd = d / H, F = (int64_t)c->mlp_mult * d;
-  const int64_t C1 = c->chunk[0], S = C1 * c->chunk[1];
+  const int64_t C1 = c->chunk[0], C2 = c->chunk[1], S = C1 * C2;
   const uint64_t eb = elem_bytes(c);
   p.n1 = P / C1;
   p.n = P / S;
   p.bs = std::max<int64_t>(1, std::min<int64_t>(B, kPrefillRows / std::max<int64_t>(1, p.n1)));
-  const int64_t R = p.bs * p.n1;
+  const int64_t R = p.bs * p.n1, R2 = p.bs * p.n;
+  // the last slice may be shorter; its GEMMs plan their own slabs
+  uint64_t part = 0;
+  for (int64_t bs : {p.bs, B % p.bs}) {
+    if (bs == 0) continue;
+    part = std::max({part, layer_part_bytes(c, bs * p.n1), layer_part_bytes(c, bs * p.n),
+                     part_bytes(dt, bs * p.n1, d, C1 * d), part_bytes(dt, bs * p.n, d, C2 * d)});
+  }
+  (void)R2;
   Cursor cur;
   p.e = cur.take((uint64_t)p.bs * P * d * eb);
   p.x = cur.take((uint64_t)R * d * 4);
   p.a = cur.take((uint64_t)R * d * eb);
-  p.qkv = cur.take((uint64_t)R * 3 * d * 4);
+  p.part = cur.take(part);
   p.q = cur.take((uint64_t)R * d * 4);
   p.o = cur.take((uint64_t)R * d * eb);
   p.hid = cur.take((uint64_t)R * F * eb);
@@ -300,6 +324,18 @@ struct photon_ctx {
   unsigned char* ws = nullptr;
   WsPlan plan;
   Tracer tr;
+  // one decode chunk captured as a HIP graph, replayed for every chunk
+  bool use_graph = true;
+  hipGraphExec_t graph = nullptr;
+  hipStream_t cap[2] = {nullptr, nullptr};
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  ~photon_ctx() {
+    if (graph) (void)hipGraphExecDestroy(graph);
+    for (auto s : cap)
+      if (s) (void)hipStreamDestroy(s);
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    if (ev_join) (void)hipEventDestroy(ev_join);
+  }
 };
 
 namespace {
@@ -382,7 +418,9 @@ double gemm_bytes(const GemmCall& g) {
   const double eb = g.dtype ? 2 : 4;
   double b = (double)g.N * g.K * eb + (double)g.M * g.K * eb;
   switch (g.epi) {
-    case EPI_STORE: b += (double)g.M * g.N * 4; break;
+    case EPI_STORE:
+      b += (double)g.M * g.N * 4 * (g.allow_split ? gemm_splits(g.dtype, g.M, g.N, g.K) : 1);
+      break;
     case EPI_ADD: b += 2.0 * g.M * g.N * 4; break;
     case EPI_GELU: b += (double)g.M * g.N * eb; break;
     default:
@@ -408,13 +446,13 @@ struct KvTarget {
 enum AttnKind { ATT_PREFILL, ATT_DECODE, ATT_CHUNK };
 
 struct StackBufs {
-  float* x;
-  void* a;
-  float* qkv;
-  float* q;
-  void* o;
-  void* hid;
-  float* part;
+  float* x;       // residual stream, fp32 [M][d]
+  void* a;        // normalized GEMM operand [M][d]
+  float* part;    // K-slab partials of the STORE GEMMs
+  float* q;       // rotated queries, fp32 [M][d]
+  void* o;        // attention output [M][d]
+  void* hid;      // MLP hidden [M][F]
+  float* apart;   // split-key attention partials
 };
 
 struct StackRun {
@@ -425,32 +463,64 @@ struct StackRun {
   AttnKind kind;
   int Q, L_host; const int* L_dev; int L_mul, L_add; int nsplit;
   int L_acct;  // keys visible to the last query (host mirror, for accounting)
-  // final norm: rows out_rows, input row r*in_stride + in_off
+  // stack output round(norm(x; gf)) for rows i < out_rows taken from input
+  // row i*in_stride + in_off
   void* out; int out_rows; int64_t in_stride, in_off;
 };
 
+double rows_epi_bytes(const RowsEpi& e, int eb) {
+  double b = (double)e.R * e.d * 4 * (e.ksplit + (e.resid ? 1 : 0) + (e.x_out ? 1 : 0));
+  if (e.ids) b += (double)e.R * (e.d * eb + 4);
+  if (e.a_out) b += (double)e.R * e.d * eb + e.d * 4.0;
+  return b;
+}
+
+photon_status rows_epi(photon_ctx* c, const RowsEpi& e, hipStream_t st) {
+  return traced(c, PHOTON_K_NORM, rows_epi_bytes(e, elem_bytes(&c->cfg)), 6.0 * e.R * e.d, st, "rows_epilogue",
+                [&] { return launch_rows_epilogue(c->cfg.dtype, e, st); });
+}
+
+// STORE GEMM into `part` (K slabs allowed); *ks receives the slab count.
+photon_status gemm_slabs(photon_ctx* c, int cls, const void* A, int64_t lda, const void* W, int M, int N, int K,
+                         float* part, int* ks, hipStream_t st) {
+  GemmCall g{};
+  g.dtype = c->cfg.dtype; g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K;
+  g.epi = EPI_STORE; g.C = part; g.ldc = N; g.allow_split = 1;
+  *ks = gemm_splits(g.dtype, M, N, K);
+  return run_gemm(c, cls, g, st);
+}
+
+// The stack input: x = sum of the producer GEMM's slabs (rows of d, row r at
+// part + r*d), and its normalized form for the first layer.
+photon_status stack_input(photon_ctx* c, const StackW& sw, const float* part, int ks, int R, float* x, void* a,
+                          hipStream_t st) {
+  RowsEpi e{};
+  e.P = part; e.ksplit = ks; e.pstride = (int64_t)R * c->cfg.d_model; e.ldp = c->cfg.d_model;
+  e.x_out = x; e.g = sw.layers[0].g1; e.a_out = a; e.a_ld = c->cfg.d_model;
+  e.R = R; e.d = c->cfg.d_model; e.row_stride = 1; e.row_off = 0; e.eps = c->cfg.norm_eps;
+  return rows_epi(c, e, st);
+}
+
+// One Transformer stack.  On entry b.x holds the stack input and b.a its
+// normalized form for layer 0; on exit r.out holds the stack output rows.
 photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, const StackRun& r, hipStream_t st) {
   const photon_config& cf = c->cfg;
   const int dt = cf.dtype, d = cf.d_model, H = cf.n_heads, hd = d / H, F = cf.mlp_mult * d;
   const int eb = elem_bytes(&cf);
-  const double norm_bytes = (double)r.M * d * (4 + eb) + d * 4.0;
-  for (size_t l = 0; l < sw.layers.size(); ++l) {
+  const int L = (int)sw.layers.size();
+  for (int l = 0; l < L; ++l) {
     const LayerW& w = sw.layers[l];
-    PH_TRY(traced(c, PHOTON_K_NORM, norm_bytes, 4.0 * r.M * d, st, "rmsnorm",
-                  [&] { return launch_rmsnorm(dt, b.x, 1, 0, w.g1, b.a, r.M, d, cf.norm_eps, st); }));
-    GemmCall g{};
-    g.dtype = dt; g.A = b.a; g.lda = d; g.W = w.Wqkv; g.M = r.M; g.N = 3 * d; g.K = d;
-    g.epi = EPI_STORE; g.C = b.qkv; g.ldc = 3 * d;
-    PH_TRY(run_gemm(c, PHOTON_K_GEMM_QKV, g, st));
+    int ks = 1;
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_QKV, b.a, d, w.Wqkv, r.M, 3 * d, d, b.part, &ks, st));
     unsigned char* kbase = r.kv.base + (r.kv.per_layer ? (int64_t)l * 2 * r.kv.plane_elems * eb : 0);
     void* Kc = kbase;
     void* Vc = kbase + r.kv.plane_elems * eb;
-    RopeKvCall rc{dt, b.qkv, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap, r.rows_per_seq, r.kv.seq0,
-                  r.pos_add, r.pos_dev, r.pos_mul, r.rope};
-    PH_TRY(traced(c, PHOTON_K_ROPE_KV, (double)r.M * d * (12 + 4 + 2 * eb), 6.0 * r.M * d, st, "rope_kv",
+    RopeKvCall rc{dt, b.part, ks, (int64_t)r.M * 3 * d, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
+                  r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
+    PH_TRY(traced(c, PHOTON_K_ROPE_KV, (double)r.M * d * (12.0 * ks + 4 + 2 * eb), 6.0 * r.M * d, st, "rope_kv",
                   [&] { return launch_rope_kv(rc, st); }));
     AttnCall ac{dt, r.G, r.Q, H, hd, b.q, d, Kc, Vc, r.kv.seq_stride, r.kv.cap, r.kv.seq0,
-                r.L_host, r.L_dev, r.L_mul, r.L_add, b.o, d, b.part, r.nsplit};
+                r.L_host, r.L_dev, r.L_mul, r.L_add, b.o, d, b.apart, r.nsplit};
     // K and V of every visible key read once, q read, output written
     double abytes = (double)r.G * H * r.L_acct * hd * eb * 2 + (double)r.M * d * (4 + eb);
     if (r.kind == ATT_DECODE && r.nsplit > 1) abytes += 2.0 * r.G * H * r.Q * r.nsplit * (hd + 2) * 4;
@@ -464,32 +534,34 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
     else
       PH_TRY(traced(c, PHOTON_K_ATTN_CHUNK, abytes, aflops, st, "attn_chunk",
                     [&] { return launch_attn_chunk(ac, st); }));
-    g = GemmCall{};
-    g.dtype = dt; g.A = b.o; g.lda = d; g.W = w.Wo; g.M = r.M; g.N = d; g.K = d;
-    g.epi = EPI_ADD; g.C = b.x; g.ldc = d;
-    PH_TRY(run_gemm(c, PHOTON_K_GEMM_O, g, st));
-    PH_TRY(traced(c, PHOTON_K_NORM, norm_bytes, 4.0 * r.M * d, st, "rmsnorm",
-                  [&] { return launch_rmsnorm(dt, b.x, 1, 0, w.g2, b.a, r.M, d, cf.norm_eps, st); }));
-    g = GemmCall{};
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_O, b.o, d, w.Wo, r.M, d, d, b.part, &ks, st));
+    {
+      RowsEpi e{};
+      e.P = b.part; e.ksplit = ks; e.pstride = (int64_t)r.M * d; e.ldp = d;
+      e.resid = b.x; e.x_out = b.x; e.g = w.g2; e.a_out = b.a; e.a_ld = d;
+      e.R = r.M; e.d = d; e.row_stride = 1; e.row_off = 0; e.eps = cf.norm_eps;
+      PH_TRY(rows_epi(c, e, st));
+    }
+    GemmCall g{};
     g.dtype = dt; g.A = b.a; g.lda = d; g.W = w.W1; g.M = r.M; g.N = F; g.K = d;
     g.epi = EPI_GELU; g.Cb = b.hid; g.ldc = F;
     PH_TRY(run_gemm(c, PHOTON_K_GEMM_UP, g, st));
-    g = GemmCall{};
-    g.dtype = dt; g.A = b.hid; g.lda = F; g.W = w.W2; g.M = r.M; g.N = d; g.K = F;
-    g.epi = EPI_ADD; g.C = b.x; g.ldc = d;
-    PH_TRY(run_gemm(c, PHOTON_K_GEMM_DOWN, g, st));
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_DOWN, b.hid, F, w.W2, r.M, d, F, b.part, &ks, st));
+    {
+      // residual add, then the next layer's first norm (or the final norm)
+      const bool last = l + 1 == L;
+      RowsEpi e{};
+      e.P = b.part; e.ksplit = ks; e.pstride = (int64_t)r.M * d; e.ldp = d;
+      e.resid = b.x; e.x_out = last ? nullptr : b.x;
+      e.g = last ? sw.gf : sw.layers[l + 1].g1;
+      e.a_out = last ? r.out : b.a; e.a_ld = d;
+      e.R = last ? r.out_rows : r.M; e.d = d;
+      e.row_stride = last ? r.in_stride : 1; e.row_off = last ? r.in_off : 0;
+      e.eps = cf.norm_eps;
+      PH_TRY(rows_epi(c, e, st));
+    }
   }
-  PH_TRY(traced(c, PHOTON_K_NORM, (double)r.out_rows * d * (4 + eb) + d * 4.0, 4.0 * r.out_rows * d, st, "rmsnorm",
-                [&] { return launch_rmsnorm(dt, b.x, r.in_stride, r.in_off, sw.gf, r.out, r.out_rows, d, cf.norm_eps, st); }));
   return ok();
-}
-
-photon_status gemm_plain(photon_ctx* c, int cls, const void* A, int64_t lda, const void* W, int M, int N, int K,
-                         float* C, int64_t ldc, hipStream_t st) {
-  GemmCall g{};
-  g.dtype = c->cfg.dtype; g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K;
-  g.epi = EPI_STORE; g.C = C; g.ldc = ldc;
-  return run_gemm(c, cls, g, st);
 }
 
 photon_status check_gemms(const photon_config* c, int64_t B, int64_t R1, int64_t R2, int mode) {
@@ -656,6 +728,10 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   unsigned char* ws = (unsigned char*)d_workspace;
   unsigned char* sc = (unsigned char*)d_scratch;
   c->prefilled = false;
+  if (c->graph) {
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+  }
   c->ws = ws;
   c->plan = wp;
   c->mode = mode;
@@ -668,7 +744,7 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   HIP_TRY(launch_rope_table(rope1, (int)std::max<int64_t>(pp.n1, 1), hd, cf.rope_theta, st));
 
   const int64_t n1 = pp.n1, n = pp.n;
-  StackBufs bufs{(float*)(sc + pp.x.off), sc + pp.a.off, (float*)(sc + pp.qkv.off), (float*)(sc + pp.q.off),
+  StackBufs bufs{(float*)(sc + pp.x.off), sc + pp.a.off, (float*)(sc + pp.part.off), (float*)(sc + pp.q.off),
                  sc + pp.o.off, sc + pp.hid.off, nullptr};
   for (int64_t b0 = 0; b0 < batch; b0 += pp.bs) {
     const int bs = (int)std::min<int64_t>(pp.bs, batch - b0);
@@ -677,10 +753,10 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
       return launch_embed_gather(dt, d_prompt + b0 * prompt_len, (int64_t)bs * prompt_len, c->E, d, cf.vocab,
                                  sc + pp.e.off, st);
     }));
-    {
-      photon_status s = gemm_plain(c, PHOTON_K_GEMM_CHUNK, sc + pp.e.off, (int64_t)C1 * d, c->W_ch1, (int)(bs * n1), d, C1 * d, bufs.x, d, st);
-      if (s) return s;
-    }
+    int ks = 1;
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, sc + pp.e.off, (int64_t)C1 * d, c->W_ch1, (int)(bs * n1), d, C1 * d,
+                      bufs.part, &ks, st));
+    PH_TRY(stack_input(c, c->enc1, bufs.part, ks, (int)(bs * n1), bufs.x, bufs.a, st));
     StackRun r{};
     r.M = (int)(bs * n1); r.rows_per_seq = (int)n1; r.G = bs;
     if (mode == PHOTON_HIERGEN) {
@@ -692,15 +768,11 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
     r.pos_add = 0; r.pos_dev = nullptr; r.pos_mul = 0; r.rope = rope1;
     r.kind = ATT_PREFILL; r.Q = (int)n1; r.L_host = (int)n1; r.nsplit = 1; r.L_acct = (int)n1;
     r.out = sc + pp.A1.off; r.out_rows = (int)(bs * n1); r.in_stride = 1; r.in_off = 0;
-    {
-      photon_status s = run_stack(c, c->enc1, bufs, r, st);
-      if (s) return s;
-    }
+    PH_TRY(run_stack(c, c->enc1, bufs, r, st));
     // Chunker^2 over groups of C2 level-1 states
-    {
-      photon_status s = gemm_plain(c, PHOTON_K_GEMM_CHUNK, sc + pp.A1.off, (int64_t)C2 * d, c->W_ch2, (int)(bs * n), d, C2 * d, bufs.x, d, st);
-      if (s) return s;
-    }
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, sc + pp.A1.off, (int64_t)C2 * d, c->W_ch2, (int)(bs * n), d, C2 * d,
+                      bufs.part, &ks, st));
+    PH_TRY(stack_input(c, c->top, bufs.part, ks, (int)(bs * n), bufs.x, bufs.a, st));
     StackRun t{};
     t.M = (int)(bs * n); t.rows_per_seq = (int)n; t.G = bs;
     t.kv = KvTarget{ws + wp.top_kv.off, (int64_t)batch * H * wp.top_cap * hd, true, (int64_t)H * wp.top_cap * hd,
@@ -709,16 +781,137 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
     t.kind = ATT_PREFILL; t.Q = (int)n; t.L_host = (int)n; t.nsplit = 1; t.L_acct = (int)n;
     // final norm only for the last top state of each sequence: h_{n-1}
     t.out = ws + wp.h.off + (uint64_t)b0 * d * eb; t.out_rows = bs; t.in_stride = n; t.in_off = n - 1;
-    {
-      photon_status s = run_stack(c, c->top, bufs, t, st);
-      if (s) return s;
-    }
+    PH_TRY(run_stack(c, c->top, bufs, t, st));
   }
   HIP_TRY(launch_set_int((int*)(ws + wp.counter.off), (int)n, st));
   c->top_len = n;
   c->tokens = prompt_len;
   c->prompt_tokens = prompt_len;
   c->prefilled = true;
+  return ok();
+}
+
+// Enqueue one decode chunk.  The level-1 decoder runs on `st`; with RecGen
+// and st_top != st the top branch forks onto st_top (after A-hat exists) and
+// joins back before the chunk ends.  Everything reads positions from the
+// device counter, so the same sequence serves every chunk.
+photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipStream_t st_top) {
+  const photon_config& cf = c->cfg;
+  const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
+  const WsPlan& wp = c->plan;
+  unsigned char* ws = c->ws;
+  const int dt = cf.dtype, d = cf.d_model, H = cf.n_heads, hd = d / H, V = cf.vocab;
+  const int B = (int)c->B, MB = B * C2;
+  const int eb = elem_bytes(&cf);
+  int* counter = (int*)(ws + wp.counter.off);
+  const float* rope = (const float*)(ws + wp.rope.off);
+  void* h = ws + wp.h.off;
+  void* Ahat = ws + wp.Ahat.off;
+  int* tok = (int*)(ws + wp.tok.off);
+  float* c0 = (float*)(ws + wp.c0.off);
+  StackBufs sb{(float*)(ws + wp.xB.off), ws + wp.aB.off, (float*)(ws + wp.partB.off), (float*)(ws + wp.qB.off),
+               ws + wp.oB.off, ws + wp.hidB.off, nullptr};
+  StackBufs sa{(float*)(ws + wp.xA.off), ws + wp.aA.off, (float*)(ws + wp.partA.off), (float*)(ws + wp.qA.off),
+               ws + wp.oA.off, ws + wp.hidA.off, (float*)(ws + wp.apartA.off)};
+  int ks = 1;
+
+  // Converter^2: h_{i-1} -> C2 conditioning vectors = level-1 decoder rows
+  PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CONV, h, d, c->W_cv2, B, C2 * d, d, sb.part, &ks, st));
+  PH_TRY(stack_input(c, c->dec1, sb.part, ks, MB, sb.x, sb.a, st));
+  // level-1 decoder over the C2 positions of the chunk -> A-hat_i
+  {
+    StackRun r{};
+    r.M = MB; r.rows_per_seq = C2; r.G = B;
+    r.kv = KvTarget{ws + wp.kv1tmp.off, (int64_t)B * H * C2 * hd, false, (int64_t)H * C2 * hd, C2, 0};
+    r.pos_add = 0; r.rope = rope;
+    r.kind = ATT_CHUNK; r.Q = C2; r.L_host = C2; r.nsplit = 1; r.L_acct = C2;
+    r.out = Ahat; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
+    PH_TRY(run_stack(c, c->dec1, sb, r, st));
+  }
+  const bool fork = c->mode == PHOTON_RECGEN && st_top != st;
+  if (fork) {
+    HIP_TRY(hipEventRecord(c->ev_fork, st));
+    HIP_TRY(hipStreamWaitEvent(st_top, c->ev_fork, 0));
+  }
+  // token branch: Converter^1 (all C1 conditioning vectors of every level-1
+  // position), then C1 sequential token-decoder steps
+  {
+    GemmCall g{};
+    g.dtype = dt; g.A = Ahat; g.lda = d; g.W = c->W_cv1; g.M = MB; g.N = C1 * d; g.K = d;
+    g.epi = EPI_STORE; g.C = c0; g.ldc = (int64_t)C1 * d;
+    PH_TRY(run_gemm(c, PHOTON_K_GEMM_CONV, g, st));
+    RowsEpi e{};   // step 0 input: x = c_0, no token yet
+    e.P = c0; e.ksplit = 1; e.pstride = 0; e.ldp = (int64_t)C1 * d;
+    e.x_out = sb.x; e.g = c->dec0.layers[0].g1; e.a_out = sb.a; e.a_ld = d;
+    e.R = MB; e.d = d; e.row_stride = 1; e.row_off = 0; e.eps = cf.norm_eps;
+    PH_TRY(rows_epi(c, e, st));
+  }
+  for (int j = 0; j < C1; ++j) {
+    StackRun r{};
+    r.M = MB; r.rows_per_seq = 1; r.G = MB;
+    r.kv = KvTarget{ws + wp.dec_kv.off, (int64_t)MB * H * C1 * hd, true, (int64_t)H * C1 * hd, C1, 0};
+    r.pos_add = j; r.rope = rope;
+    r.kind = ATT_CHUNK; r.Q = 1; r.L_host = j + 1; r.nsplit = 1; r.L_acct = j + 1;
+    r.out = ws + wp.zB.off; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
+    PH_TRY(run_stack(c, c->dec0, sb, r, st));
+    GemmCall g{};
+    g.dtype = dt; g.A = ws + wp.zB.off; g.lda = d; g.W = c->W_out; g.M = MB; g.N = V; g.K = d;
+    g.epi = EPI_ARGMAX;
+    g.C = d_logits ? d_logits + (int64_t)j * V : nullptr;
+    g.ldc = (int64_t)C1 * V;
+    g.amax_val = (float*)(ws + wp.amv.off); g.amax_idx = (int*)(ws + wp.ami.off);
+    PH_TRY(run_gemm(c, PHOTON_K_GEMM_HEAD, g, st));
+    const bool next = j + 1 < C1;
+    ArgmaxNext an{g.amax_val, g.amax_idx, wp.head_tiles, MB, C1, C2, j, tok,
+                  c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec0.layers[0].g1, d, cf.norm_eps};
+    const double nb = (double)wp.head_tiles * MB * 8 + MB * 4.0 + (next ? (double)MB * d * (8 + 2 * eb) : 0);
+    PH_TRY(traced(c, PHOTON_K_ARGMAX, nb, 0, st, "argmax_next", [&] { return launch_argmax_next(dt, an, st); }));
+  }
+  // top branch (RecGen: independent of the tokens, so it may run beside the
+  // token branch on its own stream; its counter update closes it)
+  const hipStream_t stt = fork ? st_top : st;
+  if (c->mode == PHOTON_RECGEN) {
+    // feedback: u_i = Chunker^2(A-hat_i), nothing re-encoded
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, Ahat, (int64_t)C2 * d, c->W_ch2, B, d, C2 * d, sa.part, &ks, stt));
+    PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
+  } else {
+    // HierGen: re-encode the chunk's tokens through Chunker^1 and one
+    // level-1 encoder step, then Chunker^2 of the encoder summary A_i
+    PH_TRY(traced(c, PHOTON_K_EMBED, (double)B * S * (4 + 2.0 * d * eb), 0, stt, "embed_gather",
+                  [&] { return launch_embed_gather(dt, tok, (int64_t)B * S, c->E, d, V, ws + wp.eA.off, stt); }));
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, ws + wp.eA.off, (int64_t)C1 * d, c->W_ch1, MB, d, C1 * d, sa.part, &ks,
+                      stt));
+    PH_TRY(stack_input(c, c->enc1, sa.part, ks, MB, sa.x, sa.a, stt));
+    StackRun r{};
+    r.M = MB; r.rows_per_seq = C2; r.G = B;
+    r.kv = KvTarget{ws + wp.low_kv.off, (int64_t)B * H * wp.low_cap * hd, true, (int64_t)H * wp.low_cap * hd,
+                    (int)wp.low_cap, 0};
+    r.pos_add = 0; r.pos_dev = counter; r.pos_mul = C2; r.rope = rope;
+    r.kind = ATT_DECODE; r.Q = C2; r.L_dev = counter; r.L_mul = C2; r.L_add = C2; r.nsplit = wp.nsplit_low;
+    r.L_acct = (int)((c->top_len + 1) * C2);
+    r.out = ws + wp.AA.off; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
+    PH_TRY(run_stack(c, c->enc1, sa, r, stt));
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, ws + wp.AA.off, (int64_t)C2 * d, c->W_ch2, B, d, C2 * d, sa.part, &ks,
+                      stt));
+    PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
+  }
+  {
+    StackRun r{};
+    r.M = B; r.rows_per_seq = 1; r.G = B;
+    r.kv = KvTarget{ws + wp.top_kv.off, (int64_t)B * H * wp.top_cap * hd, true, (int64_t)H * wp.top_cap * hd,
+                    (int)wp.top_cap, 0};
+    r.pos_add = 0; r.pos_dev = counter; r.pos_mul = 1; r.rope = rope;
+    r.kind = ATT_DECODE; r.Q = 1; r.L_dev = counter; r.L_mul = 1; r.L_add = 1; r.nsplit = wp.nsplit_top;
+    r.L_acct = (int)(c->top_len + 1);
+    r.out = h; r.out_rows = B; r.in_stride = 1; r.in_off = 0;
+    PH_TRY(run_stack(c, c->top, sa, r, stt));
+  }
+  HIP_TRY(launch_add_int(counter, 1, stt));
+  if (fork) {
+    HIP_TRY(hipEventRecord(c->ev_join, st_top));
+    HIP_TRY(hipStreamWaitEvent(st, c->ev_join, 0));
+  }
+  (void)S;
   return ok();
 }
 
@@ -733,92 +926,34 @@ photon_status photon_decode_chunk(photon_ctx* c, int32_t* d_tokens, float* d_log
   if (c->mode == PHOTON_HIERGEN && !c->wpre)
     return fail(PHOTON_ESTATE, "HierGen decoding needs the prefill-only weights, which were released");
   hipStream_t st = (hipStream_t)stream;
-  const WsPlan& wp = c->plan;
-  unsigned char* ws = c->ws;
-  const int dt = cf.dtype, d = cf.d_model, H = cf.n_heads, hd = d / H, V = cf.vocab;
-  const int B = (int)c->B, MB = B * C2;
-  const int eb = elem_bytes(&cf);
-  int* counter = (int*)(ws + wp.counter.off);
-  const float* rope = (const float*)(ws + wp.rope.off);
-  void* h = ws + wp.h.off;
-  void* Ahat = ws + wp.Ahat.off;
-  int* tok = (int*)(ws + wp.tok.off);
-  int* prev = (int*)(ws + wp.prev.off);
-  StackBufs sb{(float*)(ws + wp.xB.off), ws + wp.aB.off, (float*)(ws + wp.qkvB.off), (float*)(ws + wp.qB.off),
-               ws + wp.oB.off, ws + wp.hidB.off, nullptr};
-  StackBufs sa{(float*)(ws + wp.xA.off), ws + wp.aA.off, (float*)(ws + wp.qkvA.off), (float*)(ws + wp.qA.off),
-               ws + wp.oA.off, ws + wp.hidA.off, (float*)(ws + wp.partA.off)};
-  photon_status s;
-
-  // Converter^2: h_{i-1} -> C2 conditioning vectors (rows of the level-1 decoder)
-  if ((s = gemm_plain(c, PHOTON_K_GEMM_CONV, h, d, c->W_cv2, B, C2 * d, d, sb.x, (int64_t)C2 * d, st))) return s;
-  // level-1 decoder over the C2 positions of the chunk -> A-hat_i
-  {
-    StackRun r{};
-    r.M = MB; r.rows_per_seq = C2; r.G = B;
-    r.kv = KvTarget{ws + wp.kv1tmp.off, (int64_t)B * H * C2 * hd, false, (int64_t)H * C2 * hd, C2, 0};
-    r.pos_add = 0; r.rope = rope;
-    r.kind = ATT_CHUNK; r.Q = C2; r.L_host = C2; r.nsplit = 1; r.L_acct = C2;
-    r.out = Ahat; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
-    if ((s = run_stack(c, c->dec1, sb, r, st))) return s;
-  }
-  // token branch: Converter^1 then C1 sequential token-decoder steps
-  if ((s = gemm_plain(c, PHOTON_K_GEMM_CONV, Ahat, d, c->W_cv1, MB, C1 * d, d, (float*)(ws + wp.c0.off), (int64_t)C1 * d, st))) return s;
-  for (int j = 0; j < C1; ++j) {
-    PH_TRY(traced(c, PHOTON_K_EMBED, (double)MB * d * (8 + (j > 0 ? eb : 0)), (double)MB * d, st, "embed_add", [&] {
-      return launch_embed_add(dt, (const float*)(ws + wp.c0.off), (int64_t)C1 * d, j, prev, c->E, MB, d, sb.x, st);
-    }));
-    StackRun r{};
-    r.M = MB; r.rows_per_seq = 1; r.G = MB;
-    r.kv = KvTarget{ws + wp.dec_kv.off, (int64_t)MB * H * C1 * hd, true, (int64_t)H * C1 * hd, C1, 0};
-    r.pos_add = j; r.rope = rope;
-    r.kind = ATT_CHUNK; r.Q = 1; r.L_host = j + 1; r.nsplit = 1; r.L_acct = j + 1;
-    r.out = ws + wp.zB.off; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
-    if ((s = run_stack(c, c->dec0, sb, r, st))) return s;
-    GemmCall g{};
-    g.dtype = dt; g.A = ws + wp.zB.off; g.lda = d; g.W = c->W_out; g.M = MB; g.N = V; g.K = d;
-    g.epi = EPI_ARGMAX;
-    g.C = d_logits ? d_logits + (int64_t)j * V : nullptr;
-    g.ldc = (int64_t)C1 * V;
-    g.amax_val = (float*)(ws + wp.amv.off); g.amax_idx = (int*)(ws + wp.ami.off);
-    PH_TRY(run_gemm(c, PHOTON_K_GEMM_HEAD, g, st));
-    PH_TRY(traced(c, PHOTON_K_ARGMAX, (double)wp.head_tiles * MB * 8 + MB * 8.0, 0, st, "argmax", [&] {
-      return launch_argmax_finalize(g.amax_val, g.amax_idx, wp.head_tiles, MB, C1, C2, j, tok, prev, st);
-    }));
-  }
-  // top branch
-  if (c->mode == PHOTON_RECGEN) {
-    // feedback: u_i = Chunker^2(A-hat_i), nothing re-encoded
-    if ((s = gemm_plain(c, PHOTON_K_GEMM_CHUNK, Ahat, (int64_t)C2 * d, c->W_ch2, B, d, C2 * d, sa.x, d, st))) return s;
+  const int B = (int)c->B;
+  int* tok = (int*)(c->ws + c->plan.tok.off);
+  if (c->use_graph && !d_logits && c->tr.mask == 0) {
+    if (!c->graph) {
+      for (auto& cs : c->cap)
+        if (!cs) HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+      if (!c->ev_fork) HIP_TRY(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming));
+      if (!c->ev_join) HIP_TRY(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming));
+      HIP_TRY(hipStreamBeginCapture(c->cap[0], hipStreamCaptureModeRelaxed));
+      const photon_status s = enqueue_chunk(c, nullptr, c->cap[0], c->cap[1]);
+      hipGraph_t g = nullptr;
+      const hipError_t e = hipStreamEndCapture(c->cap[0], &g);
+      if (s != PHOTON_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return s;
+      }
+      if (e != hipSuccess) return fail(PHOTON_EHIP, "graph capture: %s", hipGetErrorString(e));
+      const hipError_t ie = hipGraphInstantiate(&c->graph, g, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(g);
+      if (ie != hipSuccess) {
+        c->graph = nullptr;
+        return fail(PHOTON_EHIP, "graph instantiate: %s", hipGetErrorString(ie));
+      }
+    }
+    HIP_TRY(hipGraphLaunch(c->graph, st));
   } else {
-    // HierGen: re-encode the chunk's tokens through Chunker^1 and one
-    // level-1 encoder step, then Chunker^2 of the encoder summary A_i
-    PH_TRY(traced(c, PHOTON_K_EMBED, (double)B * S * (4 + 2.0 * d * eb), 0, st, "embed_gather",
-                  [&] { return launch_embed_gather(dt, tok, (int64_t)B * S, c->E, d, V, ws + wp.eA.off, st); }));
-    if ((s = gemm_plain(c, PHOTON_K_GEMM_CHUNK, ws + wp.eA.off, (int64_t)C1 * d, c->W_ch1, MB, d, C1 * d, sa.x, d, st))) return s;
-    StackRun r{};
-    r.M = MB; r.rows_per_seq = C2; r.G = B;
-    r.kv = KvTarget{ws + wp.low_kv.off, (int64_t)B * H * wp.low_cap * hd, true, (int64_t)H * wp.low_cap * hd,
-                    (int)wp.low_cap, 0};
-    r.pos_add = 0; r.pos_dev = counter; r.pos_mul = C2; r.rope = rope;
-    r.kind = ATT_DECODE; r.Q = C2; r.L_dev = counter; r.L_mul = C2; r.L_add = C2; r.nsplit = wp.nsplit_low;
-    r.L_acct = (int)((c->top_len + 1) * C2);
-    r.out = ws + wp.AA.off; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
-    if ((s = run_stack(c, c->enc1, sa, r, st))) return s;
-    if ((s = gemm_plain(c, PHOTON_K_GEMM_CHUNK, ws + wp.AA.off, (int64_t)C2 * d, c->W_ch2, B, d, C2 * d, sa.x, d, st))) return s;
+    PH_TRY(enqueue_chunk(c, d_logits, st, st));
   }
-  {
-    StackRun r{};
-    r.M = B; r.rows_per_seq = 1; r.G = B;
-    r.kv = KvTarget{ws + wp.top_kv.off, (int64_t)B * H * wp.top_cap * hd, true, (int64_t)H * wp.top_cap * hd,
-                    (int)wp.top_cap, 0};
-    r.pos_add = 0; r.pos_dev = counter; r.pos_mul = 1; r.rope = rope;
-    r.kind = ATT_DECODE; r.Q = 1; r.L_dev = counter; r.L_mul = 1; r.L_add = 1; r.nsplit = wp.nsplit_top;
-    r.L_acct = (int)(c->top_len + 1);
-    r.out = h; r.out_rows = B; r.in_stride = 1; r.in_off = 0;
-    if ((s = run_stack(c, c->top, sa, r, st))) return s;
-  }
-  HIP_TRY(launch_add_int(counter, 1, st));
   HIP_TRY(hipMemcpyAsync(d_tokens, tok, (size_t)B * S * sizeof(int), hipMemcpyDeviceToDevice, st));
   c->top_len += 1;
   c->tokens += S;
@@ -835,6 +970,12 @@ photon_status photon_set_position(photon_ctx* c, int64_t tokens, void* stream) {
   HIP_TRY(launch_set_int((int*)(c->ws + c->plan.counter.off), (int)(tokens / S), (hipStream_t)stream));
   c->tokens = tokens;
   c->top_len = tokens / S;
+  return ok();
+}
+
+photon_status photon_use_graphs(photon_ctx* c, int32_t enable) {
+  if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  c->use_graph = enable != 0;
   return ok();
 }
 

@@ -74,8 +74,8 @@ EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
            "photon_weight_layout", "photon_weight_tensor", "photon_open",
            "photon_release_prefill_weights", "photon_close",
            "photon_last_error", "photon_prefill", "photon_decode_chunk",
-           "photon_position", "photon_set_position", "photon_trace_enable",
-           "photon_trace_read"]
+           "photon_position", "photon_set_position", "photon_use_graphs",
+           "photon_trace_enable", "photon_trace_read"]
 
 
 def _load():
@@ -98,6 +98,7 @@ def _load():
         "photon_decode_chunk": [V, V, V, V],
         "photon_position": [V, P(i64), P(i64)],
         "photon_set_position": [V, i64, V],
+        "photon_use_graphs": [V, i32],
         "photon_trace_enable": [V, ctypes.c_uint32],
         "photon_trace_read": [V, P(TraceStat)],
     }
@@ -242,6 +243,9 @@ class Photon:
         a, b = ctypes.c_int64(), ctypes.c_int64()
         _check(_lib.photon_position(self.ctx, ctypes.byref(a), ctypes.byref(b)))
         return a.value, b.value
+
+    def use_graphs(self, enable=True):
+        _check(_lib.photon_use_graphs(self.ctx, 1 if enable else 0))
 
     def set_position(self, tokens):
         _check(_lib.photon_set_position(self.ctx, tokens, _stream_handle(self.torch)))

@@ -212,6 +212,16 @@ photon_status photon_position(const photon_ctx* ctx, int64_t* top_len,
 photon_status photon_set_position(photon_ctx* ctx, int64_t tokens,
                                   void* stream);
 
+/* Decode chunks run as one captured HIP graph by default: the first
+ * photon_decode_chunk after a prefill captures the chunk (its kernels read
+ * every position from device memory, so the same graph serves every chunk)
+ * and later calls replay it on the caller's stream; with RecGen the top
+ * encoder step and the token decoder run as two parallel branches of the
+ * graph.  Calls that ask for logits, and calls while tracing is on, launch
+ * the same kernels directly on the caller's stream instead.  enable = 0
+ * turns graphs off for this context. */
+photon_status photon_use_graphs(photon_ctx* ctx, int32_t enable);
+
 /* ------------------------------------------------------------------------
  * Tracing: per kernel class, HIP events around every launch of the enabled
  * classes, with the algorithmic bytes and flops of each launch (weights,
@@ -243,7 +253,9 @@ typedef struct {
 } photon_trace_stat;
 
 /* Enable tracing for the classes whose bit (1 << class) is set; 0 turns it
- * off.  Clears previous records. */
+ * off.  Clears previous records.  Traced chunks launch their kernels directly
+ * (no graph); each event pair also holds the event markers' own cost, a few
+ * microseconds, which matters only for the smallest kernels. */
 photon_status photon_trace_enable(photon_ctx* ctx, uint32_t class_mask);
 /* Wait for the recorded events, sum them per class into out[PHOTON_K_COUNT]
  * and clear the records (tracing stays enabled). */
