@@ -167,14 +167,15 @@ class Model:
                 for l in range(n)]
 
     # ---- a Transformer stack with optional per-layer KV cache ----
-    def stack(self, prefix, n_layers, x, pos, cache=None):
+    def stack(self, prefix, n_layers, x, pos, cache=None, log=None):
         """Run a stack of pre-norm blocks then its final RMSNorm.
 
         x: [B, T, d] residual input (float); pos: [T] rotary positions of the
         new rows.  cache: None (no history, nothing kept) or a list with one
         entry per layer, each a dict {"k": [B, n, H, hd], "v": ...} holding
         the rounded K/V of earlier positions; the new K/V are appended in
-        place.  Returns the rounded stack output r(RMSNorm(x; gf)).
+        place.  Returns the rounded stack output r(RMSNorm(x; gf)).  ``log``,
+        if given, is called with a short progress string after each layer.
         """
         cfg, r = self.cfg, self.pr.r
         B, T, d = x.shape
@@ -202,6 +203,8 @@ class Model:
             a = r(rmsnorm(x, L["g2"], eps))
             hmid = r(gelu(linear(a, L["W1"])))
             x = x + linear(hmid, L["W2"])
+            if log:
+                log(f"{prefix} layer {l + 1}/{n_layers} done ({T} rows)")
         return r(rmsnorm(x, self.w[prefix + ".gf"], eps))
 
     def empty_cache(self, n_layers, B):
@@ -257,7 +260,7 @@ class State:
         return State(cp(self.top), self.h.copy(), self.top_len, cp(self.lvl1))
 
 
-def prefill(model, prompt, mode="recgen"):
+def prefill(model, prompt, mode="recgen", log=None):
     """Bottom-up pass over the prompt [modules], [recgen].
 
     tokens -> embedding -> Chunker^1 (C1 tokens -> 1) -> level-1 encoder
@@ -276,11 +279,11 @@ def prefill(model, prompt, mode="recgen"):
     u1 = model.chunker("W_ch1", e)
     n1 = P // cfg.C1
     c1 = model.empty_cache(cfg.n_enc1, B)
-    A1 = model.stack("enc1", cfg.n_enc1, u1, np.arange(n1), c1)
+    A1 = model.stack("enc1", cfg.n_enc1, u1, np.arange(n1), c1, log=log)
     u2 = model.chunker("W_ch2", A1)
     n = P // S
     ct = model.empty_cache(cfg.n_top, B)
-    h = model.stack("top", cfg.n_top, u2, np.arange(n), ct)
+    h = model.stack("top", cfg.n_top, u2, np.arange(n), ct, log=log)
     return State(ct, h[:, -1], n, c1 if mode == "hiergen" else None)
 
 
@@ -370,13 +373,14 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
     return out
 
 
-def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None):
+def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=None):
     """Prefill then new_tokens / S decode chunks.  Returns (tokens [B, N],
-    logits [B, N, V], final state, per-chunk records)."""
+    logits [B, N, V], final state, per-chunk records).  ``log`` receives
+    progress strings (per prefill layer and per decoded chunk)."""
     S = model.cfg.S
     if new_tokens % S:
         raise ValueError("new_tokens must be a multiple of C1*C2")
-    st = prefill(model, prompt, mode)
+    st = prefill(model, prompt, mode, log=log)
     toks, lg, recs = [], [], []
     for c in range(new_tokens // S):
         ft = None if forced_tokens is None else \
@@ -385,6 +389,8 @@ def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None):
         toks.append(o["tokens"])
         lg.append(o["logits"])
         recs.append(o)
+        if log and (c + 1) % 8 == 0:
+            log(f"decoded chunk {c + 1}/{new_tokens // S}")
     return np.concatenate(toks, 1), np.concatenate(lg, 1), st, recs
 
 

@@ -36,11 +36,12 @@ def gpu_generate(cfg, W, prompt, N, mode="recgen", logits=True, rows=None):
     return model, toks_np, lg_np
 
 
-def check_against_oracle(cfg, W, prompt, toks, lg, mode="recgen"):
-    """prompt/toks/lg for the same rows; returns a small report dict."""
+def check_against_oracle(cfg, W, prompt, toks, lg, mode="recgen", log=None):
+    """prompt/toks/lg for the same rows; returns a small report dict.  ``log``
+    passes the oracle's own progress lines through (long runs)."""
     m = O.Model(cfg, W)
     N = toks.shape[1]
-    ot, ol, st, _ = O.generate(m, prompt, N, mode=mode, forced_tokens=toks)
+    ot, ol, st, _ = O.generate(m, prompt, N, mode=mode, forced_tokens=toks, log=log)
     if cfg.dtype == "f32":
         scale = np.maximum(1.0, np.abs(ol).max(-1))
         err = (np.abs(lg - ol).max(-1) / scale).max()
@@ -50,7 +51,7 @@ def check_against_oracle(cfg, W, prompt, toks, lg, mode="recgen"):
         noise = (0.0, 0.0)
     else:
         _, nl, _, _ = O.generate(O.Model(cfg, W, compute="f32"), prompt, N, mode=mode,
-                                 forced_tokens=toks)
+                                 forced_tokens=toks, log=log)
         dev = np.abs(lg - ol)
         nz = np.abs(nl.astype(np.float64) - ol)
         noise = (float(nz.max()), float(nz.mean()))
