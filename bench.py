@@ -12,9 +12,11 @@ used up, so every step runs at the workload's real cache lengths.
 
 Prints one JSON line: decode tok/s (value), TPM = tok/s per GiB of resident
 decode weights + top K/V + decoder K/V + state, the whole path's fraction of
-the HBM roofline (algorithmic bytes per chunk at 8 TB/s), the dominant
-kernel's achieved bandwidth measured with HIP events over the timed region,
-and the CPU oracle timed on a bounded sample of the same workload.
+the HBM roofline (algorithmic bytes per chunk at 8 TB/s), the achieved
+bandwidth of the kernel class that moves the most bytes (HIP events around
+each of its launches, in a traced pass over the same steps right after the
+timed ones), per-class figures, and the CPU oracle timed on a bounded sample
+of the same workload.
 """
 import argparse
 import json
@@ -56,6 +58,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: photon-150m B32 P1024 N256)")
     ap.add_argument("--mode", default="recgen", choices=["recgen", "hiergen"])
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (stress runs)")
+    ap.add_argument("--prompt", type=int, default=None, help="override the workload's prompt length")
+    ap.add_argument("--new-tokens", type=int, default=None, help="override the workload's generated tokens")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path shards by batch "
@@ -70,6 +75,13 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = pi.get(args.workload)
+    if args.batch or args.prompt or args.new_tokens:
+        import dataclasses
+        b = args.batch or wl.batch
+        p = args.prompt or wl.prompt
+        n = args.new_tokens or wl.new_tokens
+        name = wl.name.split(" B")[0] + f" bf16 B{b} P{p} N{n}"
+        wl = dataclasses.replace(wl, name=name + " (override)", batch=b, prompt=p, new_tokens=n)
     cfg = wl.cfg
     K = args.steps if args.steps is not None else wl.chunks
     Wm = args.warmup if args.warmup is not None else wl.chunks
@@ -99,8 +111,10 @@ def main():
     torch.cuda.synchronize()
     per_class = model.trace_read()
     chunk_bytes = sum(v["bytes"] for v in per_class.values()) / wl.chunks
-    dominant = max(per_class, key=lambda k: per_class[k]["ms"])
-    log(f"dominant kernel class: {dominant}")
+    # the kernel class that moves the most algorithmic bytes per step is the
+    # one whose HBM roofline bounds the path
+    dominant = max(per_class, key=lambda k: per_class[k]["bytes"])
+    log(f"dominant kernel class (bytes): {dominant}")
 
     # warmup, then the timed steps: each chunk replays the captured HIP graph
     model.trace_enable([])

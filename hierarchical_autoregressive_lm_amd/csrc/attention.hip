@@ -55,9 +55,38 @@ __device__ __forceinline__ int resolve_len(int L_host, const int* L_dev, int L_m
 }
 
 // ---------------------------------------------------------------- decode
-template <typename T, int HD, int Q, int U>
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnCall a, float scale) {
+// Merge nsplit partial results (num[hd], max, sum) of one (g, h, t) query.
+template <typename T, int HD>
+__device__ __forceinline__ void combine_splits(const AttnCall& a, int g, int h, int t, int e) {
+  const float* pp = a.part + (((int64_t)g * a.H + h) * a.Q + t) * a.nsplit * (HD + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pp[s * (HD + 2) + HD]);
+  float den = 0.f, num = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ms = pp[s * (HD + 2) + HD];
+    if (ms == -INFINITY) continue;
+    const float w = expf(ms - M);
+    den = fmaf(pp[s * (HD + 2) + HD + 1], w, den);
+    num = fmaf(pp[s * (HD + 2) + e], w, num);
+  }
+  T* out = reinterpret_cast<T*>(a.out);
+  out[(int64_t)(g * a.Q + t) * a.out_ld + h * HD + e] = St<T>::st(num / den);
+}
+
+// Second pass when the keys were split: one wave per (g, h, t).  (Merging in
+// the last-arriving split instead would need agent-scope fences, which write
+// back and invalidate the L2 and cost far more than this launch.)
+template <typename T, int HD>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnCall a) {
+  const int idx = blockIdx.x;
+  const int t = idx % a.Q, h = (idx / a.Q) % a.H, g = idx / (a.Q * a.H);
+  for (int e = threadIdx.x; e < HD; e += 64) combine_splits<T, HD>(a, g, h, t, e);
+}
+
+template <typename T, int HD, int Q, int U, int SLOTS = 16>
+__global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, float scale) {
   constexpr int CE = HD / 16;
+  constexpr int NT = SLOTS * 16;
   const int tid = threadIdx.x;
   const int c = tid & 15, r = tid >> 4;
   const int nsplit = a.nsplit;
@@ -88,20 +117,24 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnCall a, float scal
     for (int e = 0; e < CE; ++e) o[t][e] = 0.f;
   }
 
-  for (int kb = k0; kb < k1; kb += 16 * U) {
+  // Row slot r visits keys k0 + r, k0 + r + SLOTS, ...; U of them per
+  // iteration, loaded together and folded into the slot's online softmax
+  // with a single rescale.
+  for (int kb = k0; kb < k1; kb += SLOTS * U) {
     float kv[U][CE], vv[U][CE];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int key = kb + r + 16 * u;
+      int key = kb + r + SLOTS * u;
       key = key < k1 ? key : k1 - 1;       // in-bounds; masked below
       Chunk<T, CE>::load(Kb + (int64_t)key * HD, kv[u]);
       Chunk<T, CE>::load(Vb + (int64_t)key * HD, vv[u]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int key = kb + r + 16 * u;
+    for (int t = 0; t < Q; ++t) {
+      float sc[U];
+      float mx = m[t];
 #pragma unroll
-      for (int t = 0; t < Q; ++t) {
+      for (int u = 0; u < U; ++u) {
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < CE; ++e) s = fmaf(qv[t][e], kv[u][e], s);
@@ -109,23 +142,30 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnCall a, float scal
         s += __shfl_xor(s, 4, 64);
         s += __shfl_xor(s, 2, 64);
         s += __shfl_xor(s, 1, 64);
-        const bool ok = key < k1 && key <= L - Q + t;
-        if (ok) {
-          const float mn = fmaxf(m[t], s);
-          const float corr = expf(m[t] - mn);
-          const float pr = expf(s - mn);
-          l[t] = l[t] * corr + pr;
-#pragma unroll
-          for (int e = 0; e < CE; ++e) o[t][e] = fmaf(pr, vv[u][e], o[t][e] * corr);
-          m[t] = mn;
-        }
+        const int key = kb + r + SLOTS * u;
+        sc[u] = (key < k1 && key <= L - Q + t) ? s : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
       }
+      if (mx == -INFINITY) continue;       // nothing visible yet (uniform per slot)
+      const float corr = expf(m[t] - mx);
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) o[t][e] *= corr;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = expf(sc[u] - mx);
+        ps += p;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) o[t][e] = fmaf(p, vv[u][e], o[t][e]);
+      }
+      l[t] = l[t] * corr + ps;
+      m[t] = mx;
     }
   }
 
-  // merge the 16 row slots
-  __shared__ float sm[16][Q], sl[16][Q];
-  __shared__ float so[16][Q][HD];
+  // merge the row slots
+  __shared__ float sm[SLOTS][Q], sl[SLOTS][Q];
+  __shared__ float so[SLOTS][Q][HD];
 #pragma unroll
   for (int t = 0; t < Q; ++t) {
     if (c == 0) { sm[r][t] = m[t]; sl[r][t] = l[t]; }
@@ -133,15 +173,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnCall a, float scal
     for (int e = 0; e < CE; ++e) so[r][t][c * CE + e] = o[t][e];
   }
   __syncthreads();
-  for (int idx = tid; idx < Q * HD; idx += 256) {
+  for (int idx = tid; idx < Q * HD; idx += NT) {
     const int t = idx / HD, e = idx % HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) M = fmaxf(M, sm[s][t]);
+    for (int s = 0; s < SLOTS; ++s) M = fmaxf(M, sm[s][t]);
     float den = 0.f, num = 0.f;
     if (M != -INFINITY) {
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
+#pragma unroll 16
+      for (int s = 0; s < SLOTS; ++s) {
         const float w = expf(sm[s][t] - M);
         den = fmaf(sl[s][t], w, den);
         num = fmaf(so[s][t][e], w, num);
@@ -155,30 +195,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnCall a, float scal
       pp[e] = num;
       if (e == 0) { pp[HD] = M; pp[HD + 1] = den; }
     }
-  }
-}
-
-template <typename T, int HD>
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnCall a) {
-  // one wave per (g, h, t)
-  const int idx = blockIdx.x;
-  const int t = idx % a.Q;
-  const int h = (idx / a.Q) % a.H;
-  const int g = idx / (a.Q * a.H);
-  const float* pp = a.part + (((int64_t)g * a.H + h) * a.Q + t) * a.nsplit * (HD + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pp[s * (HD + 2) + HD]);
-  T* out = reinterpret_cast<T*>(a.out);
-  for (int e = threadIdx.x; e < HD; e += 64) {
-    float den = 0.f, num = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = pp[s * (HD + 2) + HD];
-      if (ms == -INFINITY) continue;
-      const float w = expf(ms - M);
-      den = fmaf(pp[s * (HD + 2) + HD + 1], w, den);
-      num = fmaf(pp[s * (HD + 2) + e], w, num);
-    }
-    out[(int64_t)(g * a.Q + t) * a.out_ld + h * HD + e] = St<T>::st(num / den);
   }
 }
 
@@ -330,9 +346,16 @@ hipError_t decode_hd(const AttnCall& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)HD);
   dim3 grid(a.G * a.H * a.nsplit), block(256);
   switch (a.Q) {
-    case 1: attn_decode_kernel<T, HD, 1, 4><<<grid, block, 0, st>>>(a, scale); break;
+    case 1:
+      // fewer (sequence, head) pairs: wider workgroups keep enough keys in
+      // flight per CU (32 row slots x 4 keys); many pairs: 16 slots x 8 keys
+      if (a.G * a.H * a.nsplit < 1024)
+        attn_decode_kernel<T, HD, 1, 4, 32><<<grid, dim3(512), 0, st>>>(a, scale);
+      else
+        attn_decode_kernel<T, HD, 1, 8><<<grid, block, 0, st>>>(a, scale);
+      break;
     case 2: attn_decode_kernel<T, HD, 2, 4><<<grid, block, 0, st>>>(a, scale); break;
-    case 4: attn_decode_kernel<T, HD, 4, 2><<<grid, block, 0, st>>>(a, scale); break;
+    case 4: attn_decode_kernel<T, HD, 4, 4><<<grid, block, 0, st>>>(a, scale); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -394,12 +417,22 @@ hipError_t dispatch_prefill(const AttnCall& a, hipStream_t st) {
 
 }  // namespace
 
-int attn_decode_splits(int G, int H, int cap) {
-  // aim for ~2048 workgroups with at least 256 keys per split (a short cache
-  // is one split: no combine launch)
+int attn_decode_splits(int G, int H, int cap, int Q) {
   const int pairs = G * H;
-  int ns = (2048 + pairs - 1) / pairs;
-  const int max_ns = (cap + 255) / 256;
+  if (Q == 1) {
+    // one workgroup per (sequence, head) streams its whole cache once there
+    // are enough pairs to fill the chip (measured: no split beats split +
+    // combine from 256 pairs up); below that, split to ~256 workgroups
+    if (pairs >= 128) return 1;
+    int ns = (256 + pairs - 1) / pairs;
+    const int max_ns = (cap + 255) / 256;
+    return ns < 1 ? 1 : (ns > max_ns ? (max_ns < 1 ? 1 : max_ns) : ns);
+  }
+  // several queries per sequence (HierGen level-1 step): one round of
+  // resident workgroups (~5 per CU), splits of at least 128 keys
+  const int resident = 256 * 5;
+  int ns = (resident + pairs / 2) / pairs;
+  const int max_ns = (cap + 127) / 128;
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
   return ns;

@@ -187,6 +187,10 @@ __global__ void rope_table_kernel(float* tab, int max_pos, int hd, double theta)
 }
 
 __global__ void set_int_kernel(int* p, int v) { *p = v; }
+__global__ void zero_ints_kernel(int* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 __global__ void add_int_kernel(int* p, int v) { *p += v; }
 
 inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -234,6 +238,12 @@ hipError_t launch_rope_table(float* tab, int max_pos, int hd, float theta, hipSt
 
 hipError_t launch_set_int(int* p, int v, hipStream_t st) {
   set_int_kernel<<<1, 1, 0, st>>>(p, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  zero_ints_kernel<<<blocks(n), 256, 0, st>>>(p, n);
   return hipGetLastError();
 }
 

@@ -108,10 +108,13 @@ hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st);
 hipError_t launch_rope_table(float* tab, int max_pos, int hd, float theta,
                              hipStream_t st);
 hipError_t launch_set_int(int* p, int v, hipStream_t st);
+// p[0 .. n) = 0 with a kernel (also safe inside captured graphs).
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st);
 hipError_t launch_add_int(int* p, int v, hipStream_t st);
 
-// Number of key splits the decode attention uses for G*H pairs over a cache
-// of `cap` slots (plan-time, so one plan serves every length <= cap).
-int attn_decode_splits(int G, int H, int cap);
+// Number of key splits the decode attention uses for G*H pairs with Q
+// queries each over a cache of `cap` slots (plan-time, so one plan serves
+// every length <= cap).
+int attn_decode_splits(int G, int H, int cap, int Q);
 
 }  // namespace photon

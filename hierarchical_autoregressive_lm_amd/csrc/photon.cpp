@@ -176,8 +176,8 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.top_cap = cdiv(tokens, S);
   p.low_cap = hier ? cdiv(tokens, C1) : 0;
   p.rope_pos = std::max<int64_t>({p.top_cap, p.low_cap, C1, C2});
-  p.nsplit_top = attn_decode_splits((int)B, (int)H, (int)p.top_cap);
-  p.nsplit_low = hier ? attn_decode_splits((int)B, (int)H, (int)p.low_cap) : 1;
+  p.nsplit_top = attn_decode_splits((int)B, (int)H, (int)p.top_cap, 1);
+  p.nsplit_low = hier ? attn_decode_splits((int)B, (int)H, (int)p.low_cap, (int)C2) : 1;
   p.head_tiles = gemm_argmax_tiles(dt, (int)(B * C2), (int)V, (int)d);
   Cursor cur;
   p.top_kv = cur.take((uint64_t)c->n_top * 2 * B * H * p.top_cap * hd * eb);
