@@ -2,14 +2,19 @@
 //
 //  * attn_decode: the top encoder's step over the global coarse K/V cache
 //    (and HierGen's level-1 step).  Memory-bound: every byte of K and V is
-//    streamed once.  One workgroup per (sequence, head, key split); the 256
-//    threads form 16 row slots x 16 lanes, each lane owning hd/16 contiguous
+//    streamed once, with non-temporal loads (the cache is read once per
+//    step; keeping it out of the caches leaves them to the weights and
+//    activations).  One workgroup per (sequence, head, key split); the
+//    threads form row slots of 16 lanes, each lane owning hd/16 contiguous
 //    elements, so a wave reads 4 consecutive cache rows per instruction
 //    (contiguous bytes).  Each row slot keeps its own online-softmax state
-//    (max, sum, partial output) over the keys it visits; the 16 slots are
+//    (max, sum, partial output) over the keys it visits; the slots are
 //    merged through LDS at the end, and the splits by a combine kernel.
 //  * attn_chunk: the decoders' attention confined to the chunk (at most a
-//    few keys per query); one wave per (sequence, head).
+//    few keys per query).  16 lanes per (sequence, head) pair hold every key
+//    of the pair for hd/16 contiguous elements (non-temporal loads), so
+//    scores need one 16-lane reduction and the output is lane-local; 4 pairs
+//    per wave.
 //  * attn_prefill: causal attention over a whole prompt, fp32 FMA, 64
 //    queries per workgroup with K/V tiles of 64 keys staged in LDS.
 // q is fp32 everywhere; K and V are read in the storage dtype; softmax and
@@ -20,33 +25,27 @@
 namespace photon {
 namespace {
 
-template <typename T, int CE> struct Chunk;
-template <int CE> struct Chunk<bf16_t, CE> {
-  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[CE]) {
-    if constexpr (CE == 2) {
-      uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-      v[0] = __uint_as_float(w << 16); v[1] = __uint_as_float(w & 0xffff0000u);
-    } else if constexpr (CE == 4) {
-      uint2 w = *reinterpret_cast<const uint2*>(p);
-      v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-      v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-    } else if constexpr (CE == 6) {
-      uint32_t w0 = reinterpret_cast<const uint32_t*>(p)[0];
-      uint32_t w1 = reinterpret_cast<const uint32_t*>(p)[1];
-      uint32_t w2 = reinterpret_cast<const uint32_t*>(p)[2];
-      v[0] = __uint_as_float(w0 << 16); v[1] = __uint_as_float(w0 & 0xffff0000u);
-      v[2] = __uint_as_float(w1 << 16); v[3] = __uint_as_float(w1 & 0xffff0000u);
-      v[4] = __uint_as_float(w2 << 16); v[5] = __uint_as_float(w2 & 0xffff0000u);
+// One cache row segment of CE elements held as raw dwords (bf16 pairs or
+// fp32), loaded with plain or non-temporal loads and widened on use.
+template <typename T, int CE, bool NT> struct Raw {
+  static constexpr int W = CE * (int)sizeof(T) / 4;
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const T* p) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = NT ? __builtin_nontemporal_load(q + i) : q[i];
+  }
+  __device__ __forceinline__ void unpack(float (&v)[CE]) const {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < CE; ++e) v[e] = bf2f(p[e]);
+      for (int i = 0; i < W; ++i) v[i] = __uint_as_float(w[i]);
     }
-  }
-};
-template <int CE> struct Chunk<float, CE> {
-  static __device__ __forceinline__ void load(const float* p, float (&v)[CE]) {
-#pragma unroll
-    for (int e = 0; e < CE; ++e) v[e] = p[e];
   }
 };
 
@@ -121,14 +120,17 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
   // iteration, loaded together and folded into the slot's online softmax
   // with a single rescale.
   for (int kb = k0; kb < k1; kb += SLOTS * U) {
-    float kv[U][CE], vv[U][CE];
+    Raw<T, CE, true> kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int key = kb + r + SLOTS * u;
       key = key < k1 ? key : k1 - 1;       // in-bounds; masked below
-      Chunk<T, CE>::load(Kb + (int64_t)key * HD, kv[u]);
-      Chunk<T, CE>::load(Vb + (int64_t)key * HD, vv[u]);
+      kr[u].load(Kb + (int64_t)key * HD);
+      vr[u].load(Vb + (int64_t)key * HD);
     }
+    float kv[U][CE], vv[U][CE];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { kr[u].unpack(kv[u]); vr[u].unpack(vv[u]); }
 #pragma unroll
     for (int t = 0; t < Q; ++t) {
       float sc[U];
@@ -199,34 +201,39 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
 }
 
 // ----------------------------------------------------------------- chunk
+// Lanes 16*sub .. 16*sub+15 of a wave own pair 4*wave + sub; lane c holds
+// elements [c*hd/16, (c+1)*hd/16) of every key of the pair.
 template <typename T, int HD, int MAXL>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnCall a, float scale) {
-  constexpr int EP = (HD + 63) / 64;       // elements per lane
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.G * a.H) return;            // whole wave exits together
+  constexpr int CE = HD / 16;
+  using R = Raw<T, CE, true>;
+  const int lane = threadIdx.x & 63, c = lane & 15, sub = lane >> 4;
+  const int pair = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + sub;
+  if (pair >= a.G * a.H) return;            // whole 16-lane groups exit together
   const int h = pair % a.H, g = pair / a.H;
   const int L = resolve_len(a.L_host, a.L_dev, a.L_mul, a.L_add);
-  const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
-  const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
-  float kv[MAXL][EP], vv[MAXL][EP];
+  const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
+  const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
+  R kr[MAXL], vr[MAXL];
 #pragma unroll
-  for (int j = 0; j < MAXL; ++j)
+  for (int j = 0; j < MAXL; ++j) {
+    if (j < L) {
+      kr[j].load(Kb + j * HD);
+      vr[j].load(Vb + j * HD);
+    } else {
 #pragma unroll
-    for (int x = 0; x < EP; ++x) {
-      const int e = lane + 64 * x;
-      const bool ok = j < L && e < HD;
-      kv[j][x] = ok ? St<T>::ld(Kb[j * HD + e]) : 0.f;
-      vv[j][x] = ok ? St<T>::ld(Vb[j * HD + e]) : 0.f;
+      for (int w = 0; w < R::W; ++w) { kr[j].w[w] = 0u; vr[j].w[w] = 0u; }
     }
+  }
+  float kv[MAXL][CE], vv[MAXL][CE];
+#pragma unroll
+  for (int j = 0; j < MAXL; ++j) { kr[j].unpack(kv[j]); vr[j].unpack(vv[j]); }
   T* out = reinterpret_cast<T*>(a.out);
   for (int t = 0; t < a.Q; ++t) {
-    float q[EP];
+    const float* qp = a.q + (int64_t)(g * a.Q + t) * a.q_ld + h * HD + c * CE;
+    float q[CE];
 #pragma unroll
-    for (int x = 0; x < EP; ++x) {
-      const int e = lane + 64 * x;
-      q[x] = e < HD ? a.q[(int64_t)(g * a.Q + t) * a.q_ld + h * HD + e] * scale : 0.f;
-    }
+    for (int e = 0; e < CE; ++e) q[e] = qp[e] * scale;
     const int last = L - a.Q + t;           // last visible key
     float s[MAXL];
     float mx = -INFINITY;
@@ -234,28 +241,29 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnCall a, float scale
     for (int j = 0; j < MAXL; ++j) {
       float d = 0.f;
 #pragma unroll
-      for (int x = 0; x < EP; ++x) d = fmaf(q[x], kv[j][x], d);
-      d = wave_sum(d);
+      for (int e = 0; e < CE; ++e) d = fmaf(q[e], kv[j][e], d);
+      d += __shfl_xor(d, 8, 64);
+      d += __shfl_xor(d, 4, 64);
+      d += __shfl_xor(d, 2, 64);
+      d += __shfl_xor(d, 1, 64);
       s[j] = d;
       if (j <= last) mx = fmaxf(mx, d);
     }
-    float den = 0.f, num[EP];
+    float den = 0.f, num[CE];
 #pragma unroll
-    for (int x = 0; x < EP; ++x) num[x] = 0.f;
+    for (int e = 0; e < CE; ++e) num[e] = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXL; ++j) {
       if (j <= last) {
-        const float pr = expf(s[j] - mx);
-        den += pr;
+        const float p = expf(s[j] - mx);
+        den += p;
 #pragma unroll
-        for (int x = 0; x < EP; ++x) num[x] = fmaf(pr, vv[j][x], num[x]);
+        for (int e = 0; e < CE; ++e) num[e] = fmaf(p, vv[j][e], num[e]);
       }
     }
+    T* op = out + (int64_t)(g * a.Q + t) * a.out_ld + h * HD + c * CE;
 #pragma unroll
-    for (int x = 0; x < EP; ++x) {
-      const int e = lane + 64 * x;
-      if (e < HD) out[(int64_t)(g * a.Q + t) * a.out_ld + h * HD + e] = St<T>::st(num[x] / den);
-    }
+    for (int e = 0; e < CE; ++e) op[e] = St<T>::st(num[e] / den);
   }
 }
 
@@ -347,12 +355,13 @@ hipError_t decode_hd(const AttnCall& a, hipStream_t st) {
   dim3 grid(a.G * a.H * a.nsplit), block(256);
   switch (a.Q) {
     case 1:
-      // fewer (sequence, head) pairs: wider workgroups keep enough keys in
-      // flight per CU (32 row slots x 4 keys); many pairs: 16 slots x 8 keys
-      if (a.G * a.H * a.nsplit < 1024)
-        attn_decode_kernel<T, HD, 1, 4, 32><<<grid, dim3(512), 0, st>>>(a, scale);
+      // long caches: 32 row slots x 8 keys in flight per workgroup; short
+      // ones: 16 slots x 6 keys, so that the last pass over the keys is not
+      // nearly empty and more workgroups share the chip
+      if (a.cap >= 1024)
+        attn_decode_kernel<T, HD, 1, 8, 32><<<grid, dim3(512), 0, st>>>(a, scale);
       else
-        attn_decode_kernel<T, HD, 1, 8><<<grid, block, 0, st>>>(a, scale);
+        attn_decode_kernel<T, HD, 1, 6><<<grid, block, 0, st>>>(a, scale);
       break;
     case 2: attn_decode_kernel<T, HD, 2, 4><<<grid, block, 0, st>>>(a, scale); break;
     case 4: attn_decode_kernel<T, HD, 4, 4><<<grid, block, 0, st>>>(a, scale); break;
@@ -367,7 +376,7 @@ hipError_t decode_hd(const AttnCall& a, hipStream_t st) {
 template <typename T, int HD>
 hipError_t chunk_hd(const AttnCall& a, hipStream_t st, int maxl) {
   const float scale = 1.0f / sqrtf((float)HD);
-  dim3 grid((a.G * a.H + 3) / 4), block(256);
+  dim3 grid((a.G * a.H + 15) / 16), block(256);
   if (maxl <= 2) attn_chunk_kernel<T, HD, 2><<<grid, block, 0, st>>>(a, scale);
   else if (maxl <= 4) attn_chunk_kernel<T, HD, 4><<<grid, block, 0, st>>>(a, scale);
   else if (maxl <= 8) attn_chunk_kernel<T, HD, 8><<<grid, block, 0, st>>>(a, scale);
