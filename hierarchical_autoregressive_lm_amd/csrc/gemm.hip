@@ -32,7 +32,7 @@ struct GemmP {
   int ksplit; int64_t pstride;   // k slabs; elements between RAW slabs
 };
 
-template <int MB, int NI, int WK, int EPI>
+template <int MB, int NI, int WK, int P, int EPI, int NKB, bool NTW>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
   constexpr int WN = 4 / WK;
   constexpr int BM = 16 * MB;
@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
   constexpr int RED = (WK > 1) ? (WK - 1) * WN * MB * NI * 4 * 64 : 0;
   constexpr int BYTES_A = 2 * A_ELEMS * 2;
   constexpr int BYTES = BYTES_A > RED * 4 ? BYTES_A : RED * 4;
+  static_assert(P >= 2, "at least one k-block in flight");
   __shared__ __attribute__((aligned(16))) unsigned char smem[BYTES];
   bf16_t* As = reinterpret_cast<bf16_t*>(smem);
 
@@ -76,69 +77,83 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  uint4 areg[CH];
-  auto load_a = [&](int kb) {
+  // Ring of P k-blocks: the A rows (global -> registers -> LDS, double
+  // buffered in LDS) and this wave's W fragments (global -> registers).
+  // k-block k lives in ring slot k % P; while block k is multiplied, the
+  // loads of blocks k+1 .. k+P-1 are in flight.
+  uint4 areg[P][CH];
+  bf16x8 wreg[P][2][NI];
+  auto load_a = [&](int kb, uint4 (&ar)[CH]) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + i * 256;
       const int r = c / (KT / 8), c8 = c % (KT / 8);
       const int gm = m0 + r;
       if (c < CHUNKS && gm < M)
-        areg[i] = *reinterpret_cast<const uint4*>(p.A + (int64_t)gm * p.lda + (int64_t)kb * KT + c8 * 8);
+        ar[i] = *reinterpret_cast<const uint4*>(p.A + (int64_t)gm * p.lda + (int64_t)kb * KT + c8 * 8);
       else
-        areg[i] = make_uint4(0, 0, 0, 0);
+        ar[i] = make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](const uint4 (&ar)[CH], int buf) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + i * 256;
       const int r = c / (KT / 8), c8 = c % (KT / 8);
-      if (c < CHUNKS) *reinterpret_cast<uint4*>(As + buf * A_ELEMS + r * ROW + c8 * 8) = areg[i];
+      if (c < CHUNKS) *reinterpret_cast<uint4*>(As + buf * A_ELEMS + r * ROW + c8 * 8) = ar[i];
     }
   };
-  bf16x8 wcur[2][NI], wnxt[2][NI];
   auto load_w = [&](int kb, bf16x8 (&w)[2][NI]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        w[u][ni] = *reinterpret_cast<const bf16x8*>(wp[ni] + (int64_t)kb * KT + u * 32);
+      for (int ni = 0; ni < NI; ++ni) {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(wp[ni] + (int64_t)kb * KT + u * 32);
+        w[u][ni] = NTW ? __builtin_nontemporal_load(src) : *src;
+      }
   };
 
-  // this workgroup's k slab: k-blocks [kb0, kb0 + nkb)
-  const int nkb = K / KT / p.ksplit;
+  // this workgroup's k slab: k-blocks [kb0, kb0 + nkb).  With NKB > 0 the
+  // count is a compile-time constant and the loop below unrolls fully, which
+  // lets the compiler wait for exactly the ring slot it needs (across a
+  // loop back-edge it would wait for every load in flight).
+  const int nkb = NKB > 0 ? NKB : K / KT / p.ksplit;
   const int kb0 = ks * nkb;
-  load_a(kb0);
-  load_w(kb0, wcur);
-  store_a(0);
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s)
+    if (s < nkb) {
+      load_a(kb0 + s, areg[s]);
+      load_w(kb0 + s, wreg[s]);
+    }
+  store_a(areg[0], 0);
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      load_a(kb0 + kb + 1);
-      load_w(kb0 + kb + 1, wnxt);
-    }
+#pragma unroll(NKB > 0 ? NKB : 1)
+  for (int kb = 0; kb < nkb; kb += P) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = wk * 64 + u * 32 + kl;
+    for (int s = 0; s < P; ++s) {
+      const int k = kb + s;
+      if (k < nkb) {
+        const int sp = (s + P - 1) % P;     // slot of block k + P - 1 (freed by block k - 1)
+        if (k + P - 1 < nkb) {
+          load_a(kb0 + k + P - 1, areg[sp]);
+          load_w(kb0 + k + P - 1, wreg[sp]);
+        }
+        const int buf = k & 1;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            As + buf * A_ELEMS + (mb * 16 + (lane & 15)) * ROW + kk);
+        for (int u = 0; u < 2; ++u) {
+          const int kk = wk * 64 + u * 32 + kl;
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mb][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[u][ni], a, acc[mb][ni], 0, 0, 0);
+          for (int mb = 0; mb < MB; ++mb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                As + buf * A_ELEMS + (mb * 16 + (lane & 15)) * ROW + kk);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              acc[mb][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wreg[s][u][ni], a, acc[mb][ni], 0, 0, 0);
+          }
+        }
+        if (k + 1 < nkb) store_a(areg[(s + 1) % P], buf ^ 1);
+        __syncthreads();
       }
-    }
-    if (more) store_a(buf ^ 1);
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) wcur[u][ni] = wnxt[u][ni];
     }
   }
 
@@ -288,9 +303,82 @@ __global__ __launch_bounds__(64) void gemm_f32_kernel(GemmPF p) {
   }
 }
 
+typedef void (*GemmKernel)(GemmP);
+
 struct Plan {
   int MB, NI, WK, m_tiles, n_tiles, ksplit;
+  GemmKernel fn;   // tuned instantiation (fully unrolled k loop), or null
 };
+
+// Tuned tiles for the decode GEMMs of the PHOTON model shapes (d = 768 and
+// 1536, MLP 4d, vocab 32000, rows B or B*C2 from 16 to 512), measured on
+// MI355X with the weights streamed from HBM (weights rotated past the
+// Infinity Cache between launches).  Fields: M, N, K, epilogue, whether the
+// entry splits K into slabs (usable only by callers that sum slabs), then
+// MB, NI, WK, ring depth P, K slabs, k-blocks per workgroup, non-temporal W.
+// Most winners run ~192-250 workgroups, about one per CU.
+#define PHOTON_GEMM_TUNED(X) \
+  X(16, 1536, 1536, EPI_STORE, 1, 1, 1, 1, 3, 8, 3, true) \
+  X(16, 1536, 6144, EPI_STORE, 1, 1, 2, 4, 4, 4, 6, false) \
+  X(16, 4608, 1536, EPI_STORE, 1, 1, 1, 1, 4, 6, 4, false) \
+  X(16, 6144, 1536, EPI_GELU, 0, 1, 1, 2, 4, 1, 12, true) \
+  X(16, 6144, 1536, EPI_STORE, 1, 1, 1, 2, 4, 4, 3, false) \
+  X(32, 768, 768, EPI_STORE, 1, 1, 1, 2, 3, 2, 3, true) \
+  X(32, 768, 3072, EPI_STORE, 1, 2, 1, 2, 4, 8, 3, true) \
+  X(32, 2304, 768, EPI_STORE, 1, 2, 1, 1, 3, 6, 2, true) \
+  X(32, 3072, 768, EPI_GELU, 0, 1, 1, 2, 4, 1, 6, true) \
+  X(32, 3072, 768, EPI_STORE, 1, 2, 1, 2, 4, 2, 3, true) \
+  X(64, 1536, 1536, EPI_STORE, 1, 4, 1, 1, 4, 8, 3, true) \
+  X(64, 1536, 6144, EPI_STORE, 1, 4, 2, 2, 4, 8, 6, true) \
+  X(64, 4608, 1536, EPI_STORE, 1, 4, 2, 2, 4, 3, 4, true) \
+  X(64, 6144, 1536, EPI_GELU, 0, 2, 2, 2, 4, 1, 12, false) \
+  X(64, 6144, 1536, EPI_STORE, 1, 4, 2, 1, 4, 4, 6, false) \
+  X(64, 6144, 1536, EPI_STORE, 0, 2, 2, 2, 4, 1, 12, false) \
+  X(64, 32000, 1536, EPI_ARGMAX, 0, 4, 2, 1, 4, 1, 24, false) \
+  X(128, 768, 768, EPI_STORE, 1, 2, 1, 2, 3, 2, 3, true) \
+  X(128, 768, 3072, EPI_STORE, 1, 4, 1, 1, 4, 8, 6, true) \
+  X(128, 2304, 768, EPI_STORE, 1, 4, 1, 2, 3, 3, 2, true) \
+  X(128, 3072, 768, EPI_GELU, 0, 2, 1, 1, 4, 1, 12, true) \
+  X(128, 3072, 768, EPI_STORE, 1, 4, 1, 1, 4, 2, 6, true) \
+  X(128, 3072, 768, EPI_STORE, 0, 2, 1, 1, 4, 1, 12, true) \
+  X(128, 32000, 768, EPI_ARGMAX, 0, 8, 2, 1, 4, 1, 12, false) \
+  X(256, 1536, 1536, EPI_STORE, 1, 4, 1, 1, 4, 2, 12, true) \
+  X(256, 1536, 3072, EPI_STORE, 1, 8, 2, 1, 4, 8, 6, true) \
+  X(256, 1536, 6144, EPI_STORE, 1, 8, 2, 1, 4, 8, 12, false) \
+  X(256, 3072, 1536, EPI_STORE, 1, 4, 2, 1, 4, 2, 12, false) \
+  X(256, 4608, 1536, EPI_STORE, 1, 8, 2, 1, 4, 3, 8, false) \
+  X(256, 6144, 1536, EPI_GELU, 0, 4, 2, 1, 4, 1, 24, false) \
+  X(256, 6144, 1536, EPI_STORE, 1, 8, 2, 1, 4, 2, 12, false) \
+  X(256, 6144, 1536, EPI_STORE, 0, 4, 2, 1, 4, 1, 24, false) \
+  X(256, 32000, 1536, EPI_ARGMAX, 0, 8, 4, 1, 3, 1, 24, false) \
+  X(512, 1536, 1536, EPI_STORE, 1, 4, 2, 2, 4, 1, 12, true) \
+  X(512, 1536, 3072, EPI_STORE, 1, 8, 2, 1, 4, 4, 12, false) \
+  X(512, 1536, 6144, EPI_STORE, 1, 8, 2, 1, 4, 4, 24, false) \
+  X(512, 3072, 1536, EPI_STORE, 1, 8, 2, 1, 4, 2, 12, true) \
+  X(512, 3072, 1536, EPI_STORE, 0, 8, 2, 2, 4, 1, 12, true) \
+  X(512, 4608, 1536, EPI_STORE, 1, 8, 4, 1, 3, 3, 8, false) \
+  X(512, 6144, 1536, EPI_GELU, 0, 8, 2, 1, 4, 1, 24, false) \
+  X(512, 32000, 1536, EPI_ARGMAX, 0, 8, 2, 1, 4, 1, 24, false)
+
+struct Tuned {
+  int M, N, K, epi, split, MB, NI, WK, P, ks, nkb;
+  bool ntw;
+  GemmKernel fn;
+};
+#define PHOTON_TUNED_ENTRY(M_, N_, K_, E_, S_, MB_, NI_, WK_, P_, KS_, NKB_, NT_) \
+  {M_, N_, K_, E_, S_, MB_, NI_, WK_, P_, KS_, NKB_, NT_, gemm_bf16_kernel<MB_, NI_, WK_, P_, E_, NKB_, NT_>},
+const Tuned kTuned[] = {PHOTON_GEMM_TUNED(PHOTON_TUNED_ENTRY)};
+#undef PHOTON_TUNED_ENTRY
+
+const Tuned* find_tuned(int M, int N, int K, int epi, bool allow_split) {
+  const Tuned* hit = nullptr;
+  for (const Tuned& t : kTuned) {
+    if (t.M != M || t.N != N || t.K != K || t.epi != epi) continue;
+    if (t.split && !allow_split) continue;
+    if (!hit || (t.split && !hit->split)) hit = &t;   // slabs when the caller takes them
+  }
+  return hit;
+}
 
 // Waves along K: as many as the LDS budget of the M tile allows (4 for
 // M tiles up to 64 rows, 2 for 128, 1 for 256) and K divides into.
@@ -300,11 +388,17 @@ int wk_of(int MB, int K) {
   return wk;
 }
 
-// Tile plan.  Decode GEMMs are skinny (M = B or B*C2 rows) and their cost is
-// streaming W once, so the plan looks for enough workgroups to keep every CU
-// streaming: the widest column tile that still gives >= 256 workgroups, and
-// otherwise a split of K into slabs (RAW partials, summed by the consumer).
-Plan plan_bf16(int M, int N, int K, bool allow_split) {
+// Tile plan.  Shapes in the tuned table take their measured tile; any other
+// shape (prefill, other model sizes) gets a general plan: decode GEMMs are
+// skinny (M = B or B*C2 rows) and their cost is streaming W once, so the
+// plan looks for enough workgroups to keep every CU streaming: the widest
+// column tile that still gives >= 256 workgroups, and otherwise a split of
+// K into slabs (RAW partials, summed by the consumer).
+Plan plan_bf16(int M, int N, int K, int epi, bool allow_split) {
+  if (const Tuned* t = find_tuned(M, N, K, epi, allow_split)) {
+    const int BM = 16 * t->MB, BN = 16 * t->NI * (4 / t->WK);
+    return Plan{t->MB, t->NI, t->WK, (M + BM - 1) / BM, (N + BN - 1) / BN, t->ks, t->fn};
+  }
   Plan best{};
   const int MB0 = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 128 ? 8 : 16;
   const int target = 256;
@@ -333,7 +427,7 @@ Plan plan_bf16(int M, int N, int K, bool allow_split) {
                                  : wgs * 64 + ni;
           if (score > best_score) {
             best_score = score;
-            best = Plan{MB, ni, wk, m_tiles, n_tiles, ks};
+            best = Plan{MB, ni, wk, m_tiles, n_tiles, ks, nullptr};
           }
           if (wgs >= target) break;   // more slabs only add partial traffic
         }
@@ -347,10 +441,10 @@ template <int MB, int NI, int WK>
 hipError_t run_bf16(const GemmP& p, int epi, hipStream_t st) {
   dim3 grid(p.m_tiles * p.n_tiles * p.ksplit), block(256);
   switch (epi) {
-    case EPI_STORE: gemm_bf16_kernel<MB, NI, WK, EPI_STORE><<<grid, block, 0, st>>>(p); break;
-    case EPI_ADD: gemm_bf16_kernel<MB, NI, WK, EPI_ADD><<<grid, block, 0, st>>>(p); break;
-    case EPI_GELU: gemm_bf16_kernel<MB, NI, WK, EPI_GELU><<<grid, block, 0, st>>>(p); break;
-    default: gemm_bf16_kernel<MB, NI, WK, EPI_ARGMAX><<<grid, block, 0, st>>>(p); break;
+    case EPI_STORE: gemm_bf16_kernel<MB, NI, WK, 2, EPI_STORE, 0, false><<<grid, block, 0, st>>>(p); break;
+    case EPI_ADD: gemm_bf16_kernel<MB, NI, WK, 2, EPI_ADD, 0, false><<<grid, block, 0, st>>>(p); break;
+    case EPI_GELU: gemm_bf16_kernel<MB, NI, WK, 2, EPI_GELU, 0, false><<<grid, block, 0, st>>>(p); break;
+    default: gemm_bf16_kernel<MB, NI, WK, 2, EPI_ARGMAX, 0, false><<<grid, block, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -388,12 +482,12 @@ int gemm_supported(int dtype, int M, int N, int K) {
 
 int gemm_argmax_tiles(int dtype, int M, int N, int K) {
   if (dtype == 0) return (N + 63) / 64;
-  return plan_bf16(M, N, K, false).n_tiles;
+  return plan_bf16(M, N, K, EPI_ARGMAX, false).n_tiles;
 }
 
 int gemm_splits(int dtype, int M, int N, int K) {
   if (dtype == 0) return 1;
-  return plan_bf16(M, N, K, true).ksplit;
+  return plan_bf16(M, N, K, EPI_STORE, true).ksplit;
 }
 
 hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
@@ -409,10 +503,14 @@ hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  const Plan pl = plan_bf16(g.M, g.N, g.K, g.epi == EPI_STORE && g.allow_split);
+  const Plan pl = plan_bf16(g.M, g.N, g.K, g.epi, g.epi == EPI_STORE && g.allow_split);
   GemmP p{(const bf16_t*)g.A, g.lda, (const bf16_t*)g.W, g.M, g.N, g.K,
           g.C, g.ldc, (bf16_t*)g.Cb, g.amax_val, g.amax_idx, pl.m_tiles, pl.n_tiles,
           pl.ksplit, (int64_t)g.M * g.ldc};
+  if (pl.fn) {
+    hipLaunchKernelGGL(pl.fn, dim3(pl.m_tiles * pl.n_tiles * pl.ksplit), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
   switch (pl.MB) {
     case 1: return run_bf16_wk<1>(p, pl.NI, pl.WK, g.epi, st);
     case 2: return run_bf16_wk<2>(p, pl.NI, pl.WK, g.epi, st);
