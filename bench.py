@@ -20,6 +20,7 @@ of the same workload.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -50,6 +51,51 @@ def cpu_baseline(wl, W, prompt, seqs, threads):
     return seqs * wl.new_tokens / dt, dt
 
 
+def attn_standalone(P, torch, wl, top_len, top_cap):
+    """photon_attention alone, K/V rotated over copies larger than the
+    Infinity Cache: the chunk kernel at the token decoder's shape (one query
+    over C1 keys per (sub-chunk, head)) over enough sub-chunks for >= 1 GB of
+    K/V, and the global kernel at the workload's top step (B sequences over
+    the final top length).  Algorithmic bytes: K and V read once, q
+    (float32) read and the output written once."""
+    cfg = wl.cfg
+    H, hd = cfg.n_heads, cfg.d_model // cfg.n_heads
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    eb = 2 if cfg.dtype == "bf16" else 4
+    res = {}
+    C1 = cfg.chunk[0]
+    per_group = H * C1 * hd * 2 * eb
+    G = 1 << max(0, math.ceil(math.log2(1.05e9 / per_group)))
+    specs = [("chunk", G, 1, C1, C1), ("global", wl.batch, 1, top_len, top_cap)]
+    for kind, G, Q, L, cap in specs:
+        kv_bytes = G * H * cap * hd * eb
+        copies = max(2, math.ceil(600e6 / (2 * kv_bytes)) + 1)
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        Ks = [torch.randn((G, H, cap, hd), generator=gen, device="cuda").to(tdt) for _ in range(copies)]
+        Vs = [torch.randn((G, H, cap, hd), generator=gen, device="cuda").to(tdt) for _ in range(copies)]
+        q = torch.randn((G * Q, H * hd), generator=gen, device="cuda")
+        out = torch.empty((G * Q, H * hd), dtype=tdt, device="cuda")
+        att = P.Attention(kind, G, H, hd, Q, cap)
+        for i in range(3):
+            att(q, Ks[i % copies], Vs[i % copies], out, L)
+        iters = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            att(q, Ks[i % copies], Vs[i % copies], out, L)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        nbytes = G * H * L * hd * 2 * eb + G * Q * H * hd * (4 + eb)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[kind] = {"groups": G, "heads": H, "head_dim": hd, "queries": Q, "keys": L,
+                     "bytes_per_launch": nbytes, "avg_us": round(us, 2), "GB_s": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del Ks, Vs, q, out, att
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +107,7 @@ def main():
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (stress runs)")
     ap.add_argument("--prompt", type=int, default=None, help="override the workload's prompt length")
     ap.add_argument("--new-tokens", type=int, default=None, help="override the workload's generated tokens")
+    ap.add_argument("--no-attn-standalone", action="store_true", help="skip the stand-alone attention figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path shards by batch "
@@ -71,6 +118,7 @@ def main():
     import numpy as np
     import torch
     import photon_inputs as pi
+    from hierarchical_autoregressive_lm_amd import photon as P
     from hierarchical_autoregressive_lm_amd.photon import Photon
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -154,6 +202,14 @@ def main():
     roof_tok_s = B * S / ideal_s
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
 
+    attn = None
+    if not args.no_attn_standalone:
+        log("stand-alone attention")
+        model.close()
+        del model
+        torch.cuda.empty_cache()
+        attn = attn_standalone(P, torch, wl, wl.max_tokens // S, rep["top_len"])
+
     cpu = None
     if args.cpu_seqs > 0:
         threads = min(16, len(os.sched_getaffinity(0)))
@@ -195,6 +251,7 @@ def main():
                         "us_per_step": round(v["ms"] * 1e3 / wl.chunks, 2),
                         "GB_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
                     for k, v in sorted(per_class.items(), key=lambda kv: -kv[1]["ms"])},
+        "attn_standalone": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

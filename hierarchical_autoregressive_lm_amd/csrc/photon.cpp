@@ -1004,3 +1004,65 @@ photon_status photon_trace_read(photon_ctx* c, photon_trace_stat* out) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------ stand-alone attention
+namespace {
+photon_status check_attention(int32_t kind, int32_t groups, int32_t heads, int32_t head_dim, int32_t queries,
+                              int32_t cap) {
+  if (kind != PHOTON_ATTN_GLOBAL && kind != PHOTON_ATTN_CHUNK) return fail(PHOTON_EINVAL, "unknown attention kind %d", kind);
+  if (groups < 1 || heads < 1) return fail(PHOTON_ESHAPE, "groups and heads must be >= 1");
+  if (head_dim != 32 && head_dim != 64 && head_dim != 96 && head_dim != 128)
+    return fail(PHOTON_EUNSUPPORTED, "head_dim %d is not one of 32, 64, 96, 128", head_dim);
+  if (queries < 1 || cap < queries) return fail(PHOTON_ESHAPE, "need 1 <= queries <= cap");
+  if (kind == PHOTON_ATTN_GLOBAL && queries != 1 && queries != 2 && queries != 4)
+    return fail(PHOTON_EUNSUPPORTED, "global attention takes 1, 2 or 4 queries per group (got %d)", queries);
+  if ((int64_t)groups * heads * cap * head_dim > ((int64_t)1 << 40))
+    return fail(PHOTON_ESHAPE, "cache too large");
+  return ok();
+}
+
+uint64_t attention_part_bytes(int32_t kind, int32_t groups, int32_t heads, int32_t head_dim, int32_t queries,
+                              int32_t cap, int* nsplit) {
+  *nsplit = kind == PHOTON_ATTN_GLOBAL ? attn_decode_splits(groups, heads, cap, queries) : 1;
+  return *nsplit > 1 ? (uint64_t)groups * heads * queries * *nsplit * (head_dim + 2) * sizeof(float) : 0;
+}
+}  // namespace
+
+extern "C" {
+
+photon_status photon_attention_scratch_bytes(int32_t kind, int32_t groups, int32_t heads, int32_t head_dim,
+                                             int32_t queries, int32_t cap, uint64_t* bytes) {
+  if (!bytes) return fail(PHOTON_EINVAL, "bytes is NULL");
+  PH_TRY(check_attention(kind, groups, heads, head_dim, queries, cap));
+  int ns = 1;
+  *bytes = attention_part_bytes(kind, groups, heads, head_dim, queries, cap, &ns);
+  return ok();
+}
+
+photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q, const void* d_k, const void* d_v,
+                               void* d_out, int32_t groups, int32_t heads, int32_t head_dim, int32_t queries,
+                               int32_t keys, int32_t cap, void* d_scratch, uint64_t scratch_bytes, void* stream) {
+  PH_TRY(check_attention(kind, groups, heads, head_dim, queries, cap));
+  if (dtype != PHOTON_F32 && dtype != PHOTON_BF16) return fail(PHOTON_EINVAL, "unknown dtype %d", dtype);
+  if (!d_q || !d_k || !d_v || !d_out) return fail(PHOTON_EINVAL, "NULL buffer");
+  if (keys < queries || keys > cap) return fail(PHOTON_ESHAPE, "need queries <= keys <= cap");
+  if (kind == PHOTON_ATTN_CHUNK && keys > 16) return fail(PHOTON_EUNSUPPORTED, "chunk attention takes at most 16 keys");
+  int ns = 1;
+  const uint64_t need = attention_part_bytes(kind, groups, heads, head_dim, queries, cap, &ns);
+  if (need > 0 && (!d_scratch || scratch_bytes < need))
+    return fail(PHOTON_ESHAPE, "scratch needs %llu bytes", (unsigned long long)need);
+  if (need > 0 && ((uintptr_t)d_scratch % 256)) return fail(PHOTON_EINVAL, "scratch must be 256-byte aligned");
+  AttnCall a{};
+  a.dtype = dtype; a.G = groups; a.Q = queries; a.H = heads; a.hd = head_dim;
+  a.q = d_q; a.q_ld = (int64_t)heads * head_dim;
+  a.Kc = d_k; a.Vc = d_v; a.seq_stride = (int64_t)heads * cap * head_dim; a.cap = cap; a.seq0 = 0;
+  a.L_host = keys; a.L_dev = nullptr; a.L_mul = 0; a.L_add = 0;
+  a.out = d_out; a.out_ld = (int64_t)heads * head_dim;
+  a.part = (float*)d_scratch; a.nsplit = ns;
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = kind == PHOTON_ATTN_GLOBAL ? launch_attn_decode(a, st) : launch_attn_chunk(a, st);
+  if (e != hipSuccess) return fail(PHOTON_EHIP, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

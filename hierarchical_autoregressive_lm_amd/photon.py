@@ -20,6 +20,8 @@ OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -
 F32, BF16 = 0, 1
 RECGEN, HIERGEN = 0, 1
 _MODES = {"recgen": RECGEN, "hiergen": HIERGEN}
+ATTN_GLOBAL, ATTN_CHUNK = 0, 1
+_ATTN = {"global": ATTN_GLOBAL, "chunk": ATTN_CHUNK}
 
 
 class PhotonError(RuntimeError):
@@ -75,7 +77,8 @@ EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
            "photon_release_prefill_weights", "photon_close",
            "photon_last_error", "photon_prefill", "photon_decode_chunk",
            "photon_position", "photon_set_position", "photon_use_graphs",
-           "photon_trace_enable", "photon_trace_read"]
+           "photon_trace_enable", "photon_trace_read",
+           "photon_attention_scratch_bytes", "photon_attention"]
 
 
 def _load():
@@ -101,6 +104,8 @@ def _load():
         "photon_use_graphs": [V, i32],
         "photon_trace_enable": [V, ctypes.c_uint32],
         "photon_trace_read": [V, P(TraceStat)],
+        "photon_attention_scratch_bytes": [i32, i32, i32, i32, i32, i32, P(u64)],
+        "photon_attention": [i32, i32, V, V, V, V, i32, i32, i32, i32, i32, i32, V, u64, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -158,6 +163,40 @@ def weight_layout(cfg):
 
 def _stream_handle(torch):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def attention_scratch_bytes(kind, groups, heads, head_dim, queries, cap):
+    out = ctypes.c_uint64()
+    _check(_lib.photon_attention_scratch_bytes(_ATTN[kind], groups, heads, head_dim, queries, cap,
+                                               ctypes.byref(out)))
+    return out.value
+
+
+class Attention:
+    """photon_attention on torch tensors: q [G*Q, H*hd] float32 and K, V
+    [G, H, cap, hd] (float32 or bfloat16) on the current GPU; the scratch
+    for split partials is allocated once per shape."""
+
+    def __init__(self, kind, groups, heads, head_dim, queries, cap):
+        self.kind, self.shape = kind, (groups, heads, head_dim, queries, cap)
+        n = attention_scratch_bytes(kind, groups, heads, head_dim, queries, cap)
+        self.scratch = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device="cuda")
+        off = (-self.scratch.data_ptr()) % 256
+        self.scratch_ptr, self.scratch_bytes = self.scratch.data_ptr() + off, n
+
+    def __call__(self, q, K, V, out, keys):
+        G, H, hd, Q, cap = self.shape
+        dt = BF16 if K.dtype == torch.bfloat16 else F32
+        assert q.dtype == torch.float32 and tuple(q.shape) == (G * Q, H * hd) and q.is_contiguous()
+        assert tuple(K.shape) == (G, H, cap, hd) and K.shape == V.shape and K.dtype == V.dtype
+        assert K.is_contiguous() and V.is_contiguous() and out.is_contiguous()
+        assert out.dtype == K.dtype and tuple(out.shape) == (G * Q, H * hd)
+        _check(_lib.photon_attention(_ATTN[self.kind], dt, ctypes.c_void_p(q.data_ptr()),
+                                     ctypes.c_void_p(K.data_ptr()), ctypes.c_void_p(V.data_ptr()),
+                                     ctypes.c_void_p(out.data_ptr()), G, H, hd, Q, keys, cap,
+                                     ctypes.c_void_p(self.scratch_ptr), self.scratch_bytes,
+                                     _stream_handle(torch)))
+        return out
 
 
 class Photon:

@@ -223,6 +223,41 @@ photon_status photon_set_position(photon_ctx* ctx, int64_t tokens,
 photon_status photon_use_graphs(photon_ctx* ctx, int32_t enable);
 
 /* ------------------------------------------------------------------------
+ * Stand-alone decode attention (no context, no model): the two kernels the
+ * decode path runs over a cache, applied to caller buffers.
+ *   PHOTON_ATTN_GLOBAL  the top encoder's attention over the global coarse
+ *       K/V, the one cache that grows with the context (explainer,
+ *       recursive-generation section); split over keys into partials merged
+ *       by a second pass when there are few (group, head) pairs.
+ *   PHOTON_ATTN_CHUNK   the decoders' attention confined to the current
+ *       chunk (explainer, module table: the Context Decoder attends only
+ *       within its chunk); at most 16 keys.
+ * Layout: d_q [groups*queries][heads*head_dim] float32, row g*queries + t;
+ * d_k, d_v [groups][heads][cap][head_dim] in `dtype` (photon_dtype);
+ * d_out like d_q but in `dtype`.  Query t of group g attends to keys
+ * 0 .. keys-queries+t of its (g, h) cache, softmax(q k^T / sqrt(head_dim)) v
+ * with float32 softmax and accumulation; out is rounded to dtype (bf16:
+ * nearest, ties to even).
+ * Limits (else PHOTON_ESHAPE / PHOTON_EUNSUPPORTED): head_dim in {32, 64,
+ * 96, 128}; 1 <= queries <= keys <= cap; GLOBAL: queries in {1, 2, 4};
+ * CHUNK: keys <= 16.  d_scratch holds the split partials:
+ * photon_attention_scratch_bytes() bytes (0 when the launch does not
+ * split; d_scratch may then be NULL), 256-byte aligned.
+ * ---------------------------------------------------------------------- */
+typedef enum { PHOTON_ATTN_GLOBAL = 0, PHOTON_ATTN_CHUNK = 1 } photon_attn_kind;
+
+photon_status photon_attention_scratch_bytes(int32_t kind, int32_t groups,
+                                             int32_t heads, int32_t head_dim,
+                                             int32_t queries, int32_t cap,
+                                             uint64_t* bytes);
+photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q,
+                               const void* d_k, const void* d_v, void* d_out,
+                               int32_t groups, int32_t heads, int32_t head_dim,
+                               int32_t queries, int32_t keys, int32_t cap,
+                               void* d_scratch, uint64_t scratch_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
  * Tracing: per kernel class, HIP events around every launch of the enabled
  * classes, with the algorithmic bytes and flops of each launch (weights,
  * activations and caches read or written once; nothing for cache hits).

@@ -185,3 +185,44 @@ def test_set_position_and_trace_need_state():
     assert lib.photon_trace_read(f.ctx, out) == P.OK
     assert all(out[i].launches == 0 for i in range(len(P.KERNEL_CLASSES)))
     f.close()
+
+
+def test_attention_scratch_sizes():
+    # chunk attention never splits; global attention splits only when there
+    # are few (group, head) pairs, and then holds (num, max, sum) per split
+    for (G, H, hd, Q, cap) in [(2, 3, 64, 1, 100), (64, 16, 96, 1, 288), (4, 4, 96, 1, 2176),
+                               (2, 2, 128, 4, 300), (1, 1, 32, 2, 8)]:
+        assert P.attention_scratch_bytes("chunk", G, H, hd, Q, min(cap, 16)) == 0
+        n = P.attention_scratch_bytes("global", G, H, hd, Q, cap)
+        unit = G * H * Q * (hd + 2) * 4
+        assert n % unit == 0
+        assert n == 0 or n // unit >= 2
+    assert P.attention_scratch_bytes("global", 64, 16, 96, 1, 288) == 0   # 1024 pairs fill the chip
+
+
+def test_attention_rejects_bad_arguments_before_any_device_call():
+    lib = P._lib
+    V = ctypes.c_void_p
+    q, k, v, o = V(1 << 20), V(2 << 20), V(3 << 20), V(4 << 20)
+    G, C = P.ATTN_GLOBAL, P.ATTN_CHUNK
+
+    def call(kind=C, dtype=P.BF16, qq=q, G_=4, H=2, hd=64, Q=1, L=4, cap=4, sc=None, sb=0):
+        return lib.photon_attention(kind, dtype, qq, k, v, o, G_, H, hd, Q, L, cap, sc, sb, None)
+
+    assert call(kind=7) == P.EINVAL
+    assert call(dtype=3) == P.EINVAL
+    assert call(qq=None) == P.EINVAL
+    assert call(hd=48) == P.EUNSUPPORTED
+    assert call(G_=0) == P.ESHAPE
+    assert call(Q=5, L=4) == P.ESHAPE                     # more queries than cache slots
+    assert call(L=5, cap=4) == P.ESHAPE                   # keys beyond the cache
+    assert call(Q=2, L=1, cap=4) == P.ESHAPE              # fewer keys than queries
+    assert call(L=17, cap=17) == P.EUNSUPPORTED           # chunk attention: at most 16 keys
+    assert call(kind=G, Q=3, L=8, cap=8) == P.EUNSUPPORTED
+    # a split launch without (enough) scratch
+    need = P.attention_scratch_bytes("global", 2, 2, 64, 1, 4096)
+    assert need > 0
+    assert call(kind=G, G_=2, H=2, L=4000, cap=4096) == P.ESHAPE
+    assert "scratch" in lib.photon_last_error().decode()
+    assert call(kind=G, G_=2, H=2, L=4000, cap=4096, sc=V(8 << 20), sb=need - 1) == P.ESHAPE
+    assert call(kind=G, G_=2, H=2, L=4000, cap=4096, sc=V((8 << 20) + 16), sb=need) == P.EINVAL
