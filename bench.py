@@ -36,19 +36,56 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, W, prompt, seqs, threads):
+def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0):
     """The oracle as it stands, RecGen decode phase only (perf_counter),
-    on `seqs` sequences of the workload; prefill and weight setup untimed."""
+    prefill and weight setup untimed.  seqs = 0: one sequence is decoded
+    first to size the sample, then as many sequences (up to the batch) as
+    fill about target_s seconds; when the whole batch takes less, its decode
+    is repeated from the same prefill state until target_s is filled."""
     from threadpoolctl import threadpool_limits
     from oracle import photon_oracle as O
-    with threadpool_limits(limits=threads):
-        m = O.Model(wl.cfg, W)
-        st = O.prefill(m, prompt[:seqs])
+
+    def decode(st):
         t0 = time.perf_counter()
         for _ in range(wl.chunks):
             O.decode_chunk(m, st)
-        dt = time.perf_counter() - t0
-    return seqs * wl.new_tokens / dt, dt
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=threads):
+        m = O.Model(wl.cfg, W)
+        reps = 1
+        if seqs <= 0:
+            t1 = decode(O.prefill(m, prompt[:1]))
+            seqs = max(1, min(wl.batch, round(target_s / t1)))
+            if seqs == 1:
+                return wl.new_tokens / t1, t1, 1, 1
+        st0 = O.prefill(m, prompt[:seqs])
+        dt = decode(st0.copy())
+        if seqs == wl.batch and dt < target_s / 2:
+            reps = max(1, round(target_s / dt))
+            dt += sum(decode(st0.copy()) for _ in range(reps - 1))
+    return reps * seqs * wl.new_tokens / dt, dt, seqs, reps
+
+
+def measured_traffic(wl, cls):
+    """HBM bytes per launch of kernel class `cls` on this workload from the
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary (calibrated against a
+    plain copy), or None when there is none or the kernel's source files
+    changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json"))):
+        rec = json.load(open(path))
+        if rec.get("workload") != wl.name or rec.get("kernel_class") != cls:
+            continue
+        h = hashlib.sha256()
+        for f in rec["source_files"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            log(f"{os.path.basename(path)}: kernel sources changed since the counters were taken")
+            return None, None
+        return rec["traffic_bytes_per_launch"], os.path.relpath(path, ROOT)
+    return None, None
 
 
 def attn_standalone(P, torch, wl, top_len, top_cap):
@@ -103,7 +140,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="untimed decode chunks (default: the workload's)")
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: photon-150m B32 P1024 N256)")
     ap.add_argument("--mode", default="recgen", choices=["recgen", "hiergen"])
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=0,
+                    help="sequences in the oracle's timed sample (0: sized for ~15 s; -1: skip)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (stress runs)")
     ap.add_argument("--prompt", type=int, default=None, help="override the workload's prompt length")
     ap.add_argument("--new-tokens", type=int, default=None, help="override the workload's generated tokens")
@@ -201,6 +239,7 @@ def main():
     ideal_s = chunk_bytes / (HBM_PEAK_GBS * 1e9)
     roof_tok_s = B * S / ideal_s
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    traffic, traffic_src = measured_traffic(wl, dominant)
 
     attn = None
     if not args.no_attn_standalone:
@@ -211,13 +250,15 @@ def main():
         attn = attn_standalone(P, torch, wl, wl.max_tokens // S, rep["top_len"])
 
     cpu = None
-    if args.cpu_seqs > 0:
+    if args.cpu_seqs >= 0:
         threads = min(16, len(os.sched_getaffinity(0)))
-        log(f"oracle baseline on {args.cpu_seqs} sequences, {threads} threads")
-        cv, cdt = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads)
+        log(f"oracle baseline, {threads} threads")
+        cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads)
+        prec = "float64" if cfg.dtype == "f32" else "float64 with the bf16 rounding contract"
+        rep_txt = f", decoded {reps} times from the same prefill" if reps > 1 else ""
         cpu = {"value": round(cv, 2), "unit": "tok/s", "cores": threads, "kind": "oracle",
-               "sample": f"RecGen decode phase of {args.cpu_seqs} of {B} sequences, all {wl.chunks} chunks "
-                         f"({args.cpu_seqs * wl.new_tokens} tokens, {cdt:.1f} s), numpy float64"}
+               "sample": f"RecGen decode phase of {ns} of {B} sequences, all {wl.chunks} chunks{rep_txt} "
+                         f"({reps * ns * wl.new_tokens} tokens, {cdt:.1f} s), numpy {prec}"}
 
     out = {
         "metric": METRIC,
@@ -243,7 +284,7 @@ def main():
         "path_roofline": {"algorithmic_bytes_per_step": round(chunk_bytes), "ideal_us_per_step": round(ideal_s * 1e6, 2),
                           "roofline_tok_s": round(roof_tok_s, 1), "frac": round(tok_s / roof_tok_s, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": dominant, "launches": dom["launches"],
                      "avg_us": round(dom["ms"] * 1e3 / dom["launches"], 2),
                      "bytes_per_launch": round(dom["bytes"] / dom["launches"])},

@@ -359,17 +359,17 @@ hipError_t decode_hd(const AttnCall& a, hipStream_t st) {
       // ones: 16 slots x 6 keys, so that the last pass over the keys is not
       // nearly empty and more workgroups share the chip
       if (a.cap >= 1024)
-        attn_decode_kernel<T, HD, 1, 8, 32><<<grid, dim3(512), 0, st>>>(a, scale);
+        PH_LAUNCH((attn_decode_kernel<T, HD, 1, 8, 32>), grid, dim3(512), 0, st, a, scale);
       else
-        attn_decode_kernel<T, HD, 1, 6><<<grid, block, 0, st>>>(a, scale);
+        PH_LAUNCH((attn_decode_kernel<T, HD, 1, 6>), grid, block, 0, st, a, scale);
       break;
-    case 2: attn_decode_kernel<T, HD, 2, 4><<<grid, block, 0, st>>>(a, scale); break;
-    case 4: attn_decode_kernel<T, HD, 4, 4><<<grid, block, 0, st>>>(a, scale); break;
+    case 2: PH_LAUNCH((attn_decode_kernel<T, HD, 2, 4>), grid, block, 0, st, a, scale); break;
+    case 4: PH_LAUNCH((attn_decode_kernel<T, HD, 4, 4>), grid, block, 0, st, a, scale); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  attn_combine_kernel<T, HD><<<a.G * a.H * a.Q, 64, 0, st>>>(a);
+  PH_LAUNCH((attn_combine_kernel<T, HD>), a.G * a.H * a.Q, 64, 0, st, a);
   return hipGetLastError();
 }
 
@@ -377,10 +377,10 @@ template <typename T, int HD>
 hipError_t chunk_hd(const AttnCall& a, hipStream_t st, int maxl) {
   const float scale = 1.0f / sqrtf((float)HD);
   dim3 grid((a.G * a.H + 15) / 16), block(256);
-  if (maxl <= 2) attn_chunk_kernel<T, HD, 2><<<grid, block, 0, st>>>(a, scale);
-  else if (maxl <= 4) attn_chunk_kernel<T, HD, 4><<<grid, block, 0, st>>>(a, scale);
-  else if (maxl <= 8) attn_chunk_kernel<T, HD, 8><<<grid, block, 0, st>>>(a, scale);
-  else if (maxl <= 16) attn_chunk_kernel<T, HD, 16><<<grid, block, 0, st>>>(a, scale);
+  if (maxl <= 2) PH_LAUNCH((attn_chunk_kernel<T, HD, 2>), grid, block, 0, st, a, scale);
+  else if (maxl <= 4) PH_LAUNCH((attn_chunk_kernel<T, HD, 4>), grid, block, 0, st, a, scale);
+  else if (maxl <= 8) PH_LAUNCH((attn_chunk_kernel<T, HD, 8>), grid, block, 0, st, a, scale);
+  else if (maxl <= 16) PH_LAUNCH((attn_chunk_kernel<T, HD, 16>), grid, block, 0, st, a, scale);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -389,7 +389,7 @@ template <typename T, int HD>
 hipError_t prefill_hd(const AttnCall& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)HD);
   const int nqb = (a.Q + 63) / 64;
-  attn_prefill_kernel<T, HD><<<a.G * a.H * nqb, 256, 0, st>>>(a, scale);
+  PH_LAUNCH((attn_prefill_kernel<T, HD>), a.G * a.H * nqb, 256, 0, st, a, scale);
   return hipGetLastError();
 }
 

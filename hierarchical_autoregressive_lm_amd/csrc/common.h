@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 typedef uint16_t bf16_t;
 
 // bf16 -> fp32 is exact (the bf16 bits are the high half of the fp32 bits).

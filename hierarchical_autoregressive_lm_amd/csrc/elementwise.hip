@@ -203,52 +203,52 @@ inline unsigned row_threads(int d) { return (unsigned)(((d / 4) + 63) / 64 * 64)
 hipError_t launch_rows_epilogue(int dtype, const RowsEpi& e, hipStream_t st) {
   if (e.d > 4096 || e.d % 4) return hipErrorInvalidValue;
   dim3 grid(e.R), block(row_threads(e.d));
-  if (dtype) rows_epilogue_kernel<bf16_t><<<grid, block, 0, st>>>(e);
-  else rows_epilogue_kernel<float><<<grid, block, 0, st>>>(e);
+  if (dtype) PH_LAUNCH((rows_epilogue_kernel<bf16_t>), grid, block, 0, st, e);
+  else PH_LAUNCH((rows_epilogue_kernel<float>), grid, block, 0, st, e);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_kv(const RopeKvCall& c, hipStream_t st) {
   const int64_t n = (int64_t)c.M * c.H * (c.hd / 2);
-  if (c.dtype) rope_kv_kernel<bf16_t><<<blocks(n), 256, 0, st>>>(c);
-  else rope_kv_kernel<float><<<blocks(n), 256, 0, st>>>(c);
+  if (c.dtype) PH_LAUNCH((rope_kv_kernel<bf16_t>), blocks(n), 256, 0, st, c);
+  else PH_LAUNCH((rope_kv_kernel<float>), blocks(n), 256, 0, st, c);
   return hipGetLastError();
 }
 
 hipError_t launch_embed_gather(int dtype, const int* ids, int64_t n, const void* E, int d, int V, void* out,
                                hipStream_t st) {
-  if (dtype) embed_gather_kernel<bf16_t><<<blocks(n * d), 256, 0, st>>>(ids, n, (const bf16_t*)E, d, V, (bf16_t*)out);
-  else embed_gather_kernel<float><<<blocks(n * d), 256, 0, st>>>(ids, n, (const float*)E, d, V, (float*)out);
+  if (dtype) PH_LAUNCH((embed_gather_kernel<bf16_t>), blocks(n * d), 256, 0, st, ids, n, (const bf16_t*)E, d, V, (bf16_t*)out);
+  else PH_LAUNCH((embed_gather_kernel<float>), blocks(n * d), 256, 0, st, ids, n, (const float*)E, d, V, (float*)out);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st) {
   if (c.d > 4096 || c.d % 4) return hipErrorInvalidValue;
   dim3 grid(c.M), block(std::max(256u, row_threads(c.d)));
-  if (dtype) argmax_next_kernel<bf16_t><<<grid, block, 0, st>>>(c);
-  else argmax_next_kernel<float><<<grid, block, 0, st>>>(c);
+  if (dtype) PH_LAUNCH((argmax_next_kernel<bf16_t>), grid, block, 0, st, c);
+  else PH_LAUNCH((argmax_next_kernel<float>), grid, block, 0, st, c);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_table(float* tab, int max_pos, int hd, float theta, hipStream_t st) {
   const int64_t n = (int64_t)max_pos * (hd / 2);
-  rope_table_kernel<<<blocks(n), 256, 0, st>>>(tab, max_pos, hd, (double)theta);
+  PH_LAUNCH((rope_table_kernel), blocks(n), 256, 0, st, tab, max_pos, hd, (double)theta);
   return hipGetLastError();
 }
 
 hipError_t launch_set_int(int* p, int v, hipStream_t st) {
-  set_int_kernel<<<1, 1, 0, st>>>(p, v);
+  PH_LAUNCH((set_int_kernel), 1, 1, 0, st, p, v);
   return hipGetLastError();
 }
 
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  zero_ints_kernel<<<blocks(n), 256, 0, st>>>(p, n);
+  PH_LAUNCH((zero_ints_kernel), blocks(n), 256, 0, st, p, n);
   return hipGetLastError();
 }
 
 hipError_t launch_add_int(int* p, int v, hipStream_t st) {
-  add_int_kernel<<<1, 1, 0, st>>>(p, v);
+  PH_LAUNCH((add_int_kernel), 1, 1, 0, st, p, v);
   return hipGetLastError();
 }
 

@@ -441,10 +441,10 @@ template <int MB, int NI, int WK>
 hipError_t run_bf16(const GemmP& p, int epi, hipStream_t st) {
   dim3 grid(p.m_tiles * p.n_tiles * p.ksplit), block(256);
   switch (epi) {
-    case EPI_STORE: gemm_bf16_kernel<MB, NI, WK, 2, EPI_STORE, 0, false><<<grid, block, 0, st>>>(p); break;
-    case EPI_ADD: gemm_bf16_kernel<MB, NI, WK, 2, EPI_ADD, 0, false><<<grid, block, 0, st>>>(p); break;
-    case EPI_GELU: gemm_bf16_kernel<MB, NI, WK, 2, EPI_GELU, 0, false><<<grid, block, 0, st>>>(p); break;
-    default: gemm_bf16_kernel<MB, NI, WK, 2, EPI_ARGMAX, 0, false><<<grid, block, 0, st>>>(p); break;
+    case EPI_STORE: PH_LAUNCH((gemm_bf16_kernel<MB, NI, WK, 2, EPI_STORE, 0, false>), grid, block, 0, st, p); break;
+    case EPI_ADD: PH_LAUNCH((gemm_bf16_kernel<MB, NI, WK, 2, EPI_ADD, 0, false>), grid, block, 0, st, p); break;
+    case EPI_GELU: PH_LAUNCH((gemm_bf16_kernel<MB, NI, WK, 2, EPI_GELU, 0, false>), grid, block, 0, st, p); break;
+    default: PH_LAUNCH((gemm_bf16_kernel<MB, NI, WK, 2, EPI_ARGMAX, 0, false>), grid, block, 0, st, p); break;
   }
   return hipGetLastError();
 }
@@ -496,10 +496,10 @@ hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
              g.C, g.ldc, (float*)g.Cb, g.amax_val, g.amax_idx};
     dim3 grid((g.N + 63) / 64, g.M), block(64);
     switch (g.epi) {
-      case EPI_STORE: gemm_f32_kernel<EPI_STORE><<<grid, block, 0, st>>>(p); break;
-      case EPI_ADD: gemm_f32_kernel<EPI_ADD><<<grid, block, 0, st>>>(p); break;
-      case EPI_GELU: gemm_f32_kernel<EPI_GELU><<<grid, block, 0, st>>>(p); break;
-      default: gemm_f32_kernel<EPI_ARGMAX><<<grid, block, 0, st>>>(p); break;
+      case EPI_STORE: PH_LAUNCH((gemm_f32_kernel<EPI_STORE>), grid, block, 0, st, p); break;
+      case EPI_ADD: PH_LAUNCH((gemm_f32_kernel<EPI_ADD>), grid, block, 0, st, p); break;
+      case EPI_GELU: PH_LAUNCH((gemm_f32_kernel<EPI_GELU>), grid, block, 0, st, p); break;
+      default: PH_LAUNCH((gemm_f32_kernel<EPI_ARGMAX>), grid, block, 0, st, p); break;
     }
     return hipGetLastError();
   }
@@ -508,7 +508,7 @@ hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
           g.C, g.ldc, (bf16_t*)g.Cb, g.amax_val, g.amax_idx, pl.m_tiles, pl.n_tiles,
           pl.ksplit, (int64_t)g.M * g.ldc};
   if (pl.fn) {
-    hipLaunchKernelGGL(pl.fn, dim3(pl.m_tiles * pl.n_tiles * pl.ksplit), dim3(256), 0, st, p);
+    PH_LAUNCH(pl.fn, pl.m_tiles * pl.n_tiles * pl.ksplit, 256, 0, st, p);
     return hipGetLastError();
   }
   switch (pl.MB) {

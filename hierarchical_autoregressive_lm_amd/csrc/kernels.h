@@ -2,10 +2,35 @@
 // Every launcher enqueues on `st`, never synchronises and returns the
 // launch status.  dtype: 0 = fp32 storage, 1 = bf16 storage.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace photon {
+
+// Events that a tracer wants recorded by the kernel dispatches of one
+// operation: `start` by its first kernel, `stop` by every kernel (the last
+// one wins).  The dispatch itself records them (hipExtLaunchKernelGGL), so
+// they time the kernels without marker packets between them.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchEvents& launch_events() {
+  static thread_local LaunchEvents e;
+  return e;
+}
+
+// Every kernel launch of the library goes through this macro.
+#define PH_LAUNCH(kern, grid, block, shmem, st, ...)                                                  \
+  do {                                                                                                 \
+    photon::LaunchEvents& ev_ = photon::launch_events();                                               \
+    if (ev_.stop) {                                                                                    \
+      hipExtLaunchKernelGGL(kern, dim3(grid), dim3(block), shmem, st, ev_.start, ev_.stop, 0, __VA_ARGS__); \
+      ev_.start = nullptr;                                                                             \
+    } else {                                                                                           \
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(block), shmem, st, __VA_ARGS__);                      \
+    }                                                                                                  \
+  } while (0)
 
 enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_GELU = 2, EPI_ARGMAX = 3 };
 

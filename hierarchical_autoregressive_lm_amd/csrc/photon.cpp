@@ -392,39 +392,43 @@ void bind_weights(photon_ctx* c) {
     if (s_ != PHOTON_OK) return s_; \
   } while (0)
 
-// Launch `f` (returning hipError_t); when class `cls` is traced, bracket it
-// with HIP events on the same stream and keep its algorithmic bytes/flops.
+// Launch `f` (returning hipError_t); when class `cls` is traced, the kernel
+// dispatches of `f` record a start event (first kernel) and a stop event
+// (last kernel) themselves, and the launch keeps its algorithmic bytes and
+// flops.
 template <class F>
 photon_status traced(photon_ctx* c, int cls, double bytes, double flops, hipStream_t st, const char* what, F&& f) {
   const bool on = (c->tr.mask >> cls) & 1u;
   hipEvent_t a = nullptr, b = nullptr;
   if (on) {
     HIP_TRY(c->tr.get(&a));
-    HIP_TRY(hipEventRecord(a, st));
+    HIP_TRY(c->tr.get(&b));
+    launch_events() = LaunchEvents{a, b};
   }
   const hipError_t e = f();
+  const bool launched = launch_events().start == nullptr;
+  launch_events() = LaunchEvents{};
   if (e != hipSuccess) return fail(PHOTON_EHIP, "%s: %s", what, hipGetErrorString(e));
   if (on) {
-    HIP_TRY(c->tr.get(&b));
-    HIP_TRY(hipEventRecord(b, st));
+    if (!launched) return fail(PHOTON_EHIP, "%s: traced operation launched no kernel", what);
     c->tr.recs.push_back({cls, a, b, bytes, flops});
   }
   return PHOTON_OK;
 }
 
-// Algorithmic bytes of one GEMM launch: W and A read once, C written (and
-// read too for the residual update); the head writes its argmax partials.
+// Algorithmic bytes of one GEMM launch: W and A read once, the fp32 result
+// written once (read too for a residual update; bf16 after GELU), the head
+// its token ids (and logits when asked).  K slabs and the head's per-tile
+// argmax partials are choices of this implementation and are not counted.
 double gemm_bytes(const GemmCall& g) {
   const double eb = g.dtype ? 2 : 4;
   double b = (double)g.N * g.K * eb + (double)g.M * g.K * eb;
   switch (g.epi) {
-    case EPI_STORE:
-      b += (double)g.M * g.N * 4 * (g.allow_split ? gemm_splits(g.dtype, g.M, g.N, g.K) : 1);
-      break;
+    case EPI_STORE: b += (double)g.M * g.N * 4; break;
     case EPI_ADD: b += 2.0 * g.M * g.N * 4; break;
     case EPI_GELU: b += (double)g.M * g.N * eb; break;
     default:
-      b += (double)gemm_argmax_tiles(g.dtype, g.M, g.N, g.K) * g.M * 8;
+      b += (double)g.M * 4;
       if (g.C) b += (double)g.M * g.N * 4;
   }
   return b;
@@ -468,8 +472,9 @@ struct StackRun {
   void* out; int out_rows; int64_t in_stride, in_off;
 };
 
+// the producer's result read once (not its K slabs), residual and stream
 double rows_epi_bytes(const RowsEpi& e, int eb) {
-  double b = (double)e.R * e.d * 4 * (e.ksplit + (e.resid ? 1 : 0) + (e.x_out ? 1 : 0));
+  double b = (double)e.R * e.d * 4 * (1 + (e.resid ? 1 : 0) + (e.x_out ? 1 : 0));
   if (e.ids) b += (double)e.R * (e.d * eb + 4);
   if (e.a_out) b += (double)e.R * e.d * eb + e.d * 4.0;
   return b;
@@ -517,13 +522,13 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
     void* Vc = kbase + r.kv.plane_elems * eb;
     RopeKvCall rc{dt, b.part, ks, (int64_t)r.M * 3 * d, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
                   r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
-    PH_TRY(traced(c, PHOTON_K_ROPE_KV, (double)r.M * d * (12.0 * ks + 4 + 2 * eb), 6.0 * r.M * d, st, "rope_kv",
+    PH_TRY(traced(c, PHOTON_K_ROPE_KV, (double)r.M * d * (12.0 + 4 + 2 * eb), 6.0 * r.M * d, st, "rope_kv",
                   [&] { return launch_rope_kv(rc, st); }));
     AttnCall ac{dt, r.G, r.Q, H, hd, b.q, d, Kc, Vc, r.kv.seq_stride, r.kv.cap, r.kv.seq0,
                 r.L_host, r.L_dev, r.L_mul, r.L_add, b.o, d, b.apart, r.nsplit};
-    // K and V of every visible key read once, q read, output written
-    double abytes = (double)r.G * H * r.L_acct * hd * eb * 2 + (double)r.M * d * (4 + eb);
-    if (r.kind == ATT_DECODE && r.nsplit > 1) abytes += 2.0 * r.G * H * r.Q * r.nsplit * (hd + 2) * 4;
+    // K and V of every visible key read once, q read, output written (the
+    // split partials are not counted)
+    const double abytes = (double)r.G * H * r.L_acct * hd * eb * 2 + (double)r.M * d * (4 + eb);
     const double aflops = 4.0 * r.G * H * r.Q * (double)r.L_acct * hd;
     if (r.kind == ATT_PREFILL)
       PH_TRY(traced(c, PHOTON_K_ATTN_PREFILL, abytes, aflops / 2, st, "attn_prefill",
@@ -864,7 +869,9 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     const bool next = j + 1 < C1;
     ArgmaxNext an{g.amax_val, g.amax_idx, wp.head_tiles, MB, C1, C2, j, tok,
                   c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec0.layers[0].g1, d, cf.norm_eps};
-    const double nb = (double)wp.head_tiles * MB * 8 + MB * 4.0 + (next ? (double)MB * d * (8 + 2 * eb) : 0);
+    // the next step's input (conditioning row + embedding in, stream and its
+    // norm out); the token ids are counted with the head
+    const double nb = next ? (double)MB * d * (8 + 2 * eb) : 0;
     PH_TRY(traced(c, PHOTON_K_ARGMAX, nb, 0, st, "argmax_next", [&] { return launch_argmax_next(dt, an, st); }));
   }
   // top branch (RecGen: independent of the tokens, so it may run beside the

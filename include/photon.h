@@ -258,9 +258,11 @@ photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q,
                                void* stream);
 
 /* ------------------------------------------------------------------------
- * Tracing: per kernel class, HIP events around every launch of the enabled
- * classes, with the algorithmic bytes and flops of each launch (weights,
- * activations and caches read or written once; nothing for cache hits).
+ * Tracing: per kernel class, a start and a stop HIP event recorded by the
+ * kernel dispatches of every traced operation (the first kernel's start,
+ * the last kernel's end; no marker packets between kernels), with the
+ * algorithmic bytes and flops of each launch (weights, activations and
+ * caches read or written once: no K slabs, split partials or re-reads).
  * ---------------------------------------------------------------------- */
 typedef enum {
   PHOTON_K_GEMM_QKV = 0,   /* [Wq;Wk;Wv] projection */
@@ -289,8 +291,7 @@ typedef struct {
 
 /* Enable tracing for the classes whose bit (1 << class) is set; 0 turns it
  * off.  Clears previous records.  Traced chunks launch their kernels directly
- * (no graph); each event pair also holds the event markers' own cost, a few
- * microseconds, which matters only for the smallest kernels. */
+ * (no graph), one after the other on the caller's stream. */
 photon_status photon_trace_enable(photon_ctx* ctx, uint32_t class_mask);
 /* Wait for the recorded events, sum them per class into out[PHOTON_K_COUNT]
  * and clear the records (tracing stays enabled). */
