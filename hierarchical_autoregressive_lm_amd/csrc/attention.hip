@@ -349,6 +349,240 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnCall a, float sca
   }
 }
 
+// ------------------------------------------------------- prefill (MFMA)
+// Causal attention over a whole prompt on bf16 caches with
+// v_mfma_f32_16x16x32_bf16.  Transposed products keep every softmax step in
+// registers: S^T = K Q^T puts 4 consecutive keys of one query in each lane
+// (lane l: keys 4(l/16)+r of a 16-key block, query l%16), so a query's max
+// and sum need two shuffles across the lane's 4 groups and the running
+// rescale of O^T = V^T P^T is lane-local; the probabilities a lane holds are
+// directly the B operand of the P V product once the 32 keys of a k-step are
+// ordered (4j..4j+3, 16+4j..16+4j+3) for lane group j, with V^T read from
+// LDS in that same order.
+// q and p are float32 in the rounding contract; each enters the products as
+// hi + lo, two bf16 terms (hi = bf16(x), lo = bf16(x - hi): 16 significant
+// bits), so every product is two MFMAs accumulating in float32.
+// A workgroup: 4 waves x NQ blocks of 16 queries of one (sequence, head);
+// K and V tiles of 64 keys staged in LDS (K row-major, V transposed),
+// double-buffered; query blocks run heaviest (last) first.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split_hi_lo(float x, bf16_t& hi, bf16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+template <int HD, int NQ>
+__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
+  constexpr int TK = 64;                 // keys per tile
+  constexpr int BQ = 64 * NQ;            // queries per workgroup
+  constexpr int KS = HD / 32;            // k-steps of S^T
+  constexpr int HB = HD / 16;            // 16-row blocks of O^T
+  constexpr int KROW = HD + 8;           // padded K row (bf16)
+  constexpr int VCOL = TK + 8;           // padded V^T row (bf16)
+  constexpr int KCH = TK * HD / 8;       // 16-byte K chunks per tile
+  constexpr int VCH = TK / 2 * HD / 8;   // (2 keys x 8 dims) V items per tile
+  constexpr int KPT = (KCH + 255) / 256, VPT = (VCH + 255) / 256;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TK][KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][HD][VCOL];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, j = lane >> 4;
+  const int T = a.Q;                     // queries = keys = prompt rows
+  const int nqb = (T + BQ - 1) / BQ;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);     // heaviest first
+  const int gh = blockIdx.x / nqb;
+  const int h = gh % a.H, g = gh / a.H;
+  const int q0 = qb * BQ + wave * 16 * NQ;
+  const bf16_t* Kb = reinterpret_cast<const bf16_t*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
+  const bf16_t* Vb = reinterpret_cast<const bf16_t*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
+
+  // Q^T fragments (B operand): lane holds query q0 + 16n + c, dims 32ks + 8j .. +8
+  bf16x8_t qhi[NQ][KS], qlo[NQ][KS];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    const int qi = q0 + 16 * n + c;
+    const float* qp = a.q + (int64_t)(g * a.Q + (qi < T ? qi : T - 1)) * a.q_ld + h * HD + 8 * j;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16_t hb[8], lb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_hi_lo(qi < T ? qp[32 * ks + e] * scale : 0.f, hb[e], lb[e]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qhi[n][ks][e] = __builtin_bit_cast(__bf16, hb[e]);
+        qlo[n][ks][e] = __builtin_bit_cast(__bf16, lb[e]);
+      }
+    }
+  }
+  f32x4_t o[NQ][HB];
+  float m[NQ], l[NQ];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    m[n] = -INFINITY; l[n] = 0.f;
+#pragma unroll
+    for (int b = 0; b < HB; ++b) o[n][b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int kend = min(T, qb * BQ + BQ);  // keys any query of the block sees
+  const int ntiles = (kend + TK - 1) / TK;
+  uint4 kreg[KPT];
+  uint4 vreg[VPT][2];
+  auto load_tile = [&](int t) {
+    const int k0 = t * TK;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ch = tid + 256 * i;
+      const int key = ch / (HD / 8), c8 = ch % (HD / 8);
+      if (ch < KCH && k0 + key < T)
+        kreg[i] = *reinterpret_cast<const uint4*>(Kb + (int64_t)(k0 + key) * HD + 8 * c8);
+      else
+        kreg[i] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int it = tid + 256 * i;
+      const int kp = it / (HD / 8), c8 = it % (HD / 8);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = k0 + 2 * kp + u;
+        if (it < VCH && key < T)
+          vreg[i][u] = *reinterpret_cast<const uint4*>(Vb + (int64_t)key * HD + 8 * c8);
+        else
+          vreg[i][u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int ch = tid + 256 * i;
+      const int key = ch / (HD / 8), c8 = ch % (HD / 8);
+      if (ch < KCH) *reinterpret_cast<uint4*>(&Ks[buf][key][8 * c8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int it = tid + 256 * i;
+      const int kp = it / (HD / 8), c8 = it % (HD / 8);
+      if (it < VCH) {
+        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
+        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // dims 8c8 + 2w and 8c8 + 2w + 1 of keys 2kp and 2kp + 1
+          const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);
+          const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
+          *reinterpret_cast<uint32_t*>(&Vt[buf][8 * c8 + 2 * w][2 * kp]) = lo;
+          *reinterpret_cast<uint32_t*>(&Vt[buf][8 * c8 + 2 * w + 1][2 * kp]) = hi;
+        }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const int k0 = t * TK;
+    // S^T for 4 blocks of 16 keys x NQ blocks of 16 queries
+    f32x4_t sc[4][NQ];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) sc[kb][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][16 * kb + c][32 * ks + 8 * j]);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+          sc[kb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qhi[n][ks], sc[kb][n], 0, 0, 0);
+          sc[kb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[n][ks], sc[kb][n], 0, 0, 0);
+        }
+      }
+    // online softmax per query; p in place of the scores
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int qi = q0 + 16 * n + c;
+      float mx = m[n];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 16 * kb + 4 * j + r;
+          if (key > qi || key >= T) sc[kb][n][r] = -INFINITY;
+          mx = fmaxf(mx, sc[kb][n][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // a query sees key 0 in the first tile, so mx is finite from then on
+      const float corr = expf(m[n] - mx);
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = expf(sc[kb][n][r] - mx);
+          sc[kb][n][r] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l[n] = l[n] * corr + ps;
+      m[n] = mx;
+#pragma unroll
+      for (int b = 0; b < HB; ++b) o[n][b] *= corr;
+    }
+    // O^T += V^T P^T, two k-steps of 32 keys
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      bf16x8_t phi[NQ], plo[NQ];
+#pragma unroll
+      for (int n = 0; n < NQ; ++n)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16_t hb, lb;
+          split_hi_lo(sc[2 * ps + (e >> 2)][n][e & 3], hb, lb);
+          phi[n][e] = __builtin_bit_cast(__bf16, hb);
+          plo[n][e] = __builtin_bit_cast(__bf16, lb);
+        }
+#pragma unroll
+      for (int b = 0; b < HB; ++b) {
+        const uint2 v0 = *reinterpret_cast<const uint2*>(&Vt[buf][16 * b + c][32 * ps + 4 * j]);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(&Vt[buf][16 * b + c][32 * ps + 16 + 4 * j]);
+        const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vv);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+          o[n][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[n], o[n][b], 0, 0, 0);
+          o[n][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[n], o[n][b], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  // lane holds O^T[dims 16b + 4j + r][query 16n + c]
+  bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    const int qi = q0 + 16 * n + c;
+    if (qi >= T) continue;
+    const float inv = 1.f / l[n];
+#pragma unroll
+    for (int b = 0; b < HB; ++b) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(o[n][b][0] * inv) | ((uint32_t)f2bf(o[n][b][1] * inv) << 16);
+      pk.y = (uint32_t)f2bf(o[n][b][2] * inv) | ((uint32_t)f2bf(o[n][b][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(out + (int64_t)(g * a.Q + qi) * a.out_ld + h * HD + 16 * b + 4 * j) = pk;
+    }
+  }
+}
+
 template <typename T, int HD>
 hipError_t decode_hd(const AttnCall& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)HD);
@@ -388,8 +622,14 @@ hipError_t chunk_hd(const AttnCall& a, hipStream_t st, int maxl) {
 template <typename T, int HD>
 hipError_t prefill_hd(const AttnCall& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)HD);
-  const int nqb = (a.Q + 63) / 64;
-  PH_LAUNCH((attn_prefill_kernel<T, HD>), a.G * a.H * nqb, 256, 0, st, a, scale);
+  if constexpr (sizeof(T) == 2 && HD % 32 == 0) {
+    // bf16 caches: MFMA kernel, 128 queries per workgroup
+    const int nqb = (a.Q + 127) / 128;
+    PH_LAUNCH((attn_prefill_mfma_kernel<HD, 2>), a.G * a.H * nqb, 256, 0, st, a, scale);
+  } else {
+    const int nqb = (a.Q + 63) / 64;
+    PH_LAUNCH((attn_prefill_kernel<T, HD>), a.G * a.H * nqb, 256, 0, st, a, scale);
+  }
   return hipGetLastError();
 }
 

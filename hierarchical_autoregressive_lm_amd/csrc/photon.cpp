@@ -1016,7 +1016,8 @@ photon_status photon_trace_read(photon_ctx* c, photon_trace_stat* out) {
 namespace {
 photon_status check_attention(int32_t kind, int32_t groups, int32_t heads, int32_t head_dim, int32_t queries,
                               int32_t cap) {
-  if (kind != PHOTON_ATTN_GLOBAL && kind != PHOTON_ATTN_CHUNK) return fail(PHOTON_EINVAL, "unknown attention kind %d", kind);
+  if (kind != PHOTON_ATTN_GLOBAL && kind != PHOTON_ATTN_CHUNK && kind != PHOTON_ATTN_PREFILL)
+    return fail(PHOTON_EINVAL, "unknown attention kind %d", kind);
   if (groups < 1 || heads < 1) return fail(PHOTON_ESHAPE, "groups and heads must be >= 1");
   if (head_dim != 32 && head_dim != 64 && head_dim != 96 && head_dim != 128)
     return fail(PHOTON_EUNSUPPORTED, "head_dim %d is not one of 32, 64, 96, 128", head_dim);
@@ -1054,6 +1055,8 @@ photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q, co
   if (!d_q || !d_k || !d_v || !d_out) return fail(PHOTON_EINVAL, "NULL buffer");
   if (keys < queries || keys > cap) return fail(PHOTON_ESHAPE, "need queries <= keys <= cap");
   if (kind == PHOTON_ATTN_CHUNK && keys > 16) return fail(PHOTON_EUNSUPPORTED, "chunk attention takes at most 16 keys");
+  if (kind == PHOTON_ATTN_PREFILL && keys != queries)
+    return fail(PHOTON_ESHAPE, "prefill attention needs queries == keys (got %d, %d)", queries, keys);
   int ns = 1;
   const uint64_t need = attention_part_bytes(kind, groups, heads, head_dim, queries, cap, &ns);
   if (need > 0 && (!d_scratch || scratch_bytes < need))
@@ -1067,7 +1070,9 @@ photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q, co
   a.out = d_out; a.out_ld = (int64_t)heads * head_dim;
   a.part = (float*)d_scratch; a.nsplit = ns;
   const hipStream_t st = (hipStream_t)stream;
-  const hipError_t e = kind == PHOTON_ATTN_GLOBAL ? launch_attn_decode(a, st) : launch_attn_chunk(a, st);
+  const hipError_t e = kind == PHOTON_ATTN_GLOBAL  ? launch_attn_decode(a, st)
+                       : kind == PHOTON_ATTN_CHUNK ? launch_attn_chunk(a, st)
+                                                   : launch_attn_prefill(a, st);
   if (e != hipSuccess) return fail(PHOTON_EHIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -20,8 +20,8 @@ OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -
 F32, BF16 = 0, 1
 RECGEN, HIERGEN = 0, 1
 _MODES = {"recgen": RECGEN, "hiergen": HIERGEN}
-ATTN_GLOBAL, ATTN_CHUNK = 0, 1
-_ATTN = {"global": ATTN_GLOBAL, "chunk": ATTN_CHUNK}
+ATTN_GLOBAL, ATTN_CHUNK, ATTN_PREFILL = 0, 1, 2
+_ATTN = {"global": ATTN_GLOBAL, "chunk": ATTN_CHUNK, "prefill": ATTN_PREFILL}
 
 
 class PhotonError(RuntimeError):

@@ -232,6 +232,12 @@ photon_status photon_use_graphs(photon_ctx* ctx, int32_t enable);
  *   PHOTON_ATTN_CHUNK   the decoders' attention confined to the current
  *       chunk (explainer, module table: the Context Decoder attends only
  *       within its chunk); at most 16 keys.
+ *   PHOTON_ATTN_PREFILL causal self-attention over a whole prompt, the
+ *       encoders' attention in prefill (explainer, module table: each
+ *       Context Encoder is causal over its level's stream); queries == keys.
+ *       bf16 caches run on MFMA with q and the probabilities entering each
+ *       product as two bf16 terms (hi + lo: at most 2^-18 relative error per
+ *       operand), float32 caches on FMA.
  * Layout: d_q [groups*queries][heads*head_dim] float32, row g*queries + t;
  * d_k, d_v [groups][heads][cap][head_dim] in `dtype` (photon_dtype);
  * d_out like d_q but in `dtype`.  Query t of group g attends to keys
@@ -240,11 +246,11 @@ photon_status photon_use_graphs(photon_ctx* ctx, int32_t enable);
  * nearest, ties to even).
  * Limits (else PHOTON_ESHAPE / PHOTON_EUNSUPPORTED): head_dim in {32, 64,
  * 96, 128}; 1 <= queries <= keys <= cap; GLOBAL: queries in {1, 2, 4};
- * CHUNK: keys <= 16.  d_scratch holds the split partials:
+ * CHUNK: keys <= 16; PREFILL: queries == keys.  d_scratch holds the split partials:
  * photon_attention_scratch_bytes() bytes (0 when the launch does not
  * split; d_scratch may then be NULL), 256-byte aligned.
  * ---------------------------------------------------------------------- */
-typedef enum { PHOTON_ATTN_GLOBAL = 0, PHOTON_ATTN_CHUNK = 1 } photon_attn_kind;
+typedef enum { PHOTON_ATTN_GLOBAL = 0, PHOTON_ATTN_CHUNK = 1, PHOTON_ATTN_PREFILL = 2 } photon_attn_kind;
 
 photon_status photon_attention_scratch_bytes(int32_t kind, int32_t groups,
                                              int32_t heads, int32_t head_dim,

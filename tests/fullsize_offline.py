@@ -1,0 +1,88 @@
+"""Full-size parity in two halves, for the workloads whose oracle prefill
+takes many minutes per sequence (photon-600m long context: P = 32768;
+photon-600m 2x2: B = 256, P = 8192).
+
+  python tests/fullsize_offline.py gpu OUTDIR       (on the GPU)
+      runs every case's whole batch at the full prompt and generation length
+      in the launch configuration the benchmark times (captured graphs, no
+      logits), then again with logits (direct launches), checks that both
+      runs emit the same tokens, and saves the sampled row's prompt index,
+      tokens and logits to OUTDIR/<case>.npz.
+
+  python tests/fullsize_offline.py check OUTDIR     (CPU only)
+      recomputes each saved row with the oracle, teacher-forced with the
+      GPU's tokens, and applies the same bar as tests/parity.py
+      (check_against_oracle); prints one line per case.
+
+Same cases as tests/test_gpu_fullsize.py behind PHOTON_FULLSIZE=1.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+sys.path.insert(0, HERE)
+
+import photon_inputs as pi  # noqa: E402
+
+CASES = [("long_recgen_row0", 4, 0, "recgen"),
+         ("long_hiergen_row7", 4, 7, "hiergen"),
+         ("2x2_recgen_row137", 5, 137, "recgen")]
+
+
+def gpu(outdir, only=None):
+    import torch
+    from hierarchical_autoregressive_lm_amd.photon import Photon
+    os.makedirs(outdir, exist_ok=True)
+    for name, idx, row, mode in CASES:
+        if only and name not in only:
+            continue
+        wl = pi.get(idx)
+        print(f"[gpu] {name}: {wl.name} {mode} row {row}", flush=True)
+        W = pi.gen_weights(wl.cfg, wl.seed)
+        pr = pi.gen_prompts(wl.cfg, wl.batch, wl.prompt, wl.seed)
+        model = Photon(wl.cfg, W)
+        prompt = torch.from_numpy(pr).cuda()
+        t0 = time.time()
+        toks_g, _ = model.generate(prompt, wl.new_tokens, mode=mode, logits=False)
+        toks_e, lg = model.generate(prompt, wl.new_tokens, mode=mode, logits=True)
+        torch.cuda.synchronize()
+        same = bool((toks_g == toks_e).all().item())
+        print(f"[gpu] {name}: generated in {time.time() - t0:.1f} s, graph == direct tokens: {same}", flush=True)
+        assert same, "graph and direct runs emitted different tokens"
+        assert model.position() == (wl.max_tokens // wl.cfg.S, wl.max_tokens)
+        np.savez(os.path.join(outdir, f"{name}.npz"), row=row, tokens=toks_e[row:row + 1].cpu().numpy(),
+                 logits=lg[row:row + 1].cpu().numpy())
+        del lg, model, toks_e, toks_g
+        torch.cuda.empty_cache()
+
+
+def check(outdir, only=None):
+    from parity import check_against_oracle
+    for name, idx, row, mode in CASES:
+        if only and name not in only:
+            continue
+        path = os.path.join(outdir, f"{name}.npz")
+        if not os.path.exists(path):
+            print(f"[check] {name}: no GPU output at {path}", flush=True)
+            continue
+        d = np.load(path)
+        assert int(d["row"]) == row
+        wl = pi.get(idx)
+        W = pi.gen_weights(wl.cfg, wl.seed)
+        pr = pi.gen_prompts(wl.cfg, wl.batch, wl.prompt, wl.seed)
+        t0 = time.time()
+        r = check_against_oracle(wl.cfg, W, pr[row:row + 1], d["tokens"], d["logits"], mode,
+                                 log=lambda msg: print(f"[oracle] {name}: {msg}", flush=True))
+        print(f"[check] {name}: PASS {wl.name} {mode} row {row}: max_err={r['max_err']:.4g} "
+              f"noise_max={r['noise_max']:.4g} near_ties={r['near_ties']}/{r['tokens']} "
+              f"({time.time() - t0:.0f} s)", flush=True)
+
+
+if __name__ == "__main__":
+    what, outdir = sys.argv[1], sys.argv[2]
+    only = set(sys.argv[3:]) or None
+    {"gpu": gpu, "check": check}[what](outdir, only)

@@ -219,6 +219,7 @@ def test_attention_rejects_bad_arguments_before_any_device_call():
     assert call(Q=2, L=1, cap=4) == P.ESHAPE              # fewer keys than queries
     assert call(L=17, cap=17) == P.EUNSUPPORTED           # chunk attention: at most 16 keys
     assert call(kind=G, Q=3, L=8, cap=8) == P.EUNSUPPORTED
+    assert call(kind=P.ATTN_PREFILL, Q=4, L=8, cap=8) == P.ESHAPE   # prefill: queries == keys
     # a split launch without (enough) scratch
     need = P.attention_scratch_bytes("global", 2, 2, 64, 1, 4096)
     assert need > 0

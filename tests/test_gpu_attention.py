@@ -16,6 +16,15 @@ are that float32 value rounded to nearest: |gpu - ref| <= 1 bf16 ulp of ref
 + delta (half an ulp for the rounding, half for a float32 error that moves
 the value across a rounding boundary).  delta matters only where the output
 is a small average of many values of both signs.
+
+Prompt (prefill) attention on bf16 caches runs on MFMA with q and the
+probabilities entering each product as hi + lo bf16 terms; each operand is
+then off by at most 2^-18 relative (hi = bf16(x) is within 2^-9|x|, lo
+rounds the remainder to within 2^-9 of itself).  A score moves by at most
+eps_s = 2^-18 * max_j sum_i |q_i k_ji|, so each weight p_j by a factor within
+exp(+-2 eps_s), and the P V product adds 2^-18 * sum_j p_j |v_j|: the
+allowance adds (4 eps_s + 2^-18) * sum_j p_j |v_j| (its first-order bound,
+doubled).
 """
 import math
 
@@ -51,15 +60,21 @@ def make_inputs(seed, G, H, hd, Q, cap, dtype):
     return q, K, V
 
 
-def oracle_out(q, K, V, groups, H, hd, Q, L):
+def oracle_out(q, K, V, groups, H, hd, Q, L, split=False):
     """Reference for the given groups, [len(groups)*Q, H*hd] float64, and
-    the float32 accumulation allowance delta of the same shape."""
+    the allowance delta of the same shape (float32 accumulation; plus the
+    hi + lo operand split when ``split``)."""
     qq = q.reshape(-1, Q, H, hd)[groups].astype(np.float64)           # [g, Q, H, hd]
     kk = K[groups][:, :, :L].transpose(0, 2, 1, 3).astype(np.float64)  # [g, L, H, hd]
     vv = V[groups][:, :, :L].transpose(0, 2, 1, 3).astype(np.float64)
     out = O.attention(qq, kk, vv, L - Q)                               # [g, Q, H, hd]
     mag = O.attention(qq, kk, np.abs(vv), L - Q)                       # sum_j p_j |v_j|
     delta = 4.0 * math.sqrt(L + 16) * 2.0 ** -24 * mag
+    if split:
+        # max over keys of sum_i |q_i k_ji| / sqrt(hd), per (g, query, head)
+        qk = np.einsum("gthe,gshe->gths", np.abs(qq), np.abs(kk)).max(axis=-1) / math.sqrt(hd)
+        eps_s = 2.0 ** -18 * qk                                        # [g, Q, H]
+        delta = delta + (4.0 * eps_s[..., None] + 2.0 ** -18) * mag
     n = len(groups) * Q
     return out.reshape(n, H * hd), delta.reshape(n, H * hd)
 
@@ -127,6 +142,40 @@ def test_chunk_attention_matches_oracle(P, G, H, hd, Q, L, cap, dtype):
     q, K, V = make_inputs(G * 100 + L, G, H, hd, Q, cap, dtype)
     got = run(P, "chunk", dtype, q, K, V, G, H, hd, Q, L, cap)
     check(got, oracle_out(q, K, V, np.arange(G), H, hd, Q, L), dtype)
+
+
+PREFILL_CASES = [
+    # G, H, hd, T, cap, dtype
+    (1, 1, 64, 1, 1, "bf16"),           # a one-row prompt
+    (2, 3, 64, 37, 40, "bf16"),         # shorter than one key tile, ragged
+    (2, 2, 96, 300, 300, "bf16"),       # several query blocks and key tiles
+    (1, 2, 128, 129, 130, "bf16"),      # one row past a query block
+    (3, 2, 32, 200, 200, "bf16"),
+    (2, 2, 64, 150, 150, "f32"),        # float32 caches: FMA kernel
+]
+
+
+@pytest.mark.parametrize("G,H,hd,T,cap,dtype", PREFILL_CASES)
+def test_prefill_attention_matches_oracle(P, G, H, hd, T, cap, dtype):
+    q, K, V = make_inputs(G * 10000 + T, G, H, hd, T, cap, dtype)
+    got = run(P, "prefill", dtype, q, K, V, G, H, hd, T, T, cap)
+    check(got, oracle_out(q, K, V, np.arange(G), H, hd, T, T, split=dtype == "bf16"), dtype)
+
+
+def test_prefill_attention_long_prompt_sampled(P):
+    """A level-1 encoder's prompt at the 600M 2x2 shape: 4096 rows, 16
+    heads, hd 96; sampled query rows against the oracle."""
+    G, H, hd, T = 2, 16, 96, 4096
+    q, K, V = make_inputs(77, G, H, hd, T, T, "bf16")
+    got = run(P, "prefill", "bf16", q, K, V, G, H, hd, T, T, T)
+    rows = np.array([0, 1, 63, 64, 127, 128, 2049, 4094, 4095])
+    for g in range(G):
+        for t in rows:
+            # the oracle's attention for one query row t: a cache of t keys
+            qq = q.reshape(G, T, H * hd)[g:g + 1, t:t + 1]
+            ref = oracle_out(qq.reshape(1, H * hd), K[g:g + 1], V[g:g + 1], np.arange(1), H, hd, 1, t + 1,
+                             split=True)
+            check(got[g * T + t:g * T + t + 1], ref, "bf16")
 
 
 def test_chunk_attention_standalone_size_sampled(P):
