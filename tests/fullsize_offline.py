@@ -12,7 +12,9 @@ photon-600m 2x2: B = 256, P = 8192).
   python tests/fullsize_offline.py check OUTDIR     (CPU only)
       recomputes each saved row with the oracle, teacher-forced with the
       GPU's tokens, and applies the same bar as tests/parity.py
-      (check_against_oracle); prints one line per case.
+      (check_against_oracle); prints one line per case.  The oracle's
+      outputs are kept in OUTDIR/<case>.oracle.npz with the tokens they were
+      forced with, and reused while a later GPU dump emits the same tokens.
 
 Same cases as tests/test_gpu_fullsize.py behind PHOTON_FULLSIZE=1.
 """
@@ -61,7 +63,7 @@ def gpu(outdir, only=None):
 
 
 def check(outdir, only=None):
-    from parity import check_against_oracle
+    from parity import compare, oracle_reference
     for name, idx, row, mode in CASES:
         if only and name not in only:
             continue
@@ -75,10 +77,20 @@ def check(outdir, only=None):
         W = pi.gen_weights(wl.cfg, wl.seed)
         pr = pi.gen_prompts(wl.cfg, wl.batch, wl.prompt, wl.seed)
         t0 = time.time()
-        r = check_against_oracle(wl.cfg, W, pr[row:row + 1], d["tokens"], d["logits"], mode,
-                                 log=lambda msg: print(f"[oracle] {name}: {msg}", flush=True))
+        toks = d["tokens"]
+        cache = os.path.join(outdir, f"{name}.oracle.npz")
+        if os.path.exists(cache) and np.array_equal(np.load(cache)["forced"], toks):
+            c = np.load(cache)
+            ot, ol, nl = c["ot"], c["ol"], c["nl"]
+            print(f"[check] {name}: oracle outputs reused (same forced tokens)", flush=True)
+        else:
+            ot, ol, nl, _ = oracle_reference(wl.cfg, W, pr[row:row + 1], toks, mode,
+                                             log=lambda msg: print(f"[oracle] {name}: {msg}", flush=True))
+            np.savez(cache, forced=toks, ot=ot, ol=ol, nl=nl)
+        r = compare(wl.cfg, toks, d["logits"], ot, ol, nl)
         print(f"[check] {name}: PASS {wl.name} {mode} row {row}: max_err={r['max_err']:.4g} "
-              f"noise_max={r['noise_max']:.4g} near_ties={r['near_ties']}/{r['tokens']} "
+              f"noise_max={r['noise_max']:.4g} mean_err={r['mean_err']:.4g} noise_mean={r['noise_mean']:.4g} "
+              f"near_ties={r['near_ties']}/{r['tokens']} "
               f"({time.time() - t0:.0f} s)", flush=True)
 
 

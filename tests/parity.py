@@ -36,12 +36,21 @@ def gpu_generate(cfg, W, prompt, N, mode="recgen", logits=True, rows=None):
     return model, toks_np, lg_np
 
 
-def check_against_oracle(cfg, W, prompt, toks, lg, mode="recgen", log=None):
-    """prompt/toks/lg for the same rows; returns a small report dict.  ``log``
-    passes the oracle's own progress lines through (long runs)."""
+def oracle_reference(cfg, W, prompt, toks, mode="recgen", log=None):
+    """The oracle teacher-forced with ``toks``: its ids and float64 logits,
+    and for bf16 models the same run in float32 (the noise probe)."""
     m = O.Model(cfg, W)
     N = toks.shape[1]
     ot, ol, st, _ = O.generate(m, prompt, N, mode=mode, forced_tokens=toks, log=log)
+    nl = None
+    if cfg.dtype != "f32":
+        _, nl, _, _ = O.generate(O.Model(cfg, W, compute="f32"), prompt, N, mode=mode,
+                                 forced_tokens=toks, log=log)
+    return ot, ol, nl, st
+
+
+def compare(cfg, toks, lg, ot, ol, nl):
+    """Apply the bar of the module docstring; returns a small report dict."""
     if cfg.dtype == "f32":
         scale = np.maximum(1.0, np.abs(ol).max(-1))
         err = (np.abs(lg - ol).max(-1) / scale).max()
@@ -50,8 +59,6 @@ def check_against_oracle(cfg, W, prompt, toks, lg, mode="recgen", log=None):
         ties = 0
         noise = (0.0, 0.0)
     else:
-        _, nl, _, _ = O.generate(O.Model(cfg, W, compute="f32"), prompt, N, mode=mode,
-                                 forced_tokens=toks, log=log)
         dev = np.abs(lg - ol)
         nz = np.abs(nl.astype(np.float64) - ol)
         noise = (float(nz.max()), float(nz.mean()))
@@ -66,8 +73,17 @@ def check_against_oracle(cfg, W, prompt, toks, lg, mode="recgen", log=None):
         assert (gap[diff] <= 2 * tol).all(), \
             f"ids differ beyond a near-tie: gaps {gap[diff].max():.3g}"
         ties = int(diff.sum())
-    return {"max_err": float(err), "near_ties": ties, "state": st, "tokens": int(toks.size),
-            "noise_max": noise[0], "noise_mean": noise[1]}
+    return {"max_err": float(err), "near_ties": ties, "tokens": int(toks.size),
+            "noise_max": noise[0], "noise_mean": noise[1], "mean_err": float(np.abs(lg - ol).mean())}
+
+
+def check_against_oracle(cfg, W, prompt, toks, lg, mode="recgen", log=None):
+    """prompt/toks/lg for the same rows; returns a small report dict.  ``log``
+    passes the oracle's own progress lines through (long runs)."""
+    ot, ol, nl, st = oracle_reference(cfg, W, prompt, toks, mode, log)
+    r = compare(cfg, toks, lg, ot, ol, nl)
+    r["state"] = st
+    return r
 
 
 def small_cfg(**kw):
