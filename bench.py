@@ -71,7 +71,8 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0):
 def measured_traffic(wl, cls):
     """HBM bytes per launch of kernel class `cls` on this workload from the
     committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary (calibrated against a
-    plain copy), or None when there is none or the kernel's source files
+    plain copy) and their ratio to the algorithmic bytes of the profiled
+    launches, or None when there is none or the kernel's source files
     changed since the counters were taken."""
     import glob
     import hashlib
@@ -84,9 +85,9 @@ def measured_traffic(wl, cls):
             h.update(open(os.path.join(ROOT, f), "rb").read())
         if h.hexdigest() != rec["source_sha256"]:
             log(f"{os.path.basename(path)}: kernel sources changed since the counters were taken")
-            return None, None
-        return rec["traffic_bytes_per_launch"], os.path.relpath(path, ROOT)
-    return None, None
+            return None, None, None
+        return rec["traffic_bytes_per_launch"], rec["traffic_over_algorithmic"], os.path.relpath(path, ROOT)
+    return None, None, None
 
 
 def attn_standalone(P, torch, wl, top_len, top_cap):
@@ -147,6 +148,9 @@ def main():
     ap.add_argument("--prompt", type=int, default=None, help="override the workload's prompt length")
     ap.add_argument("--new-tokens", type=int, default=None, help="override the workload's generated tokens")
     ap.add_argument("--no-attn-standalone", action="store_true", help="skip the stand-alone attention figures")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="skip the traced passes (per-class figures, roofline): for runs under a profiler, "
+                         "which gives its own per-kernel figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the decode path shards by batch "
@@ -180,7 +184,7 @@ def main():
     # prefill (untimed for the decode metric): wall time and per-class kernel
     # time of the one prefill, against the bf16 dense MFMA peak
     d_prompt = torch.from_numpy(prompt).cuda()
-    model.trace_enable(None)
+    model.trace_enable([] if args.no_trace else None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     model.prefill(d_prompt, wl.max_tokens, args.mode)
@@ -215,16 +219,17 @@ def main():
         pos[0] += 1
 
     # one traced pass over the workload's chunks: per-kernel bytes and times
-    model.trace_enable(None)
-    for _ in range(wl.chunks):
-        step()
-    torch.cuda.synchronize()
-    per_class = model.trace_read()
-    chunk_bytes = sum(v["bytes"] for v in per_class.values()) / wl.chunks
-    # the kernel class that moves the most algorithmic bytes per step is the
-    # one whose HBM roofline bounds the path
-    dominant = max(per_class, key=lambda k: per_class[k]["bytes"])
-    log(f"dominant kernel class (bytes): {dominant}")
+    per_class, dominant = {}, None
+    if not args.no_trace:
+        model.trace_enable(None)
+        for _ in range(wl.chunks):
+            step()
+        torch.cuda.synchronize()
+        per_class = model.trace_read()
+        # the kernel class that moves the most algorithmic bytes per step is
+        # the one whose HBM roofline bounds the path
+        dominant = max(per_class, key=lambda k: per_class[k]["bytes"])
+        log(f"dominant kernel class (bytes): {dominant}")
 
     # warmup, then the timed steps: each chunk replays the captured HIP graph
     model.trace_enable([])
@@ -244,14 +249,16 @@ def main():
     # the same K steps again with HIP events around every launch of the
     # dominant kernel (tracing launches the chunk's kernels directly instead
     # of through the graph; the kernels are the same)
-    model.state_restore(snap, wl.prompt)
-    pos[0] = 0
-    model.trace_enable([dominant])
-    for _ in range(K):
-        step()
-    torch.cuda.synchronize()
-    dom = model.trace_read()[dominant]
-    model.trace_enable([])
+    dom = None
+    if dominant:
+        model.state_restore(snap, wl.prompt)
+        pos[0] = 0
+        model.trace_enable([dominant])
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        dom = model.trace_read()[dominant]
+        model.trace_enable([])
 
     tok_s = B * S * K / dt
     rep = model.report(B, wl.max_tokens, args.mode)
@@ -260,10 +267,21 @@ def main():
         resident += rep["weights_prefill_only"] + rep["lower_kv"]
     gib = resident / 2 ** 30
     kv_gib = (rep["top_kv"] + rep["dec_kv"] + rep["lower_kv"]) / 2 ** 30
-    ideal_s = chunk_bytes / (HBM_PEAK_GBS * 1e9)
-    roof_tok_s = B * S / ideal_s
-    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
-    traffic, traffic_src = measured_traffic(wl, dominant)
+    path_roof = roofline = None
+    if dom:
+        chunk_bytes = sum(v["bytes"] for v in per_class.values()) / wl.chunks
+        ideal_s = chunk_bytes / (HBM_PEAK_GBS * 1e9)
+        roof_tok_s = B * S / ideal_s
+        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        traffic, traffic_ratio, traffic_src = measured_traffic(wl, dominant)
+        path_roof = {"algorithmic_bytes_per_step": round(chunk_bytes), "ideal_us_per_step": round(ideal_s * 1e6, 2),
+                     "roofline_tok_s": round(roof_tok_s, 1), "frac": round(tok_s / roof_tok_s, 4)}
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "traffic_over_algorithmic": traffic_ratio, "traffic_source": traffic_src,
+                    "kernel": dominant, "launches": dom["launches"],
+                    "avg_us": round(dom["ms"] * 1e3 / dom["launches"], 2),
+                    "bytes_per_launch": round(dom["bytes"] / dom["launches"])}
 
     attn = None
     if not args.no_attn_standalone:
@@ -305,16 +323,15 @@ def main():
         "tpm_unit": "tok/s/GiB (decode weights + top K/V + decoder K/V + state)",
         "resident_gib": round(gib, 4),
         "tpm_kv_only": round(tok_s / kv_gib, 1),
-        "path_roofline": {"algorithmic_bytes_per_step": round(chunk_bytes), "ideal_us_per_step": round(ideal_s * 1e6, 2),
-                          "roofline_tok_s": round(roof_tok_s, 1), "frac": round(tok_s / roof_tok_s, 4)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
-                     "kernel": dominant, "launches": dom["launches"],
-                     "avg_us": round(dom["ms"] * 1e3 / dom["launches"], 2),
-                     "bytes_per_launch": round(dom["bytes"] / dom["launches"])},
+        "path_roofline": path_roof,
+        "roofline": roofline,
         "kernels": {k: {"launches_per_step": v["launches"] // wl.chunks,
                         "us_per_step": round(v["ms"] * 1e3 / wl.chunks, 2),
-                        "GB_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+                        "GB_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "TFLOP_s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2),
+                        "mfma_frac": (round(v["flops"] / (v["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+                                      if k.startswith("gemm") else None)}
                     for k, v in sorted(per_class.items(), key=lambda kv: -kv[1]["ms"])},
         "prefill": prefill,
         "attn_standalone": attn,
