@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
+#include <thread>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -997,7 +999,17 @@ photon_status photon_trace_read(photon_ctx* c, photon_trace_stat* out) {
   if (!c || !out) return fail(PHOTON_EINVAL, "NULL argument");
   memset(out, 0, sizeof(photon_trace_stat) * PHOTON_K_COUNT);
   for (const auto& r : c->tr.recs) {
-    HIP_TRY(hipEventSynchronize(r.b));
+    // wait with a deadline: a dispatch-recorded event that never completes
+    // (e.g. under a tool that rewrites dispatch packets) is an error, not a hang
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+      const hipError_t q = hipEventQuery(r.b);
+      if (q == hipSuccess) break;
+      if (q != hipErrorNotReady) return fail(PHOTON_EHIP, "trace event: %s", hipGetErrorString(q));
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60))
+        return fail(PHOTON_EHIP, "trace event did not complete within 60 s");
+      std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
     float ms = 0.f;
     HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
     photon_trace_stat& o = out[r.cls];
