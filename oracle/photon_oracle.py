@@ -395,6 +395,66 @@ def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=N
 
 
 # --------------------------------------------------------------------------
+# flat (vanilla) Transformer baseline [tpm]: the comparison model of the
+# decode-heavy table, whose cache holds the K/V of every token.  Same blocks
+# and rounding contract as the PHOTON stacks; Model works with a
+# photon_inputs.VanillaConfig (weights E, layers.*, layers.gf, W_out).
+# --------------------------------------------------------------------------
+class VanillaState:
+    """K/V of every layer over every token so far, the rounded final-norm
+    output z of the last position (which the next head reads), and the
+    number of tokens."""
+
+    def __init__(self, cache, z, n):
+        self.cache, self.z, self.n = cache, z, n
+
+
+def vanilla_prefill(model, prompt, log=None):
+    """The prompt through the causal stack at positions 0..P-1, keeping the
+    K/V of every position; z = the stack output at the last position."""
+    B, P = prompt.shape
+    cache = model.empty_cache(model.cfg.n_layers, B)
+    z = model.stack("layers", model.cfg.n_layers, model.embed(prompt), np.arange(P), cache=cache, log=log)
+    return VanillaState(cache, z[:, -1], P)
+
+
+def vanilla_decode(model, st, steps, forced_tokens=None):
+    """``steps`` greedy tokens per sequence: logits = W_out z, y = first
+    argmax (or the forced token), then z = stack(E[y]) at the next position
+    over the cache.  Returns tokens [B, steps] and logits [B, steps, V]."""
+    toks, lgs = [], []
+    for j in range(steps):
+        lg = model.logits(st.z)
+        y = np.argmax(lg, axis=-1) if forced_tokens is None else np.asarray(forced_tokens)[:, j]
+        toks.append(y.astype(np.int64))
+        lgs.append(lg)
+        z = model.stack("layers", model.cfg.n_layers, model.embed(y[:, None]), np.array([st.n]), cache=st.cache)
+        st.z = z[:, 0]
+        st.n += 1
+    return np.stack(toks, 1), np.stack(lgs, 1)
+
+
+def vanilla_generate(model, prompt, new_tokens, forced_tokens=None, log=None):
+    st = vanilla_prefill(model, prompt, log=log)
+    toks, lgs = vanilla_decode(model, st, new_tokens, forced_tokens)
+    return toks, lgs, st
+
+
+def vanilla_full_logits(model, tokens):
+    """Causal forward over tokens [B, T] with no cache: the logits at every
+    position (the prediction of the token after it)."""
+    T = tokens.shape[1]
+    z = model.stack("layers", model.cfg.n_layers, model.embed(tokens), np.arange(T))
+    return model.logits(z)
+
+
+def vanilla_kv_bytes(cfg, batch, tokens):
+    """K and V of every layer for every token: the baseline's cache."""
+    eb = 4 if cfg.dtype == "f32" else 2
+    return cfg.n_layers * 2 * batch * tokens * cfg.d_model * eb
+
+
+# --------------------------------------------------------------------------
 # full recompute (no caches), for the incremental == full checks
 # --------------------------------------------------------------------------
 def top_full(model, u_all):

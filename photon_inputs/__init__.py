@@ -11,10 +11,10 @@ Generation"), abstract; PHOTON explainer (mokumoku.ipfde.com, Fujitsu PHOTON
 vertical scan), module table and the hierarchy-shape paragraph under it
 (L = 2 levels, C1 = C2 = 4 main setting, C1 = C2 = 2 quality setting).
 """
-from .configs import PhotonConfig, Workload, CONFIGS, WORKLOADS, get
+from .configs import PhotonConfig, VanillaConfig, vanilla_of, Workload, CONFIGS, WORKLOADS, get
 from .gen import (weight_names, weight_shapes, gen_weights, gen_prompts,
                   bf16_bits, MATRIX_STD)
 
-__all__ = ["PhotonConfig", "Workload", "CONFIGS", "WORKLOADS", "get",
+__all__ = ["PhotonConfig", "VanillaConfig", "vanilla_of", "Workload", "CONFIGS", "WORKLOADS", "get",
            "weight_names", "weight_shapes", "gen_weights", "gen_prompts",
            "bf16_bits", "MATRIX_STD"]

@@ -51,6 +51,39 @@ class PhotonConfig:
 
 
 @dataclass(frozen=True)
+class VanillaConfig:
+    """A flat decoder-only Transformer for the decode baseline: one causal
+    stack over the tokens (its K/V cache holds every token) with the same
+    blocks as the PHOTON stacks, an embedding and an untied output head."""
+    d_model: int
+    n_heads: int
+    vocab: int
+    n_layers: int
+    dtype: str = "bf16"
+    mlp_mult: int = 4
+    norm_eps: float = 1e-5
+    rope_theta: float = 10000.0
+
+    @property
+    def head_dim(self):
+        return self.d_model // self.n_heads
+
+    @property
+    def d_ff(self):
+        return self.mlp_mult * self.d_model
+
+
+def vanilla_of(cfg):
+    """The baseline matched to a PHOTON shape: same width, heads, MLP,
+    vocabulary and precision, and as many layers as all PHOTON stacks
+    together (top + level-1 encoder + both decoders)."""
+    return VanillaConfig(d_model=cfg.d_model, n_heads=cfg.n_heads, vocab=cfg.vocab,
+                         n_layers=cfg.n_top + cfg.n_enc1 + cfg.n_dec1 + cfg.n_dec0,
+                         dtype=cfg.dtype, mlp_mult=cfg.mlp_mult, norm_eps=cfg.norm_eps,
+                         rope_theta=cfg.rope_theta)
+
+
+@dataclass(frozen=True)
 class Workload:
     name: str
     cfg: PhotonConfig

@@ -13,6 +13,8 @@ Matrices are W[out, in]; a linear layer computes y = x W^T.
 from collections import OrderedDict
 import numpy as np
 
+from .configs import VanillaConfig
+
 MATRIX_STD = np.float32(0.02)
 LAYER_PARTS = ("g1", "Wq", "Wk", "Wv", "Wo", "g2", "W1", "W2")
 
@@ -30,6 +32,9 @@ def _layer_shapes(prefix, n, d, dff):
 
 def weight_shapes(cfg):
     """Canonical (name, shape) list, in generation order."""
+    if isinstance(cfg, VanillaConfig):
+        d, dff, V = cfg.d_model, cfg.d_ff, cfg.vocab
+        return [("E", (V, d))] + _layer_shapes("layers", cfg.n_layers, d, dff) + [("W_out", (V, d))]
     d, dff, V, C1, C2 = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.C1, cfg.C2
     s = [("E", (V, d)), ("W_ch1", (d, C1 * d))]
     s += _layer_shapes("enc1", cfg.n_enc1, d, dff)
