@@ -420,13 +420,16 @@ def vanilla_prefill(model, prompt, log=None):
 
 def vanilla_decode(model, st, steps, forced_tokens=None):
     """``steps`` greedy tokens per sequence: logits = W_out z, y = first
-    argmax (or the forced token), then z = stack(E[y]) at the next position
-    over the cache.  Returns tokens [B, steps] and logits [B, steps, V]."""
+    argmax, then z = stack(E[y]) at the next position over the cache.
+    Returns tokens [B, steps] and logits [B, steps, V].  forced_tokens
+    [B, steps] replaces the fed-back token (teacher forcing); the argmax is
+    still reported."""
     toks, lgs = [], []
     for j in range(steps):
         lg = model.logits(st.z)
-        y = np.argmax(lg, axis=-1) if forced_tokens is None else np.asarray(forced_tokens)[:, j]
-        toks.append(y.astype(np.int64))
+        am = np.argmax(lg, axis=-1).astype(np.int64)
+        y = am if forced_tokens is None else np.asarray(forced_tokens)[:, j]
+        toks.append(am)
         lgs.append(lg)
         z = model.stack("layers", model.cfg.n_layers, model.embed(y[:, None]), np.array([st.n]), cache=st.cache)
         st.z = z[:, 0]

@@ -41,10 +41,12 @@ def test_greedy_is_the_first_argmax_and_forcing_replays():
     assert (toks == np.argmax(lg, -1)).all()
     t2, lg2, _ = O.vanilla_generate(m, pr, 6, forced_tokens=toks)
     assert (t2 == toks).all() and np.array_equal(lg2, lg)
-    # forcing other tokens changes the later logits but not the first step's
+    # forcing other tokens changes the later logits but not the first step's;
+    # the reported ids stay the argmax of the forced trajectory's logits
     other = (toks + 1) % v.vocab
-    _, lg3, _ = O.vanilla_generate(m, pr, 6, forced_tokens=other)
+    t3, lg3, _ = O.vanilla_generate(m, pr, 6, forced_tokens=other)
     assert np.array_equal(lg3[:, 0], lg[:, 0]) and not np.allclose(lg3[:, 1:], lg[:, 1:])
+    assert (t3 == np.argmax(lg3, -1)).all()
 
 
 def test_off_by_one_position_is_caught():
