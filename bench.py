@@ -37,34 +37,41 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0):
+def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False):
     """The oracle as it stands, RecGen decode phase only (perf_counter),
     prefill and weight setup untimed.  seqs = 0: one sequence is decoded
     first to size the sample, then as many sequences (up to the batch) as
     fill about target_s seconds; when the whole batch takes less, its decode
     is repeated from the same prefill state until target_s is filled."""
     from threadpoolctl import threadpool_limits
+    import photon_inputs as pi
     from oracle import photon_oracle as O
 
     def decode(st):
         t0 = time.perf_counter()
-        for _ in range(wl.chunks):
-            O.decode_chunk(m, st)
+        if vanilla:
+            O.vanilla_decode(m, st, wl.new_tokens)
+        else:
+            for _ in range(wl.chunks):
+                O.decode_chunk(m, st)
         return time.perf_counter() - t0
 
+    prefill = O.vanilla_prefill if vanilla else O.prefill
     with threadpool_limits(limits=threads):
-        m = O.Model(wl.cfg, W)
+        m = O.Model(pi.vanilla_of(wl.cfg) if vanilla else wl.cfg, W)
         reps = 1
         if seqs <= 0:
-            t1 = decode(O.prefill(m, prompt[:1]))
+            t1 = decode(prefill(m, prompt[:1]))
             seqs = max(1, min(wl.batch, round(target_s / t1)))
             if seqs == 1:
                 return wl.new_tokens / t1, t1, 1, 1
-        st0 = O.prefill(m, prompt[:seqs])
-        dt = decode(st0.copy())
+        st0 = prefill(m, prompt[:seqs])
+        copy = (lambda st: O.VanillaState([{"k": e["k"].copy(), "v": e["v"].copy()} for e in st.cache],
+                                          st.z.copy(), st.n)) if vanilla else (lambda st: st.copy())
+        dt = decode(copy(st0))
         if seqs == wl.batch and dt < target_s / 2:
             reps = max(1, round(target_s / dt))
-            dt += sum(decode(st0.copy()) for _ in range(reps - 1))
+            dt += sum(decode(copy(st0)) for _ in range(reps - 1))
     return reps * seqs * wl.new_tokens / dt, dt, seqs, reps
 
 
@@ -141,7 +148,9 @@ def main():
     ap.add_argument("--steps", type=int, default=None, help="timed decode chunks (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed decode chunks (default: the workload's)")
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: photon-150m B32 P1024 N256)")
-    ap.add_argument("--mode", default="recgen", choices=["recgen", "hiergen"])
+    ap.add_argument("--mode", default="recgen", choices=["recgen", "hiergen", "vanilla"],
+                    help="PHOTON RecGen / HierGen, or the flat Transformer baseline matched to the workload's "
+                         "shape (same width, heads, vocabulary; as many layers as the PHOTON stacks)")
     ap.add_argument("--cpu-seqs", type=int, default=0,
                     help="sequences in the oracle's timed sample (0: sized for ~15 s; -1: skip)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (stress runs)")
@@ -162,7 +171,7 @@ def main():
     import torch
     import photon_inputs as pi
     from hierarchical_autoregressive_lm_amd import photon as P
-    from hierarchical_autoregressive_lm_amd.photon import Photon
+    from hierarchical_autoregressive_lm_amd.photon import Photon, Vanilla
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = pi.get(args.workload)
@@ -178,9 +187,11 @@ def main():
     Wm = args.warmup if args.warmup is not None else wl.chunks
     B, S = wl.batch, cfg.S
     log(f"workload {wl.name}: generating weights")
-    W = pi.gen_weights(cfg, wl.seed)
+    vanilla = args.mode == "vanilla"
+    mcfg = pi.vanilla_of(cfg) if vanilla else cfg
+    W = pi.gen_weights(mcfg, wl.seed)
     prompt = pi.gen_prompts(cfg, B, wl.prompt, wl.seed)
-    model = Photon(cfg, W)
+    model = Vanilla(mcfg, W, S) if vanilla else Photon(cfg, W)
     # prefill (untimed for the decode metric): wall time and per-class kernel
     # time of the one prefill, against the bf16 dense MFMA peak
     d_prompt = torch.from_numpy(prompt).cuda()
@@ -265,6 +276,7 @@ def main():
     resident = rep["weights_decode"] + rep["top_kv"] + rep["dec_kv"] + rep["state"]
     if args.mode == "hiergen":
         resident += rep["weights_prefill_only"] + rep["lower_kv"]
+    # vanilla: weights_decode is its one blob, top_kv its token K/V
     gib = resident / 2 ** 30
     kv_gib = (rep["top_kv"] + rep["dec_kv"] + rep["lower_kv"]) / 2 ** 30
     path_roof = roofline = None
@@ -284,7 +296,7 @@ def main():
                     "bytes_per_launch": round(dom["bytes"] / dom["launches"])}
 
     attn = None
-    if not args.no_attn_standalone:
+    if not args.no_attn_standalone and not vanilla:
         log("stand-alone attention")
         model.close()
         del model
@@ -295,11 +307,12 @@ def main():
     if args.cpu_seqs >= 0:
         threads = min(16, len(os.sched_getaffinity(0)))
         log(f"oracle baseline, {threads} threads")
-        cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads)
+        cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads, vanilla=vanilla)
         prec = "float64" if cfg.dtype == "f32" else "float64 with the bf16 rounding contract"
         rep_txt = f", decoded {reps} times from the same prefill" if reps > 1 else ""
+        what = "flat-baseline" if vanilla else "RecGen"
         cpu = {"value": round(cv, 2), "unit": "tok/s", "cores": threads, "kind": "oracle",
-               "sample": f"RecGen decode phase of {ns} of {B} sequences, all {wl.chunks} chunks{rep_txt} "
+               "sample": f"{what} decode phase of {ns} of {B} sequences, all {wl.chunks} chunks{rep_txt} "
                          f"({reps * ns * wl.new_tokens} tokens, {cdt:.1f} s), numpy {prec}"}
 
     out = {
@@ -317,10 +330,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "mode": args.mode, "batch": B, "prompt": wl.prompt,
                    "new_tokens": wl.new_tokens, "d_model": cfg.d_model, "heads": cfg.n_heads,
-                   "chunk": list(cfg.chunk), "layers_top_enc1_dec1_dec0": [cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0],
+                   "chunk": list(cfg.chunk),
+                   **({"layers": mcfg.n_layers} if vanilla else
+                      {"layers_top_enc1_dec1_dec0": [cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0]}),
                    "vocab": cfg.vocab, "tokens_per_step": B * S},
         "tpm": round(tok_s / gib, 1),
-        "tpm_unit": "tok/s/GiB (decode weights + top K/V + decoder K/V + state)",
+        "tpm_unit": ("tok/s/GiB (weights + token K/V + state)" if vanilla else
+                     "tok/s/GiB (decode weights + top K/V + decoder K/V + state)"),
         "resident_gib": round(gib, 4),
         "tpm_kv_only": round(tok_s / kv_gib, 1),
         "path_roofline": path_roof,

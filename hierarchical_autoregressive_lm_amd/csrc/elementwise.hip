@@ -157,7 +157,7 @@ __global__ __launch_bounds__(1024) void argmax_next_kernel(ArgmaxNext c) {
   const bool act = col < d;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (act) {
-    acc = *reinterpret_cast<const float4*>(c.c0 + (int64_t)m * c.c0_ld + (int64_t)(c.j + 1) * d + col);
+    if (c.c0) acc = *reinterpret_cast<const float4*>(c.c0 + (int64_t)m * c.c0_ld + (int64_t)(c.j + 1) * d + col);
     const T* erow = reinterpret_cast<const T*>(c.E) + (int64_t)bi * d;
     acc.x += St<T>::ld(erow[col]); acc.y += St<T>::ld(erow[col + 1]);
     acc.z += St<T>::ld(erow[col + 2]); acc.w += St<T>::ld(erow[col + 3]);

@@ -121,7 +121,8 @@ hipError_t launch_embed_gather(int dtype, const int* ids, int64_t n,
                                hipStream_t st);
 // Greedy head of token step j: reduce the ARGMAX tiles of row m = b*C2 + k
 // to its token (tokens[b*S + k*C1 + j]); if x is set, also write the next
-// step's input x[m] = c0[m*c0_ld + (j+1)*d ..] + E[token] and its norm a[m].
+// step's input x[m] = c0[m*c0_ld + (j+1)*d ..] + E[token] (E[token] alone
+// when c0 is null) and its norm a[m].
 struct ArgmaxNext {
   const float* val; const int* idx; int n_tiles, M, C1, C2, j;
   int* tokens;

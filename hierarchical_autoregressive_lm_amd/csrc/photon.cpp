@@ -74,6 +74,12 @@ photon_status check_config(const photon_config* c) {
 
 int elem_bytes(const photon_config* c) { return c->dtype == PHOTON_BF16 ? 2 : 4; }
 
+#define PH_CHECK(expr)            \
+  do {                            \
+    photon_status s_ = (expr);    \
+    if (s_ != PHOTON_OK) return s_; \
+  } while (0)
+
 // ------------------------------------------------------------ weight layout
 struct TensorDesc {
   std::string name;
@@ -265,6 +271,116 @@ PrePlan plan_prefill(const photon_config* c, int64_t B, int64_t P, int mode) {
   return p;
 }
 
+// ------------------------------------------------------- flat baseline plan
+photon_status check_vconfig(const photon_vanilla_config* v) {
+  if (!v) return fail(PHOTON_EINVAL, "config is NULL");
+  photon_config c{};
+  c.n_levels = 2;
+  c.chunk[0] = 1; c.chunk[1] = 1;
+  c.d_model = v->d_model; c.n_heads = v->n_heads; c.mlp_mult = v->mlp_mult; c.vocab = v->vocab;
+  c.n_top = v->n_layers; c.n_enc1 = c.n_dec1 = c.n_dec0 = 1;
+  c.dtype = v->dtype; c.norm_eps = v->norm_eps; c.rope_theta = v->rope_theta;
+  PH_CHECK(check_config(&c));
+  if (v->n_layers < 1) return fail(PHOTON_ESHAPE, "n_layers must be >= 1");
+  if (v->steps < 1 || v->steps > 64) return fail(PHOTON_ESHAPE, "steps must be in [1, 64]");
+  return ok();
+}
+
+// the photon_config the shared helpers read (dtype, widths, norm, rope)
+photon_config vanilla_as_config(const photon_vanilla_config* v) {
+  photon_config c{};
+  c.n_levels = 2;
+  c.chunk[0] = v->steps; c.chunk[1] = 1;
+  c.d_model = v->d_model; c.n_heads = v->n_heads; c.mlp_mult = v->mlp_mult; c.vocab = v->vocab;
+  c.n_top = v->n_layers; c.n_enc1 = c.n_dec1 = c.n_dec0 = 1;
+  c.dtype = v->dtype; c.norm_eps = v->norm_eps; c.rope_theta = v->rope_theta;
+  return c;
+}
+
+std::vector<TensorDesc> vlayout(const photon_vanilla_config* v, uint64_t* bytes) {
+  const int64_t d = v->d_model, F = (int64_t)v->mlp_mult * d, V = v->vocab;
+  std::vector<TensorDesc> t;
+  t.push_back({"E", 0, 0, V, d, 0});
+  add_stack(t, "layers", v->n_layers, 0, d, F);
+  t.push_back({"W_out", 0, 0, V, d, 0});
+  uint64_t off = 0;
+  const int eb = v->dtype == PHOTON_BF16 ? 2 : 4;
+  for (auto& x : t) {
+    x.offset = align_up(off);
+    off = x.offset + (uint64_t)x.rows * x.cols * (x.is_gain ? 4 : eb);
+  }
+  if (bytes) *bytes = align_up(off);
+  return t;
+}
+
+struct VPlan {
+  int64_t cap = 0;
+  int nsplit = 1, head_tiles = 1;
+  Region kv, z, counter, rope, tok;
+  Region x, a, part, q, o, hid, apart, amv, ami;
+  uint64_t state_bytes = 0, scratch_bytes = 0, total = 0, off_state = 0, off_scratch = 0;
+};
+
+VPlan plan_vworkspace(const photon_vanilla_config* v, int64_t B, int64_t tokens) {
+  VPlan p;
+  const photon_config c = vanilla_as_config(v);
+  const int dt = c.dtype;
+  const int64_t d = v->d_model, H = v->n_heads, hd = d / H, F = (int64_t)v->mlp_mult * d, V = v->vocab;
+  const uint64_t eb = elem_bytes(&c);
+  p.cap = tokens;
+  p.nsplit = attn_decode_splits((int)B, (int)H, (int)tokens, 1);
+  p.head_tiles = gemm_argmax_tiles(dt, (int)B, (int)V, (int)d);
+  Cursor cur;
+  p.kv = cur.take((uint64_t)v->n_layers * 2 * B * H * tokens * hd * eb);
+  p.off_state = align_up(cur.pos);
+  p.z = cur.take((uint64_t)B * d * eb);
+  p.counter = cur.take(sizeof(int));
+  p.rope = cur.take((uint64_t)tokens * (hd / 2) * 2 * sizeof(float));
+  p.tok = cur.take((uint64_t)B * v->steps * sizeof(int));
+  p.off_scratch = align_up(cur.pos);
+  p.state_bytes = p.off_scratch - p.off_state;
+  p.x = cur.take((uint64_t)B * d * 4);
+  p.a = cur.take((uint64_t)B * d * eb);
+  p.part = cur.take(layer_part_bytes(&c, B));
+  p.q = cur.take((uint64_t)B * d * 4);
+  p.o = cur.take((uint64_t)B * d * eb);
+  p.hid = cur.take((uint64_t)B * F * eb);
+  p.apart = cur.take((uint64_t)B * H * p.nsplit * (hd + 2) * 4);
+  p.amv = cur.take((uint64_t)p.head_tiles * B * 4);
+  p.ami = cur.take((uint64_t)p.head_tiles * B * 4);
+  p.total = align_up(cur.pos);
+  p.scratch_bytes = p.total - p.off_scratch;
+  return p;
+}
+
+// prefill scratch: bs sequences of P tokens at a time (bs * P <= 65536 rows)
+struct VPrePlan {
+  int64_t bs = 1;
+  Region x, a, part, q, o, hid;
+  uint64_t total = 0;
+};
+
+VPrePlan plan_vprefill(const photon_vanilla_config* v, int64_t B, int64_t P) {
+  VPrePlan p;
+  const photon_config c = vanilla_as_config(v);
+  const int64_t d = v->d_model, F = (int64_t)v->mlp_mult * d;
+  const uint64_t eb = elem_bytes(&c);
+  p.bs = std::max<int64_t>(1, std::min<int64_t>(B, kPrefillRows / std::max<int64_t>(1, P)));
+  const int64_t R = p.bs * P;
+  uint64_t part = 0;
+  for (int64_t bs : {p.bs, B % p.bs})
+    if (bs) part = std::max(part, layer_part_bytes(&c, bs * P));
+  Cursor cur;
+  p.x = cur.take((uint64_t)R * d * 4);
+  p.a = cur.take((uint64_t)R * d * eb);
+  p.part = cur.take(part);
+  p.q = cur.take((uint64_t)R * d * 4);
+  p.o = cur.take((uint64_t)R * d * eb);
+  p.hid = cur.take((uint64_t)R * F * eb);
+  p.total = align_up(cur.pos);
+  return p;
+}
+
 // ------------------------------------------------------------ context
 struct LayerW {
   const float* g1;
@@ -313,6 +429,11 @@ struct Tracer {
 
 struct photon_ctx {
   photon_config cfg;
+  // flat baseline context (photon_vanilla_open): cfg mirrors vcfg's widths
+  bool vanilla = false;
+  photon_vanilla_config vcfg{};
+  StackW vlayers;
+  VPlan vplan;
   const unsigned char* wdec = nullptr;
   const unsigned char* wpre = nullptr;
   std::vector<TensorDesc> tensors;
@@ -685,6 +806,7 @@ photon_status photon_open(const photon_config* cfg, const void* d_w_decode, cons
 
 photon_status photon_release_prefill_weights(photon_ctx* c) {
   if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  if (c->vanilla) return fail(PHOTON_ESTATE, "a flat-baseline context has no prefill-only weights");
   c->wpre = nullptr;
   bind_weights(c);
   return ok();
@@ -706,6 +828,7 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
                              uint64_t scratch_bytes, const int32_t* d_prompt, int32_t batch, int32_t prompt_len,
                              int64_t max_tokens, void* stream) {
   if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  if (c->vanilla) return fail(PHOTON_ESTATE, "a flat-baseline context (use photon_vanilla_prefill)");
   if (mode != PHOTON_RECGEN && mode != PHOTON_HIERGEN) return fail(PHOTON_EINVAL, "bad mode %d", mode);
   if (!d_workspace || !d_scratch || !d_prompt) return fail(PHOTON_EINVAL, "NULL device pointer");
   if (((uintptr_t)d_workspace | (uintptr_t)d_scratch) % kAlign)
@@ -926,6 +1049,7 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
 
 photon_status photon_decode_chunk(photon_ctx* c, int32_t* d_tokens, float* d_logits, void* stream) {
   if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  if (c->vanilla) return fail(PHOTON_ESTATE, "a flat-baseline context (use photon_vanilla_decode)");
   if (!d_tokens) return fail(PHOTON_EINVAL, "d_tokens is NULL");
   if (!c->prefilled) return fail(PHOTON_ESTATE, "decode before prefill");
   const photon_config& cf = c->cfg;
@@ -972,13 +1096,16 @@ photon_status photon_decode_chunk(photon_ctx* c, int32_t* d_tokens, float* d_log
 photon_status photon_set_position(photon_ctx* c, int64_t tokens, void* stream) {
   if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
   if (!c->prefilled) return fail(PHOTON_ESTATE, "no prefill to rewind to");
-  const int64_t S = (int64_t)c->cfg.chunk[0] * c->cfg.chunk[1];
+  // a flat-baseline context counts tokens (steps per call), PHOTON top states
+  const int64_t S = c->vanilla ? c->vcfg.steps : (int64_t)c->cfg.chunk[0] * c->cfg.chunk[1];
   if (tokens % S || tokens < c->prompt_tokens || tokens > c->tokens)
     return fail(PHOTON_ESHAPE, "position %lld must be a multiple of %lld within [%lld, %lld]", (long long)tokens,
                 (long long)S, (long long)c->prompt_tokens, (long long)c->tokens);
-  HIP_TRY(launch_set_int((int*)(c->ws + c->plan.counter.off), (int)(tokens / S), (hipStream_t)stream));
+  int* counter = (int*)(c->ws + (c->vanilla ? c->vplan.counter.off : c->plan.counter.off));
+  const int64_t pos = c->vanilla ? tokens : tokens / S;
+  HIP_TRY(launch_set_int(counter, (int)pos, (hipStream_t)stream));
   c->tokens = tokens;
-  c->top_len = tokens / S;
+  c->top_len = pos;
   return ok();
 }
 
@@ -1086,6 +1213,251 @@ photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q, co
                        : kind == PHOTON_ATTN_CHUNK ? launch_attn_chunk(a, st)
                                                    : launch_attn_prefill(a, st);
   if (e != hipSuccess) return fail(PHOTON_EHIP, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------- flat baseline
+namespace {
+
+// One decode call of the flat baseline: `steps` tokens per sequence.  Every
+// position is read from the device counter, so one captured graph serves
+// every call.
+photon_status enqueue_vanilla(photon_ctx* c, float* d_logits, hipStream_t st) {
+  const photon_config& cf = c->cfg;
+  const photon_vanilla_config& v = c->vcfg;
+  const VPlan& wp = c->vplan;
+  unsigned char* ws = c->ws;
+  const int dt = cf.dtype, d = cf.d_model, H = cf.n_heads, hd = d / H, V = cf.vocab;
+  const int B = (int)c->B, steps = v.steps;
+  int* counter = (int*)(ws + wp.counter.off);
+  StackBufs b{(float*)(ws + wp.x.off), ws + wp.a.off, (float*)(ws + wp.part.off), (float*)(ws + wp.q.off),
+              ws + wp.o.off, ws + wp.hid.off, (float*)(ws + wp.apart.off)};
+  void* z = ws + wp.z.off;
+  int* tok = (int*)(ws + wp.tok.off);
+  const int eb = elem_bytes(&cf);
+  for (int j = 0; j < steps; ++j) {
+    GemmCall g{};
+    g.dtype = dt; g.A = z; g.lda = d; g.W = c->W_out; g.M = B; g.N = V; g.K = d;
+    g.epi = EPI_ARGMAX;
+    g.C = d_logits ? d_logits + (int64_t)j * V : nullptr;
+    g.ldc = (int64_t)steps * V;
+    g.amax_val = (float*)(ws + wp.amv.off); g.amax_idx = (int*)(ws + wp.ami.off);
+    PH_TRY(run_gemm(c, PHOTON_K_GEMM_HEAD, g, st));
+    // token j of every sequence, then its embedding and norm as the stack input
+    ArgmaxNext an{g.amax_val, g.amax_idx, wp.head_tiles, B, steps, 1, j, tok,
+                  nullptr, 0, c->E, b.x, b.a, c->vlayers.layers[0].g1, d, cf.norm_eps};
+    PH_TRY(traced(c, PHOTON_K_ARGMAX, (double)B * d * (4 + 2 * eb), 0, st, "argmax_next",
+                  [&] { return launch_argmax_next(dt, an, st); }));
+    StackRun r{};
+    r.M = B; r.rows_per_seq = 1; r.G = B;
+    r.kv = KvTarget{ws + wp.kv.off, (int64_t)B * H * wp.cap * hd, true, (int64_t)H * wp.cap * hd, (int)wp.cap, 0};
+    r.pos_add = 0; r.pos_dev = counter; r.pos_mul = 1; r.rope = (const float*)(ws + wp.rope.off);
+    r.kind = ATT_DECODE; r.Q = 1; r.L_dev = counter; r.L_mul = 1; r.L_add = 1; r.nsplit = wp.nsplit;
+    r.L_acct = (int)(c->tokens + j + 1);
+    r.out = z; r.out_rows = B; r.in_stride = 1; r.in_off = 0;
+    PH_TRY(run_stack(c, c->vlayers, b, r, st));
+    HIP_TRY(launch_add_int(counter, 1, st));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+photon_status photon_vanilla_kv_bytes(const photon_vanilla_config* cfg, int32_t batch, int64_t tokens,
+                                      photon_kv_report* out) {
+  PH_TRY(check_vconfig(cfg));
+  if (!out) return fail(PHOTON_EINVAL, "out is NULL");
+  if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
+  if (tokens < 1) return fail(PHOTON_ESHAPE, "tokens must be >= 1");
+  const VPlan p = plan_vworkspace(cfg, batch, tokens);
+  memset(out, 0, sizeof *out);
+  out->top_len = p.cap;
+  out->top_kv = p.kv.bytes;
+  out->state = p.state_bytes;
+  out->decode_scratch = p.scratch_bytes;
+  out->workspace_total = p.total;
+  vlayout(cfg, &out->weights_decode);
+  out->off_top_kv = p.kv.off;
+  out->off_state = p.z.off;
+  out->off_scratch = p.off_scratch;
+  return ok();
+}
+
+photon_status photon_vanilla_prefill_scratch_bytes(const photon_vanilla_config* cfg, int32_t batch,
+                                                   int32_t prompt_len, uint64_t* out) {
+  PH_TRY(check_vconfig(cfg));
+  if (!out) return fail(PHOTON_EINVAL, "out is NULL");
+  if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
+  if (prompt_len < cfg->steps || prompt_len % cfg->steps)
+    return fail(PHOTON_ESHAPE, "prompt_len %d must be a positive multiple of steps = %d", prompt_len, cfg->steps);
+  *out = plan_vprefill(cfg, batch, prompt_len).total;
+  return ok();
+}
+
+photon_status photon_vanilla_weight_layout(const photon_vanilla_config* cfg, uint64_t* bytes, int32_t* n_tensors) {
+  PH_TRY(check_vconfig(cfg));
+  auto t = vlayout(cfg, bytes);
+  if (n_tensors) *n_tensors = (int32_t)t.size();
+  return ok();
+}
+
+photon_status photon_vanilla_weight_tensor(const photon_vanilla_config* cfg, int32_t index,
+                                           photon_tensor_info* out) {
+  PH_TRY(check_vconfig(cfg));
+  if (!out) return fail(PHOTON_EINVAL, "out is NULL");
+  auto v = vlayout(cfg, nullptr);
+  if (index < 0 || index >= (int32_t)v.size()) return fail(PHOTON_EINVAL, "tensor index %d out of range", index);
+  const TensorDesc& t = v[index];
+  memset(out, 0, sizeof *out);
+  snprintf(out->name, sizeof out->name, "%s", t.name.c_str());
+  out->blob = 0;
+  out->dtype = t.is_gain ? PHOTON_F32 : cfg->dtype;
+  out->offset = t.offset;
+  out->rows = t.rows;
+  out->cols = t.cols;
+  return ok();
+}
+
+photon_status photon_vanilla_open(const photon_vanilla_config* cfg, const void* d_weights, photon_ctx** out) {
+  PH_TRY(check_vconfig(cfg));
+  if (!out) return fail(PHOTON_EINVAL, "out is NULL");
+  if (!d_weights) return fail(PHOTON_EINVAL, "weight blob is NULL");
+  if ((uintptr_t)d_weights % kAlign) return fail(PHOTON_EINVAL, "weight blob must be 256-byte aligned");
+  photon_ctx* c = new (std::nothrow) photon_ctx();
+  if (!c) return fail(PHOTON_EINVAL, "out of host memory");
+  c->vanilla = true;
+  c->vcfg = *cfg;
+  c->cfg = vanilla_as_config(cfg);
+  c->wdec = (const unsigned char*)d_weights;
+  c->tensors = vlayout(cfg, nullptr);
+  c->E = tensor_ptr(c, "E");
+  c->W_out = tensor_ptr(c, "W_out");
+  bind_stack(c, c->vlayers, "layers", cfg->n_layers);
+  *out = c;
+  return ok();
+}
+
+photon_status photon_vanilla_prefill(photon_ctx* c, void* d_workspace, uint64_t ws_bytes, void* d_scratch,
+                                     uint64_t scratch_bytes, const int32_t* d_prompt, int32_t batch,
+                                     int32_t prompt_len, int64_t max_tokens, void* stream) {
+  if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  if (!c->vanilla) return fail(PHOTON_ESTATE, "not a flat-baseline context (use photon_prefill)");
+  if (!d_workspace || !d_scratch || !d_prompt) return fail(PHOTON_EINVAL, "NULL device pointer");
+  if (((uintptr_t)d_workspace | (uintptr_t)d_scratch) % kAlign)
+    return fail(PHOTON_EINVAL, "workspace and scratch must be 256-byte aligned");
+  const photon_vanilla_config& v = c->vcfg;
+  const photon_config& cf = c->cfg;
+  if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
+  if (prompt_len < v.steps || prompt_len % v.steps)
+    return fail(PHOTON_ESHAPE, "prompt_len %d must be a positive multiple of steps = %d", prompt_len, v.steps);
+  if (max_tokens < prompt_len) return fail(PHOTON_ECAPACITY, "max_tokens %lld < prompt_len %d", (long long)max_tokens, prompt_len);
+  const VPlan wp = plan_vworkspace(&v, batch, max_tokens);
+  if (ws_bytes < wp.total)
+    return fail(PHOTON_ECAPACITY, "workspace holds %llu bytes, needs %llu", (unsigned long long)ws_bytes,
+                (unsigned long long)wp.total);
+  const VPrePlan pp = plan_vprefill(&v, batch, prompt_len);
+  if (scratch_bytes < pp.total)
+    return fail(PHOTON_ECAPACITY, "prefill scratch holds %llu bytes, needs %llu", (unsigned long long)scratch_bytes,
+                (unsigned long long)pp.total);
+  {
+    const int d = cf.d_model, F = cf.mlp_mult * d;
+    for (int64_t M : {(int64_t)batch, pp.bs * prompt_len, (batch % pp.bs) * (int64_t)prompt_len}) {
+      if (M == 0) continue;
+      for (auto nk : {std::pair<int, int>{3 * d, d}, {d, d}, {F, d}, {d, F}})
+        if (M > 0x7fffffff || !gemm_supported(cf.dtype, (int)M, nk.first, nk.second))
+          return fail(PHOTON_EUNSUPPORTED, "GEMM %lldx%dx%d unsupported", (long long)M, nk.first, nk.second);
+    }
+    if (!gemm_supported(cf.dtype, batch, cf.vocab, d)) return fail(PHOTON_EUNSUPPORTED, "head GEMM unsupported");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = cf.dtype, d = cf.d_model, H = cf.n_heads, hd = d / H;
+  const int eb = elem_bytes(&cf);
+  unsigned char* ws = (unsigned char*)d_workspace;
+  unsigned char* sc = (unsigned char*)d_scratch;
+  c->prefilled = false;
+  if (c->graph) {
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+  }
+  c->ws = ws;
+  c->vplan = wp;
+  c->B = batch;
+  c->max_tokens = max_tokens;
+  float* rope = (float*)(ws + wp.rope.off);
+  HIP_TRY(launch_rope_table(rope, (int)wp.cap, hd, cf.rope_theta, st));
+  StackBufs bufs{(float*)(sc + pp.x.off), sc + pp.a.off, (float*)(sc + pp.part.off), (float*)(sc + pp.q.off),
+                 sc + pp.o.off, sc + pp.hid.off, nullptr};
+  for (int64_t b0 = 0; b0 < batch; b0 += pp.bs) {
+    const int bs = (int)std::min<int64_t>(pp.bs, batch - b0);
+    const int R = bs * prompt_len;
+    // stack input: x = E[token], a = its first norm
+    RowsEpi e{};
+    e.P = bufs.x; e.ksplit = 0; e.pstride = 0; e.ldp = d;   // no slabs: x is the embedding alone
+    e.ids = d_prompt + b0 * prompt_len; e.E = c->E;
+    e.x_out = bufs.x; e.g = c->vlayers.layers[0].g1; e.a_out = bufs.a; e.a_ld = d;
+    e.R = R; e.d = d; e.row_stride = 1; e.row_off = 0; e.eps = cf.norm_eps;
+    PH_TRY(traced(c, PHOTON_K_EMBED, (double)R * (4 + d * (eb + 4.0 + eb)), 0, st, "rows_epilogue",
+                  [&] { return launch_rows_epilogue(dt, e, st); }));
+    StackRun r{};
+    r.M = R; r.rows_per_seq = prompt_len; r.G = bs;
+    r.kv = KvTarget{ws + wp.kv.off, (int64_t)batch * H * wp.cap * hd, true, (int64_t)H * wp.cap * hd, (int)wp.cap,
+                    (int)b0};
+    r.pos_add = 0; r.pos_dev = nullptr; r.pos_mul = 0; r.rope = rope;
+    r.kind = ATT_PREFILL; r.Q = prompt_len; r.L_host = prompt_len; r.nsplit = 1; r.L_acct = prompt_len;
+    // final norm only for the last position of each sequence: z
+    r.out = ws + wp.z.off + (uint64_t)b0 * d * eb; r.out_rows = bs; r.in_stride = prompt_len;
+    r.in_off = prompt_len - 1;
+    PH_TRY(run_stack(c, c->vlayers, bufs, r, st));
+  }
+  HIP_TRY(launch_set_int((int*)(ws + wp.counter.off), prompt_len, st));
+  c->top_len = prompt_len;
+  c->tokens = prompt_len;
+  c->prompt_tokens = prompt_len;
+  c->prefilled = true;
+  return ok();
+}
+
+photon_status photon_vanilla_decode(photon_ctx* c, int32_t* d_tokens, float* d_logits, void* stream) {
+  if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  if (!c->vanilla) return fail(PHOTON_ESTATE, "not a flat-baseline context (use photon_decode_chunk)");
+  if (!d_tokens) return fail(PHOTON_EINVAL, "d_tokens is NULL");
+  if (!c->prefilled) return fail(PHOTON_ESTATE, "decode before prefill");
+  const int steps = c->vcfg.steps;
+  if (c->tokens + steps > c->max_tokens)
+    return fail(PHOTON_ECAPACITY, "decode would pass max_tokens %lld", (long long)c->max_tokens);
+  hipStream_t st = (hipStream_t)stream;
+  const int B = (int)c->B;
+  int* tok = (int*)(c->ws + c->vplan.tok.off);
+  if (c->use_graph && !d_logits && c->tr.mask == 0) {
+    if (!c->graph) {
+      if (!c->cap[0]) HIP_TRY(hipStreamCreateWithFlags(&c->cap[0], hipStreamNonBlocking));
+      HIP_TRY(hipStreamBeginCapture(c->cap[0], hipStreamCaptureModeRelaxed));
+      const photon_status s = enqueue_vanilla(c, nullptr, c->cap[0]);
+      hipGraph_t g = nullptr;
+      const hipError_t e = hipStreamEndCapture(c->cap[0], &g);
+      if (s != PHOTON_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return s;
+      }
+      if (e != hipSuccess) return fail(PHOTON_EHIP, "graph capture: %s", hipGetErrorString(e));
+      const hipError_t ie = hipGraphInstantiate(&c->graph, g, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(g);
+      if (ie != hipSuccess) {
+        c->graph = nullptr;
+        return fail(PHOTON_EHIP, "graph instantiate: %s", hipGetErrorString(ie));
+      }
+    }
+    HIP_TRY(hipGraphLaunch(c->graph, st));
+  } else {
+    PH_TRY(enqueue_vanilla(c, d_logits, st));
+  }
+  HIP_TRY(hipMemcpyAsync(d_tokens, tok, (size_t)B * steps * sizeof(int), hipMemcpyDeviceToDevice, st));
+  c->tokens += steps;
+  c->top_len = c->tokens;
   return ok();
 }
 

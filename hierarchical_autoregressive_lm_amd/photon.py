@@ -40,6 +40,14 @@ class Config(ctypes.Structure):
                 ("rope_theta", ctypes.c_float)]
 
 
+class VanillaConfig_(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("mlp_mult", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("steps", ctypes.c_int32)]
+
+
 class KvReport(ctypes.Structure):
     _fields_ = [("top_len", ctypes.c_int64), ("lower_len", ctypes.c_int64),
                 ("top_kv", ctypes.c_uint64), ("lower_kv", ctypes.c_uint64),
@@ -78,7 +86,10 @@ EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
            "photon_last_error", "photon_prefill", "photon_decode_chunk",
            "photon_position", "photon_set_position", "photon_use_graphs",
            "photon_trace_enable", "photon_trace_read",
-           "photon_attention_scratch_bytes", "photon_attention"]
+           "photon_attention_scratch_bytes", "photon_attention",
+           "photon_vanilla_kv_bytes", "photon_vanilla_prefill_scratch_bytes",
+           "photon_vanilla_weight_layout", "photon_vanilla_weight_tensor",
+           "photon_vanilla_open", "photon_vanilla_prefill", "photon_vanilla_decode"]
 
 
 def _load():
@@ -106,6 +117,13 @@ def _load():
         "photon_trace_read": [V, P(TraceStat)],
         "photon_attention_scratch_bytes": [i32, i32, i32, i32, i32, i32, P(u64)],
         "photon_attention": [i32, i32, V, V, V, V, i32, i32, i32, i32, i32, i32, V, u64, V],
+        "photon_vanilla_kv_bytes": [P(VanillaConfig_), i32, i64, P(KvReport)],
+        "photon_vanilla_prefill_scratch_bytes": [P(VanillaConfig_), i32, i32, P(u64)],
+        "photon_vanilla_weight_layout": [P(VanillaConfig_), P(u64), P(i32)],
+        "photon_vanilla_weight_tensor": [P(VanillaConfig_), i32, P(TensorInfo)],
+        "photon_vanilla_open": [P(VanillaConfig_), V, P(V)],
+        "photon_vanilla_prefill": [V, V, u64, V, u64, V, i32, i32, i64, V],
+        "photon_vanilla_decode": [V, V, V, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -159,6 +177,25 @@ def weight_layout(cfg):
         tensors.append({"name": t.name.decode(), "blob": t.blob, "dtype": t.dtype,
                         "offset": t.offset, "rows": t.rows, "cols": t.cols})
     return dec.value, pre.value, tensors
+
+
+def make_vanilla_config(cfg, steps):
+    """photon_vanilla_config from a photon_inputs.VanillaConfig; `steps`
+    tokens per sequence per decode call."""
+    c = VanillaConfig_()
+    c.d_model, c.n_heads, c.mlp_mult, c.vocab = cfg.d_model, cfg.n_heads, cfg.mlp_mult, cfg.vocab
+    c.n_layers = cfg.n_layers
+    c.dtype = BF16 if cfg.dtype == "bf16" else F32
+    c.norm_eps, c.rope_theta = cfg.norm_eps, cfg.rope_theta
+    c.steps = steps
+    return c
+
+
+def vanilla_kv_bytes(cfg, steps, batch, tokens):
+    rep = KvReport()
+    _check(_lib.photon_vanilla_kv_bytes(ctypes.byref(make_vanilla_config(cfg, steps)), batch, tokens,
+                                        ctypes.byref(rep)))
+    return rep.as_dict()
 
 
 def _stream_handle(torch):
@@ -347,3 +384,96 @@ class Photon:
         eb = 2 if cfg.dtype == "bf16" else 4
         off = self.report_["off_state"]
         return self.workspace[off:off + self.batch * cfg.d_model * eb].view(dt).view(self.batch, cfg.d_model)
+
+
+class Vanilla(Photon):
+    """The flat Transformer baseline on the current GPU (one weight blob and
+    a context from photon_vanilla_open); decode calls emit `steps` tokens per
+    sequence.  Shares Photon's position, graph, tracing and snapshot
+    helpers (the state region holds the last position's stack output)."""
+
+    def __init__(self, cfg, weights, steps, device="cuda"):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.steps = steps
+        self.device = torch.device(device)
+        self.c = make_vanilla_config(cfg, steps)
+        nbytes, n = ctypes.c_uint64(), ctypes.c_int32()
+        _check(_lib.photon_vanilla_weight_layout(ctypes.byref(self.c), ctypes.byref(nbytes), ctypes.byref(n)))
+        blob = torch.zeros(nbytes.value, dtype=torch.uint8, device=self.device)
+        for i in range(n.value):
+            t = TensorInfo()
+            _check(_lib.photon_vanilla_weight_tensor(ctypes.byref(self.c), i, ctypes.byref(t)))
+            w = np.ascontiguousarray(weights[t.name.decode()], dtype=np.float32)
+            assert w.size == t.rows * t.cols, t.name
+            src = torch.from_numpy(w.reshape(-1)).to(self.device)
+            if t.dtype == BF16:
+                src = src.to(torch.bfloat16)
+            raw = src.view(torch.uint8)
+            blob[t.offset:t.offset + raw.numel()].copy_(raw)
+        self.w_decode, self.w_prefill = blob, None
+        self.weight_bytes = {"decode": nbytes.value, "prefill_only": 0}
+        ctx = ctypes.c_void_p()
+        _check(_lib.photon_vanilla_open(ctypes.byref(self.c), ctypes.c_void_p(blob.data_ptr()), ctypes.byref(ctx)))
+        self.ctx = ctx
+        self.workspace = None
+        self.mode = "vanilla"
+        self.batch = None
+
+    def release_prefill_weights(self):
+        pass
+
+    def report(self, batch, tokens, mode=None):
+        return vanilla_kv_bytes(self.cfg, self.steps, batch, tokens)
+
+    def prefill(self, prompt, max_tokens, mode=None):
+        torch = self.torch
+        B, P = prompt.shape
+        rep = self.report(B, max_tokens)
+        if self.workspace is None or self.workspace.numel() < rep["workspace_total"]:
+            self.workspace = torch.empty(rep["workspace_total"], dtype=torch.uint8, device=self.device)
+        n = ctypes.c_uint64()
+        _check(_lib.photon_vanilla_prefill_scratch_bytes(ctypes.byref(self.c), B, P, ctypes.byref(n)))
+        scratch = torch.empty(n.value, dtype=torch.uint8, device=self.device)
+        prompt = prompt.to(device=self.device, dtype=torch.int32).contiguous()
+        _check(_lib.photon_vanilla_prefill(self.ctx, ctypes.c_void_p(self.workspace.data_ptr()),
+                                           self.workspace.numel(), ctypes.c_void_p(scratch.data_ptr()), n.value,
+                                           ctypes.c_void_p(prompt.data_ptr()), B, P, max_tokens,
+                                           _stream_handle(torch)))
+        self._scratch_hold = (scratch, prompt)
+        self.report_ = rep
+        self.batch = B
+
+    def decode_chunk(self, tokens_out, logits_out=None):
+        """tokens_out: int32 CUDA [B, steps]; logits_out: float32 [B, steps, V] or None."""
+        lp = ctypes.c_void_p(logits_out.data_ptr()) if logits_out is not None else None
+        _check(_lib.photon_vanilla_decode(self.ctx, ctypes.c_void_p(tokens_out.data_ptr()), lp,
+                                          _stream_handle(self.torch)))
+
+    def generate(self, prompt, new_tokens, mode=None, logits=False, max_tokens=None):
+        torch = self.torch
+        B, P = prompt.shape
+        S = self.steps
+        if new_tokens % S:
+            raise ValueError("new_tokens must be a multiple of steps")
+        self.prefill(prompt, max_tokens or P + new_tokens)
+        toks = torch.empty((new_tokens // S, B, S), dtype=torch.int32, device=self.device)
+        lg = torch.empty((new_tokens // S, B, S, self.cfg.vocab), dtype=torch.float32,
+                         device=self.device) if logits else None
+        for c in range(new_tokens // S):
+            self.decode_chunk(toks[c], lg[c] if logits else None)
+        toks = toks.permute(1, 0, 2).reshape(B, new_tokens)
+        if logits:
+            lg = lg.permute(1, 0, 2, 3).reshape(B, new_tokens, self.cfg.vocab)
+        return toks, lg
+
+    def kv(self):
+        """Token K/V as a tensor [n_layers, 2, B, H, cap, hd] (storage dtype)."""
+        torch = self.torch
+        rep, cfg = self.report_, self.cfg
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        eb = 2 if cfg.dtype == "bf16" else 4
+        raw = self.workspace[rep["off_top_kv"]:rep["off_top_kv"] + rep["top_kv"]]
+        return raw.view(dt).view(cfg.n_layers, 2, self.batch, cfg.n_heads, rep["top_len"], cfg.head_dim)
+

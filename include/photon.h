@@ -223,6 +223,61 @@ photon_status photon_set_position(photon_ctx* ctx, int64_t tokens,
 photon_status photon_use_graphs(photon_ctx* ctx, int32_t enable);
 
 /* ------------------------------------------------------------------------
+ * Flat Transformer baseline: the comparison model of the explainer's
+ * decode-heavy table (a vanilla decoder whose K/V cache holds every token).
+ * One causal stack of n_layers blocks -- the same pre-norm blocks as the
+ * PHOTON stacks -- over the tokens, an embedding E[vocab][d] and an untied
+ * output head W_out[vocab][d], in one weight blob with tensors "E",
+ * "layers.<l>.{g1,Wq,Wk,Wv,Wo,g2,W1,W2}", "layers.gf", "W_out".
+ * A context from photon_vanilla_open works with photon_close,
+ * photon_position (top_len reports tokens), photon_set_position,
+ * photon_use_graphs and the tracing calls; photon_vanilla_prefill and
+ * photon_vanilla_decode take the place of photon_prefill and
+ * photon_decode_chunk (each pair returns PHOTON_ESTATE on the other kind of
+ * context).  Same rounding contract, limits and conventions as above.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t d_model, n_heads, mlp_mult, vocab, n_layers;
+  photon_dtype dtype;
+  float norm_eps, rope_theta;
+  int32_t steps;          /* tokens per sequence per photon_vanilla_decode */
+} photon_vanilla_config;
+
+/* top_len / top_kv: the token K/V ([n_layers][K,V][batch][heads][tokens]
+ * [head_dim]); the level-1 and decoder fields are 0; weights_decode is the
+ * blob, weights_prefill_only 0. */
+photon_status photon_vanilla_kv_bytes(const photon_vanilla_config* cfg,
+                                      int32_t batch, int64_t tokens,
+                                      photon_kv_report* out);
+photon_status photon_vanilla_prefill_scratch_bytes(
+    const photon_vanilla_config* cfg, int32_t batch, int32_t prompt_len,
+    uint64_t* out);
+photon_status photon_vanilla_weight_layout(const photon_vanilla_config* cfg,
+                                           uint64_t* bytes, int32_t* n_tensors);
+photon_status photon_vanilla_weight_tensor(const photon_vanilla_config* cfg,
+                                           int32_t index,
+                                           photon_tensor_info* out);
+photon_status photon_vanilla_open(const photon_vanilla_config* cfg,
+                                  const void* d_weights, photon_ctx** out);
+/* The prompt through the causal stack at positions 0 .. prompt_len-1,
+ * writing every position's K/V and the last position's stack output.
+ * prompt_len: a positive multiple of steps.  Workspace and scratch as for
+ * photon_prefill, sized by the two vanilla size queries. */
+photon_status photon_vanilla_prefill(photon_ctx* ctx, void* d_workspace,
+                                     uint64_t ws_bytes, void* d_scratch,
+                                     uint64_t scratch_bytes,
+                                     const int32_t* d_prompt, int32_t batch,
+                                     int32_t prompt_len, int64_t max_tokens,
+                                     void* stream);
+/* `steps` greedy tokens per sequence: logits = W_out z, token = first
+ * argmax, then the token's embedding through the stack at the next position
+ * over every cached token gives the next z.  d_tokens [batch][steps];
+ * d_logits NULL or [batch][steps][vocab].  PHOTON_ECAPACITY past
+ * max_tokens. */
+photon_status photon_vanilla_decode(photon_ctx* ctx, int32_t* d_tokens,
+                                    float* d_logits, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stand-alone decode attention (no context, no model): the two kernels the
  * decode path runs over a cache, applied to caller buffers.
  *   PHOTON_ATTN_GLOBAL  the top encoder's attention over the global coarse

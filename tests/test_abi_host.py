@@ -227,3 +227,53 @@ def test_attention_rejects_bad_arguments_before_any_device_call():
     assert "scratch" in lib.photon_last_error().decode()
     assert call(kind=G, G_=2, H=2, L=4000, cap=4096, sc=V(8 << 20), sb=need - 1) == P.ESHAPE
     assert call(kind=G, G_=2, H=2, L=4000, cap=4096, sc=V((8 << 20) + 16), sb=need) == P.EINVAL
+
+
+def test_vanilla_kv_bytes_and_layout():
+    # the flat baseline's cache: K and V of every layer for every token
+    for idx in (1, 2, 3):
+        wl = pi.get(idx)
+        v = pi.vanilla_of(wl.cfg)
+        r = P.vanilla_kv_bytes(v, wl.cfg.S, wl.batch, wl.max_tokens)
+        assert r["top_kv"] == O.vanilla_kv_bytes(v, wl.batch, wl.max_tokens)
+        assert r["top_len"] == wl.max_tokens and r["lower_kv"] == 0 and r["dec_kv"] == 0
+        assert r["weights_prefill_only"] == 0
+        mats = sum(int(np.prod(s)) for n, s in pi.weight_shapes(v) if len(s) == 2)
+        gains = sum(int(np.prod(s)) for n, s in pi.weight_shapes(v) if len(s) == 1)
+        eb = 2 if v.dtype == "bf16" else 4
+        assert mats * eb + gains * 4 <= r["weights_decode"] <= mats * eb + gains * 4 + 256 * len(pi.weight_shapes(v))
+    c = P.make_vanilla_config(pi.vanilla_of(pi.get(2).cfg), 16)
+    nb, n = ctypes.c_uint64(), ctypes.c_int32()
+    assert P._lib.photon_vanilla_weight_layout(ctypes.byref(c), ctypes.byref(nb), ctypes.byref(n)) == P.OK
+    names = []
+    for i in range(n.value):
+        t = P.TensorInfo()
+        assert P._lib.photon_vanilla_weight_tensor(ctypes.byref(c), i, ctypes.byref(t)) == P.OK
+        names.append(t.name.decode())
+    assert names == pi.weight_names(pi.vanilla_of(pi.get(2).cfg))
+
+
+def test_vanilla_errors_before_any_device_call():
+    lib = P._lib
+    V = ctypes.c_void_p
+    v = pi.vanilla_of(pi.get(1).cfg)
+    c = P.make_vanilla_config(v, 16)
+    ctx = ctypes.c_void_p()
+    assert lib.photon_vanilla_open(ctypes.byref(c), V(1 << 20), ctypes.byref(ctx)) == P.OK
+    ws, sc, pr, tok = V(4 << 20), V(8 << 20), V(12 << 20), V(16 << 20)
+    assert lib.photon_vanilla_decode(ctx, tok, None, None) == P.ESTATE          # before prefill
+    assert lib.photon_decode_chunk(ctx, tok, None, None) == P.ESTATE           # wrong kind of context
+    assert lib.photon_prefill(ctx, 0, ws, 1 << 30, sc, 1 << 30, pr, 2, 64, 96, None) == P.ESTATE
+    need = P.vanilla_kv_bytes(v, 16, 2, 96)["workspace_total"]
+    assert lib.photon_vanilla_prefill(ctx, ws, need, sc, 1 << 30, pr, 2, 60, 96, None) == P.ESHAPE  # 60 % 16
+    assert lib.photon_vanilla_prefill(ctx, ws, need - 1, sc, 1 << 30, pr, 2, 64, 96, None) == P.ECAPACITY
+    assert lib.photon_vanilla_prefill(ctx, ws, need, sc, 1 << 30, pr, 2, 64, 32, None) == P.ECAPACITY
+    assert lib.photon_vanilla_prefill(ctx, V((4 << 20) + 8), need, sc, 1 << 30, pr, 2, 64, 96, None) == P.EINVAL
+    lib.photon_close(ctx)
+    bad = P.make_vanilla_config(v, 0)
+    assert lib.photon_vanilla_open(ctypes.byref(bad), V(1 << 20), ctypes.byref(ctx)) == P.ESHAPE
+    # a PHOTON context rejects the flat-baseline calls
+    f = FakeCtx()
+    assert lib.photon_vanilla_decode(f.ctx, tok, None, None) == P.ESTATE
+    assert lib.photon_vanilla_prefill(f.ctx, ws, need, sc, 1 << 30, pr, 2, 64, 96, None) == P.ESTATE
+    f.close()
