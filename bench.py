@@ -15,7 +15,8 @@ decode weights + top K/V + decoder K/V + state, the whole path's fraction of
 the HBM roofline (algorithmic bytes per chunk at 8 TB/s), the achieved
 bandwidth of the kernel class that moves the most bytes (HIP events around
 each of its launches, in a traced pass over the same steps right after the
-timed ones), per-class figures, and the CPU oracle timed on a bounded sample
+timed ones) against 8 TB/s and against a measured plain copy, per-class
+figures, and the CPU oracle timed on a bounded sample
 of the same workload.
 """
 import argparse
@@ -73,6 +74,43 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False):
             reps = max(1, round(target_s / dt))
             dt += sum(decode(copy(st0)) for _ in range(reps - 1))
     return reps * seqs * wl.new_tokens / dt, dt, seqs, reps
+
+
+def host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS numpy calls."""
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+    return model, ", ".join(blas) or None
+
+
+def copy_peak(torch):
+    """Achievable HBM bandwidth: a plain device-to-device copy of 1 GiB
+    (read + write counted), alternating two sources so no pass is served
+    from the Infinity Cache; GB/s."""
+    n = 1 << 28
+    srcs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    dst = torch.empty(n, dtype=torch.float32, device="cuda")
+    for i in range(3):
+        dst.copy_(srcs[i % 2])
+    iters = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        dst.copy_(srcs[i % 2])
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del srcs, dst
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def measured_traffic(wl, cls):
@@ -291,9 +329,16 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "traffic_over_algorithmic": traffic_ratio, "traffic_source": traffic_src,
+                    "copy_peak": None, "frac_of_copy": None,
                     "kernel": dominant, "launches": dom["launches"],
                     "avg_us": round(dom["ms"] * 1e3 / dom["launches"], 2),
                     "bytes_per_launch": round(dom["bytes"] / dom["launches"])}
+
+    if roofline:
+        cp = copy_peak(torch)
+        roofline["copy_peak"] = round(cp, 1)
+        roofline["frac_of_copy"] = round(roofline["achieved"] / cp, 4)
+        log(f"copy peak {cp:.0f} GB/s")
 
     attn = None
     if not args.no_attn_standalone and not vanilla:
@@ -311,7 +356,9 @@ def main():
         prec = "float64" if cfg.dtype == "f32" else "float64 with the bf16 rounding contract"
         rep_txt = f", decoded {reps} times from the same prefill" if reps > 1 else ""
         what = "flat-baseline" if vanilla else "RecGen"
+        cpu_model, blas = host_info()
         cpu = {"value": round(cv, 2), "unit": "tok/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model, "blas": blas,
                "sample": f"{what} decode phase of {ns} of {B} sequences, all {wl.chunks} chunks{rep_txt} "
                          f"({reps * ns * wl.new_tokens} tokens, {cdt:.1f} s), numpy {prec}"}
 

@@ -45,6 +45,8 @@ import math
 import numpy as np
 from scipy.special import erf
 
+from . import photon_sampling as S_
+
 F64 = np.float64
 
 
@@ -287,7 +289,7 @@ def prefill(model, prompt, mode="recgen", log=None):
     return State(ct, h[:, -1], n, c1 if mode == "hiergen" else None)
 
 
-def _decode_tokens(model, A_hat, forced_tokens=None):
+def _decode_tokens(model, A_hat, forced_tokens=None, sampling=None, t0=0):
     """Top-down token generation for one chunk [modules], [recgen].
 
     A_hat: [B, C2, d] level-1 decoder outputs.  Each of the B*C2 level-1
@@ -299,6 +301,9 @@ def _decode_tokens(model, A_hat, forced_tokens=None):
     Returns (tokens [B, C2*C1], logits [B, C2*C1, V]) in k-major order,
     token index k*C1 + j.  forced_tokens [B, C2*C1] replaces the fed-back
     token (teacher forcing); the argmax is still reported.
+    sampling = dict(temperature, top_k, seed) draws every token instead
+    (photon_sampling.sample; sequence b, absolute position t0 + k*C1 + j)
+    in place of the argmax.
     """
     cfg = model.cfg
     B, C2, d = A_hat.shape
@@ -318,7 +323,12 @@ def _decode_tokens(model, A_hat, forced_tokens=None):
         z = model.stack("dec0", cfg.n_dec0, x[:, None, :], np.array([j]), cache)
         lg = model.logits(z[:, 0, :])
         logits[:, j] = lg
-        toks[:, j] = np.argmax(lg, axis=-1)           # first maximum
+        if sampling is None:
+            toks[:, j] = np.argmax(lg, axis=-1)       # first maximum
+        else:
+            for r in range(B * C2):
+                toks[r, j] = S_.sample(lg[r], sampling["temperature"], sampling["top_k"], sampling["seed"],
+                                       r // C2, t0 + (r % C2) * C1 + j)
         prev = toks[:, j] if forced is None else forced[:, j]
     return toks.reshape(B, C2 * C1), logits.reshape(B, C2 * C1, cfg.vocab)
 
@@ -334,7 +344,7 @@ def _top_step(model, state, u):
 
 
 def decode_chunk(model, state, mode="recgen", forced_tokens=None,
-                 forced_u=None):
+                 forced_u=None, sampling=None):
     """Generate the next chunk of S = C1*C2 tokens; updates ``state``.
 
     Converter^2 expands h_{i-1} into C2 conditioning vectors; the level-1
@@ -346,6 +356,9 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
               C2 new level-1 positions with the kept level-1 cache ->
               A_i -> u_i = Chunker^2(A_i).
     forced_u replaces u_i (used to force the premise of Theorem A.6).
+    sampling (dict(temperature, top_k, seed)) draws the tokens instead of
+    the argmax; the chunk's first token is at absolute position
+    top_len * S.
     Returns a dict with tokens, logits, A_hat, u (and A for HierGen).
     """
     cfg = model.cfg
@@ -353,7 +366,7 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
     C1, C2, d = cfg.C1, cfg.C2, cfg.d_model
     c1 = model.converter("W_cv2", state.h)            # [B, C2, d]
     A_hat = model.stack("dec1", cfg.n_dec1, c1, np.arange(C2), None)
-    toks, logits = _decode_tokens(model, A_hat, forced_tokens)
+    toks, logits = _decode_tokens(model, A_hat, forced_tokens, sampling, state.top_len * cfg.S)
     out = {"tokens": toks, "logits": logits, "A_hat": A_hat}
     if mode == "recgen":
         u = model.chunker("W_ch2", A_hat)[:, 0]
@@ -373,7 +386,7 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
     return out
 
 
-def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=None):
+def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=None, sampling=None):
     """Prefill then new_tokens / S decode chunks.  Returns (tokens [B, N],
     logits [B, N, V], final state, per-chunk records).  ``log`` receives
     progress strings (per prefill layer and per decoded chunk)."""
@@ -385,7 +398,7 @@ def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=N
     for c in range(new_tokens // S):
         ft = None if forced_tokens is None else \
             np.asarray(forced_tokens)[:, c * S:(c + 1) * S]
-        o = decode_chunk(model, st, mode, ft)
+        o = decode_chunk(model, st, mode, ft, sampling=sampling)
         toks.append(o["tokens"])
         lg.append(o["logits"])
         recs.append(o)
