@@ -38,7 +38,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False):
+def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sampling=None):
     """The oracle as it stands, RecGen decode phase only (perf_counter),
     prefill and weight setup untimed.  seqs = 0: one sequence is decoded
     first to size the sample, then as many sequences (up to the batch) as
@@ -54,7 +54,7 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False):
             O.vanilla_decode(m, st, wl.new_tokens)
         else:
             for _ in range(wl.chunks):
-                O.decode_chunk(m, st)
+                O.decode_chunk(m, st, sampling=sampling)
         return time.perf_counter() - t0
 
     prefill = O.vanilla_prefill if vanilla else O.prefill
@@ -195,6 +195,9 @@ def main():
     ap.add_argument("--prompt", type=int, default=None, help="override the workload's prompt length")
     ap.add_argument("--new-tokens", type=int, default=None, help="override the workload's generated tokens")
     ap.add_argument("--no-attn-standalone", action="store_true", help="skip the stand-alone attention figures")
+    ap.add_argument("--sample", default=None, metavar="T,K",
+                    help="sampling decode at temperature T with a top-K cut (K = 0: whole vocabulary) instead of "
+                         "greedy; also times the multi-query aggregation of the batch in groups of 9")
     ap.add_argument("--no-trace", action="store_true",
                     help="skip the traced passes (per-class figures, roofline): for runs under a profiler, "
                          "which gives its own per-kernel figures")
@@ -256,6 +259,13 @@ def main():
     log(f"prefill {pre_s:.3f} s ({prefill['tflop_s']} TFLOP/s)")
     if args.mode == "recgen":
         model.release_prefill_weights()
+    sampling = None
+    if args.sample:
+        if vanilla:
+            raise SystemExit("--sample applies to the PHOTON modes")
+        t_, k_ = args.sample.split(",")
+        sampling = {"temperature": float(t_), "top_k": int(k_), "seed": wl.seed}
+        model.set_sampling(sampling["temperature"], sampling["top_k"], sampling["seed"], B)
     snap = model.state_snapshot()
     tok = torch.empty((B, S), dtype=torch.int32, device="cuda")
     pos = [0]
@@ -340,6 +350,24 @@ def main():
         roofline["frac_of_copy"] = round(roofline["achieved"] / cp, 4)
         log(f"copy peak {cp:.0f} GB/s")
 
+    agg = None
+    if sampling:
+        # best-of-N and majority vote over groups of 9 queries of the batch,
+        # on the workload's shape (B sequences x new_tokens)
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        at = torch.randint(0, cfg.vocab, (B, wl.new_tokens), generator=gen, device="cuda", dtype=torch.int32)
+        al = -torch.rand((B, wl.new_tokens), generator=gen, device="cuda") * 8
+        for _ in range(3):
+            P.aggregate(at, al, 9)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            P.aggregate(at, al, 9)
+        e1.record()
+        torch.cuda.synchronize()
+        agg = {"group": 9, "groups": (B + 8) // 9, "tokens_per_query": wl.new_tokens,
+               "us": round(e0.elapsed_time(e1) * 1e3 / 20, 2)}
+
     attn = None
     if not args.no_attn_standalone and not vanilla:
         log("stand-alone attention")
@@ -352,10 +380,11 @@ def main():
     if args.cpu_seqs >= 0:
         threads = min(16, len(os.sched_getaffinity(0)))
         log(f"oracle baseline, {threads} threads")
-        cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads, vanilla=vanilla)
+        cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads, vanilla=vanilla,
+                                         sampling=sampling)
         prec = "float64" if cfg.dtype == "f32" else "float64 with the bf16 rounding contract"
         rep_txt = f", decoded {reps} times from the same prefill" if reps > 1 else ""
-        what = "flat-baseline" if vanilla else "RecGen"
+        what = "flat-baseline" if vanilla else ("sampled " if sampling else "") + "RecGen"
         cpu_model, blas = host_info()
         cpu = {"value": round(cv, 2), "unit": "tok/s", "cores": threads, "kind": "oracle",
                "cpu_model": cpu_model, "blas": blas,
@@ -380,7 +409,9 @@ def main():
                    "chunk": list(cfg.chunk),
                    **({"layers": mcfg.n_layers} if vanilla else
                       {"layers_top_enc1_dec1_dec0": [cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0]}),
-                   "vocab": cfg.vocab, "tokens_per_step": B * S},
+                   "vocab": cfg.vocab, "tokens_per_step": B * S,
+                   **({"sampling": {"temperature": sampling["temperature"], "top_k": sampling["top_k"]}}
+                      if sampling else {})},
         "tpm": round(tok_s / gib, 1),
         "tpm_unit": ("tok/s/GiB (weights + token K/V + state)" if vanilla else
                      "tok/s/GiB (decode weights + top K/V + decoder K/V + state)"),
@@ -397,6 +428,7 @@ def main():
                                       if k.startswith("gemm") else None)}
                     for k, v in sorted(per_class.items(), key=lambda kv: -kv[1]["ms"])},
         "prefill": prefill,
+        "aggregate": agg,
         "attn_standalone": attn,
         "cpu_baseline": cpu,
     }

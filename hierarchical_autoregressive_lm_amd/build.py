@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "photon.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "sampling.hip", "photon.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 instructions stay off (see the build notes)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -138,6 +138,42 @@ hipError_t launch_set_int(int* p, int v, hipStream_t st);
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t st);
 hipError_t launch_add_int(int* p, int v, hipStream_t st);
 
+// Sampling: row r of logits [rows][ld] (vocab V <= 65536, sample_supported)
+// draws ids[r] = first maximum over the top-k-kept ids (every id whose logit
+// reaches the k-th largest; top_k = 0 or >= V keeps all) of
+// logit / temperature + Gumbel(u), u from Philox-4x32-10 with key (k0, k1),
+// counter (id / 4, pos, seq, 0), word id % 4, u = ((word >> 9) + 1/2) 2^-23.
+// seq/pos per row from the arrays, or (decode layout, arrays null) row
+// r = b*C2 + k: seq b, pos = *counter * C1*C2 + k*C1 + j.  val[r] (nullable)
+// gets the perturbed score; logprob (nullable) the log-likelihood of the id
+// under the whole-vocabulary softmax at temperature 1, at index r (arrays)
+// or b*C1*C2 + k*C1 + j (decode layout).
+struct SampleCall {
+  const float* logits; int64_t ld;
+  int rows, V;
+  float temperature; int top_k; uint32_t k0, k1;
+  const int* seq; const int* pos;
+  const int* counter; int C1, C2, j;
+  int* ids; float* val;
+  float* logprob;
+};
+int sample_supported(int V);
+hipError_t launch_sample(const SampleCall& c, hipStream_t st);
+
+// Multi-query aggregation over groups of `group` (<= 64) consecutive
+// sequences (the last group may be shorter): score[b] (nullable) = sum of
+// logprobs[b][0 .. n_tok); per group g: best[g] = member with the highest
+// score (lowest on ties), votes = members whose tokens[span0, span1) equal
+// a member's, major[g] = the member with the most votes (then the higher
+// score, then the lower index), votes[g] its count.
+struct AggregateCall {
+  const int* tokens; int64_t tok_ld;
+  const float* logprobs; int64_t lp_ld;
+  int B, group, n_tok, span0, span1;
+  int* best; int* major; int* votes; float* score;
+};
+hipError_t launch_aggregate(const AggregateCall& c, hipStream_t st);
+
 // Number of key splits the decode attention uses for G*H pairs with Q
 // queries each over a cache of `cap` slots (plan-time, so one plan serves
 // every length <= cap).

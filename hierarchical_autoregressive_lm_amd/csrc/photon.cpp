@@ -447,6 +447,12 @@ struct photon_ctx {
   unsigned char* ws = nullptr;
   WsPlan plan;
   Tracer tr;
+  // sampling decode (photon_set_sampling): caller-owned workspace holding
+  // one token step's logits and the chunk's log-likelihoods
+  bool sampling = false;
+  photon_sampling samp{};
+  unsigned char* sws = nullptr;
+  uint64_t sws_bytes = 0;
   // one decode chunk captured as a HIP graph, replayed for every chunk
   bool use_graph = true;
   hipGraphExec_t graph = nullptr;
@@ -514,6 +520,22 @@ void bind_weights(photon_ctx* c) {
     photon_status s_ = (expr);  \
     if (s_ != PHOTON_OK) return s_; \
   } while (0)
+
+// Sampling workspace: one token step's logits [B*C2][V] fp32, then the
+// chunk's log-likelihoods [B][S] fp32.
+uint64_t sampling_lp_off(const photon_config& cf, int64_t B) {
+  return align_up((uint64_t)B * cf.chunk[1] * cf.vocab * 4);
+}
+uint64_t sampling_bytes(const photon_config& cf, int64_t B) {
+  return sampling_lp_off(cf, B) + align_up((uint64_t)B * cf.chunk[0] * cf.chunk[1] * 4);
+}
+photon_status check_sampling(const photon_sampling* sp, int vocab) {
+  if (!(sp->temperature >= 1e-4f && sp->temperature <= 1e4f))
+    return fail(PHOTON_EINVAL, "temperature %g must lie in [1e-4, 1e4]", (double)sp->temperature);
+  if (sp->top_k < 0) return fail(PHOTON_EINVAL, "top_k %d must be >= 0", sp->top_k);
+  if (!sample_supported(vocab)) return fail(PHOTON_EUNSUPPORTED, "sampling supports vocabularies up to 65536 (got %d)", vocab);
+  return ok();
+}
 
 // Launch `f` (returning hipError_t); when class `cls` is traced, the kernel
 // dispatches of `f` record a start event (first kernel) and a stop event
@@ -987,12 +1009,22 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     GemmCall g{};
     g.dtype = dt; g.A = ws + wp.zB.off; g.lda = d; g.W = c->W_out; g.M = MB; g.N = V; g.K = d;
     g.epi = EPI_ARGMAX;
-    g.C = d_logits ? d_logits + (int64_t)j * V : nullptr;
-    g.ldc = (int64_t)C1 * V;
+    // sampling reads the logits back: the caller's buffer when it asked for
+    // them, else the sampling workspace
+    g.C = d_logits ? d_logits + (int64_t)j * V : c->sampling ? (float*)c->sws : nullptr;
+    g.ldc = d_logits ? (int64_t)C1 * V : V;
     g.amax_val = (float*)(ws + wp.amv.off); g.amax_idx = (int*)(ws + wp.ami.off);
     PH_TRY(run_gemm(c, PHOTON_K_GEMM_HEAD, g, st));
+    if (c->sampling) {
+      // the sampler's id takes the place of the argmax tiles (one tile)
+      SampleCall sc{g.C, g.ldc, MB, V, c->samp.temperature, c->samp.top_k, (uint32_t)c->samp.seed,
+                    (uint32_t)(c->samp.seed >> 32), nullptr, nullptr, counter, C1, C2, j,
+                    g.amax_idx, g.amax_val, (float*)(c->sws + sampling_lp_off(cf, B))};
+      PH_TRY(traced(c, PHOTON_K_SAMPLE, (double)MB * V * 4 + (double)MB * 12, 0, st, "sample",
+                    [&] { return launch_sample(sc, st); }));
+    }
     const bool next = j + 1 < C1;
-    ArgmaxNext an{g.amax_val, g.amax_idx, wp.head_tiles, MB, C1, C2, j, tok,
+    ArgmaxNext an{g.amax_val, g.amax_idx, c->sampling ? 1 : wp.head_tiles, MB, C1, C2, j, tok,
                   c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec0.layers[0].g1, d, cf.norm_eps};
     // the next step's input (conditioning row + embedding in, stream and its
     // norm out); the token ids are counted with the head
@@ -1038,26 +1070,37 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     r.out = h; r.out_rows = B; r.in_stride = 1; r.in_off = 0;
     PH_TRY(run_stack(c, c->top, sa, r, stt));
   }
-  HIP_TRY(launch_add_int(counter, 1, stt));
+  // the position advances once both branches are done: the sampler of the
+  // token branch reads it while the top branch runs
   if (fork) {
     HIP_TRY(hipEventRecord(c->ev_join, st_top));
     HIP_TRY(hipStreamWaitEvent(st, c->ev_join, 0));
   }
+  HIP_TRY(launch_add_int(counter, 1, st));
   (void)S;
   return ok();
 }
 
 photon_status photon_decode_chunk(photon_ctx* c, int32_t* d_tokens, float* d_logits, void* stream) {
+  return photon_decode_chunk_lp(c, d_tokens, d_logits, nullptr, stream);
+}
+
+photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_logits, float* d_logprobs,
+                                     void* stream) {
   if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
   if (c->vanilla) return fail(PHOTON_ESTATE, "a flat-baseline context (use photon_vanilla_decode)");
   if (!d_tokens) return fail(PHOTON_EINVAL, "d_tokens is NULL");
   if (!c->prefilled) return fail(PHOTON_ESTATE, "decode before prefill");
+  if (d_logprobs && !c->sampling) return fail(PHOTON_ESTATE, "log-likelihoods need a sampling context");
   const photon_config& cf = c->cfg;
   const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
   if (c->tokens + S > c->max_tokens)
     return fail(PHOTON_ECAPACITY, "chunk would pass max_tokens %lld", (long long)c->max_tokens);
   if (c->mode == PHOTON_HIERGEN && !c->wpre)
     return fail(PHOTON_ESTATE, "HierGen decoding needs the prefill-only weights, which were released");
+  if (c->sampling && c->sws_bytes < sampling_bytes(cf, c->B))
+    return fail(PHOTON_ECAPACITY, "sampling workspace holds %llu bytes, batch %lld needs %llu",
+                (unsigned long long)c->sws_bytes, (long long)c->B, (unsigned long long)sampling_bytes(cf, c->B));
   hipStream_t st = (hipStream_t)stream;
   const int B = (int)c->B;
   int* tok = (int*)(c->ws + c->plan.tok.off);
@@ -1088,8 +1131,74 @@ photon_status photon_decode_chunk(photon_ctx* c, int32_t* d_tokens, float* d_log
     PH_TRY(enqueue_chunk(c, d_logits, st, st));
   }
   HIP_TRY(hipMemcpyAsync(d_tokens, tok, (size_t)B * S * sizeof(int), hipMemcpyDeviceToDevice, st));
+  if (d_logprobs)
+    HIP_TRY(hipMemcpyAsync(d_logprobs, c->sws + sampling_lp_off(cf, B), (size_t)B * S * sizeof(float),
+                           hipMemcpyDeviceToDevice, st));
   c->top_len += 1;
   c->tokens += S;
+  return ok();
+}
+
+photon_status photon_sampling_bytes(const photon_config* cfg, int32_t batch, uint64_t* bytes) {
+  photon_status s = check_config(cfg);
+  if (s) return s;
+  if (!bytes) return fail(PHOTON_EINVAL, "bytes is NULL");
+  if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
+  *bytes = sampling_bytes(*cfg, batch);
+  return ok();
+}
+
+photon_status photon_set_sampling(photon_ctx* c, const photon_sampling* sp, void* d_ws, uint64_t ws_bytes) {
+  if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  if (c->vanilla) return fail(PHOTON_ESTATE, "sampling is not offered on a flat-baseline context");
+  if (sp) {
+    photon_status s = check_sampling(sp, c->cfg.vocab);
+    if (s) return s;
+    if (!d_ws) return fail(PHOTON_EINVAL, "sampling workspace is NULL");
+    if ((uintptr_t)d_ws % kAlign) return fail(PHOTON_EINVAL, "sampling workspace must be 256-byte aligned");
+  }
+  if (c->graph) {
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+  }
+  c->sampling = sp != nullptr;
+  c->samp = sp ? *sp : photon_sampling{};
+  c->sws = sp ? (unsigned char*)d_ws : nullptr;
+  c->sws_bytes = sp ? ws_bytes : 0;
+  return ok();
+}
+
+photon_status photon_sample(int32_t rows, int32_t vocab, const float* d_logits, int64_t ld, const photon_sampling* sp,
+                            const int32_t* d_seq, const int32_t* d_pos, int32_t* d_ids, float* d_logprobs,
+                            void* stream) {
+  if (!sp) return fail(PHOTON_EINVAL, "sampling parameters are NULL");
+  photon_status s = check_sampling(sp, vocab);
+  if (s) return s;
+  if (rows < 1 || vocab < 1 || ld < vocab)
+    return fail(PHOTON_ESHAPE, "rows %d, vocab %d, ld %lld: need rows, vocab >= 1 and ld >= vocab", rows, vocab,
+                (long long)ld);
+  if (!d_logits || !d_seq || !d_pos || !d_ids) return fail(PHOTON_EINVAL, "NULL device pointer");
+  SampleCall sc{d_logits, ld, rows, vocab, sp->temperature, sp->top_k, (uint32_t)sp->seed, (uint32_t)(sp->seed >> 32),
+                d_seq, d_pos, nullptr, 1, 1, 0, d_ids, nullptr, d_logprobs};
+  const hipError_t e = launch_sample(sc, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PHOTON_EHIP, "sample: %s", hipGetErrorString(e));
+  return ok();
+}
+
+photon_status photon_aggregate(int32_t batch, int32_t group, int32_t n_tok, const int32_t* d_tokens, int64_t tok_ld,
+                               const float* d_logprobs, int64_t lp_ld, int32_t span_begin, int32_t span_end,
+                               int32_t* d_best, int32_t* d_major, int32_t* d_votes, float* d_scores, void* stream) {
+  if (batch < 1 || group < 1 || group > 64 || n_tok < 0)
+    return fail(PHOTON_ESHAPE, "batch %d, group %d, n_tok %d: need batch >= 1, 1 <= group <= 64, n_tok >= 0", batch,
+                group, n_tok);
+  if (span_begin < 0 || span_end < span_begin || tok_ld < span_end || tok_ld < n_tok || lp_ld < n_tok)
+    return fail(PHOTON_ESHAPE, "span [%d, %d), n_tok %d must fit rows of %lld tokens and %lld log-likelihoods",
+                span_begin, span_end, n_tok, (long long)tok_ld, (long long)lp_ld);
+  if (!d_tokens || !d_logprobs || !d_best || !d_major || !d_votes) return fail(PHOTON_EINVAL, "NULL device pointer");
+  AggregateCall ac{d_tokens, tok_ld, d_logprobs, lp_ld, batch, group, n_tok, span_begin, span_end,
+                   d_best, d_major, d_votes, d_scores};
+  const hipError_t e = launch_aggregate(ac, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PHOTON_EHIP, "aggregate: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -70,6 +70,14 @@ class TensorInfo(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
+class Sampling_(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+def make_sampling(temperature, top_k=0, seed=0):
+    return Sampling_(float(temperature), int(top_k), int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
 class TraceStat(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("ms", ctypes.c_double),
                 ("bytes", ctypes.c_double), ("flops", ctypes.c_double)]
@@ -78,7 +86,7 @@ class TraceStat(ctypes.Structure):
 # kernel classes of photon_trace_enable, in photon_kernel_class order
 KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_up", "gemm_down", "gemm_head",
                   "gemm_conv", "gemm_chunk", "attn_top", "attn_chunk",
-                  "attn_prefill", "norm", "rope_kv", "embed", "argmax"]
+                  "attn_prefill", "norm", "rope_kv", "embed", "argmax", "sample"]
 
 EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
            "photon_weight_layout", "photon_weight_tensor", "photon_open",
@@ -89,7 +97,9 @@ EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
            "photon_attention_scratch_bytes", "photon_attention",
            "photon_vanilla_kv_bytes", "photon_vanilla_prefill_scratch_bytes",
            "photon_vanilla_weight_layout", "photon_vanilla_weight_tensor",
-           "photon_vanilla_open", "photon_vanilla_prefill", "photon_vanilla_decode"]
+           "photon_vanilla_open", "photon_vanilla_prefill", "photon_vanilla_decode",
+           "photon_sampling_bytes", "photon_set_sampling", "photon_decode_chunk_lp", "photon_sample",
+           "photon_aggregate"]
 
 
 def _load():
@@ -124,6 +134,11 @@ def _load():
         "photon_vanilla_open": [P(VanillaConfig_), V, P(V)],
         "photon_vanilla_prefill": [V, V, u64, V, u64, V, i32, i32, i64, V],
         "photon_vanilla_decode": [V, V, V, V],
+        "photon_sampling_bytes": [P(Config), i32, P(u64)],
+        "photon_set_sampling": [V, P(Sampling_), V, u64],
+        "photon_decode_chunk_lp": [V, V, V, V, V],
+        "photon_sample": [i32, i32, V, i64, P(Sampling_), V, V, V, V, V],
+        "photon_aggregate": [i32, i32, i32, V, i64, V, i64, i32, i32, V, V, V, V, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -200,6 +215,51 @@ def vanilla_kv_bytes(cfg, steps, batch, tokens):
 
 def _stream_handle(torch):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def sampling_bytes(cfg, batch):
+    out = ctypes.c_uint64()
+    c = make_config(cfg)
+    _check(_lib.photon_sampling_bytes(ctypes.byref(c), batch, ctypes.byref(out)))
+    return out.value
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def sample(logits, temperature, top_k, seed, seq, pos, logprobs=True):
+    """photon_sample on torch tensors: logits [rows, V] float32 (row stride
+    logits.stride(0)), seq and pos int32 [rows]; returns (ids int32 [rows],
+    log-likelihoods float32 [rows] or None)."""
+    rows, V = logits.shape
+    assert logits.dtype == torch.float32 and logits.stride(1) == 1
+    seq = seq.to(device=logits.device, dtype=torch.int32).contiguous()
+    pos = pos.to(device=logits.device, dtype=torch.int32).contiguous()
+    ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    lp = torch.empty(rows, dtype=torch.float32, device=logits.device) if logprobs else None
+    sp = make_sampling(temperature, top_k, seed)
+    _check(_lib.photon_sample(rows, V, _ptr(logits), logits.stride(0), ctypes.byref(sp), _ptr(seq), _ptr(pos),
+                              _ptr(ids), _ptr(lp), _stream_handle(torch)))
+    return ids, lp
+
+
+def aggregate(tokens, logprobs, group, span=None, n_tok=None):
+    """photon_aggregate on torch tensors tokens int32 [B, N], logprobs
+    float32 [B, N]; returns (best, major, votes, scores)."""
+    B, N = tokens.shape
+    n_tok = N if n_tok is None else n_tok
+    b0, b1 = (0, N) if span is None else span
+    assert tokens.dtype == torch.int32 and tokens.stride(1) == 1 and logprobs.stride(1) == 1
+    G = (B + group - 1) // group
+    dev = tokens.device
+    best = torch.empty(G, dtype=torch.int32, device=dev)
+    major = torch.empty(G, dtype=torch.int32, device=dev)
+    votes = torch.empty(G, dtype=torch.int32, device=dev)
+    scores = torch.empty(B, dtype=torch.float32, device=dev)
+    _check(_lib.photon_aggregate(B, group, n_tok, _ptr(tokens), tokens.stride(0), _ptr(logprobs), logprobs.stride(0),
+                                 b0, b1, _ptr(best), _ptr(major), _ptr(votes), _ptr(scores), _stream_handle(torch)))
+    return best, major, votes, scores
 
 
 def attention_scratch_bytes(kind, groups, heads, head_dim, queries, cap):
@@ -309,11 +369,30 @@ class Photon:
         self.mode = mode
         self.batch = B
 
-    def decode_chunk(self, tokens_out, logits_out=None):
-        """tokens_out: int32 CUDA [B, S]; logits_out: float32 [B, S, V] or None."""
-        lp = ctypes.c_void_p(logits_out.data_ptr()) if logits_out is not None else None
-        _check(_lib.photon_decode_chunk(self.ctx, ctypes.c_void_p(tokens_out.data_ptr()), lp,
-                                        _stream_handle(self.torch)))
+    def set_sampling(self, temperature=None, top_k=0, seed=0, batch=None):
+        """Sampling decode from the next chunk on (temperature None: greedy).
+        The sampling workspace is sized for `batch` (default: the prefilled
+        batch)."""
+        torch = self.torch
+        if temperature is None:
+            _check(_lib.photon_set_sampling(self.ctx, None, None, 0))
+            self.sampling_ws = None
+            return
+        batch = batch or self.batch
+        if batch is None:
+            raise ValueError("set_sampling needs a batch size before the first prefill")
+        n = sampling_bytes(self.cfg, batch)
+        ws = torch.empty(n + 256, dtype=torch.uint8, device=self.device)
+        off = (-ws.data_ptr()) % 256
+        sp = make_sampling(temperature, top_k, seed)
+        _check(_lib.photon_set_sampling(self.ctx, ctypes.byref(sp), ctypes.c_void_p(ws.data_ptr() + off), n))
+        self.sampling_ws = ws
+
+    def decode_chunk(self, tokens_out, logits_out=None, logprobs_out=None):
+        """tokens_out: int32 CUDA [B, S]; logits_out: float32 [B, S, V] or
+        None; logprobs_out: float32 [B, S] or None (sampling only)."""
+        _check(_lib.photon_decode_chunk_lp(self.ctx, _ptr(tokens_out), _ptr(logits_out), _ptr(logprobs_out),
+                                           _stream_handle(self.torch)))
 
     def position(self):
         a, b = ctypes.c_int64(), ctypes.c_int64()
@@ -348,21 +427,32 @@ class Photon:
         return {n: {"launches": out[i].launches, "ms": out[i].ms, "bytes": out[i].bytes,
                     "flops": out[i].flops} for i, n in enumerate(KERNEL_CLASSES) if out[i].launches}
 
-    def generate(self, prompt, new_tokens, mode="recgen", logits=False, max_tokens=None):
+    def generate(self, prompt, new_tokens, mode="recgen", logits=False, max_tokens=None, sampling=None,
+                 logprobs=False):
+        """Prefill, then new_tokens / S chunks.  sampling: None (greedy) or
+        dict(temperature, top_k, seed).  Returns (tokens, logits or None),
+        plus the log-likelihoods [B, N] when logprobs (sampling only)."""
         torch = self.torch
         B, P = prompt.shape
         S = self.cfg.S
         if new_tokens % S:
             raise ValueError("new_tokens must be a multiple of C1*C2")
         self.prefill(prompt, max_tokens or P + new_tokens, mode)
+        if sampling is not None:
+            self.set_sampling(sampling["temperature"], sampling.get("top_k", 0), sampling.get("seed", 0), B)
+        else:
+            self.set_sampling(None)
         toks = torch.empty((new_tokens // S, B, S), dtype=torch.int32, device=self.device)
         lg = torch.empty((new_tokens // S, B, S, self.cfg.vocab), dtype=torch.float32,
                          device=self.device) if logits else None
+        lp = torch.empty((new_tokens // S, B, S), dtype=torch.float32, device=self.device) if logprobs else None
         for c in range(new_tokens // S):
-            self.decode_chunk(toks[c], lg[c] if logits else None)
+            self.decode_chunk(toks[c], lg[c] if logits else None, lp[c] if logprobs else None)
         toks = toks.permute(1, 0, 2).reshape(B, new_tokens)
         if logits:
             lg = lg.permute(1, 0, 2, 3).reshape(B, new_tokens, self.cfg.vocab)
+        if logprobs:
+            return toks, lg, lp.permute(1, 0, 2).reshape(B, new_tokens)
         return toks, lg
 
     # ---- views into the workspace (tests read the caches directly) ----

@@ -319,6 +319,78 @@ photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q,
                                void* stream);
 
 /* ------------------------------------------------------------------------
+ * Sampling decode and multi-query aggregation (explainer, the paragraph on
+ * recovering quality: several slightly varied queries are run and bound by
+ * majority vote or best-of-N).  The variation is stochastic decoding, one
+ * independent random stream per sequence:
+ *   - top_k = 0 keeps the whole vocabulary; k >= 1 keeps every id whose
+ *     logit reaches the k-th largest logit (ties at the cut are kept);
+ *   - a token is the first maximum over the kept ids of
+ *     logit / temperature + G, G = -log(-log u) standard Gumbel noise
+ *     (the Gumbel-max identity: this samples the tempered softmax of the
+ *     kept ids);
+ *   - u = ((x >> 9) + 1/2) * 2^-23 with x word (id % 4) of
+ *     Philox-4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1,
+ *     2, 3", SC 2011) keyed by `seed` (low word first), counter
+ *     (id / 4, absolute token position, sequence index, 0).  The absolute
+ *     position of token k*C1 + j of the chunk that starts at token T is
+ *     T + k*C1 + j; prompts start at position 0.
+ * The log-likelihood of a token is logit[y] - logsumexp(logits) under the
+ * model's distribution (temperature 1, whole vocabulary), float32.
+ * Vocabularies up to 65536 (else PHOTON_EUNSUPPORTED).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float temperature;   /* in [1e-4, 1e4] (else PHOTON_EINVAL) */
+  int32_t top_k;       /* >= 0 */
+  uint64_t seed;
+} photon_sampling;
+
+/* Bytes of the sampling workspace of a context decoding `batch` sequences:
+ * the logits of one token step ([batch*C2][vocab] float32) and the chunk's
+ * log-likelihoods ([batch][S] float32).  Pure host. */
+photon_status photon_sampling_bytes(const photon_config* cfg, int32_t batch,
+                                    uint64_t* bytes);
+/* Switch a PHOTON context to sampling (s != NULL) or back to greedy
+ * decoding (s == NULL; d_ws may then be NULL).  d_ws: caller-owned device
+ * memory of >= photon_sampling_bytes(cfg, batch) bytes, 256-byte aligned,
+ * valid while sampling; a decode chunk with a larger batch than it holds
+ * returns PHOTON_ECAPACITY.  Takes effect at the next decode chunk (the
+ * captured graph is rebuilt).  PHOTON_ESTATE on a flat-baseline context. */
+photon_status photon_set_sampling(photon_ctx* ctx, const photon_sampling* s,
+                                  void* d_ws, uint64_t ws_bytes);
+/* photon_decode_chunk plus d_logprobs: NULL, or [batch][S] float32 out, the
+ * log-likelihood of every token (sampling contexts only, else
+ * PHOTON_ESTATE). */
+photon_status photon_decode_chunk_lp(photon_ctx* ctx, int32_t* d_tokens,
+                                     float* d_logits, float* d_logprobs,
+                                     void* stream);
+/* The sampler alone on caller rows: row r of d_logits [rows][ld] float32
+ * (ld >= vocab) draws d_ids[r] for sequence d_seq[r] at absolute position
+ * d_pos[r] (int32 device arrays); d_logprobs (nullable) [rows] gets its
+ * log-likelihood. */
+photon_status photon_sample(int32_t rows, int32_t vocab, const float* d_logits,
+                            int64_t ld, const photon_sampling* s,
+                            const int32_t* d_seq, const int32_t* d_pos,
+                            int32_t* d_ids, float* d_logprobs, void* stream);
+/* Multi-query aggregation over groups of `group` (1..64) consecutive
+ * sequences of the batch (the last group may be shorter):
+ *   d_tokens [batch][tok_ld] int32, d_logprobs [batch][lp_ld] float32: the
+ *   generated tokens and their log-likelihoods (first n_tok of each row).
+ *   A query's score is the sum of its n_tok log-likelihoods (float32);
+ *   its answer is tokens [span_begin, span_end).
+ * Out, per group g (ceil(batch / group) of them), member indices within
+ * the group: d_best[g] the highest score (lowest index on ties);
+ * d_major[g] the member whose answer the most members share (ties: higher
+ * score, then lower index); d_votes[g] how many share it.  d_scores
+ * (nullable) [batch] the scores. */
+photon_status photon_aggregate(int32_t batch, int32_t group, int32_t n_tok,
+                               const int32_t* d_tokens, int64_t tok_ld,
+                               const float* d_logprobs, int64_t lp_ld,
+                               int32_t span_begin, int32_t span_end,
+                               int32_t* d_best, int32_t* d_major,
+                               int32_t* d_votes, float* d_scores, void* stream);
+
+/* ------------------------------------------------------------------------
  * Tracing: per kernel class, a start and a stop HIP event recorded by the
  * kernel dispatches of every traced operation (the first kernel's start,
  * the last kernel's end; no marker packets between kernels), with the
@@ -340,6 +412,7 @@ typedef enum {
   PHOTON_K_ROPE_KV,        /* rotary embedding + K/V cache append */
   PHOTON_K_EMBED,          /* embedding gather / conditioning add */
   PHOTON_K_ARGMAX,         /* argmax reduction across column tiles */
+  PHOTON_K_SAMPLE,         /* sampling: top-k cut + Gumbel-max per row */
   PHOTON_K_COUNT
 } photon_kernel_class;
 

@@ -277,3 +277,73 @@ def test_vanilla_errors_before_any_device_call():
     assert lib.photon_vanilla_decode(f.ctx, tok, None, None) == P.ESTATE
     assert lib.photon_vanilla_prefill(f.ctx, ws, need, sc, 1 << 30, pr, 2, 64, 96, None) == P.ESTATE
     f.close()
+
+
+def align256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("idx", [1, 2, 5])
+def test_sampling_bytes_closed_form(idx):
+    w = pi.get(idx)
+    c = P.make_config(w.cfg)
+    out = ctypes.c_uint64()
+    assert P._lib.photon_sampling_bytes(ctypes.byref(c), w.batch, ctypes.byref(out)) == P.OK
+    C1, C2 = w.cfg.chunk
+    assert out.value == align256(w.batch * C2 * w.cfg.vocab * 4) + align256(w.batch * C1 * C2 * 4)
+    assert P._lib.photon_sampling_bytes(ctypes.byref(c), 0, ctypes.byref(out)) == P.ESHAPE
+
+
+def test_sampling_errors_before_any_device_call():
+    lib = P._lib
+    V = ctypes.c_void_p
+    f = FakeCtx()
+    ws = V(4 << 20)
+    for temp, k in [(0.0, 0), (-1.0, 0), (float("nan"), 0), (1e5, 0), (1.0, -1)]:
+        sp = P.make_sampling(temp, k, 1)
+        assert lib.photon_set_sampling(f.ctx, ctypes.byref(sp), ws, 1 << 20) == P.EINVAL, (temp, k)
+    sp = P.make_sampling(0.8, 40, 12345)
+    assert lib.photon_set_sampling(f.ctx, ctypes.byref(sp), None, 1 << 20) == P.EINVAL
+    assert lib.photon_set_sampling(f.ctx, ctypes.byref(sp), V((4 << 20) + 8), 1 << 20) == P.EINVAL
+    assert lib.photon_set_sampling(f.ctx, ctypes.byref(sp), ws, 1 << 20) == P.OK
+    assert lib.photon_set_sampling(f.ctx, None, None, 0) == P.OK
+    # log-likelihoods are only produced while sampling (state is checked first)
+    assert lib.photon_decode_chunk_lp(f.ctx, V(3 << 20), None, V(5 << 20), None) == P.ESTATE
+    f.close()
+    # the flat baseline offers no sampling
+    v = pi.vanilla_of(pi.get(1).cfg)
+    vc = P.make_vanilla_config(v, 16)
+    ctx = ctypes.c_void_p()
+    assert lib.photon_vanilla_open(ctypes.byref(vc), V(1 << 20), ctypes.byref(ctx)) == P.OK
+    assert lib.photon_set_sampling(ctx, ctypes.byref(sp), ws, 1 << 20) == P.ESTATE
+    lib.photon_close(ctx)
+    # vocabularies beyond 65536 are refused
+    big = P.make_config(pi.PhotonConfig(d_model=64, n_heads=2, chunk=(4, 4), vocab=70000, n_top=1, n_enc1=1,
+                                        n_dec1=1, n_dec0=1, dtype="bf16"))
+    ctx = ctypes.c_void_p()
+    assert lib.photon_open(ctypes.byref(big), V(1 << 20), V(2 << 20), ctypes.byref(ctx)) == P.OK
+    assert lib.photon_set_sampling(ctx, ctypes.byref(sp), ws, 1 << 30) == P.EUNSUPPORTED
+    lib.photon_close(ctx)
+
+
+def test_sample_and_aggregate_reject_bad_arguments():
+    lib = P._lib
+    V = ctypes.c_void_p
+    sp = P.make_sampling(1.0, 0, 7)
+    lg, seq, pos, ids, lp = V(1 << 20), V(2 << 20), V(3 << 20), V(4 << 20), V(5 << 20)
+    assert lib.photon_sample(0, 100, lg, 100, ctypes.byref(sp), seq, pos, ids, lp, None) == P.ESHAPE
+    assert lib.photon_sample(4, 100, lg, 99, ctypes.byref(sp), seq, pos, ids, lp, None) == P.ESHAPE
+    assert lib.photon_sample(4, 70000, lg, 70000, ctypes.byref(sp), seq, pos, ids, lp, None) == P.EUNSUPPORTED
+    assert lib.photon_sample(4, 100, None, 100, ctypes.byref(sp), seq, pos, ids, lp, None) == P.EINVAL
+    assert lib.photon_sample(4, 100, lg, 100, ctypes.byref(sp), seq, None, ids, lp, None) == P.EINVAL
+    assert lib.photon_sample(4, 100, lg, 100, None, seq, pos, ids, lp, None) == P.EINVAL
+    bad = P.make_sampling(0.0, 0, 7)
+    assert lib.photon_sample(4, 100, lg, 100, ctypes.byref(bad), seq, pos, ids, lp, None) == P.EINVAL
+    t, l, b, m, v = V(1 << 20), V(2 << 20), V(3 << 20), V(4 << 20), V(5 << 20)
+    assert lib.photon_aggregate(8, 0, 4, t, 4, l, 4, 0, 4, b, m, v, None, None) == P.ESHAPE
+    assert lib.photon_aggregate(8, 65, 4, t, 4, l, 4, 0, 4, b, m, v, None, None) == P.ESHAPE
+    assert lib.photon_aggregate(0, 2, 4, t, 4, l, 4, 0, 4, b, m, v, None, None) == P.ESHAPE
+    assert lib.photon_aggregate(8, 2, 4, t, 4, l, 4, 2, 5, b, m, v, None, None) == P.ESHAPE   # span past the row
+    assert lib.photon_aggregate(8, 2, 4, t, 4, l, 4, 3, 2, b, m, v, None, None) == P.ESHAPE   # reversed span
+    assert lib.photon_aggregate(8, 2, 5, t, 4, l, 4, 0, 4, b, m, v, None, None) == P.ESHAPE   # n_tok past the row
+    assert lib.photon_aggregate(8, 2, 4, t, 4, l, 4, 0, 4, None, m, v, None, None) == P.EINVAL
