@@ -24,6 +24,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kCap = kThreads;   // band keys listed in LDS, one per thread
+constexpr int kSmall = 64;       // band keys one wave ranks directly
 
 // Philox-4x32 with 10 rounds: words 0 and 2 are multiplied by the two round
 // constants; the high halves of the products are mixed with words 1 and 3
@@ -35,9 +37,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;   // one 32x32 -> 64 multiply each
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
   }
   return c;
 }
@@ -46,6 +48,22 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// One band-search step: the counts n1 <= ... of keys >= the three
+// candidates c1 < c2 < c3 pick the highest candidate still reached by k keys.
+__device__ __forceinline__ void band_step(int n1, int n2, int n3, uint32_t c1, uint32_t c2, uint32_t c3, int k,
+                                          uint32_t& t, int& nt, int& nu) {
+  if (n3 >= k) { t = c3; nt = n3; }
+  else if (n2 >= k) { t = c2; nt = n2; nu = n3; }
+  else if (n1 >= k) { t = c1; nt = n1; nu = n2; }
+  else { nu = n1; }
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -110,8 +128,11 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
   __shared__ int redn[2 * 3 * kWaves];
   __shared__ float arg_s[kWaves], arg_x[kWaves];
   __shared__ int arg_i[kWaves];
+  __shared__ uint32_t cand[kCap], small[kSmall], t_sh;
+  __shared__ int n_list[2];
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) n_list[0] = n_list[1] = 0;   // visible after the first block reduction
   const int V = c.V;
   const float* row = c.logits + (int64_t)r * c.ld;
   const bool vec = (c.ld % 4 == 0) && (reinterpret_cast<uintptr_t>(c.logits) % 16 == 0);
@@ -142,18 +163,30 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
 #pragma unroll
   for (int q = 0; q < Q; ++q)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) s += expf(x[q][w] - m);   // padding: exp(-inf) = 0
+    for (int w = 0; w < 4; ++w) s += __expf(x[q][w] - m);   // padding: exp(-inf) = 0
   s = red.sum(s, wave, lane);
   const float lse = m + logf(s);
 
-  // the k-th largest key t: the largest t with #(key >= t) >= k, two bits a
-  // pass from the top; padding ids get key 0, which no candidate (>= 1)
-  // counts
+  // The cut t = the k-th largest key (ids with key >= t are kept).  Band
+  // search two bits a pass from the top: before the pass at bit b the k-th
+  // largest key lies in the band [t, t + 2^(b+2)), with nt = #(key >= t) >= k
+  // and nu = #(key >= band top) < k.  While the band is wide every element is
+  // counted from registers; once it holds <= kCap keys they are listed in LDS
+  // (one per thread) and the passes count that list; once <= kSmall remain,
+  // one wave ranks them directly: a key is kept iff fewer than k keys are
+  // strictly greater.  Padding ids are never counted.
   const bool cut = c.top_k > 0 && c.top_k < V;
+  const int k = c.top_k;
   uint32_t t = 0;
   if (cut) {
-    for (int b = 30; b >= 0; b -= 2) {
+    int nt = V, nu = 0, b = 30;
+    const uint32_t kmax = order_key(m);   // no key exceeds the row maximum's
+    for (; b >= 0 && nt - nu > kCap; b -= 2) {
       const uint32_t c1 = t | (1u << b), c2 = t | (2u << b), c3 = t | (3u << b);
+      if (c1 > kmax) {   // every candidate above the maximum: digit 0, nothing to count
+        band_step(0, 0, 0, c1, c2, c3, k, t, nt, nu);
+        continue;
+      }
       int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
       for (int q = 0; q < Q; ++q)
@@ -165,7 +198,43 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
           n3 += key >= c3;
         }
       red.count3(n1, n2, n3, wave, lane);
-      t = n3 >= c.top_k ? c3 : n2 >= c.top_k ? c2 : n1 >= c.top_k ? c1 : t;
+      band_step(n1, n2, n3, c1, c2, c3, k, t, nt, nu);
+    }
+    if (b >= 0) {
+      // list the band's keys (nt - nu <= kCap of them)
+      const uint64_t top = (uint64_t)t + (4ull << b);
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t key = order_key(x[q][w]);
+          if (4 * (tid + kThreads * q) + w < V && key >= t && (uint64_t)key < top) cand[atomicAdd(&n_list[0], 1)] = key;
+        }
+      __syncthreads();
+      const int n = n_list[0];
+      const uint32_t mine = tid < n ? cand[tid] : 0u;
+      const int nu0 = nu;   // keys above the listed band
+      for (; b >= 0 && nt - nu > kSmall; b -= 2) {
+        const uint32_t c1 = t | (1u << b), c2 = t | (2u << b), c3 = t | (3u << b);
+        int n1 = tid < n && mine >= c1, n2 = tid < n && mine >= c2, n3 = tid < n && mine >= c3;
+        red.count3(n1, n2, n3, wave, lane);
+        band_step(nu0 + n1, nu0 + n2, nu0 + n3, c1, c2, c3, k, t, nt, nu);
+      }
+      if (b >= 0) {
+        const uint64_t top2 = (uint64_t)t + (4ull << b);
+        if (tid < n && mine >= t && (uint64_t)mine < top2) small[atomicAdd(&n_list[1], 1)] = mine;
+        __syncthreads();
+        if (wave == 0) {
+          const int m2 = n_list[1];
+          const uint32_t kk = lane < m2 ? small[lane] : 0u;
+          int greater = 0;
+          for (int j = 0; j < m2; ++j) greater += small[j] > kk;
+          const uint32_t tk = wave_min_u(lane < m2 && nu + greater < k ? kk : 0xFFFFFFFFu);
+          if (lane == 0) t_sh = tk;
+        }
+        __syncthreads();
+        t = t_sh;
+      }
     }
   }
 
@@ -180,7 +249,11 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
     pos = *c.counter * S + (r % c.C2) * c.C1 + c.j;
   }
 
-  // Gumbel-max over the kept ids: first maximum of x / T + g
+  // Gumbel-max over the kept ids: first maximum of x / T + g, with
+  // g = -log(E), E = -log(u): E keeps full relative accuracy through the
+  // library log (u near 1 gives the small E that win); the outer log only
+  // needs absolute accuracy
+  const float inv_t = 1.0f / c.temperature;
   float best = -INFINITY, bx = 0.f;
   int bi = 0x7fffffff;
 #pragma unroll
@@ -198,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
       const int v = base + w;
       if (v >= V || (cut && order_key(x[q][w]) < t)) continue;
       const float u = ((float)(word[w] >> 9) + 0.5f) * 0x1p-23f;
-      const float sc = x[q][w] / c.temperature - logf(-logf(u));
+      const float sc = x[q][w] * inv_t - __logf(-logf(u));
       if (sc > best) { best = sc; bi = v; bx = x[q][w]; }
     }
   }

@@ -41,6 +41,10 @@ SAMPLE_CASES = [
     (3, 65536, 65536, 1.0, 65535, False),     # the largest vocabulary
     (2, 4097, 4097, 1.0, 4102, False),   # k > V
     (64, 50000, 50000, 0.7, 1, False),   # top-1
+    (8, 800, 800, 1.0, 600, False),      # whole row fits the LDS list; negative cut
+    (8, 32000, 32000, 1.0, 31000, False),     # cut deep in the negative logits
+    (4, 32000, 32000, 1.0, 100, True),   # ties inside the band
+    (4, 5000, 5000, 1.0, 10, "const"),   # every logit equal: all kept
 ]
 
 
@@ -48,7 +52,9 @@ SAMPLE_CASES = [
 def test_sampler_matches_oracle(P, rows, V, ld, temp, k, quant):
     rng = np.random.default_rng([rows, V, k])
     lg = rng.standard_normal((rows, ld), dtype=np.float32) * 2
-    if quant:
+    if quant == "const":
+        lg[:] = 1.25
+    elif quant:
         lg = np.round(lg * 4) / 4
     seq = rng.integers(0, 1 << 31, rows, dtype=np.int64).astype(np.int32)
     pos = rng.integers(0, 1 << 31, rows, dtype=np.int64).astype(np.int32)
