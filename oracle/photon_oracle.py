@@ -386,6 +386,18 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
     return out
 
 
+def consistency(A_hat, A):
+    """The recursive loss of the pages (Eq. 1) as a diagnostic [recgen]: the
+    cosine distance 1 - cos(A-hat_i[k], A_i[k]) between the level-1
+    decoder's reconstruction and the level-1 encoder's summary at each of
+    the C2 level-1 positions of a chunk, on the values as stored (post-norm,
+    rounded).  A_hat, A: [B, C2, d]; returns [B, C2] float64."""
+    a = np.asarray(A_hat, dtype=F64)
+    e = np.asarray(A, dtype=F64)
+    dot = (a * e).sum(axis=-1)
+    return 1.0 - dot / (np.sqrt((a * a).sum(axis=-1)) * np.sqrt((e * e).sum(axis=-1)))
+
+
 def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=None, sampling=None):
     """Prefill then new_tokens / S decode chunks.  Returns (tokens [B, N],
     logits [B, N, V], final state, per-chunk records).  ``log`` receives

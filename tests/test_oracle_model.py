@@ -255,3 +255,32 @@ def test_prefill_rejects_ragged_prompt():
         O.prefill(m, prompts(cfg, 1, 24))
     with pytest.raises(ValueError):
         O.prefill(m, prompts(cfg, 1, 8))
+
+
+def test_consistency_is_the_cosine_distance():
+    from scipy.spatial.distance import cosine
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((3, 4, 64))
+    e = rng.standard_normal((3, 4, 64))
+    d = O.consistency(a, e)
+    ref = np.array([[cosine(a[i, k], e[i, k]) for k in range(4)] for i in range(3)])
+    assert np.allclose(d, ref, rtol=0, atol=1e-12)
+    assert np.allclose(O.consistency(a, a), 0, atol=1e-12)           # identical
+    assert np.allclose(O.consistency(a, -a), 2, atol=1e-12)          # opposite
+    assert np.allclose(O.consistency(a, 3.5 * a), 0, atol=1e-12)     # scale free
+    x = np.zeros((1, 1, 8)); y = np.zeros((1, 1, 8))
+    x[..., 0] = 1; y[..., 1] = 2
+    assert O.consistency(x, y)[0, 0] == 1.0                          # orthogonal
+
+
+def test_consistency_in_hiergen_decoding():
+    # HierGen computes both A-hat_i and A_i every chunk; the distance is a
+    # proper cosine distance of them, and it is not identically zero (the
+    # decoder's reconstruction is not the encoder's summary)
+    wl = pi.get(1)
+    m = O.Model(wl.cfg, pi.gen_weights(wl.cfg, wl.seed))
+    st = O.prefill(m, pi.gen_prompts(wl.cfg, 2, wl.prompt, wl.seed), "hiergen")
+    o = O.decode_chunk(m, st, "hiergen")
+    d = O.consistency(o["A_hat"], o["A"])
+    assert d.shape == (2, wl.cfg.C2)
+    assert (d >= 0).all() and (d <= 2).all() and d.max() > 1e-3
