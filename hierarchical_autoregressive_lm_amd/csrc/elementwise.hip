@@ -195,6 +195,27 @@ __global__ void add_int_kernel(int* p, int v) { *p += v; }
 
 inline unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+// Cosine distance of row pairs, one wave per row: 1 - a.e / (|a| |e|) with
+// float32 sums of the stored values.
+template <typename T>
+__global__ __launch_bounds__(256) void cosine_distance_kernel(const T* a, const T* e, int R, int d, float* out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= R) return;
+  const T* pa = a + (int64_t)row * d;
+  const T* pe = e + (int64_t)row * d;
+  float dot = 0.f, na = 0.f, ne = 0.f;
+  for (int i = lane; i < d; i += 64) {
+    const float x = St<T>::ld(pa[i]), y = St<T>::ld(pe[i]);
+    dot = fmaf(x, y, dot);
+    na = fmaf(x, x, na);
+    ne = fmaf(y, y, ne);
+  }
+  dot = wave_sum(dot);
+  na = wave_sum(na);
+  ne = wave_sum(ne);
+  if (lane == 0) out[row] = 1.0f - dot / (sqrtf(na) * sqrtf(ne));
+}
+
 }  // namespace
 
 // threads for one row of d elements, one float4 each, whole waves
@@ -227,6 +248,13 @@ hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st) {
   dim3 grid(c.M), block(std::max(256u, row_threads(c.d)));
   if (dtype) PH_LAUNCH((argmax_next_kernel<bf16_t>), grid, block, 0, st, c);
   else PH_LAUNCH((argmax_next_kernel<float>), grid, block, 0, st, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_cosine_distance(int dtype, const void* a, const void* e, int R, int d, float* out, hipStream_t st) {
+  const unsigned g = (unsigned)((R + 3) / 4);
+  if (dtype) PH_LAUNCH((cosine_distance_kernel<bf16_t>), g, 256, 0, st, (const bf16_t*)a, (const bf16_t*)e, R, d, out);
+  else PH_LAUNCH((cosine_distance_kernel<float>), g, 256, 0, st, (const float*)a, (const float*)e, R, d, out);
   return hipGetLastError();
 }
 

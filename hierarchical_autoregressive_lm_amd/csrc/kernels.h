@@ -130,6 +130,8 @@ struct ArgmaxNext {
   float* x; void* a; const float* g; int d; float eps;
 };
 hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st);
+// out[r] = 1 - cos(a[r], e[r]) for R rows of d storage-dtype elements.
+hipError_t launch_cosine_distance(int dtype, const void* a, const void* e, int R, int d, float* out, hipStream_t st);
 // tab[p][i] = (cos, sin)(p * theta^(-2i/hd)), angles in double precision.
 hipError_t launch_rope_table(float* tab, int max_pos, int hd, float theta,
                              hipStream_t st);

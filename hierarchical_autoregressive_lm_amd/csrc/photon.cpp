@@ -1139,6 +1139,25 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
   return ok();
 }
 
+photon_status photon_consistency(photon_ctx* c, float* d_dist, void* d_ahat, void* d_a, void* stream) {
+  if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
+  if (c->vanilla) return fail(PHOTON_ESTATE, "a flat-baseline context has no hierarchy");
+  if (!d_dist) return fail(PHOTON_EINVAL, "d_dist is NULL");
+  if (!c->prefilled || c->mode != PHOTON_HIERGEN)
+    return fail(PHOTON_ESTATE, "the diagnostic needs a HierGen context (RecGen never computes A_i)");
+  if (c->tokens <= c->prompt_tokens) return fail(PHOTON_ESTATE, "no chunk decoded yet");
+  const photon_config& cf = c->cfg;
+  const int R = (int)c->B * cf.chunk[1], d = cf.d_model;
+  const size_t bytes = (size_t)R * d * elem_bytes(&cf);
+  const void* Ahat = c->ws + c->plan.Ahat.off;
+  const void* A = c->ws + c->plan.AA.off;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(launch_cosine_distance(cf.dtype, Ahat, A, R, d, d_dist, st));
+  if (d_ahat) HIP_TRY(hipMemcpyAsync(d_ahat, Ahat, bytes, hipMemcpyDeviceToDevice, st));
+  if (d_a) HIP_TRY(hipMemcpyAsync(d_a, A, bytes, hipMemcpyDeviceToDevice, st));
+  return ok();
+}
+
 photon_status photon_sampling_bytes(const photon_config* cfg, int32_t batch, uint64_t* bytes) {
   photon_status s = check_config(cfg);
   if (s) return s;

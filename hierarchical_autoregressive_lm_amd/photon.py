@@ -99,7 +99,7 @@ EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
            "photon_vanilla_weight_layout", "photon_vanilla_weight_tensor",
            "photon_vanilla_open", "photon_vanilla_prefill", "photon_vanilla_decode",
            "photon_sampling_bytes", "photon_set_sampling", "photon_decode_chunk_lp", "photon_sample",
-           "photon_aggregate"]
+           "photon_aggregate", "photon_consistency"]
 
 
 def _load():
@@ -139,6 +139,7 @@ def _load():
         "photon_decode_chunk_lp": [V, V, V, V, V],
         "photon_sample": [i32, i32, V, i64, P(Sampling_), V, V, V, V, V],
         "photon_aggregate": [i32, i32, i32, V, i64, V, i64, i32, i32, V, V, V, V, V],
+        "photon_consistency": [V, V, V, V, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -393,6 +394,19 @@ class Photon:
         None; logprobs_out: float32 [B, S] or None (sampling only)."""
         _check(_lib.photon_decode_chunk_lp(self.ctx, _ptr(tokens_out), _ptr(logits_out), _ptr(logprobs_out),
                                            _stream_handle(self.torch)))
+
+    def consistency(self, copies=False):
+        """The Eq. 1 diagnostic of the last HierGen chunk: [B, C2] float32
+        (and, with copies, A-hat_i and A_i as [B, C2, d] storage-dtype
+        tensors)."""
+        torch = self.torch
+        B, C2, d = self.batch, self.cfg.chunk[1], self.cfg.d_model
+        dist = torch.empty((B, C2), dtype=torch.float32, device=self.device)
+        dt = torch.bfloat16 if self.cfg.dtype == "bf16" else torch.float32
+        ah = torch.empty((B, C2, d), dtype=dt, device=self.device) if copies else None
+        a = torch.empty((B, C2, d), dtype=dt, device=self.device) if copies else None
+        _check(_lib.photon_consistency(self.ctx, _ptr(dist), _ptr(ah), _ptr(a), _stream_handle(torch)))
+        return (dist, ah, a) if copies else dist
 
     def position(self):
         a, b = ctypes.c_int64(), ctypes.c_int64()

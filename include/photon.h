@@ -197,6 +197,18 @@ photon_status photon_prefill(photon_ctx* ctx, int32_t mode, void* d_workspace,
 photon_status photon_decode_chunk(photon_ctx* ctx, int32_t* d_tokens,
                                   float* d_logits, void* stream);
 
+/* Consistency diagnostic: the recursive loss of the paper (explainer,
+ * recursive-generation section: Eq. 1, a cosine distance that training may
+ * add with weight alpha) measured on the chunk a HierGen context decoded
+ * last.  d_dist [batch][C2] float32 out: 1 - cos(A-hat_i[k], A_i[k]) between
+ * the level-1 decoder's reconstruction and the level-1 encoder's summary at
+ * each level-1 position k, on the stored (post-norm, storage-dtype) values,
+ * float32 sums.  d_ahat, d_a: NULL, or [batch][C2][d_model] storage-dtype
+ * copies of A-hat_i and A_i.  PHOTON_ESTATE for a RecGen context (it never
+ * computes A_i) or before the first decoded chunk. */
+photon_status photon_consistency(photon_ctx* ctx, float* d_dist, void* d_ahat,
+                                 void* d_a, void* stream);
+
 /* Position bookkeeping: top states held and tokens (prompt + generated). */
 photon_status photon_position(const photon_ctx* ctx, int64_t* top_len,
                               int64_t* tokens);

@@ -347,3 +347,13 @@ def test_sample_and_aggregate_reject_bad_arguments():
     assert lib.photon_aggregate(8, 2, 4, t, 4, l, 4, 3, 2, b, m, v, None, None) == P.ESHAPE   # reversed span
     assert lib.photon_aggregate(8, 2, 5, t, 4, l, 4, 0, 4, b, m, v, None, None) == P.ESHAPE   # n_tok past the row
     assert lib.photon_aggregate(8, 2, 4, t, 4, l, 4, 0, 4, None, m, v, None, None) == P.EINVAL
+
+
+def test_consistency_needs_state():
+    lib = P._lib
+    f = FakeCtx()
+    V = ctypes.c_void_p
+    assert lib.photon_consistency(f.ctx, None, None, None, None) == P.EINVAL
+    assert lib.photon_consistency(f.ctx, V(1 << 20), None, None, None) == P.ESTATE
+    assert lib.photon_consistency(None, V(1 << 20), None, None, None) == P.EINVAL
+    f.close()
