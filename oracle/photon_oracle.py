@@ -250,16 +250,18 @@ class State:
     the latest top output h, the number of top states, and (HierGen only)
     the level-1 encoder K/V."""
 
-    def __init__(self, top_cache, h_last, n_top_states, lvl1_cache=None):
+    def __init__(self, top_cache, h_last, n_top_states, lvl1_cache=None, tail=None):
         self.top = top_cache
         self.h = h_last
         self.top_len = n_top_states
         self.lvl1 = lvl1_cache
+        self.tail = tail      # prompt tokens past the last whole chunk, or None
 
     def copy(self):
         cp = lambda c: None if c is None else [
             {"k": e["k"].copy(), "v": e["v"].copy()} for e in c]
-        return State(cp(self.top), self.h.copy(), self.top_len, cp(self.lvl1))
+        return State(cp(self.top), self.h.copy(), self.top_len, cp(self.lvl1),
+                     None if self.tail is None else self.tail.copy())
 
 
 def prefill(model, prompt, mode="recgen", log=None):
@@ -275,8 +277,15 @@ def prefill(model, prompt, mode="recgen", log=None):
     prompt = np.asarray(prompt)
     B, P = prompt.shape
     S = cfg.S
-    if P < S or P % S:
-        raise ValueError("prompt length must be a positive multiple of C1*C2")
+    if P < S:
+        raise ValueError("the prompt must hold at least one chunk of C1*C2 tokens")
+    # a ragged prompt: only whole chunks form top states; the r = P mod S
+    # tail tokens open the next chunk, whose decoders take them as given
+    # tokens (teacher forcing) before drawing the rest
+    n = P // S
+    tail = prompt[:, n * S:].copy() if P % S else None
+    prompt = prompt[:, :n * S]
+    P = n * S
     e = model.embed(prompt)
     u1 = model.chunker("W_ch1", e)
     n1 = P // cfg.C1
@@ -286,10 +295,10 @@ def prefill(model, prompt, mode="recgen", log=None):
     n = P // S
     ct = model.empty_cache(cfg.n_top, B)
     h = model.stack("top", cfg.n_top, u2, np.arange(n), ct, log=log)
-    return State(ct, h[:, -1], n, c1 if mode == "hiergen" else None)
+    return State(ct, h[:, -1], n, c1 if mode == "hiergen" else None, tail)
 
 
-def _decode_tokens(model, A_hat, forced_tokens=None, sampling=None, t0=0):
+def _decode_tokens(model, A_hat, forced_tokens=None, sampling=None, t0=0, tail=None):
     """Top-down token generation for one chunk [modules], [recgen].
 
     A_hat: [B, C2, d] level-1 decoder outputs.  Each of the B*C2 level-1
@@ -303,7 +312,8 @@ def _decode_tokens(model, A_hat, forced_tokens=None, sampling=None, t0=0):
     token (teacher forcing); the argmax is still reported.
     sampling = dict(temperature, top_k, seed) draws every token instead
     (photon_sampling.sample; sequence b, absolute position t0 + k*C1 + j)
-    in place of the argmax.
+    in place of the argmax.  tail [B, r] (the end of a ragged prompt) fixes
+    the chunk's first r tokens: they are reported and fed as given.
     """
     cfg = model.cfg
     B, C2, d = A_hat.shape
@@ -315,6 +325,10 @@ def _decode_tokens(model, A_hat, forced_tokens=None, sampling=None, t0=0):
     logits = np.zeros((B * C2, C1, cfg.vocab), dtype=model.dt)
     forced = None if forced_tokens is None else \
         np.asarray(forced_tokens).reshape(B * C2, C1)
+    given = np.full((B, C2 * C1), -1, dtype=np.int64)
+    if tail is not None:
+        given[:, :tail.shape[1]] = tail
+    given = given.reshape(B * C2, C1)
     prev = None
     for j in range(C1):
         x = rows[:, j, :].copy()
@@ -329,7 +343,9 @@ def _decode_tokens(model, A_hat, forced_tokens=None, sampling=None, t0=0):
             for r in range(B * C2):
                 toks[r, j] = S_.sample(lg[r], sampling["temperature"], sampling["top_k"], sampling["seed"],
                                        r // C2, t0 + (r % C2) * C1 + j)
-        prev = toks[:, j] if forced is None else forced[:, j]
+        fixed = given[:, j] >= 0
+        toks[fixed, j] = given[fixed, j]
+        prev = toks[:, j] if forced is None else np.where(fixed, given[:, j], forced[:, j])
     return toks.reshape(B, C2 * C1), logits.reshape(B, C2 * C1, cfg.vocab)
 
 
@@ -366,7 +382,8 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
     C1, C2, d = cfg.C1, cfg.C2, cfg.d_model
     c1 = model.converter("W_cv2", state.h)            # [B, C2, d]
     A_hat = model.stack("dec1", cfg.n_dec1, c1, np.arange(C2), None)
-    toks, logits = _decode_tokens(model, A_hat, forced_tokens, sampling, state.top_len * cfg.S)
+    tail, state.tail = state.tail, None
+    toks, logits = _decode_tokens(model, A_hat, forced_tokens, sampling, state.top_len * cfg.S, tail)
     out = {"tokens": toks, "logits": logits, "A_hat": A_hat}
     if mode == "recgen":
         u = model.chunker("W_ch2", A_hat)[:, 0]
@@ -399,15 +416,23 @@ def consistency(A_hat, A):
 
 
 def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=None, sampling=None):
-    """Prefill then new_tokens / S decode chunks.  Returns (tokens [B, N],
-    logits [B, N, V], final state, per-chunk records).  ``log`` receives
-    progress strings (per prefill layer and per decoded chunk)."""
+    """Prefill then the decode chunks up to P + new_tokens (which must end
+    on a chunk boundary).  Returns (tokens [B, N], logits [B, N, V], final
+    state, per-chunk records) for the N new tokens: with a ragged prompt the
+    first chunk's leading r tokens are the prompt's tail and are left out.
+    ``log`` receives progress strings (per prefill layer and per decoded
+    chunk)."""
     S = model.cfg.S
-    if new_tokens % S:
-        raise ValueError("new_tokens must be a multiple of C1*C2")
+    P = np.asarray(prompt).shape[1]
+    if (P + new_tokens) % S:
+        raise ValueError("prompt + new tokens must end on a multiple of C1*C2")
     st = prefill(model, prompt, mode, log=log)
+    r = P % S
+    chunks = (P + new_tokens) // S - P // S
+    if forced_tokens is not None and r:
+        forced_tokens = np.concatenate([np.asarray(prompt)[:, P - r:], np.asarray(forced_tokens)], 1)
     toks, lg, recs = [], [], []
-    for c in range(new_tokens // S):
+    for c in range(chunks):
         ft = None if forced_tokens is None else \
             np.asarray(forced_tokens)[:, c * S:(c + 1) * S]
         o = decode_chunk(model, st, mode, ft, sampling=sampling)
@@ -415,8 +440,8 @@ def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=N
         lg.append(o["logits"])
         recs.append(o)
         if log and (c + 1) % 8 == 0:
-            log(f"decoded chunk {c + 1}/{new_tokens // S}")
-    return np.concatenate(toks, 1), np.concatenate(lg, 1), st, recs
+            log(f"decoded chunk {c + 1}/{chunks}")
+    return np.concatenate(toks, 1)[:, r:], np.concatenate(lg, 1)[:, r:], st, recs
 
 
 # --------------------------------------------------------------------------

@@ -248,13 +248,13 @@ def test_bf16_contract_values_are_bf16():
         np.testing.assert_array_equal(O.round_bf16(a), a)
 
 
-def test_prefill_rejects_ragged_prompt():
+def test_prefill_needs_one_whole_chunk():
     cfg = tiny()
     m = make(cfg)
     with pytest.raises(ValueError):
-        O.prefill(m, prompts(cfg, 1, 24))
-    with pytest.raises(ValueError):
         O.prefill(m, prompts(cfg, 1, 8))
+    st = O.prefill(m, prompts(cfg, 1, 24))         # one whole chunk + an 8-token tail
+    assert st.top_len == 1 and st.tail.shape == (1, 8)
 
 
 def test_consistency_is_the_cosine_distance():
@@ -284,3 +284,46 @@ def test_consistency_in_hiergen_decoding():
     d = O.consistency(o["A_hat"], o["A"])
     assert d.shape == (2, wl.cfg.C2)
     assert (d >= 0).all() and (d <= 2).all() and d.max() > 1e-3
+
+
+# ---------------- ragged prompts (P mod S != 0) ----------------
+@pytest.mark.parametrize("P,N", [(21, 27), (31, 17), (17, 47)])
+def test_ragged_prompt_hiergen_equals_teacher_forced_full(P, N):
+    # the tail tokens open the next chunk as given tokens: HierGen's
+    # incremental logits at the new positions equal the cache-free forward
+    # over the whole sequence (which sees the chunks in full)
+    cfg = tiny()
+    m = make(cfg, seed=15)
+    pr = prompts(cfg, 2, P, seed=15)
+    toks, lg, st, recs = O.generate(m, pr, N, mode="hiergen")
+    assert toks.shape == (2, N) and lg.shape == (2, N, cfg.vocab)
+    seq = np.concatenate([pr, toks], 1)
+    full = O.hier_full_logits(m, seq, P // 16)        # positions (P // 16) * 16 onwards
+    r = P % 16
+    np.testing.assert_allclose(lg, full[:, r:], rtol=1e-10, atol=1e-12)
+    # the first chunk reports the tail as its leading tokens
+    assert np.array_equal(recs[0]["tokens"][:, :r], pr[:, P - r:])
+    assert st.top_len == (P + N) // 16
+
+
+def test_ragged_prompt_recgen_top_stream_ignores_the_tail():
+    # RecGen's top stream reads no token, so a ragged prompt gives the top
+    # stream of its whole-chunk part, bit for bit; the tokens differ
+    cfg = tiny()
+    m = make(cfg, seed=16)
+    pr = prompts(cfg, 2, 16 * 3 + 5, seed=16)
+    _, _, st_r, recs_r = O.generate(m, pr, 16 * 2 - 5, mode="recgen")
+    _, _, st_w, recs_w = O.generate(m, pr[:, :48], 32, mode="recgen")
+    assert np.array_equal(st_r.h, st_w.h)
+    for a, b in zip(st_r.top, st_w.top):
+        assert np.array_equal(a["k"], b["k"]) and np.array_equal(a["v"], b["v"])
+    assert not np.array_equal(recs_r[0]["tokens"], recs_w[0]["tokens"])
+
+
+def test_ragged_prompt_limits():
+    cfg = tiny()
+    m = make(cfg, seed=17)
+    with pytest.raises(ValueError):
+        O.prefill(m, prompts(cfg, 1, 15, seed=17))          # shorter than a chunk
+    with pytest.raises(ValueError):
+        O.generate(m, prompts(cfg, 1, 20, seed=17), 16)     # does not end on a chunk boundary
