@@ -109,13 +109,24 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeKvCall c) {
 // ids outside [0, V) are clamped so that a bad caller id cannot read past E
 __device__ __forceinline__ int64_t clamp_id(int id, int V) { return id < 0 ? 0 : (id >= V ? V - 1 : id); }
 
+// id i of the gathered list sits at ids[(i / L) * ld + i % L]
 template <typename T>
-__global__ __launch_bounds__(256) void embed_gather_kernel(const int* ids, int64_t n, const T* E, int d, int V, T* out) {
+__global__ __launch_bounds__(256) void embed_gather_kernel(const int* ids, int64_t n, int L, int64_t ld, const T* E,
+                                                           int d, int V, T* out) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n * d) return;
   const int64_t r = idx / d;
   const int e = (int)(idx % d);
-  out[idx] = E[clamp_id(ids[r], V) * d + e];
+  out[idx] = E[clamp_id(ids[(r / L) * ld + r % L], V) * d + e];
+}
+
+__global__ __launch_bounds__(256) void copy_ids_kernel(int* dst, int64_t dst_ld, const int* src, int64_t src_ld,
+                                                       int rows, int cols, int V) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rows * cols) return;
+  const int64_t r = idx / cols;
+  const int i = (int)(idx % cols);
+  dst[r * dst_ld + i] = (int)clamp_id(src[r * src_ld + i], V);
 }
 
 // Greedy head, step j: one workgroup per row m = b*C2 + k reduces the
@@ -147,9 +158,10 @@ __global__ __launch_bounds__(1024) void argmax_next_kernel(ArgmaxNext c) {
   best = bvs[0]; bi = bis[0];
   for (int i = 1; i < nw; ++i)
     if (bvs[i] > best || (bvs[i] == best && bis[i] < bi)) { best = bvs[i]; bi = bis[i]; }
-  if (threadIdx.x == 0) {
-    const int b = m / c.C2, k = m % c.C2;
-    c.tokens[(int64_t)b * c.C1 * c.C2 + k * c.C1 + c.j] = bi;
+  {
+    const int b = m / c.C2, p = (m % c.C2) * c.C1 + c.j;
+    if (p < c.given_r) bi = c.given[(int64_t)b * c.C1 * c.C2 + p];   // block-uniform
+    if (threadIdx.x == 0) c.tokens[(int64_t)b * c.C1 * c.C2 + p] = bi;
   }
   if (!c.x) return;                      // uniform across the block
   const int d = c.d;
@@ -236,10 +248,31 @@ hipError_t launch_rope_kv(const RopeKvCall& c, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_embed_gather_rows(int dtype, const int* ids, int64_t rows, int L, int64_t ld, const void* E, int d,
+                                    int V, void* out, hipStream_t st) {
+  const int64_t n = rows * L;
+  if (n <= 0) return hipSuccess;
+  if (dtype)
+    PH_LAUNCH((embed_gather_kernel<bf16_t>), blocks(n * d), 256, 0, st, ids, n, L, ld, (const bf16_t*)E, d, V,
+              (bf16_t*)out);
+  else
+    PH_LAUNCH((embed_gather_kernel<float>), blocks(n * d), 256, 0, st, ids, n, L, ld, (const float*)E, d, V,
+              (float*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed_gather(int dtype, const int* ids, int64_t n, const void* E, int d, int V, void* out,
                                hipStream_t st) {
-  if (dtype) PH_LAUNCH((embed_gather_kernel<bf16_t>), blocks(n * d), 256, 0, st, ids, n, (const bf16_t*)E, d, V, (bf16_t*)out);
-  else PH_LAUNCH((embed_gather_kernel<float>), blocks(n * d), 256, 0, st, ids, n, (const float*)E, d, V, (float*)out);
+  if (n <= 0) return hipSuccess;
+  if (n > 0x7fffffff) return hipErrorInvalidValue;
+  return launch_embed_gather_rows(dtype, ids, 1, (int)n, n, E, d, V, out, st);
+}
+
+hipError_t launch_copy_ids(int* dst, int64_t dst_ld, const int* src, int64_t src_ld, int rows, int cols, int V,
+                           hipStream_t st) {
+  const int64_t n = (int64_t)rows * cols;
+  if (n <= 0) return hipSuccess;
+  PH_LAUNCH((copy_ids_kernel), blocks(n), 256, 0, st, dst, dst_ld, src, src_ld, rows, cols, V);
   return hipGetLastError();
 }
 

@@ -119,15 +119,24 @@ hipError_t launch_attn_prefill(const AttnCall& a, hipStream_t st);
 hipError_t launch_embed_gather(int dtype, const int* ids, int64_t n,
                                const void* E, int d, int V, void* out,
                                hipStream_t st);
+// The same over `rows` rows of L ids each, row r starting at ids + r*ld.
+hipError_t launch_embed_gather_rows(int dtype, const int* ids, int64_t rows, int L, int64_t ld,
+                                    const void* E, int d, int V, void* out, hipStream_t st);
+// dst[r*dst_ld + i] = clamp(src[r*src_ld + i], 0, V-1) for i < cols, r < rows.
+hipError_t launch_copy_ids(int* dst, int64_t dst_ld, const int* src, int64_t src_ld, int rows, int cols, int V,
+                           hipStream_t st);
 // Greedy head of token step j: reduce the ARGMAX tiles of row m = b*C2 + k
 // to its token (tokens[b*S + k*C1 + j]); if x is set, also write the next
 // step's input x[m] = c0[m*c0_ld + (j+1)*d ..] + E[token] (E[token] alone
 // when c0 is null) and its norm a[m].
+// Positions p = k*C1 + j < given_r take the token given[b*S + p] instead
+// (the tail of a ragged prompt), ids already in [0, V).
 struct ArgmaxNext {
   const float* val; const int* idx; int n_tiles, M, C1, C2, j;
   int* tokens;
   const float* c0; int64_t c0_ld; const void* E;
   float* x; void* a; const float* g; int d; float eps;
+  const int* given; int given_r;
 };
 hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st);
 // out[r] = 1 - cos(a[r], e[r]) for R rows of d storage-dtype elements.
@@ -158,6 +167,7 @@ struct SampleCall {
   const int* counter; int C1, C2, j;
   int* ids; float* val;
   float* logprob;
+  const int* given; int given_r;   // decode layout: positions < given_r take given[b*S + p]
 };
 int sample_supported(int V);
 hipError_t launch_sample(const SampleCall& c, hipStream_t st);

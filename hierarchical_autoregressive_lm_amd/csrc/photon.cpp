@@ -143,7 +143,7 @@ struct WsPlan {
   int nsplit_top = 1, nsplit_low = 1;
   int head_tiles = 1;
   // persistent
-  Region top_kv, low_kv, dec_kv, h, counter, rope, tok;
+  Region top_kv, low_kv, dec_kv, h, counter, rope, tok, tail;
   // decode scratch, set A (top branch) and set B (level-1 decoder + tokens)
   Region xA, aA, partA, qA, oA, hidA, apartA, eA, AA;
   Region xB, aB, partB, qB, oB, hidB, c0, Ahat, zB, kv1tmp, amv, ami;
@@ -196,6 +196,7 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.counter = cur.take(sizeof(int));
   p.rope = cur.take((uint64_t)p.rope_pos * (hd / 2) * 2 * sizeof(float));
   p.tok = cur.take((uint64_t)B * S * sizeof(int));
+  p.tail = cur.take((uint64_t)B * S * sizeof(int));   // a ragged prompt's tail tokens
   p.off_scratch = align_up(cur.pos);
   p.state_bytes = p.off_scratch - p.off_state;
   const int64_t MA = hier ? B * C2 : B, MB = B * C2;
@@ -444,6 +445,10 @@ struct photon_ctx {
   bool prefilled = false;
   int mode = 0;
   int64_t B = 0, max_tokens = 0, top_len = 0, tokens = 0, prompt_tokens = 0;
+  // ragged prompt: tail_r = prompt_len mod S tokens open the next chunk as
+  // given tokens; pending until that chunk is decoded
+  int tail_r = 0;
+  bool tail_pending = false;
   unsigned char* ws = nullptr;
   WsPlan plan;
   Tracer tr;
@@ -775,9 +780,9 @@ photon_status photon_prefill_scratch_bytes(const photon_config* cfg, int32_t bat
   if (mode != PHOTON_RECGEN && mode != PHOTON_HIERGEN) return fail(PHOTON_EINVAL, "bad mode %d", mode);
   if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
   const int S = cfg->chunk[0] * cfg->chunk[1];
-  if (prompt_len < S || prompt_len % S)
-    return fail(PHOTON_ESHAPE, "prompt_len %d must be a positive multiple of C1*C2 = %d", prompt_len, S);
-  *out = plan_prefill(cfg, batch, prompt_len, mode).total;
+  if (prompt_len < S)
+    return fail(PHOTON_ESHAPE, "prompt_len %d must hold at least one chunk of C1*C2 = %d tokens", prompt_len, S);
+  *out = plan_prefill(cfg, batch, prompt_len / S * S, mode).total;   // whole chunks only
   return ok();
 }
 
@@ -859,14 +864,16 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   const photon_config& cf = c->cfg;
   const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
   if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
-  if (prompt_len < S || prompt_len % S)
-    return fail(PHOTON_ESHAPE, "prompt_len %d must be a positive multiple of C1*C2 = %d", prompt_len, S);
+  if (prompt_len < S)
+    return fail(PHOTON_ESHAPE, "prompt_len %d must hold at least one chunk of C1*C2 = %d tokens", prompt_len, S);
   if (max_tokens < prompt_len) return fail(PHOTON_ECAPACITY, "max_tokens %lld < prompt_len %d", (long long)max_tokens, prompt_len);
   const WsPlan wp = plan_workspace(&cf, batch, max_tokens, mode);
   if (ws_bytes < wp.total)
     return fail(PHOTON_ECAPACITY, "workspace holds %llu bytes, needs %llu", (unsigned long long)ws_bytes,
                 (unsigned long long)wp.total);
-  const PrePlan pp = plan_prefill(&cf, batch, prompt_len, mode);
+  // whole chunks are encoded; a ragged tail opens the next chunk
+  const int P_enc = prompt_len / S * S, tail_r = prompt_len - P_enc;
+  const PrePlan pp = plan_prefill(&cf, batch, P_enc, mode);
   if (scratch_bytes < pp.total)
     return fail(PHOTON_ECAPACITY, "prefill scratch holds %llu bytes, needs %llu", (unsigned long long)scratch_bytes,
                 (unsigned long long)pp.total);
@@ -901,9 +908,9 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   for (int64_t b0 = 0; b0 < batch; b0 += pp.bs) {
     const int bs = (int)std::min<int64_t>(pp.bs, batch - b0);
     // embedding rows of bs*P tokens == Chunker^1 input [bs*n1][C1*d]
-    PH_TRY(traced(c, PHOTON_K_EMBED, (double)bs * prompt_len * (4 + 2.0 * d * eb), 0, st, "embed_gather", [&] {
-      return launch_embed_gather(dt, d_prompt + b0 * prompt_len, (int64_t)bs * prompt_len, c->E, d, cf.vocab,
-                                 sc + pp.e.off, st);
+    PH_TRY(traced(c, PHOTON_K_EMBED, (double)bs * P_enc * (4 + 2.0 * d * eb), 0, st, "embed_gather", [&] {
+      return launch_embed_gather_rows(dt, d_prompt + b0 * prompt_len, bs, P_enc, prompt_len, c->E, d, cf.vocab,
+                                      sc + pp.e.off, st);
     }));
     int ks = 1;
     PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, sc + pp.e.off, (int64_t)C1 * d, c->W_ch1, (int)(bs * n1), d, C1 * d,
@@ -936,9 +943,13 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
     PH_TRY(run_stack(c, c->top, bufs, t, st));
   }
   HIP_TRY(launch_set_int((int*)(ws + wp.counter.off), (int)n, st));
+  if (tail_r)
+    HIP_TRY(launch_copy_ids((int*)(ws + wp.tail.off), S, d_prompt + P_enc, prompt_len, batch, tail_r, cf.vocab, st));
   c->top_len = n;
   c->tokens = prompt_len;
   c->prompt_tokens = prompt_len;
+  c->tail_r = tail_r;
+  c->tail_pending = tail_r > 0;
   c->prefilled = true;
   return ok();
 }
@@ -947,7 +958,7 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
 // and st_top != st the top branch forks onto st_top (after A-hat exists) and
 // joins back before the chunk ends.  Everything reads positions from the
 // device counter, so the same sequence serves every chunk.
-photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipStream_t st_top) {
+photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipStream_t st_top, int given_r = 0) {
   const photon_config& cf = c->cfg;
   const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
   const WsPlan& wp = c->plan;
@@ -1019,13 +1030,15 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
       // the sampler's id takes the place of the argmax tiles (one tile)
       SampleCall sc{g.C, g.ldc, MB, V, c->samp.temperature, c->samp.top_k, (uint32_t)c->samp.seed,
                     (uint32_t)(c->samp.seed >> 32), nullptr, nullptr, counter, C1, C2, j,
-                    g.amax_idx, g.amax_val, (float*)(c->sws + sampling_lp_off(cf, B))};
+                    g.amax_idx, g.amax_val, (float*)(c->sws + sampling_lp_off(cf, B)),
+                    (const int*)(ws + wp.tail.off), given_r};
       PH_TRY(traced(c, PHOTON_K_SAMPLE, (double)MB * V * 4 + (double)MB * 12, 0, st, "sample",
                     [&] { return launch_sample(sc, st); }));
     }
     const bool next = j + 1 < C1;
     ArgmaxNext an{g.amax_val, g.amax_idx, c->sampling ? 1 : wp.head_tiles, MB, C1, C2, j, tok,
-                  c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec0.layers[0].g1, d, cf.norm_eps};
+                  c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec0.layers[0].g1, d, cf.norm_eps,
+                  (const int*)(ws + wp.tail.off), given_r};
     // the next step's input (conditioning row + embedding in, stream and its
     // norm out); the token ids are counted with the head
     const double nb = next ? (double)MB * d * (8 + 2 * eb) : 0;
@@ -1094,7 +1107,7 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
   if (d_logprobs && !c->sampling) return fail(PHOTON_ESTATE, "log-likelihoods need a sampling context");
   const photon_config& cf = c->cfg;
   const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
-  if (c->tokens + S > c->max_tokens)
+  if ((c->top_len + 1) * S > c->max_tokens)
     return fail(PHOTON_ECAPACITY, "chunk would pass max_tokens %lld", (long long)c->max_tokens);
   if (c->mode == PHOTON_HIERGEN && !c->wpre)
     return fail(PHOTON_ESTATE, "HierGen decoding needs the prefill-only weights, which were released");
@@ -1104,7 +1117,11 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
   hipStream_t st = (hipStream_t)stream;
   const int B = (int)c->B;
   int* tok = (int*)(c->ws + c->plan.tok.off);
-  if (c->use_graph && !d_logits && c->tr.mask == 0) {
+  if (c->tail_pending) {
+    // the chunk a ragged prompt opened: its first tail_r tokens are given
+    // (direct launches; the captured graph serves the whole chunks)
+    PH_TRY(enqueue_chunk(c, d_logits, st, st, c->tail_r));
+  } else if (c->use_graph && !d_logits && c->tr.mask == 0) {
     if (!c->graph) {
       for (auto& cs : c->cap)
         if (!cs) HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
@@ -1135,7 +1152,8 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
     HIP_TRY(hipMemcpyAsync(d_logprobs, c->sws + sampling_lp_off(cf, B), (size_t)B * S * sizeof(float),
                            hipMemcpyDeviceToDevice, st));
   c->top_len += 1;
-  c->tokens += S;
+  c->tokens = c->top_len * S;
+  c->tail_pending = false;
   return ok();
 }
 
@@ -1226,14 +1244,15 @@ photon_status photon_set_position(photon_ctx* c, int64_t tokens, void* stream) {
   if (!c->prefilled) return fail(PHOTON_ESTATE, "no prefill to rewind to");
   // a flat-baseline context counts tokens (steps per call), PHOTON top states
   const int64_t S = c->vanilla ? c->vcfg.steps : (int64_t)c->cfg.chunk[0] * c->cfg.chunk[1];
-  if (tokens % S || tokens < c->prompt_tokens || tokens > c->tokens)
-    return fail(PHOTON_ESHAPE, "position %lld must be a multiple of %lld within [%lld, %lld]", (long long)tokens,
-                (long long)S, (long long)c->prompt_tokens, (long long)c->tokens);
+  if ((tokens % S && tokens != c->prompt_tokens) || tokens < c->prompt_tokens || tokens > c->tokens)
+    return fail(PHOTON_ESHAPE, "position %lld must be the prompt end or a multiple of %lld within [%lld, %lld]",
+                (long long)tokens, (long long)S, (long long)c->prompt_tokens, (long long)c->tokens);
   int* counter = (int*)(c->ws + (c->vanilla ? c->vplan.counter.off : c->plan.counter.off));
   const int64_t pos = c->vanilla ? tokens : tokens / S;
   HIP_TRY(launch_set_int(counter, (int)pos, (hipStream_t)stream));
   c->tokens = tokens;
   c->top_len = pos;
+  c->tail_pending = !c->vanilla && c->tail_r > 0 && tokens == c->prompt_tokens;
   return ok();
 }
 

@@ -287,6 +287,13 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
     for (int i = 1; i < kWaves; ++i)
       if (arg_s[i] > best || (arg_s[i] == best && arg_i[i] < bi)) { best = arg_s[i]; bi = arg_i[i]; bx = arg_x[i]; }
     bi = bi < V ? bi : 0;
+    if (!c.seq) {
+      const int p = (r % c.C2) * c.C1 + c.j;
+      if (p < c.given_r) {   // a given token (ragged prompt tail): no draw
+        bi = c.given[(int64_t)(r / c.C2) * c.C1 * c.C2 + p];
+        bx = row[bi];
+      }
+    }
     c.ids[r] = bi;
     if (c.val) c.val[r] = best;
     if (c.logprob) {

@@ -443,30 +443,35 @@ class Photon:
 
     def generate(self, prompt, new_tokens, mode="recgen", logits=False, max_tokens=None, sampling=None,
                  logprobs=False):
-        """Prefill, then new_tokens / S chunks.  sampling: None (greedy) or
-        dict(temperature, top_k, seed).  Returns (tokens, logits or None),
-        plus the log-likelihoods [B, N] when logprobs (sampling only)."""
+        """Prefill, then the chunks up to P + new_tokens (a multiple of S;
+        with a ragged prompt the first chunk's leading P mod S tokens are the
+        prompt's tail and are left out of the result).  sampling: None
+        (greedy) or dict(temperature, top_k, seed).  Returns (tokens [B, N],
+        logits [B, N, V] or None), plus the log-likelihoods [B, N] when
+        logprobs (sampling only)."""
         torch = self.torch
         B, P = prompt.shape
         S = self.cfg.S
-        if new_tokens % S:
-            raise ValueError("new_tokens must be a multiple of C1*C2")
+        if (P + new_tokens) % S:
+            raise ValueError("prompt + new tokens must end on a multiple of C1*C2")
+        r = P % S
+        chunks = (P + new_tokens) // S - P // S
         self.prefill(prompt, max_tokens or P + new_tokens, mode)
         if sampling is not None:
             self.set_sampling(sampling["temperature"], sampling.get("top_k", 0), sampling.get("seed", 0), B)
         else:
             self.set_sampling(None)
-        toks = torch.empty((new_tokens // S, B, S), dtype=torch.int32, device=self.device)
-        lg = torch.empty((new_tokens // S, B, S, self.cfg.vocab), dtype=torch.float32,
+        toks = torch.empty((chunks, B, S), dtype=torch.int32, device=self.device)
+        lg = torch.empty((chunks, B, S, self.cfg.vocab), dtype=torch.float32,
                          device=self.device) if logits else None
-        lp = torch.empty((new_tokens // S, B, S), dtype=torch.float32, device=self.device) if logprobs else None
-        for c in range(new_tokens // S):
+        lp = torch.empty((chunks, B, S), dtype=torch.float32, device=self.device) if logprobs else None
+        for c in range(chunks):
             self.decode_chunk(toks[c], lg[c] if logits else None, lp[c] if logprobs else None)
-        toks = toks.permute(1, 0, 2).reshape(B, new_tokens)
+        toks = toks.permute(1, 0, 2).reshape(B, chunks * S)[:, r:]
         if logits:
-            lg = lg.permute(1, 0, 2, 3).reshape(B, new_tokens, self.cfg.vocab)
+            lg = lg.permute(1, 0, 2, 3).reshape(B, chunks * S, self.cfg.vocab)[:, r:]
         if logprobs:
-            return toks, lg, lp.permute(1, 0, 2).reshape(B, new_tokens)
+            return toks, lg, lp.permute(1, 0, 2).reshape(B, chunks * S)[:, r:]
         return toks, lg
 
     # ---- views into the workspace (tests read the caches directly) ----

@@ -162,11 +162,15 @@ const char* photon_last_error(void);
 
 /* Prefill (explainer, module table and recursive-generation section):
  * embedding -> Chunker^1 -> level-1 encoder (causal) -> Chunker^2 -> top
- * encoder (causal), writing top K/V slots 0 .. P/S - 1 and the last top
- * output h into the workspace.  RecGen keeps no level-1 K/V; HierGen writes
- * it into the workspace's level-1 region.
+ * encoder (causal), writing top K/V slots 0 .. n - 1 (n = prompt_len / S,
+ * whole chunks) and the last top output h into the workspace.  RecGen keeps
+ * no level-1 K/V; HierGen writes it into the workspace's level-1 region.
+ * A ragged prompt (prompt_len mod S = r > 0): only whole chunks form top
+ * states; the r tail tokens open chunk n, whose decoders take them as given
+ * tokens (the next photon_decode_chunk reports them as its first r tokens
+ * and draws the other S - r).
  *   d_prompt   [batch][prompt_len] int32 device ids.
- *   prompt_len positive multiple of S (else PHOTON_ESHAPE).
+ *   prompt_len >= S (else PHOTON_ESHAPE).
  *   max_tokens the capacity the workspace was sized for; prompt_len plus
  *              every later decoded chunk must fit (else PHOTON_ECAPACITY).
  *   d_workspace >= photon_kv_bytes(cfg, batch, max_tokens, mode)
@@ -213,8 +217,9 @@ photon_status photon_consistency(photon_ctx* ctx, float* d_dist, void* d_ahat,
 photon_status photon_position(const photon_ctx* ctx, int64_t* top_len,
                               int64_t* tokens);
 
-/* Move the decode position back to `tokens` (a multiple of S between the
- * prompt length and the current position), enqueued on `stream`.  The top
+/* Move the decode position back to `tokens` (the prompt end, or a multiple
+ * of S between it and the current position), enqueued on `stream`; back at
+ * a ragged prompt's end, the next chunk takes the tail as given again.  The top
  * K/V slots from tokens/S on become free and are rewritten by the next
  * chunks.  The caller must first restore the workspace's h region (the
  * photon_kv_report state region, [batch][d] at off_state) to the value it

@@ -111,9 +111,12 @@ def test_prompt_shape_errors():
     out = ctypes.c_uint64()
     c = _cfg()
     lib = P._lib
-    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 24, 0, ctypes.byref(out)) == P.ESHAPE
     assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 8, 0, ctypes.byref(out)) == P.ESHAPE
     assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 32, 0, ctypes.byref(out)) == P.OK
+    whole = out.value
+    # a ragged prompt is prefilled over its whole chunks only
+    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 47, 0, ctypes.byref(out)) == P.OK
+    assert out.value == whole
 
 
 class FakeCtx:
@@ -144,8 +147,8 @@ def test_state_and_capacity_errors_before_any_device_call():
     need = P.kv_bytes(pi.CONFIGS["tiny"], 2, 96)["workspace_total"]
     # prefill scratch too small
     assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 16, pr, 2, 64, 96, None) == P.ECAPACITY
-    # ragged prompt, max_tokens below the prompt, misaligned workspace
-    assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 1 << 30, pr, 2, 60, 96, None) == P.ESHAPE
+    # prompt shorter than one chunk, max_tokens below the prompt, misaligned workspace
+    assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 1 << 30, pr, 2, 12, 96, None) == P.ESHAPE
     assert lib.photon_prefill(f.ctx, 0, ws, need, sc, 1 << 30, pr, 2, 64, 32, None) == P.ECAPACITY
     assert lib.photon_prefill(f.ctx, 0, V((4 << 20) + 8), need, sc, 1 << 30, pr, 2, 64, 96, None) == P.EINVAL
     assert lib.photon_prefill(f.ctx, 5, ws, need, sc, 1 << 30, pr, 2, 64, 96, None) == P.EINVAL
