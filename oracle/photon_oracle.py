@@ -147,8 +147,11 @@ def attention(q, k, v, n_prev):
 
 
 def linear(x, W):
-    """y = x W^T, W[out, in]."""
-    return x @ W.T
+    """y = x W^T, W[out, in], row by row over every leading axis of x (one
+    library matrix product over the flattened rows)."""
+    x = np.asarray(x)
+    y = x.reshape(-1, x.shape[-1]) @ W.T
+    return y.reshape(x.shape[:-1] + (W.shape[0],))
 
 
 # --------------------------------------------------------------------------
