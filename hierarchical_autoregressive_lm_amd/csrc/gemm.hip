@@ -12,6 +12,8 @@
 // use WK = 4 (each wave streams a quarter of every k-block, partial sums
 // reduced through LDS at the end) so that narrow GEMMs still spread over
 // many CUs; the largest M tile uses WK = 1.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -260,6 +262,191 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
   }
 }
 
+// ---- decode GEMM with the tiles streamed into LDS by direct loads ----
+//
+// gfx950's global_load_lds_dwordx4 writes 16 bytes per lane straight into
+// LDS, so the prefetch depth costs LDS, not registers.  A ring of P stages,
+// each one 64-wide k-block of the tile's A rows (first) and W rows (then),
+// 128 bytes per row with the 16-byte chunks XOR-swizzled by the row so that
+// the MFMA fragment reads spread over the banks.  Every wave issues its
+// share of a stage's loads; before computing on stage kb it waits until at
+// most the loads of the stages after kb are in flight (an explicit vmcnt)
+// and meets the others at a barrier, which also frees the slot the next
+// stage is loaded into.  Each ring slot is an LDS object of its own: the
+// compiler then tells the slots apart and inserts no wait of its own.  The
+// k loop is unrolled at compile time (NKB k-blocks per workgroup), so every
+// slot index and wait count is a constant.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt not waited on
+constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+#define PH_LDS_SLOTS(X) X(0) X(1) X(2) X(3) X(4) X(5)
+
+template <int BM, int BN, int WM, int P, int EPI, int NKB>
+__global__ __launch_bounds__(256) void gemm_lds_kernel(GemmP p) {
+  constexpr int WN = 4 / WM, TM = BM / WM, TN = BN / WN, MF = TM / 16, NF = TN / 16;
+  constexpr int ROWS = BM + BN;             // A rows, then W rows; 128 B each
+  constexpr int SLOT_U4 = ROWS * 8;         // 16-byte units per slot
+  constexpr int I = ROWS / 32;              // direct-load instructions per wave per stage
+  static_assert(ROWS % 32 == 0 && TM % 16 == 0 && TN % 16 == 0 && P >= 2 && P <= 6, "tile");
+  static_assert(EPI != EPI_ARGMAX || 2 * WN * BM * 4 <= ROWS * 128, "argmax partials fit a slot");
+#define PH_DECL(s) __shared__ __attribute__((aligned(16))) uint4 L##s[s < P ? SLOT_U4 : 1];
+  PH_LDS_SLOTS(PH_DECL)
+#undef PH_DECL
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int total = p.m_tiles * p.n_tiles;
+  const int ks = blockIdx.x % p.ksplit;
+  const int bid = blockIdx.x / p.ksplit;
+  const int tile = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  const int mt = tile % p.m_tiles, nt = tile / p.m_tiles;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int K = p.K;
+  const int kb0 = ks * NKB;
+
+  // the source row of this lane in each of its load instructions (rows past
+  // M or N are clamped: their results are never stored)
+  const bf16_t* src[I];
+#pragma unroll
+  for (int q = 0; q < I; ++q) {
+    const int row = (wave * I + q) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    if (row < BM) src[q] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + chunk * 8;
+    else src[q] = p.W + (int64_t)min(n0 + row - BM, p.N - 1) * K + chunk * 8;
+  }
+  auto issue = [&](auto sc, int kb) {
+    constexpr int s = decltype(sc)::value;
+    uint4* Ls = s == 0 ? L0 : s == 1 ? L1 : s == 2 ? L2 : s == 3 ? L3 : s == 4 ? L4 : L5;
+#pragma unroll
+    for (int q = 0; q < I; ++q)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src[q] + (int64_t)kb * 64),
+                                       (lds_void_t*)(Ls + (wave * I + q) * 64), 16, 0, 0);
+  };
+
+  f32x4 acc[MF][NF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    const uint4* Ls = s == 0 ? L0 : s == 1 ? L1 : s == 2 ? L2 : s == 3 ? L3 : s == 4 ? L4 : L5;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kc = u * 4 + (lane >> 4);   // this lane's 8 k values
+      bf16x8 a[MF], w[NF];
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int row = wm * TM + i * 16 + (lane & 15);
+        a[i] = *reinterpret_cast<const bf16x8*>(Ls + row * 8 + (kc ^ (row & 7)));
+      }
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        const int row = BM + wn * TN + j * 16 + (lane & 15);
+        w[j] = *reinterpret_cast<const bf16x8*>(Ls + row * 8 + (kc ^ (row & 7)));
+      }
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j], a[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  static_for([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s < NKB) issue(sc, kb0 + s);
+  }, std::make_integer_sequence<int, P - 1>{});
+  static_for([&](auto kbc) {
+    constexpr int kb = decltype(kbc)::value;
+    constexpr int ahead = (P - 2 < NKB - 1 - kb) ? P - 2 : NKB - 1 - kb;   // later stages still in flight
+    __builtin_amdgcn_s_waitcnt(vm_wait(ahead * I));
+    __builtin_amdgcn_s_barrier();
+    if constexpr (kb + P - 1 < NKB) issue(std::integral_constant<int, (kb + P - 1) % P>{}, kb0 + kb + P - 1);
+    compute(std::integral_constant<int, kb % P>{});
+  }, std::make_integer_sequence<int, NKB>{});
+
+  // epilogue: each lane holds features 4*(lane>>4)..+3 of row (lane&15)
+  const int fl = (lane >> 4) * 4;
+  if constexpr (EPI != EPI_ARGMAX) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int row = m0 + wm * TM + i * 16 + (lane & 15);
+      if (row >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        const int f = n0 + wn * TN + j * 16 + fl;
+        if (f >= p.N) continue;
+        const f32x4 v = acc[i][j];
+        if constexpr (EPI == EPI_STORE) {
+          *reinterpret_cast<float4*>(p.C + ks * p.pstride + (int64_t)row * p.ldc + f) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == EPI_ADD) {
+          float4* o = reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f);
+          float4 c = *o;
+          c.x += v[0]; c.y += v[1]; c.z += v[2]; c.w += v[3];
+          *o = c;
+        } else {   // GELU, rounded to bf16
+          uint2 pk;
+          pk.x = (uint32_t)f2bf(gelu_f(v[0])) | ((uint32_t)f2bf(gelu_f(v[1])) << 16);
+          pk.y = (uint32_t)f2bf(gelu_f(v[2])) | ((uint32_t)f2bf(gelu_f(v[3])) << 16);
+          *reinterpret_cast<uint2*>(p.Cb + (int64_t)row * p.ldc + f) = pk;
+        }
+      }
+    }
+  } else {
+    // greedy head: optional logits, then the per-row first maximum of the
+    // tile; the partials go through ring slot 0 once every wave is done
+    __builtin_amdgcn_s_barrier();
+    float* bv = reinterpret_cast<float*>(L0);
+    int* bi = reinterpret_cast<int*>(L0) + WN * BM;
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int rl = wm * TM + i * 16 + (lane & 15);
+      const int row = m0 + rl;
+      float best = -INFINITY;
+      int bidx = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        const int f = n0 + wn * TN + j * 16 + fl;
+        if (f >= p.N) continue;
+        const f32x4 v = acc[i][j];
+        if (p.C && row < p.M)
+          *reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (v[r] > best) { best = v[r]; bidx = f + r; }
+      }
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bidx, o, 64);
+        if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+      }
+      if ((lane >> 4) == 0) { bv[wn * BM + rl] = best; bi[wn * BM + rl] = bidx; }
+    }
+    __syncthreads();
+    for (int rl = tid; rl < BM; rl += 256) {
+      const int row = m0 + rl;
+      if (row >= p.M) continue;
+      float best = bv[rl];
+      int bidx = bi[rl];
+#pragma unroll
+      for (int w = 1; w < WN; ++w)
+        if (bv[w * BM + rl] > best) { best = bv[w * BM + rl]; bidx = bi[w * BM + rl]; }
+      p.av[(int64_t)nt * p.M + row] = best;
+      p.ai[(int64_t)nt * p.M + row] = bidx;
+    }
+  }
+}
+
 // ---- fp32 models: plain FMA kernel, one thread per output ----
 struct GemmPF {
   const float* A; int64_t lda;
@@ -360,11 +547,72 @@ struct Plan {
   X(512, 6144, 1536, EPI_GELU, 0, 8, 2, 1, 4, 1, 24, false) \
   X(512, 32000, 1536, EPI_ARGMAX, 0, 8, 2, 1, 4, 1, 24, false)
 
+// Shapes where the LDS-streaming kernel (gemm_lds_kernel) measured faster
+// than every register-streaming tile above, same conditions (weights
+// rotated past the Infinity Cache).  Fields: M, N, K, epilogue, whether the
+// entry splits K into slabs, then rows x features per workgroup (BM, BN),
+// waves along M (WM; 4 / WM along N), ring depth P, K slabs, k-blocks per
+// workgroup; the comment gives the register kernel's time and this one's.
+#define PHOTON_GEMM_LDS_TUNED(X) \
+  X(32, 768, 768, EPI_STORE, 1, 32, 32, 2, 4, 4, 3) /* 3.8 -> 2.7 us */ \
+  X(32, 768, 3072, EPI_STORE, 1, 32, 32, 2, 6, 8, 6) /* 4.5 -> 3.2 us */ \
+  X(32, 2304, 768, EPI_STORE, 1, 32, 64, 1, 4, 4, 3) /* 3.8 -> 3.2 us */ \
+  X(32, 3072, 768, EPI_GELU, 0, 32, 32, 2, 6, 1, 12) /* 5.4 -> 3.9 us */ \
+  X(32, 3072, 768, EPI_STORE, 1, 32, 32, 2, 6, 2, 6) /* 4.2 -> 3.2 us */ \
+  X(64, 1536, 1536, EPI_STORE, 1, 32, 64, 1, 6, 4, 6) /* 4.9 -> 3.5 us */ \
+  X(64, 1536, 6144, EPI_STORE, 1, 64, 64, 2, 6, 8, 12) /* 10.0 -> 7.1 us */ \
+  X(64, 4608, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12) /* 7.8 -> 5.3 us */ \
+  X(64, 6144, 1536, EPI_GELU, 0, 64, 32, 2, 6, 1, 24) /* 12.9 -> 8.9 us */ \
+  X(64, 6144, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12) /* 9.9 -> 7.6 us */ \
+  X(64, 6144, 1536, EPI_STORE, 0, 64, 32, 2, 6, 1, 24) /* 10.9 -> 8.0 us */ \
+  X(64, 32000, 1536, EPI_ARGMAX, 0, 64, 128, 2, 4, 1, 24) /* 25.1 -> 22.8 us */ \
+  X(128, 768, 768, EPI_STORE, 1, 32, 32, 2, 6, 2, 6) /* 4.0 -> 3.1 us */ \
+  X(128, 768, 3072, EPI_STORE, 1, 64, 32, 2, 6, 4, 12) /* 6.1 -> 4.2 us */ \
+  X(128, 2304, 768, EPI_STORE, 1, 32, 32, 2, 4, 2, 6) /* 5.5 -> 4.0 us */ \
+  X(128, 3072, 768, EPI_GELU, 0, 32, 32, 2, 6, 1, 12) /* 7.8 -> 4.8 us */ \
+  X(128, 3072, 768, EPI_STORE, 1, 64, 32, 4, 6, 1, 12) /* 6.0 -> 4.1 us */ \
+  X(128, 3072, 768, EPI_STORE, 0, 32, 64, 2, 6, 1, 12) /* 7.1 -> 4.2 us */ \
+  X(128, 32000, 768, EPI_ARGMAX, 0, 128, 128, 2, 4, 1, 12) /* 20.4 -> 17.2 us */ \
+  X(256, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 4, 2, 12) /* 8.5 -> 5.2 us */ \
+  X(256, 1536, 3072, EPI_STORE, 1, 64, 64, 2, 6, 2, 24) /* 12.0 -> 7.0 us */ \
+  X(256, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 8, 12) /* 17.0 -> 12.9 us */ \
+  X(256, 3072, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24) /* 11.9 -> 7.0 us */ \
+  X(256, 4608, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24) /* 14.0 -> 9.7 us */ \
+  X(256, 6144, 1536, EPI_GELU, 0, 128, 64, 4, 4, 1, 24) /* 22.2 -> 17.1 us */ \
+  X(256, 6144, 1536, EPI_STORE, 1, 128, 128, 2, 4, 2, 12) /* 17.1 -> 13.3 us */ \
+  X(256, 6144, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24) /* 19.1 -> 13.8 us */ \
+  X(512, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24) /* 12.8 -> 6.9 us */ \
+  X(512, 1536, 3072, EPI_STORE, 1, 128, 64, 4, 4, 2, 24) /* 16.5 -> 10.2 us */ \
+  X(512, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 4, 24) /* 25.7 -> 18.9 us */ \
+  X(512, 3072, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24) /* 16.9 -> 9.9 us */ \
+  X(512, 3072, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24) /* 18.5 -> 10.1 us */ \
+  X(512, 4608, 1536, EPI_STORE, 1, 64, 64, 4, 3, 2, 12) /* 20.7 -> 15.0 us */ \
+  X(512, 6144, 1536, EPI_GELU, 0, 64, 64, 2, 3, 1, 24) /* 32.5 -> 23.5 us */ \
+  X(512, 32000, 1536, EPI_ARGMAX, 0, 128, 128, 2, 4, 1, 24) /* 83.0 -> 78.8 us */
+
 struct Tuned {
   int M, N, K, epi, split, MB, NI, WK, P, ks, nkb;
   bool ntw;
   GemmKernel fn;
 };
+struct TunedL {
+  int M, N, K, epi, split, BM, BN, WM, P, ks, nkb;
+  GemmKernel fn;
+};
+#define PHOTON_LDS_ENTRY(M_, N_, K_, E_, S_, BM_, BN_, WM_, P_, KS_, NKB_) \
+  {M_, N_, K_, E_, S_, BM_, BN_, WM_, P_, KS_, NKB_, gemm_lds_kernel<BM_, BN_, WM_, P_, E_, NKB_>},
+const TunedL kTunedL[] = {PHOTON_GEMM_LDS_TUNED(PHOTON_LDS_ENTRY)};
+#undef PHOTON_LDS_ENTRY
+
+const TunedL* find_tuned_lds(int M, int N, int K, int epi, bool allow_split) {
+  const TunedL* hit = nullptr;
+  for (const TunedL& t : kTunedL) {
+    if (t.M != M || t.N != N || t.K != K || t.epi != epi) continue;
+    if (t.split && !allow_split) continue;
+    if (!hit || (t.split && !hit->split)) hit = &t;
+  }
+  return hit;
+}
 #define PHOTON_TUNED_ENTRY(M_, N_, K_, E_, S_, MB_, NI_, WK_, P_, KS_, NKB_, NT_) \
   {M_, N_, K_, E_, S_, MB_, NI_, WK_, P_, KS_, NKB_, NT_, gemm_bf16_kernel<MB_, NI_, WK_, P_, E_, NKB_, NT_>},
 const Tuned kTuned[] = {PHOTON_GEMM_TUNED(PHOTON_TUNED_ENTRY)};
@@ -395,6 +643,8 @@ int wk_of(int MB, int K) {
 // column tile that still gives >= 256 workgroups, and otherwise a split of
 // K into slabs (RAW partials, summed by the consumer).
 Plan plan_bf16(int M, int N, int K, int epi, bool allow_split) {
+  if (const TunedL* t = find_tuned_lds(M, N, K, epi, allow_split))
+    return Plan{0, 0, 0, (M + t->BM - 1) / t->BM, (N + t->BN - 1) / t->BN, t->ks, t->fn};
   if (const Tuned* t = find_tuned(M, N, K, epi, allow_split)) {
     const int BM = 16 * t->MB, BN = 16 * t->NI * (4 / t->WK);
     return Plan{t->MB, t->NI, t->WK, (M + BM - 1) / BM, (N + BN - 1) / BN, t->ks, t->fn};
