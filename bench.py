@@ -13,8 +13,8 @@ used up, so every step runs at the workload's real cache lengths.
 Prints one JSON line: decode tok/s (value), TPM = tok/s per GiB of resident
 decode weights + top K/V + decoder K/V + state, the whole path's fraction of
 the HBM roofline (algorithmic bytes per chunk at 8 TB/s), the achieved
-bandwidth of the kernel class that moves the most bytes (HIP events around
-each of its launches, in a traced pass over the same steps right after the
+bandwidth of the kernel class that moves the most bytes (events recorded by
+every kernel dispatch, in a traced pass over the same steps right after the
 timed ones) against 8 TB/s and against a measured plain copy, per-class
 figures, and the CPU oracle timed on a bounded sample
 of the same workload.
@@ -277,19 +277,6 @@ def main():
         model.decode_chunk(tok)
         pos[0] += 1
 
-    # one traced pass over the workload's chunks: per-kernel bytes and times
-    per_class, dominant = {}, None
-    if not args.no_trace:
-        model.trace_enable(None)
-        for _ in range(wl.chunks):
-            step()
-        torch.cuda.synchronize()
-        per_class = model.trace_read()
-        # the kernel class that moves the most algorithmic bytes per step is
-        # the one whose HBM roofline bounds the path
-        dominant = max(per_class, key=lambda k: per_class[k]["bytes"])
-        log(f"dominant kernel class (bytes): {dominant}")
-
     # warmup, then the timed steps: each chunk replays the captured HIP graph
     model.trace_enable([])
     model.state_restore(snap, wl.prompt)
@@ -305,19 +292,24 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
-    # the same K steps again with HIP events around every launch of the
-    # dominant kernel (tracing launches the chunk's kernels directly instead
-    # of through the graph; the kernels are the same)
-    dom = None
-    if dominant:
+    # the same K steps again, traced: every kernel dispatch records its own
+    # start and stop events (tracing launches the chunk's kernels directly
+    # instead of through the graph; the kernels are the same), giving the
+    # per-class times and bytes; the class that moves the most algorithmic
+    # bytes per step is the one whose HBM roofline bounds the path
+    per_class, dominant, dom = {}, None, None
+    if not args.no_trace:
         model.state_restore(snap, wl.prompt)
         pos[0] = 0
-        model.trace_enable([dominant])
+        model.trace_enable(None)
         for _ in range(K):
             step()
         torch.cuda.synchronize()
-        dom = model.trace_read()[dominant]
+        per_class = model.trace_read()
         model.trace_enable([])
+        dominant = max(per_class, key=lambda k: per_class[k]["bytes"])
+        dom = per_class[dominant]
+        log(f"dominant kernel class (bytes): {dominant}")
 
     tok_s = B * S * K / dt
     rep = model.report(B, wl.max_tokens, args.mode)
@@ -329,7 +321,7 @@ def main():
     kv_gib = (rep["top_kv"] + rep["dec_kv"] + rep["lower_kv"]) / 2 ** 30
     path_roof = roofline = None
     if dom:
-        chunk_bytes = sum(v["bytes"] for v in per_class.values()) / wl.chunks
+        chunk_bytes = sum(v["bytes"] for v in per_class.values()) / K
         ideal_s = chunk_bytes / (HBM_PEAK_GBS * 1e9)
         roof_tok_s = B * S / ideal_s
         achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
@@ -419,8 +411,8 @@ def main():
         "tpm_kv_only": round(tok_s / kv_gib, 1),
         "path_roofline": path_roof,
         "roofline": roofline,
-        "kernels": {k: {"launches_per_step": v["launches"] // wl.chunks,
-                        "us_per_step": round(v["ms"] * 1e3 / wl.chunks, 2),
+        "kernels": {k: {"launches_per_step": v["launches"] // K,
+                        "us_per_step": round(v["ms"] * 1e3 / K, 2),
                         "GB_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
                         "hbm_frac": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "TFLOP_s": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2),
