@@ -310,7 +310,10 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmP p) {
   const int mt = tile % p.m_tiles, nt = tile / p.m_tiles;
   const int m0 = mt * BM, n0 = nt * BN;
   const int K = p.K;
-  const int kb0 = ks * NKB;
+  // k-blocks of this workgroup's slab: compile-time (fully unrolled loop) or,
+  // with NKB = 0, K / 64 / ksplit at run time, a multiple of P
+  const int nkb = NKB > 0 ? NKB : K / 64 / p.ksplit;
+  const int kb0 = ks * nkb;
 
   // the source row of this lane in each of its load instructions (rows past
   // M or N are clamped: their results are never stored)
@@ -361,18 +364,44 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmP p) {
     }
   };
 
-  static_for([&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    if constexpr (s < NKB) issue(sc, kb0 + s);
-  }, std::make_integer_sequence<int, P - 1>{});
-  static_for([&](auto kbc) {
-    constexpr int kb = decltype(kbc)::value;
-    constexpr int ahead = (P - 2 < NKB - 1 - kb) ? P - 2 : NKB - 1 - kb;   // later stages still in flight
-    __builtin_amdgcn_s_waitcnt(vm_wait(ahead * I));
-    __builtin_amdgcn_s_barrier();
-    if constexpr (kb + P - 1 < NKB) issue(std::integral_constant<int, (kb + P - 1) % P>{}, kb0 + kb + P - 1);
-    compute(std::integral_constant<int, kb % P>{});
-  }, std::make_integer_sequence<int, NKB>{});
+  if constexpr (NKB > 0) {
+    static_for([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s < NKB) issue(sc, kb0 + s);
+    }, std::make_integer_sequence<int, P - 1>{});
+    static_for([&](auto kbc) {
+      constexpr int kb = decltype(kbc)::value;
+      constexpr int ahead = (P - 2 < NKB - 1 - kb) ? P - 2 : NKB - 1 - kb;   // later stages still in flight
+      __builtin_amdgcn_s_waitcnt(vm_wait(ahead * I));
+      __builtin_amdgcn_s_barrier();
+      if constexpr (kb + P - 1 < NKB) issue(std::integral_constant<int, (kb + P - 1) % P>{}, kb0 + kb + P - 1);
+      compute(std::integral_constant<int, kb % P>{});
+    }, std::make_integer_sequence<int, NKB>{});
+  } else {
+    // run-time loop over groups of P stages (slot s of a group is stage
+    // kb + s, so slots stay compile-time constants); in every group but the
+    // last each stage issues its successor P - 1 stages ahead, so P - 2
+    // later stages are in flight at every wait; the last group is peeled
+    static_for([&](auto sc) { issue(sc, kb0 + decltype(sc)::value); }, std::make_integer_sequence<int, P - 1>{});
+    int kb = 0;
+    for (; kb + P < nkb; kb += P) {
+      static_for([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        __builtin_amdgcn_s_waitcnt(vm_wait((P - 2) * I));
+        __builtin_amdgcn_s_barrier();
+        issue(std::integral_constant<int, (s + P - 1) % P>{}, kb0 + kb + s + P - 1);
+        compute(sc);
+      }, std::make_integer_sequence<int, P>{});
+    }
+    static_for([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int ahead = (P - 2 < P - 1 - s) ? P - 2 : P - 1 - s;
+      __builtin_amdgcn_s_waitcnt(vm_wait(ahead * I));
+      __builtin_amdgcn_s_barrier();
+      if constexpr (s == 0) issue(std::integral_constant<int, P - 1>{}, kb0 + kb + P - 1);
+      compute(sc);
+    }, std::make_integer_sequence<int, P>{});
+  }
 
   // epilogue: each lane holds features 4*(lane>>4)..+3 of row (lane&15)
   const int fl = (lane >> 4) * 4;
@@ -628,6 +657,9 @@ const Tuned* find_tuned(int M, int N, int K, int epi, bool allow_split) {
   return hit;
 }
 
+constexpr int kBigM = 2048;   // rows from which the prompt-sized plan applies
+constexpr int kBigP = 3;
+
 // Waves along K: as many as the LDS budget of the M tile allows (4 for
 // M tiles up to 64 rows, 2 for 128, 1 for 256) and K divides into.
 int wk_of(int MB, int K) {
@@ -648,6 +680,14 @@ Plan plan_bf16(int M, int N, int K, int epi, bool allow_split) {
   if (const Tuned* t = find_tuned(M, N, K, epi, allow_split)) {
     const int BM = 16 * t->MB, BN = 16 * t->NI * (4 / t->WK);
     return Plan{t->MB, t->NI, t->WK, (M + BM - 1) / BM, (N + BN - 1) / BN, t->ks, t->fn};
+  }
+  // prompt-sized GEMMs (many row tiles): the LDS-streaming kernel with a run
+  // time k loop, 128 rows x 256 features per workgroup (one wave row, four
+  // 64-feature columns), three stages; 1.4-1.7x the register tiles
+  if (M >= kBigM && (K / 64) % kBigP == 0 && K % 64 == 0 && (epi == EPI_STORE || epi == EPI_GELU)) {
+    GemmKernel fn = epi == EPI_STORE ? gemm_lds_kernel<128, 256, 1, kBigP, EPI_STORE, 0>
+                                     : gemm_lds_kernel<128, 256, 1, kBigP, EPI_GELU, 0>;
+    return Plan{0, 0, 0, (M + 127) / 128, (N + 255) / 256, 1, fn};
   }
   Plan best{};
   const int MB0 = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 128 ? 8 : 16;

@@ -154,3 +154,15 @@ def test_graph_replay_matches_direct_launches(mode):
         assert model.position() == (6, 96)
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("mode", ["recgen", "hiergen"])
+def test_bf16_prompt_sized_gemms(mode):
+    # 2 x 4096 prompt tokens at C1 = 2: 4096 level-1 rows, so the prefill
+    # GEMMs take the prompt-sized plan (run-time k loop, 128 x 256 tiles);
+    # d = 384 and 4d = 1536 are multiples of its 3 x 64 k stages
+    cfg = small_cfg(d_model=384, n_heads=4, chunk=(2, 2), vocab=2000, n_top=2)
+    W, pr = _inputs(cfg, 2, 4096, 13)
+    model, toks, lg = gpu_generate(cfg, W, pr, 16, mode)
+    r = check_against_oracle(cfg, W, pr, toks, lg, mode)
+    _report(f"bf16 long prompt {mode}", r)
