@@ -395,6 +395,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnCall a, floa
   const int gh = blockIdx.x / nqb;
   const int h = gh % a.H, g = gh / a.H;
   const int q0 = qb * BQ + wave * 16 * NQ;
+  // scores in base-2 units: q carries log2(e), the softmax uses exp2
+  const float scale2 = scale * 1.44269504088896341f;
   const bf16_t* Kb = reinterpret_cast<const bf16_t*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
   const bf16_t* Vb = reinterpret_cast<const bf16_t*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
 
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnCall a, floa
     for (int ks = 0; ks < KS; ++ks) {
       bf16_t hb[8], lb[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) split_hi_lo(qi < T ? qp[32 * ks + e] * scale : 0.f, hb[e], lb[e]);
+      for (int e = 0; e < 8; ++e) split_hi_lo(qi < T ? qp[32 * ks + e] * scale2 : 0.f, hb[e], lb[e]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         qhi[n][ks][e] = __builtin_bit_cast(__bf16, hb[e]);
@@ -504,29 +506,36 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnCall a, floa
           sc[kb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[n][ks], sc[kb][n], 0, 0, 0);
         }
       }
-    // online softmax per query; p in place of the scores
+    // online softmax per query; p in place of the scores.  Only a tile that
+    // reaches past this wave's first query or past the prompt needs masking.
+    const bool masked = k0 + TK - 1 > q0 || k0 + TK > T;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
       const int qi = q0 + 16 * n + c;
       float mx = m[n];
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + 16 * kb + 4 * j + r;
+            if (key > qi || key >= T) sc[kb][n][r] = -INFINITY;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + 16 * kb + 4 * j + r;
-          if (key > qi || key >= T) sc[kb][n][r] = -INFINITY;
-          mx = fmaxf(mx, sc[kb][n][r]);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][n][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // a query sees key 0 in the first tile, so mx is finite from then on
-      const float corr = expf(m[n] - mx);
+      const float corr = __builtin_amdgcn_exp2f(m[n] - mx);
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = expf(sc[kb][n][r] - mx);
+          const float p = __builtin_amdgcn_exp2f(sc[kb][n][r] - mx);
           sc[kb][n][r] = p;
           ps += p;
         }

@@ -11,12 +11,13 @@ __device__ __forceinline__ float bf2f(bf16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
+// fp32 -> bf16, round to nearest, ties to even (NaN stays a NaN): gfx950's
+// v_cvt_pk_bf16_f32, which a __bf16 conversion compiles to.  It gives the
+// same bits as rounding the fp32 bit pattern in integer arithmetic (add
+// 0x7fff plus the lowest kept bit, truncate) for every non-NaN input,
+// checked on the GPU over 2^25 inputs including every tie.
 __device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 // Storage traits: T is float (fp32 models) or bf16_t (bf16 models).
