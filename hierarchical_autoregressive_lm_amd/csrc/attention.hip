@@ -374,7 +374,7 @@ __device__ __forceinline__ void split_hi_lo(float x, bf16_t& hi, bf16_t& lo) {
 }
 
 template <int HD, int NQ>
-__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
+__global__ __launch_bounds__(256, NQ == 1 ? 2 : 1) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
   constexpr int TK = 64;                 // keys per tile
   constexpr int BQ = 64 * NQ;            // queries per workgroup
   constexpr int KS = HD / 32;            // k-steps of S^T
@@ -632,9 +632,10 @@ template <typename T, int HD>
 hipError_t prefill_hd(const AttnCall& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)HD);
   if constexpr (sizeof(T) == 2 && HD % 32 == 0) {
-    // bf16 caches: MFMA kernel, 128 queries per workgroup
-    const int nqb = (a.Q + 127) / 128;
-    PH_LAUNCH((attn_prefill_mfma_kernel<HD, 2>), a.G * a.H * nqb, 256, 0, st, a, scale);
+    // bf16 caches: MFMA kernel, 64 queries per workgroup (16 per wave), two
+    // waves per SIMD so one's softmax overlaps the other's matrix products
+    const int nqb = (a.Q + 63) / 64;
+    PH_LAUNCH((attn_prefill_mfma_kernel<HD, 1>), a.G * a.H * nqb, 256, 0, st, a, scale);
   } else {
     const int nqb = (a.Q + 63) / 64;
     PH_LAUNCH((attn_prefill_kernel<T, HD>), a.G * a.H * nqb, 256, 0, st, a, scale);
