@@ -251,37 +251,42 @@ class Model:
 class State:
     """Decode state kept after prefill: the top-level K/V of every top layer,
     the latest top output h, the number of top states, and (HierGen only)
-    the level-1 encoder K/V."""
+    the K/V of the encoder of every level below the top (``lower[l]``,
+    l = 1 .. L-1)."""
 
-    def __init__(self, top_cache, h_last, n_top_states, lvl1_cache=None, tail=None):
+    def __init__(self, top_cache, h_last, n_top_states, lower=None, tail=None):
         self.top = top_cache
         self.h = h_last
         self.top_len = n_top_states
-        self.lvl1 = lvl1_cache
+        self.lower = lower
         self.tail = tail      # prompt tokens past the last whole chunk, or None
 
+    @property
+    def lvl1(self):
+        return None if self.lower is None else self.lower[1]
+
     def copy(self):
-        cp = lambda c: None if c is None else [
-            {"k": e["k"].copy(), "v": e["v"].copy()} for e in c]
-        return State(cp(self.top), self.h.copy(), self.top_len, cp(self.lvl1),
+        cp = lambda c: [{"k": e["k"].copy(), "v": e["v"].copy()} for e in c]
+        low = None if self.lower is None else {l: cp(c) for l, c in self.lower.items()}
+        return State(cp(self.top), self.h.copy(), self.top_len, low,
                      None if self.tail is None else self.tail.copy())
 
 
 def prefill(model, prompt, mode="recgen", log=None):
     """Bottom-up pass over the prompt [modules], [recgen].
 
-    tokens -> embedding -> Chunker^1 (C1 tokens -> 1) -> level-1 encoder
-    (causal, pos = level-1 index) -> Chunker^2 (C2 states -> 1) -> top
-    encoder (causal, pos = top index).  RecGen keeps only the top K/V and the
-    last top output; HierGen also keeps the level-1 K/V (the lower cache
-    that RecGen drops after prefill).
+    tokens -> embedding, then for every level l = 1 .. L-1: Chunker^l (C_l
+    states of level l-1 -> 1) -> level-l encoder (causal, pos = level-l
+    index); then Chunker^L -> top encoder (causal, pos = top index).  RecGen
+    keeps only the top K/V and the last top output; HierGen also keeps the
+    K/V of every lower encoder (the caches RecGen drops after prefill).
     """
     cfg = model.cfg
     prompt = np.asarray(prompt)
     B, P = prompt.shape
     S = cfg.S
     if P < S:
-        raise ValueError("the prompt must hold at least one chunk of C1*C2 tokens")
+        raise ValueError("the prompt must hold at least one chunk of S tokens")
     # a ragged prompt: only whole chunks form top states; the r = P mod S
     # tail tokens open the next chunk, whose decoders take them as given
     # tokens (teacher forcing) before drawing the rest
@@ -289,23 +294,24 @@ def prefill(model, prompt, mode="recgen", log=None):
     tail = prompt[:, n * S:].copy() if P % S else None
     prompt = prompt[:, :n * S]
     P = n * S
-    e = model.embed(prompt)
-    u1 = model.chunker("W_ch1", e)
-    n1 = P // cfg.C1
-    c1 = model.empty_cache(cfg.n_enc1, B)
-    A1 = model.stack("enc1", cfg.n_enc1, u1, np.arange(n1), c1, log=log)
-    u2 = model.chunker("W_ch2", A1)
-    n = P // S
+    z = model.embed(prompt)
+    lower = {}
+    for l in range(1, cfg.L):
+        u = model.chunker(f"W_ch{l}", z)
+        lower[l] = model.empty_cache(cfg.enc_layers(l), B)
+        z = model.stack(f"enc{l}", cfg.enc_layers(l), u, np.arange(P // cfg.span(l)), lower[l], log=log)
+    u = model.chunker(f"W_ch{cfg.L}", z)
     ct = model.empty_cache(cfg.n_top, B)
-    h = model.stack("top", cfg.n_top, u2, np.arange(n), ct, log=log)
-    return State(ct, h[:, -1], n, c1 if mode == "hiergen" else None, tail)
+    h = model.stack("top", cfg.n_top, u, np.arange(n), ct, log=log)
+    return State(ct, h[:, -1], n, lower if mode == "hiergen" else None, tail)
 
 
 def _decode_tokens(model, A_hat, forced_tokens=None, sampling=None, t0=0, tail=None):
     """Top-down token generation for one chunk [modules], [recgen].
 
-    A_hat: [B, C2, d] level-1 decoder outputs.  Each of the B*C2 level-1
-    positions is expanded independently: Converter^1 gives C1 conditioning
+    A_hat: [B, K, d] level-1 decoder outputs, K = S / C1 level-1 positions
+    per chunk (C2 for two levels; written C2 below).  Each of the B*C2
+    level-1 positions is expanded independently: Converter^1 gives C1 conditioning
     vectors c_0..c_{C1-1}; the token decoder runs C1 steps with attention
     confined to the sub-chunk (in-chunk KV, positions 0..j); step j's input
     is c_j plus the embedding of the previous token of the same sub-chunk
@@ -362,18 +368,42 @@ def _top_step(model, state, u):
     return state.h
 
 
+def decode_down(model, h):
+    """The decoders of one chunk below the top [modules], [recgen].
+
+    Converter^L expands h [B, d] into C_L conditioning vectors and the
+    level-(L-1) decoder (causal inside the chunk, pos 0..C_L-1, no cache
+    kept) gives the bottleneck reconstruction A-hat [B, C_L, d]; then for
+    l = L-1 down to 2 every level-l vector is expanded the same way by
+    Converter^l and the level-(l-1) decoder, each group of C_l positions on
+    its own.  Returns (A-hat at level L-1, the level-1 outputs
+    [B, S/C1, d], in time order); for two levels both are the level-1
+    decoder's output."""
+    cfg = model.cfg
+    L, B, d = cfg.L, h.shape[0], cfg.d_model
+    c = model.converter(f"W_cv{L}", h)                # [B, C_L, d]
+    top_hat = model.stack(f"dec{L - 1}", cfg.dec_layers(L - 1), c, np.arange(cfg.chunk[L - 1]), None)
+    z = top_hat
+    for l in range(L - 1, 1, -1):
+        m, C = z.shape[1], cfg.chunk[l - 1]
+        c = model.converter(f"W_cv{l}", z).reshape(B * m, C, d)
+        z = model.stack(f"dec{l - 1}", cfg.dec_layers(l - 1), c, np.arange(C), None).reshape(B, m * C, d)
+    return top_hat, z
+
+
 def decode_chunk(model, state, mode="recgen", forced_tokens=None,
                  forced_u=None, sampling=None):
-    """Generate the next chunk of S = C1*C2 tokens; updates ``state``.
+    """Generate the next chunk of S = C1*...*CL tokens; updates ``state``.
 
-    Converter^2 expands h_{i-1} into C2 conditioning vectors; the level-1
-    decoder (causal inside the chunk, pos 0..C2-1, no cache kept) gives the
-    bottleneck reconstruction A-hat_i; tokens are written top-down.
-      RecGen  [recgen]: u_i = Chunker^2(A-hat_i), fed straight to the top.
+    The decoders below the top (decode_down) turn h_{i-1} into the
+    bottleneck reconstruction A-hat_i (level L-1) and the level-1 outputs,
+    from which the tokens are written (_decode_tokens).
+      RecGen  [recgen]: u_i = Chunker^L(A-hat_i), fed straight to the top.
       HierGen [recgen]: the chunk's tokens are re-encoded bottom-up:
-              embedding -> Chunker^1 -> one level-1 encoder step over the
-              C2 new level-1 positions with the kept level-1 cache ->
-              A_i -> u_i = Chunker^2(A_i).
+              embedding, then for l = 1 .. L-1 Chunker^l and one level-l
+              encoder step over the chunk's S/span(l) new level-l positions
+              with the kept level-l cache, ending in A_i (level L-1) ->
+              u_i = Chunker^L(A_i).
     forced_u replaces u_i (used to force the premise of Theorem A.6).
     sampling (dict(temperature, top_k, seed)) draws the tokens instead of
     the argmax; the chunk's first token is at absolute position
@@ -381,24 +411,22 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
     Returns a dict with tokens, logits, A_hat, u (and A for HierGen).
     """
     cfg = model.cfg
-    B = state.h.shape[0]
-    C1, C2, d = cfg.C1, cfg.C2, cfg.d_model
-    c1 = model.converter("W_cv2", state.h)            # [B, C2, d]
-    A_hat = model.stack("dec1", cfg.n_dec1, c1, np.arange(C2), None)
+    A_hat, A_hat1 = decode_down(model, state.h)
     tail, state.tail = state.tail, None
-    toks, logits = _decode_tokens(model, A_hat, forced_tokens, sampling, state.top_len * cfg.S, tail)
+    toks, logits = _decode_tokens(model, A_hat1, forced_tokens, sampling, state.top_len * cfg.S, tail)
     out = {"tokens": toks, "logits": logits, "A_hat": A_hat}
     if mode == "recgen":
-        u = model.chunker("W_ch2", A_hat)[:, 0]
+        u = model.chunker(f"W_ch{cfg.L}", A_hat)[:, 0]
     else:
         fed = toks if forced_tokens is None else np.asarray(forced_tokens)
-        e = model.embed(fed)                           # [B, S, d]
-        u1 = model.chunker("W_ch1", e)                # [B, C2, d]
-        base = state.top_len * C2
-        A = model.stack("enc1", cfg.n_enc1, u1, base + np.arange(C2),
-                        state.lvl1)
-        out["A"] = A
-        u = model.chunker("W_ch2", A)[:, 0]
+        z = model.embed(fed)                           # [B, S, d]
+        for l in range(1, cfg.L):
+            u_l = model.chunker(f"W_ch{l}", z)        # [B, S/span(l), d]
+            m = cfg.S // cfg.span(l)
+            z = model.stack(f"enc{l}", cfg.enc_layers(l), u_l, state.top_len * m + np.arange(m),
+                            state.lower[l])
+        out["A"] = z
+        u = model.chunker(f"W_ch{cfg.L}", z)[:, 0]
     if forced_u is not None:
         u = np.asarray(forced_u, dtype=model.dt)
     out["u"] = u
@@ -408,10 +436,11 @@ def decode_chunk(model, state, mode="recgen", forced_tokens=None,
 
 def consistency(A_hat, A):
     """The recursive loss of the pages (Eq. 1) as a diagnostic [recgen]: the
-    cosine distance 1 - cos(A-hat_i[k], A_i[k]) between the level-1
-    decoder's reconstruction and the level-1 encoder's summary at each of
-    the C2 level-1 positions of a chunk, on the values as stored (post-norm,
-    rounded).  A_hat, A: [B, C2, d]; returns [B, C2] float64."""
+    cosine distance 1 - cos(A-hat_i[k], A_i[k]) between the decoder's
+    reconstruction and the encoder's summary at each of the C_L positions
+    of a chunk at level L-1 (the level the top reads: level 1 for two
+    levels), on the values as stored (post-norm, rounded).  A_hat, A:
+    [B, C_L, d]; returns [B, C_L] float64."""
     a = np.asarray(A_hat, dtype=F64)
     e = np.asarray(A, dtype=F64)
     dot = (a * e).sum(axis=-1)
@@ -428,7 +457,7 @@ def generate(model, prompt, new_tokens, mode="recgen", forced_tokens=None, log=N
     S = model.cfg.S
     P = np.asarray(prompt).shape[1]
     if (P + new_tokens) % S:
-        raise ValueError("prompt + new tokens must end on a multiple of C1*C2")
+        raise ValueError("prompt + new tokens must end on a multiple of S")
     st = prefill(model, prompt, mode, log=log)
     r = P % S
     chunks = (P + new_tokens) // S - P // S
@@ -521,23 +550,25 @@ def top_full(model, u_all):
 
 def hier_full_logits(model, tokens, n_prompt_states):
     """Teacher-forced HierGen forward over a whole token sequence [B, T]:
-    bottom-up over all tokens, then for every chunk i >= n_prompt_states the
-    top-down pass conditioned on h_{i-1}, with the true previous tokens fed
-    to the token decoder.  Returns logits [B, T - P, V]."""
+    bottom-up over all tokens (every encoder level over its whole stream at
+    once, no cache), then for every chunk i >= n_prompt_states the top-down
+    pass conditioned on h_{i-1}, with the true previous tokens fed to the
+    token decoder.  Returns logits [B, T - P, V]."""
     cfg = model.cfg
     tokens = np.asarray(tokens)
     B, T = tokens.shape
-    S, C1, C2 = cfg.S, cfg.C1, cfg.C2
-    e = model.embed(tokens)
-    A1 = model.stack("enc1", cfg.n_enc1, model.chunker("W_ch1", e),
-                     np.arange(T // C1), None)
-    h = top_full(model, model.chunker("W_ch2", A1))     # [B, T/S, d]
+    S, C1 = cfg.S, cfg.C1
+    K = S // C1
+    z = model.embed(tokens)
+    for l in range(1, cfg.L):
+        z = model.stack(f"enc{l}", cfg.enc_layers(l), model.chunker(f"W_ch{l}", z),
+                        np.arange(T // cfg.span(l)), None)
+    h = top_full(model, model.chunker(f"W_ch{cfg.L}", z))     # [B, T/S, d]
     out = []
     for i in range(n_prompt_states, T // S):
-        c1 = model.converter("W_cv2", h[:, i - 1])
-        A_hat = model.stack("dec1", cfg.n_dec1, c1, np.arange(C2), None)
-        c0 = model.converter("W_cv1", A_hat).reshape(B * C2, C1, -1)
-        y = tokens[:, i * S:(i + 1) * S].reshape(B * C2, C1)
+        _, A_hat1 = decode_down(model, h[:, i - 1])
+        c0 = model.converter("W_cv1", A_hat1).reshape(B * K, C1, -1)
+        y = tokens[:, i * S:(i + 1) * S].reshape(B * K, C1)
         x = c0.copy()
         x[:, 1:] += model.embed(y[:, :-1])
         z = model.stack("dec0", cfg.n_dec0, x, np.arange(C1), None)
@@ -549,7 +580,7 @@ def hier_full_logits(model, tokens, n_prompt_states):
 # memory accounting (the TPM denominator) [tpm], [recgen]
 # --------------------------------------------------------------------------
 def top_states(cfg, tokens):
-    """Top-level KV length after ``tokens`` tokens: ceil(T / (C1*C2))."""
+    """Top-level KV length after ``tokens`` tokens: ceil(T / S)."""
     return -(-tokens // cfg.S)
 
 
@@ -557,18 +588,18 @@ def kv_bytes(cfg, batch, tokens, mode="recgen"):
     """Resident cache bytes after ``tokens`` tokens.
 
     top: n_top layers x K,V x B x ceil(T/S) states x d, the only O(T) state.
-    dec: the token decoder's in-chunk K/V, n_dec0 x K,V x B*C2 sub-chunks x
-         C1 positions x d -- independent of T (the decoder's span is the
+    dec: the token decoder's in-chunk K/V, n_dec0 x K,V x B*S/C1 sub-chunks
+         x C1 positions x d -- independent of T (the decoder's span is the
          chunk).
-    lower: HierGen's level-1 K/V, n_enc1 x K,V x B x ceil(T/C1) x d; RecGen
-         drops it after prefill (0).
+    lower: HierGen's encoder K/V of every level l below the top, layers x
+         K,V x B x ceil(T/span(l)) x d; RecGen drops them after prefill (0).
     """
     b = 2 if cfg.dtype == "bf16" else 4
     d = cfg.d_model
     top = cfg.n_top * 2 * batch * top_states(cfg, tokens) * d * b
-    dec = cfg.n_dec0 * 2 * batch * cfg.C2 * cfg.C1 * d * b
+    dec = cfg.n_dec0 * 2 * batch * cfg.S * d * b
     lower = 0 if mode == "recgen" else \
-        cfg.n_enc1 * 2 * batch * (-(-tokens // cfg.C1)) * d * b
+        sum(cfg.enc_layers(l) * 2 * batch * (-(-tokens // cfg.span(l))) * d * b for l in range(1, cfg.L))
     return {"top": top, "dec": dec, "lower": lower}
 
 

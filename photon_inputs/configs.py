@@ -8,10 +8,14 @@ from dataclasses import dataclass, replace
 
 @dataclass(frozen=True)
 class PhotonConfig:
-    """Shape of a two-level PHOTON hourglass.
+    """Shape of an L-level PHOTON hourglass (L = len(chunk) >= 2).
 
-    chunk = (C1, C2): level-0 tokens per level-1 state, level-1 states per
-    top state. One top state covers S = C1*C2 tokens.
+    chunk = (C1, ..., CL): C_l level-(l-1) states form one level-l state
+    (level 0 = tokens, level L = the top).  One level-l state covers
+    span(l) = C1*...*C_l tokens; one top state covers S = span(L).
+    Layer counts: n_top (top encoder), n_enc1 / n_dec1 (level-1 encoder /
+    decoder), n_dec0 (token decoder); for L > 2, n_enc_hi[l-2] and
+    n_dec_hi[l-2] are the level-l encoder and decoder, l = 2 .. L-1.
     """
     d_model: int
     n_heads: int
@@ -25,10 +29,22 @@ class PhotonConfig:
     mlp_mult: int = 4
     norm_eps: float = 1e-5
     rope_theta: float = 10000.0
+    n_enc_hi: tuple = ()
+    n_dec_hi: tuple = ()
+
+    def __post_init__(self):
+        if len(self.chunk) < 2:
+            raise ValueError("a hierarchy needs at least two levels")
+        if len(self.n_enc_hi) != len(self.chunk) - 2 or len(self.n_dec_hi) != len(self.chunk) - 2:
+            raise ValueError("n_enc_hi and n_dec_hi need one entry per level 2 .. L-1")
 
     @property
     def head_dim(self):
         return self.d_model // self.n_heads
+
+    @property
+    def L(self):
+        return len(self.chunk)
 
     @property
     def C1(self):
@@ -38,9 +54,24 @@ class PhotonConfig:
     def C2(self):
         return self.chunk[1]
 
+    def span(self, l):
+        """Tokens per level-l state (1 for level 0)."""
+        out = 1
+        for c in self.chunk[:l]:
+            out *= c
+        return out
+
     @property
     def S(self):
-        return self.chunk[0] * self.chunk[1]
+        return self.span(self.L)
+
+    def enc_layers(self, l):
+        """Layers of the level-l encoder, 1 <= l <= L-1."""
+        return self.n_enc1 if l == 1 else self.n_enc_hi[l - 2]
+
+    def dec_layers(self, l):
+        """Layers of the level-l decoder, 0 <= l <= L-1."""
+        return (self.n_dec0, self.n_dec1)[l] if l < 2 else self.n_dec_hi[l - 2]
 
     @property
     def d_ff(self):
@@ -76,9 +107,10 @@ class VanillaConfig:
 def vanilla_of(cfg):
     """The baseline matched to a PHOTON shape: same width, heads, MLP,
     vocabulary and precision, and as many layers as all PHOTON stacks
-    together (top + level-1 encoder + both decoders)."""
+    together (top + every encoder + every decoder)."""
+    n = cfg.n_top + sum(cfg.enc_layers(l) for l in range(1, cfg.L)) + sum(cfg.dec_layers(l) for l in range(cfg.L))
     return VanillaConfig(d_model=cfg.d_model, n_heads=cfg.n_heads, vocab=cfg.vocab,
-                         n_layers=cfg.n_top + cfg.n_enc1 + cfg.n_dec1 + cfg.n_dec0,
+                         n_layers=n,
                          dtype=cfg.dtype, mlp_mult=cfg.mlp_mult, norm_eps=cfg.norm_eps,
                          rope_theta=cfg.rope_theta)
 

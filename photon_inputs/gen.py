@@ -31,19 +31,25 @@ def _layer_shapes(prefix, n, d, dff):
 
 
 def weight_shapes(cfg):
-    """Canonical (name, shape) list, in generation order."""
+    """Canonical (name, shape) list, in generation order: the embedding,
+    then bottom-up the chunker and encoder of every level below the top,
+    the top chunker and encoder, then top-down the converter and decoder of
+    every level, then the output head.  Level l's tensors are W_ch<l>,
+    enc<l>.*, W_cv<l> and dec<l-1>.* (the converter of level l feeds the
+    decoder one level down)."""
     if isinstance(cfg, VanillaConfig):
         d, dff, V = cfg.d_model, cfg.d_ff, cfg.vocab
         return [("E", (V, d))] + _layer_shapes("layers", cfg.n_layers, d, dff) + [("W_out", (V, d))]
-    d, dff, V, C1, C2 = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.C1, cfg.C2
-    s = [("E", (V, d)), ("W_ch1", (d, C1 * d))]
-    s += _layer_shapes("enc1", cfg.n_enc1, d, dff)
-    s += [("W_ch2", (d, C2 * d))]
+    d, dff, V, L = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.L
+    s = [("E", (V, d))]
+    for l in range(1, L):
+        s += [(f"W_ch{l}", (d, cfg.chunk[l - 1] * d))]
+        s += _layer_shapes(f"enc{l}", cfg.enc_layers(l), d, dff)
+    s += [(f"W_ch{L}", (d, cfg.chunk[L - 1] * d))]
     s += _layer_shapes("top", cfg.n_top, d, dff)
-    s += [("W_cv2", (C2 * d, d))]
-    s += _layer_shapes("dec1", cfg.n_dec1, d, dff)
-    s += [("W_cv1", (C1 * d, d))]
-    s += _layer_shapes("dec0", cfg.n_dec0, d, dff)
+    for l in range(L, 0, -1):
+        s += [(f"W_cv{l}", (cfg.chunk[l - 1] * d, d))]
+        s += _layer_shapes(f"dec{l - 1}", cfg.dec_layers(l - 1), d, dff)
     s += [("W_out", (V, d))]
     return s
 
