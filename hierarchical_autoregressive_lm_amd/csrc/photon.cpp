@@ -51,12 +51,50 @@ uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------ config checks
+// The levels of a (checked) configuration: C[l] for l = 1 .. L, span[l] =
+// C1*...*C_l tokens per level-l state (span[0] = 1), enc[l] encoder layers
+// (l = 1 .. L-1), dec[l] decoder layers (l = 0 .. L-1).
+struct Levels {
+  int L = 2;
+  int C[PHOTON_MAX_LEVELS + 1] = {};
+  int64_t span[PHOTON_MAX_LEVELS + 1] = {};
+  int enc[PHOTON_MAX_LEVELS] = {};
+  int dec[PHOTON_MAX_LEVELS] = {};
+  int64_t S() const { return span[L]; }
+  // level-l states per chunk (one top state); K1 = level-1 states
+  int64_t per_chunk(int l) const { return span[L] / span[l]; }
+  int64_t K1() const { return per_chunk(1); }
+};
+
+Levels levels(const photon_config* c) {
+  Levels v;
+  v.L = c->n_levels;
+  v.span[0] = 1;
+  for (int l = 1; l <= v.L; ++l) {
+    v.C[l] = c->chunk[l - 1];
+    v.span[l] = v.span[l - 1] * v.C[l];
+  }
+  v.enc[1] = c->n_enc1;
+  v.dec[0] = c->n_dec0;
+  v.dec[1] = c->n_dec1;
+  for (int l = 2; l < v.L; ++l) {
+    v.enc[l] = c->n_enc_hi[l - 2];
+    v.dec[l] = c->n_dec_hi[l - 2];
+  }
+  return v;
+}
+
 photon_status check_config(const photon_config* c) {
   if (!c) return fail(PHOTON_EINVAL, "config is NULL");
-  if (c->n_levels != 2) return fail(PHOTON_EUNSUPPORTED, "n_levels must be 2 (got %d)", c->n_levels);
-  if (c->chunk[0] < 1 || c->chunk[1] < 1) return fail(PHOTON_ESHAPE, "chunk sizes must be >= 1");
-  if (c->chunk[0] > 16 || c->chunk[1] > 16)
-    return fail(PHOTON_EUNSUPPORTED, "chunk sizes above 16 are not supported");
+  if (c->n_levels < 2 || c->n_levels > PHOTON_MAX_LEVELS)
+    return fail(PHOTON_EUNSUPPORTED, "n_levels must be in [2, %d] (got %d)", PHOTON_MAX_LEVELS, c->n_levels);
+  for (int l = 0; l < c->n_levels; ++l) {
+    if (c->chunk[l] < 1) return fail(PHOTON_ESHAPE, "chunk sizes must be >= 1");
+    if (c->chunk[l] > 16) return fail(PHOTON_EUNSUPPORTED, "chunk sizes above 16 are not supported");
+  }
+  for (int l = 2; l < c->n_levels; ++l)
+    if (c->n_enc_hi[l - 2] < 1 || c->n_dec_hi[l - 2] < 1)
+      return fail(PHOTON_ESHAPE, "every stack needs at least one layer (level %d)", l);
   if (c->d_model < 1 || c->n_heads < 1) return fail(PHOTON_ESHAPE, "d_model and n_heads must be >= 1");
   if (c->d_model % c->n_heads) return fail(PHOTON_ESHAPE, "d_model %% n_heads != 0");
   const int hd = c->d_model / c->n_heads;
@@ -106,21 +144,32 @@ void add_stack(std::vector<TensorDesc>& v, const char* pre, int n, int blob, int
   v.push_back({std::string(pre) + ".gf", blob, 1, d, 1, 0});
 }
 
-// Blob order follows the decode call order (decode blob) and prefill order.
+std::string lname(const char* pre, int l) {
+  char b[16];
+  snprintf(b, sizeof b, "%s%d", pre, l);
+  return b;
+}
+
+// Blob order follows the decode call order (decode blob: the top chunker,
+// the top, then converter and decoder level by level downwards, the head)
+// and the prefill order (chunker and encoder level by level upwards).
 std::vector<TensorDesc> layout(const photon_config* c, uint64_t* dec_bytes, uint64_t* pre_bytes) {
   const int64_t d = c->d_model, F = (int64_t)c->mlp_mult * d, V = c->vocab;
-  const int64_t C1 = c->chunk[0], C2 = c->chunk[1];
+  const Levels lv = levels(c);
+  const int L = lv.L;
   std::vector<TensorDesc> v;
   v.push_back({"E", 0, 0, V, d, 0});
-  v.push_back({"W_ch2", 0, 0, d, C2 * d, 0});
+  v.push_back({lname("W_ch", L), 0, 0, d, lv.C[L] * d, 0});
   add_stack(v, "top", c->n_top, 0, d, F);
-  v.push_back({"W_cv2", 0, 0, C2 * d, d, 0});
-  add_stack(v, "dec1", c->n_dec1, 0, d, F);
-  v.push_back({"W_cv1", 0, 0, C1 * d, d, 0});
-  add_stack(v, "dec0", c->n_dec0, 0, d, F);
+  for (int l = L; l >= 1; --l) {
+    v.push_back({lname("W_cv", l), 0, 0, lv.C[l] * d, d, 0});
+    add_stack(v, lname("dec", l - 1).c_str(), lv.dec[l - 1], 0, d, F);
+  }
   v.push_back({"W_out", 0, 0, V, d, 0});
-  v.push_back({"W_ch1", 1, 0, d, C1 * d, 0});
-  add_stack(v, "enc1", c->n_enc1, 1, d, F);
+  for (int l = 1; l < L; ++l) {
+    v.push_back({lname("W_ch", l), 1, 0, d, lv.C[l] * d, 0});
+    add_stack(v, lname("enc", l).c_str(), lv.enc[l], 1, d, F);
+  }
   uint64_t off[2] = {0, 0};
   const int eb = elem_bytes(c);
   for (auto& t : v) {
@@ -139,14 +188,20 @@ struct Region {
 };
 
 struct WsPlan {
+  // low_cap: the level-1 capacity (HierGen), low_caps[l] every lower level's
   int64_t top_cap = 0, low_cap = 0, rope_pos = 0;
-  int nsplit_top = 1, nsplit_low = 1;
+  int64_t low_caps[PHOTON_MAX_LEVELS] = {};
+  int nsplit_top = 1;
+  int nsplit_low[PHOTON_MAX_LEVELS] = {1, 1, 1, 1};
   int head_tiles = 1;
-  // persistent
+  // persistent; low_kv spans the lower levels' regions lowl[1 .. L-1]
   Region top_kv, low_kv, dec_kv, h, counter, rope, tok, tail;
-  // decode scratch, set A (top branch) and set B (level-1 decoder + tokens)
+  Region lowl[PHOTON_MAX_LEVELS];
+  // decode scratch, set A (top branch) and set B (decoders + tokens);
+  // Ahat[l] holds the level-l decoder outputs of the chunk (l = 1 .. L-1)
   Region xA, aA, partA, qA, oA, hidA, apartA, eA, AA;
-  Region xB, aB, partB, qB, oB, hidB, c0, Ahat, zB, kv1tmp, amv, ami;
+  Region xB, aB, partB, qB, oB, hidB, c0, zB, kv1tmp, amv, ami;
+  Region Ahat[PHOTON_MAX_LEVELS];
   uint64_t state_bytes = 0, scratch_bytes = 0, total = 0;
   uint64_t off_state = 0, off_scratch = 0;
 };
@@ -178,19 +233,28 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   WsPlan p;
   const int dt = c->dtype;
   const int64_t d = c->d_model, H = c->n_heads, hd = d / H, F = (int64_t)c->mlp_mult * d, V = c->vocab;
-  const int64_t C1 = c->chunk[0], C2 = c->chunk[1], S = C1 * C2;
+  const Levels lv = levels(c);
+  const int L = lv.L;
+  const int64_t C1 = lv.C[1], CL = lv.C[L], S = lv.S(), K1 = lv.K1();
   const uint64_t eb = elem_bytes(c);
   const bool hier = mode == PHOTON_HIERGEN;
   p.top_cap = cdiv(tokens, S);
-  p.low_cap = hier ? cdiv(tokens, C1) : 0;
-  p.rope_pos = std::max<int64_t>({p.top_cap, p.low_cap, C1, C2});
+  p.rope_pos = p.top_cap;
+  for (int l = 1; l <= L; ++l) p.rope_pos = std::max<int64_t>(p.rope_pos, lv.C[l]);
+  for (int l = 1; l < L; ++l) {
+    p.low_caps[l] = hier ? cdiv(tokens, lv.span[l]) : 0;
+    p.rope_pos = std::max(p.rope_pos, p.low_caps[l]);
+    p.nsplit_low[l] = hier ? attn_decode_splits((int)B, (int)H, (int)p.low_caps[l], (int)lv.per_chunk(l)) : 1;
+  }
+  p.low_cap = p.low_caps[1];
   p.nsplit_top = attn_decode_splits((int)B, (int)H, (int)p.top_cap, 1);
-  p.nsplit_low = hier ? attn_decode_splits((int)B, (int)H, (int)p.low_cap, (int)C2) : 1;
-  p.head_tiles = gemm_argmax_tiles(dt, (int)(B * C2), (int)V, (int)d);
+  p.head_tiles = gemm_argmax_tiles(dt, (int)(B * K1), (int)V, (int)d);
   Cursor cur;
   p.top_kv = cur.take((uint64_t)c->n_top * 2 * B * H * p.top_cap * hd * eb);
-  p.low_kv = cur.take((uint64_t)c->n_enc1 * 2 * B * H * p.low_cap * hd * eb);
-  p.dec_kv = cur.take((uint64_t)c->n_dec0 * 2 * B * C2 * H * C1 * hd * eb);
+  p.low_kv.off = align_up(cur.pos);
+  for (int l = 1; l < L; ++l) p.lowl[l] = cur.take((uint64_t)lv.enc[l] * 2 * B * H * p.low_caps[l] * hd * eb);
+  p.low_kv.bytes = cur.pos - p.low_kv.off;
+  p.dec_kv = cur.take((uint64_t)c->n_dec0 * 2 * B * K1 * H * C1 * hd * eb);
   p.off_state = align_up(cur.pos);
   p.h = cur.take((uint64_t)B * d * eb);
   p.counter = cur.take(sizeof(int));
@@ -199,20 +263,34 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.tail = cur.take((uint64_t)B * S * sizeof(int));   // a ragged prompt's tail tokens
   p.off_scratch = align_up(cur.pos);
   p.state_bytes = p.off_scratch - p.off_state;
-  const int64_t MA = hier ? B * C2 : B, MB = B * C2;
-  uint64_t partA = std::max(layer_part_bytes(c, B), part_bytes(dt, B, d, C2 * d));
-  if (hier) partA = std::max({partA, layer_part_bytes(c, MB), part_bytes(dt, MB, d, C1 * d)});
+  // the top branch runs B rows, HierGen's re-encoding up to B*K1 (level 1);
+  // the decoders run up to B*K1 rows (the level-1 decoder, the token decoder)
+  const int64_t MA = hier ? B * K1 : B, MB = B * K1;
+  uint64_t partA = std::max(layer_part_bytes(c, B), part_bytes(dt, B, d, CL * d));
+  if (hier)
+    for (int l = 1; l < L; ++l) {
+      const int64_t M = B * lv.per_chunk(l);
+      partA = std::max({partA, layer_part_bytes(c, M), part_bytes(dt, M, d, lv.C[l] * d)});
+    }
   p.xA = cur.take((uint64_t)MA * d * 4);
   p.aA = cur.take((uint64_t)MA * d * eb);
   p.partA = cur.take(partA);
   p.qA = cur.take((uint64_t)MA * d * 4);
   p.oA = cur.take((uint64_t)MA * d * eb);
   p.hidA = cur.take((uint64_t)MA * F * eb);
-  const int64_t parts = std::max<int64_t>((int64_t)B * H * p.nsplit_top, hier ? (int64_t)B * H * C2 * p.nsplit_low : 0);
+  int64_t parts = (int64_t)B * H * p.nsplit_top;
+  if (hier)
+    for (int l = 1; l < L; ++l) parts = std::max<int64_t>(parts, B * H * lv.per_chunk(l) * p.nsplit_low[l]);
   p.apartA = cur.take((uint64_t)parts * (hd + 2) * 4);
   p.eA = cur.take(hier ? (uint64_t)B * S * d * eb : 0);
-  p.AA = cur.take(hier ? (uint64_t)B * C2 * d * eb : 0);
-  const uint64_t partB = std::max(layer_part_bytes(c, MB), part_bytes(dt, B, C2 * d, d));
+  p.AA = cur.take(hier ? (uint64_t)B * K1 * d * eb : 0);
+  // slabs of every decoder's layers (the level-l decoder runs B*per_chunk(l)
+  // rows; fewer rows may take more K slabs) and of the converters above
+  // level 1 (Converter^1 stores one slab)
+  uint64_t partB = 0;
+  for (int l = 1; l < L; ++l) partB = std::max(partB, layer_part_bytes(c, B * lv.per_chunk(l)));
+  for (int l = 2; l <= L; ++l)
+    partB = std::max(partB, part_bytes(dt, B * lv.per_chunk(l), lv.C[l] * d, d));
   p.xB = cur.take((uint64_t)MB * d * 4);
   p.aB = cur.take((uint64_t)MB * d * eb);
   p.partB = cur.take(partB);
@@ -220,9 +298,11 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.oB = cur.take((uint64_t)MB * d * eb);
   p.hidB = cur.take((uint64_t)MB * F * eb);
   p.c0 = cur.take((uint64_t)MB * C1 * d * 4);
-  p.Ahat = cur.take((uint64_t)MB * d * eb);
+  for (int l = 1; l < L; ++l) p.Ahat[l] = cur.take((uint64_t)B * lv.per_chunk(l) * d * eb);
   p.zB = cur.take((uint64_t)MB * d * eb);
-  p.kv1tmp = cur.take((uint64_t)2 * B * H * C2 * hd * eb);
+  // the chunk-confined decoders above the token decoder: C_l keys for each
+  // of B*per_chunk(l) groups, at most B*K1 rows of K and V
+  p.kv1tmp = cur.take((uint64_t)2 * B * H * K1 * hd * eb);
   p.amv = cur.take((uint64_t)p.head_tiles * MB * 4);
   p.ami = cur.take((uint64_t)p.head_tiles * MB * 4);
   p.total = align_up(cur.pos);
@@ -233,8 +313,13 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
 // prefill scratch: one batch slice of bs sequences at a time
 constexpr int64_t kPrefillRows = 65536;
 
+// nl[l]: level-l states per sequence of the prompt (l = 1 .. L; n1 = nl[1],
+// n = nl[L] top states).  One buffer A holds the output of the current
+// encoder level: a level's chunker has read it before that level's stack
+// writes it again.
 struct PrePlan {
   int64_t bs = 1, n1 = 0, n = 0;
+  int64_t nl[PHOTON_MAX_LEVELS + 1] = {};
   Region e, x, a, part, q, o, hid, A1, kv1, rope1;
   uint64_t total = 0;
 };
@@ -243,20 +328,20 @@ PrePlan plan_prefill(const photon_config* c, int64_t B, int64_t P, int mode) {
   PrePlan p;
   const int dt = c->dtype;
   const int64_t d = c->d_model, H = c->n_heads, hd = d / H, F = (int64_t)c->mlp_mult * d;
-  const int64_t C1 = c->chunk[0], C2 = c->chunk[1], S = C1 * C2;
+  const Levels lv = levels(c);
   const uint64_t eb = elem_bytes(c);
-  p.n1 = P / C1;
-  p.n = P / S;
+  for (int l = 1; l <= lv.L; ++l) p.nl[l] = P / lv.span[l];
+  p.n1 = p.nl[1];
+  p.n = p.nl[lv.L];
   p.bs = std::max<int64_t>(1, std::min<int64_t>(B, kPrefillRows / std::max<int64_t>(1, p.n1)));
-  const int64_t R = p.bs * p.n1, R2 = p.bs * p.n;
+  const int64_t R = p.bs * p.n1;
   // the last slice may be shorter; its GEMMs plan their own slabs
   uint64_t part = 0;
   for (int64_t bs : {p.bs, B % p.bs}) {
     if (bs == 0) continue;
-    part = std::max({part, layer_part_bytes(c, bs * p.n1), layer_part_bytes(c, bs * p.n),
-                     part_bytes(dt, bs * p.n1, d, C1 * d), part_bytes(dt, bs * p.n, d, C2 * d)});
+    for (int l = 1; l <= lv.L; ++l)
+      part = std::max({part, layer_part_bytes(c, bs * p.nl[l]), part_bytes(dt, bs * p.nl[l], d, lv.C[l] * d)});
   }
-  (void)R2;
   Cursor cur;
   p.e = cur.take((uint64_t)p.bs * P * d * eb);
   p.x = cur.take((uint64_t)R * d * 4);
@@ -439,8 +524,13 @@ struct photon_ctx {
   const unsigned char* wpre = nullptr;
   std::vector<TensorDesc> tensors;
   const void* E = nullptr;
-  const void *W_ch1 = nullptr, *W_ch2 = nullptr, *W_cv2 = nullptr, *W_cv1 = nullptr, *W_out = nullptr;
-  StackW enc1, top, dec1, dec0;
+  // W_ch[l], W_cv[l] for l = 1 .. L; enc[l] for l = 1 .. L-1; dec[l] for
+  // l = 0 .. L-1
+  const void* W_ch[PHOTON_MAX_LEVELS + 1] = {};
+  const void* W_cv[PHOTON_MAX_LEVELS + 1] = {};
+  const void* W_out = nullptr;
+  StackW top;
+  StackW enc[PHOTON_MAX_LEVELS], dec[PHOTON_MAX_LEVELS];
   // decode state
   bool prefilled = false;
   int mode = 0;
@@ -502,16 +592,16 @@ void bind_stack(photon_ctx* c, StackW& s, const char* pre, int n) {
 }
 
 void bind_weights(photon_ctx* c) {
+  const Levels lv = levels(&c->cfg);
   c->E = tensor_ptr(c, "E");
-  c->W_ch2 = tensor_ptr(c, "W_ch2");
-  c->W_cv2 = tensor_ptr(c, "W_cv2");
-  c->W_cv1 = tensor_ptr(c, "W_cv1");
   c->W_out = tensor_ptr(c, "W_out");
-  c->W_ch1 = tensor_ptr(c, "W_ch1");
   bind_stack(c, c->top, "top", c->cfg.n_top);
-  bind_stack(c, c->dec1, "dec1", c->cfg.n_dec1);
-  bind_stack(c, c->dec0, "dec0", c->cfg.n_dec0);
-  bind_stack(c, c->enc1, "enc1", c->cfg.n_enc1);
+  for (int l = 1; l <= lv.L; ++l) {
+    c->W_ch[l] = tensor_ptr(c, lname("W_ch", l));
+    c->W_cv[l] = tensor_ptr(c, lname("W_cv", l));
+    bind_stack(c, c->dec[l - 1], lname("dec", l - 1).c_str(), lv.dec[l - 1]);
+    if (l < lv.L) bind_stack(c, c->enc[l], lname("enc", l).c_str(), lv.enc[l]);
+  }
 }
 
 #define HIP_TRY(expr)                                                                    \
@@ -526,13 +616,13 @@ void bind_weights(photon_ctx* c) {
     if (s_ != PHOTON_OK) return s_; \
   } while (0)
 
-// Sampling workspace: one token step's logits [B*C2][V] fp32, then the
+// Sampling workspace: one token step's logits [B*K1][V] fp32, then the
 // chunk's log-likelihoods [B][S] fp32.
 uint64_t sampling_lp_off(const photon_config& cf, int64_t B) {
-  return align_up((uint64_t)B * cf.chunk[1] * cf.vocab * 4);
+  return align_up((uint64_t)B * levels(&cf).K1() * cf.vocab * 4);
 }
 uint64_t sampling_bytes(const photon_config& cf, int64_t B) {
-  return sampling_lp_off(cf, B) + align_up((uint64_t)B * cf.chunk[0] * cf.chunk[1] * 4);
+  return sampling_lp_off(cf, B) + align_up((uint64_t)B * levels(&cf).S() * 4);
 }
 photon_status check_sampling(const photon_sampling* sp, int vocab) {
   if (!(sp->temperature >= 1e-4f && sp->temperature <= 1e4f))
@@ -719,19 +809,38 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
   return ok();
 }
 
-photon_status check_gemms(const photon_config* c, int64_t B, int64_t R1, int64_t R2, int mode) {
+// Every GEMM shape of prefill (slices of bs sequences, nl[l] level-l states
+// each) and of the decode chunk, checked before anything is enqueued; and
+// HierGen's encoder steps, which run S/span(l) queries per sequence through
+// the global attention (1, 2 or 4).
+photon_status check_gemms(const photon_config* c, int64_t B, const PrePlan& pp, int mode) {
   const int dt = c->dtype, d = c->d_model, F = c->mlp_mult * d, V = c->vocab;
-  const int C1 = c->chunk[0], C2 = c->chunk[1];
+  const Levels lv = levels(c);
+  const int L = lv.L;
   struct S3 { int64_t M; int N, K; };
-  std::vector<S3> shapes = {{B, C2 * d, d}, {B * C2, C1 * d, d}, {B * C2, V, d}, {B, d, C2 * d},
-                            {R1, d, C1 * d}, {R2, d, C2 * d}};
-  for (int64_t M : {B, B * C2, R1, R2}) {
+  std::vector<S3> shapes = {{B * lv.K1(), lv.C[1] * d, d}, {B * lv.K1(), V, d}, {B, d, lv.C[L] * d}};
+  std::vector<int64_t> rows = {B};
+  for (int l = 1; l <= L; ++l) {
+    shapes.push_back({pp.bs * pp.nl[l], d, lv.C[l] * d});          // prefill chunkers
+    rows.push_back(pp.bs * pp.nl[l]);
+    if (l >= 2) shapes.push_back({B * lv.per_chunk(l), lv.C[l] * d, d});   // converters above level 1
+    if (l < L) {
+      rows.push_back(B * lv.per_chunk(l));
+      if (mode == PHOTON_HIERGEN) {
+        shapes.push_back({B * lv.per_chunk(l), d, lv.C[l] * d});  // re-encoding chunkers
+        const int64_t q = lv.per_chunk(l);
+        if (q != 1 && q != 2 && q != 4)
+          return fail(PHOTON_EUNSUPPORTED, "HierGen's level-%d encoder step would take %lld queries per sequence "
+                      "(1, 2 or 4 supported)", l, (long long)q);
+      }
+    }
+  }
+  for (int64_t M : rows) {
     shapes.push_back({M, 3 * d, d});
     shapes.push_back({M, d, d});
     shapes.push_back({M, F, d});
     shapes.push_back({M, d, F});
   }
-  if (mode == PHOTON_HIERGEN) shapes.push_back({B * C2, d, C1 * d});
   for (const auto& s : shapes)
     if (s.M > 0x7fffffff || !gemm_supported(dt, (int)s.M, s.N, s.K))
       return fail(PHOTON_EUNSUPPORTED, "GEMM shape M=%lld N=%d K=%d is not supported", (long long)s.M, s.N, s.K);
@@ -779,9 +888,9 @@ photon_status photon_prefill_scratch_bytes(const photon_config* cfg, int32_t bat
   if (!out) return fail(PHOTON_EINVAL, "out is NULL");
   if (mode != PHOTON_RECGEN && mode != PHOTON_HIERGEN) return fail(PHOTON_EINVAL, "bad mode %d", mode);
   if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
-  const int S = cfg->chunk[0] * cfg->chunk[1];
+  const int S = (int)levels(cfg).S();
   if (prompt_len < S)
-    return fail(PHOTON_ESHAPE, "prompt_len %d must hold at least one chunk of C1*C2 = %d tokens", prompt_len, S);
+    return fail(PHOTON_ESHAPE, "prompt_len %d must hold at least one chunk of S = %d tokens", prompt_len, S);
   *out = plan_prefill(cfg, batch, prompt_len / S * S, mode).total;   // whole chunks only
   return ok();
 }
@@ -862,10 +971,11 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
     return fail(PHOTON_EINVAL, "workspace and scratch must be 256-byte aligned");
   if (!c->wpre) return fail(PHOTON_ESTATE, "prefill needs the prefill-only weights, which were released");
   const photon_config& cf = c->cfg;
-  const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
+  const Levels lv = levels(&cf);
+  const int L = lv.L, S = (int)lv.S();
   if (batch < 1) return fail(PHOTON_ESHAPE, "batch must be >= 1");
   if (prompt_len < S)
-    return fail(PHOTON_ESHAPE, "prompt_len %d must hold at least one chunk of C1*C2 = %d tokens", prompt_len, S);
+    return fail(PHOTON_ESHAPE, "prompt_len %d must hold at least one chunk of S = %d tokens", prompt_len, S);
   if (max_tokens < prompt_len) return fail(PHOTON_ECAPACITY, "max_tokens %lld < prompt_len %d", (long long)max_tokens, prompt_len);
   const WsPlan wp = plan_workspace(&cf, batch, max_tokens, mode);
   if (ws_bytes < wp.total)
@@ -878,7 +988,7 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
     return fail(PHOTON_ECAPACITY, "prefill scratch holds %llu bytes, needs %llu", (unsigned long long)scratch_bytes,
                 (unsigned long long)pp.total);
   {
-    photon_status s = check_gemms(&cf, batch, pp.bs * pp.n1, pp.bs * pp.n, mode);
+    photon_status s = check_gemms(&cf, batch, pp, mode);
     if (s) return s;
   }
   hipStream_t st = (hipStream_t)stream;
@@ -902,7 +1012,7 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   HIP_TRY(launch_rope_table(rope_ws, (int)wp.rope_pos, hd, cf.rope_theta, st));
   HIP_TRY(launch_rope_table(rope1, (int)std::max<int64_t>(pp.n1, 1), hd, cf.rope_theta, st));
 
-  const int64_t n1 = pp.n1, n = pp.n;
+  const int64_t n = pp.n;
   StackBufs bufs{(float*)(sc + pp.x.off), sc + pp.a.off, (float*)(sc + pp.part.off), (float*)(sc + pp.q.off),
                  sc + pp.o.off, sc + pp.hid.off, nullptr};
   for (int64_t b0 = 0; b0 < batch; b0 += pp.bs) {
@@ -912,24 +1022,34 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
       return launch_embed_gather_rows(dt, d_prompt + b0 * prompt_len, bs, P_enc, prompt_len, c->E, d, cf.vocab,
                                       sc + pp.e.off, st);
     }));
+    // every level below the top: Chunker^l over groups of C_l states of the
+    // level beneath (the embeddings for l = 1), then the level-l encoder;
+    // its output replaces its input in buffer A
     int ks = 1;
-    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, sc + pp.e.off, (int64_t)C1 * d, c->W_ch1, (int)(bs * n1), d, C1 * d,
-                      bufs.part, &ks, st));
-    PH_TRY(stack_input(c, c->enc1, bufs.part, ks, (int)(bs * n1), bufs.x, bufs.a, st));
-    StackRun r{};
-    r.M = (int)(bs * n1); r.rows_per_seq = (int)n1; r.G = bs;
-    if (mode == PHOTON_HIERGEN) {
-      r.kv = KvTarget{ws + wp.low_kv.off, (int64_t)batch * H * wp.low_cap * hd, true, (int64_t)H * wp.low_cap * hd,
-                      (int)wp.low_cap, (int)b0};
-    } else {
-      r.kv = KvTarget{sc + pp.kv1.off, (int64_t)pp.bs * H * n1 * hd, false, (int64_t)H * n1 * hd, (int)n1, 0};
+    const unsigned char* in = sc + pp.e.off;
+    for (int l = 1; l < L; ++l) {
+      const int64_t nl = pp.nl[l];
+      const int rows = (int)(bs * nl);
+      PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, in, (int64_t)lv.C[l] * d, c->W_ch[l], rows, d, lv.C[l] * d,
+                        bufs.part, &ks, st));
+      PH_TRY(stack_input(c, c->enc[l], bufs.part, ks, rows, bufs.x, bufs.a, st));
+      StackRun r{};
+      r.M = rows; r.rows_per_seq = (int)nl; r.G = bs;
+      if (mode == PHOTON_HIERGEN) {
+        const int64_t cap = wp.low_caps[l];
+        r.kv = KvTarget{ws + wp.lowl[l].off, (int64_t)batch * H * cap * hd, true, (int64_t)H * cap * hd, (int)cap,
+                        (int)b0};
+      } else {
+        r.kv = KvTarget{sc + pp.kv1.off, (int64_t)pp.bs * H * nl * hd, false, (int64_t)H * nl * hd, (int)nl, 0};
+      }
+      r.pos_add = 0; r.pos_dev = nullptr; r.pos_mul = 0; r.rope = rope1;
+      r.kind = ATT_PREFILL; r.Q = (int)nl; r.L_host = (int)nl; r.nsplit = 1; r.L_acct = (int)nl;
+      r.out = sc + pp.A1.off; r.out_rows = rows; r.in_stride = 1; r.in_off = 0;
+      PH_TRY(run_stack(c, c->enc[l], bufs, r, st));
+      in = sc + pp.A1.off;
     }
-    r.pos_add = 0; r.pos_dev = nullptr; r.pos_mul = 0; r.rope = rope1;
-    r.kind = ATT_PREFILL; r.Q = (int)n1; r.L_host = (int)n1; r.nsplit = 1; r.L_acct = (int)n1;
-    r.out = sc + pp.A1.off; r.out_rows = (int)(bs * n1); r.in_stride = 1; r.in_off = 0;
-    PH_TRY(run_stack(c, c->enc1, bufs, r, st));
-    // Chunker^2 over groups of C2 level-1 states
-    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, sc + pp.A1.off, (int64_t)C2 * d, c->W_ch2, (int)(bs * n), d, C2 * d,
+    // Chunker^L over groups of C_L states of level L-1
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, in, (int64_t)lv.C[L] * d, c->W_ch[L], (int)(bs * n), d, lv.C[L] * d,
                       bufs.part, &ks, st));
     PH_TRY(stack_input(c, c->top, bufs.part, ks, (int)(bs * n), bufs.x, bufs.a, st));
     StackRun t{};
@@ -954,22 +1074,23 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   return ok();
 }
 
-// Enqueue one decode chunk.  The level-1 decoder runs on `st`; with RecGen
-// and st_top != st the top branch forks onto st_top (after A-hat exists) and
+// Enqueue one decode chunk.  The decoders run on `st`; with RecGen and
+// st_top != st the top branch forks onto st_top (after A-hat exists) and
 // joins back before the chunk ends.  Everything reads positions from the
 // device counter, so the same sequence serves every chunk.
 photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipStream_t st_top, int given_r = 0) {
   const photon_config& cf = c->cfg;
-  const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
+  const Levels lv = levels(&cf);
+  const int L = lv.L, C1 = lv.C[1], CL = lv.C[L], K1 = (int)lv.K1();
   const WsPlan& wp = c->plan;
   unsigned char* ws = c->ws;
   const int dt = cf.dtype, d = cf.d_model, H = cf.n_heads, hd = d / H, V = cf.vocab;
-  const int B = (int)c->B, MB = B * C2;
+  const int B = (int)c->B, MB = B * K1;
   const int eb = elem_bytes(&cf);
   int* counter = (int*)(ws + wp.counter.off);
   const float* rope = (const float*)(ws + wp.rope.off);
   void* h = ws + wp.h.off;
-  void* Ahat = ws + wp.Ahat.off;
+  void* Ahat_top = ws + wp.Ahat[L - 1].off;   // A-hat_i: the level-(L-1) decoder outputs
   int* tok = (int*)(ws + wp.tok.off);
   float* c0 = (float*)(ws + wp.c0.off);
   StackBufs sb{(float*)(ws + wp.xB.off), ws + wp.aB.off, (float*)(ws + wp.partB.off), (float*)(ws + wp.qB.off),
@@ -978,34 +1099,43 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
                ws + wp.oA.off, ws + wp.hidA.off, (float*)(ws + wp.apartA.off)};
   int ks = 1;
 
-  // Converter^2: h_{i-1} -> C2 conditioning vectors = level-1 decoder rows
-  PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CONV, h, d, c->W_cv2, B, C2 * d, d, sb.part, &ks, st));
-  PH_TRY(stack_input(c, c->dec1, sb.part, ks, MB, sb.x, sb.a, st));
-  // level-1 decoder over the C2 positions of the chunk -> A-hat_i
-  {
+  // Converter^l on M level-l rows -> C_l conditioning vectors each, then the
+  // level-(l-1) decoder over each group's C_l positions (attention confined
+  // to the group, positions 0 .. C_l-1, no cache kept) -> out [M*C_l][d]
+  auto expand = [&](int l, const void* in, int M, void* out) -> photon_status {
+    const int C = lv.C[l];
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CONV, in, d, c->W_cv[l], M, C * d, d, sb.part, &ks, st));
+    PH_TRY(stack_input(c, c->dec[l - 1], sb.part, ks, M * C, sb.x, sb.a, st));
     StackRun r{};
-    r.M = MB; r.rows_per_seq = C2; r.G = B;
-    r.kv = KvTarget{ws + wp.kv1tmp.off, (int64_t)B * H * C2 * hd, false, (int64_t)H * C2 * hd, C2, 0};
+    r.M = M * C; r.rows_per_seq = C; r.G = M;
+    r.kv = KvTarget{ws + wp.kv1tmp.off, (int64_t)M * H * C * hd, false, (int64_t)H * C * hd, C, 0};
     r.pos_add = 0; r.rope = rope;
-    r.kind = ATT_CHUNK; r.Q = C2; r.L_host = C2; r.nsplit = 1; r.L_acct = C2;
-    r.out = Ahat; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
-    PH_TRY(run_stack(c, c->dec1, sb, r, st));
-  }
+    r.kind = ATT_CHUNK; r.Q = C; r.L_host = C; r.nsplit = 1; r.L_acct = C;
+    r.out = out; r.out_rows = M * C; r.in_stride = 1; r.in_off = 0;
+    return run_stack(c, c->dec[l - 1], sb, r, st);
+  };
+  // Converter^L: h_{i-1} -> C_L conditioning vectors; the level-(L-1)
+  // decoder over them -> A-hat_i
+  PH_TRY(expand(L, h, B, Ahat_top));
   const bool fork = c->mode == PHOTON_RECGEN && st_top != st;
   if (fork) {
     HIP_TRY(hipEventRecord(c->ev_fork, st));
     HIP_TRY(hipStreamWaitEvent(st_top, c->ev_fork, 0));
   }
-  // token branch: Converter^1 (all C1 conditioning vectors of every level-1
-  // position), then C1 sequential token-decoder steps
+  // token branch: the decoders of the levels between (every level-l vector
+  // expanded on its own, l = L-1 .. 2), Converter^1 (all C1 conditioning
+  // vectors of every level-1 position), then C1 sequential token-decoder
+  // steps
+  for (int l = L - 1; l >= 2; --l)
+    PH_TRY(expand(l, ws + wp.Ahat[l].off, (int)(B * lv.per_chunk(l)), ws + wp.Ahat[l - 1].off));
   {
     GemmCall g{};
-    g.dtype = dt; g.A = Ahat; g.lda = d; g.W = c->W_cv1; g.M = MB; g.N = C1 * d; g.K = d;
+    g.dtype = dt; g.A = ws + wp.Ahat[1].off; g.lda = d; g.W = c->W_cv[1]; g.M = MB; g.N = C1 * d; g.K = d;
     g.epi = EPI_STORE; g.C = c0; g.ldc = (int64_t)C1 * d;
     PH_TRY(run_gemm(c, PHOTON_K_GEMM_CONV, g, st));
     RowsEpi e{};   // step 0 input: x = c_0, no token yet
     e.P = c0; e.ksplit = 1; e.pstride = 0; e.ldp = (int64_t)C1 * d;
-    e.x_out = sb.x; e.g = c->dec0.layers[0].g1; e.a_out = sb.a; e.a_ld = d;
+    e.x_out = sb.x; e.g = c->dec[0].layers[0].g1; e.a_out = sb.a; e.a_ld = d;
     e.R = MB; e.d = d; e.row_stride = 1; e.row_off = 0; e.eps = cf.norm_eps;
     PH_TRY(rows_epi(c, e, st));
   }
@@ -1016,7 +1146,7 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     r.pos_add = j; r.rope = rope;
     r.kind = ATT_CHUNK; r.Q = 1; r.L_host = j + 1; r.nsplit = 1; r.L_acct = j + 1;
     r.out = ws + wp.zB.off; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
-    PH_TRY(run_stack(c, c->dec0, sb, r, st));
+    PH_TRY(run_stack(c, c->dec[0], sb, r, st));
     GemmCall g{};
     g.dtype = dt; g.A = ws + wp.zB.off; g.lda = d; g.W = c->W_out; g.M = MB; g.N = V; g.K = d;
     g.epi = EPI_ARGMAX;
@@ -1026,18 +1156,19 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     g.ldc = d_logits ? (int64_t)C1 * V : V;
     g.amax_val = (float*)(ws + wp.amv.off); g.amax_idx = (int*)(ws + wp.ami.off);
     PH_TRY(run_gemm(c, PHOTON_K_GEMM_HEAD, g, st));
+    // rows m = b*K1 + k: sequence b, level-1 position k (token k*C1 + j)
     if (c->sampling) {
       // the sampler's id takes the place of the argmax tiles (one tile)
       SampleCall sc{g.C, g.ldc, MB, V, c->samp.temperature, c->samp.top_k, (uint32_t)c->samp.seed,
-                    (uint32_t)(c->samp.seed >> 32), nullptr, nullptr, counter, C1, C2, j,
+                    (uint32_t)(c->samp.seed >> 32), nullptr, nullptr, counter, C1, K1, j,
                     g.amax_idx, g.amax_val, (float*)(c->sws + sampling_lp_off(cf, B)),
                     (const int*)(ws + wp.tail.off), given_r};
       PH_TRY(traced(c, PHOTON_K_SAMPLE, (double)MB * V * 4 + (double)MB * 12, 0, st, "sample",
                     [&] { return launch_sample(sc, st); }));
     }
     const bool next = j + 1 < C1;
-    ArgmaxNext an{g.amax_val, g.amax_idx, c->sampling ? 1 : wp.head_tiles, MB, C1, C2, j, tok,
-                  c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec0.layers[0].g1, d, cf.norm_eps,
+    ArgmaxNext an{g.amax_val, g.amax_idx, c->sampling ? 1 : wp.head_tiles, MB, C1, K1, j, tok,
+                  c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec[0].layers[0].g1, d, cf.norm_eps,
                   (const int*)(ws + wp.tail.off), given_r};
     // the next step's input (conditioning row + embedding in, stream and its
     // norm out); the token ids are counted with the head
@@ -1048,28 +1179,34 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
   // token branch on its own stream; its counter update closes it)
   const hipStream_t stt = fork ? st_top : st;
   if (c->mode == PHOTON_RECGEN) {
-    // feedback: u_i = Chunker^2(A-hat_i), nothing re-encoded
-    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, Ahat, (int64_t)C2 * d, c->W_ch2, B, d, C2 * d, sa.part, &ks, stt));
+    // feedback: u_i = Chunker^L(A-hat_i), nothing re-encoded
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, Ahat_top, (int64_t)CL * d, c->W_ch[L], B, d, CL * d, sa.part, &ks, stt));
     PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
   } else {
-    // HierGen: re-encode the chunk's tokens through Chunker^1 and one
-    // level-1 encoder step, then Chunker^2 of the encoder summary A_i
-    PH_TRY(traced(c, PHOTON_K_EMBED, (double)B * S * (4 + 2.0 * d * eb), 0, stt, "embed_gather",
-                  [&] { return launch_embed_gather(dt, tok, (int64_t)B * S, c->E, d, V, ws + wp.eA.off, stt); }));
-    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, ws + wp.eA.off, (int64_t)C1 * d, c->W_ch1, MB, d, C1 * d, sa.part, &ks,
-                      stt));
-    PH_TRY(stack_input(c, c->enc1, sa.part, ks, MB, sa.x, sa.a, stt));
-    StackRun r{};
-    r.M = MB; r.rows_per_seq = C2; r.G = B;
-    r.kv = KvTarget{ws + wp.low_kv.off, (int64_t)B * H * wp.low_cap * hd, true, (int64_t)H * wp.low_cap * hd,
-                    (int)wp.low_cap, 0};
-    r.pos_add = 0; r.pos_dev = counter; r.pos_mul = C2; r.rope = rope;
-    r.kind = ATT_DECODE; r.Q = C2; r.L_dev = counter; r.L_mul = C2; r.L_add = C2; r.nsplit = wp.nsplit_low;
-    r.L_acct = (int)((c->top_len + 1) * C2);
-    r.out = ws + wp.AA.off; r.out_rows = MB; r.in_stride = 1; r.in_off = 0;
-    PH_TRY(run_stack(c, c->enc1, sa, r, stt));
-    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, ws + wp.AA.off, (int64_t)C2 * d, c->W_ch2, B, d, C2 * d, sa.part, &ks,
-                      stt));
+    // HierGen: re-encode the chunk's tokens bottom-up, through Chunker^l and
+    // one level-l encoder step for l = 1 .. L-1 (the chunk's S/span(l) new
+    // level-l positions over the kept level-l cache), then Chunker^L of the
+    // encoder summary A_i
+    PH_TRY(traced(c, PHOTON_K_EMBED, (double)B * lv.S() * (4 + 2.0 * d * eb), 0, stt, "embed_gather",
+                  [&] { return launch_embed_gather(dt, tok, (int64_t)B * lv.S(), c->E, d, V, ws + wp.eA.off, stt); }));
+    const void* in = ws + wp.eA.off;
+    for (int l = 1; l < L; ++l) {
+      const int q = (int)lv.per_chunk(l), M = B * q;
+      const int64_t cap = wp.low_caps[l];
+      PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, in, (int64_t)lv.C[l] * d, c->W_ch[l], M, d, lv.C[l] * d, sa.part, &ks,
+                        stt));
+      PH_TRY(stack_input(c, c->enc[l], sa.part, ks, M, sa.x, sa.a, stt));
+      StackRun r{};
+      r.M = M; r.rows_per_seq = q; r.G = B;
+      r.kv = KvTarget{ws + wp.lowl[l].off, (int64_t)B * H * cap * hd, true, (int64_t)H * cap * hd, (int)cap, 0};
+      r.pos_add = 0; r.pos_dev = counter; r.pos_mul = q; r.rope = rope;
+      r.kind = ATT_DECODE; r.Q = q; r.L_dev = counter; r.L_mul = q; r.L_add = q; r.nsplit = wp.nsplit_low[l];
+      r.L_acct = (int)((c->top_len + 1) * q);
+      r.out = ws + wp.AA.off; r.out_rows = M; r.in_stride = 1; r.in_off = 0;
+      PH_TRY(run_stack(c, c->enc[l], sa, r, stt));
+      in = ws + wp.AA.off;
+    }
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, in, (int64_t)CL * d, c->W_ch[L], B, d, CL * d, sa.part, &ks, stt));
     PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
   }
   {
@@ -1090,7 +1227,6 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     HIP_TRY(hipStreamWaitEvent(st, c->ev_join, 0));
   }
   HIP_TRY(launch_add_int(counter, 1, st));
-  (void)S;
   return ok();
 }
 
@@ -1106,7 +1242,7 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
   if (!c->prefilled) return fail(PHOTON_ESTATE, "decode before prefill");
   if (d_logprobs && !c->sampling) return fail(PHOTON_ESTATE, "log-likelihoods need a sampling context");
   const photon_config& cf = c->cfg;
-  const int C1 = cf.chunk[0], C2 = cf.chunk[1], S = C1 * C2;
+  const int S = (int)levels(&cf).S();
   if ((c->top_len + 1) * S > c->max_tokens)
     return fail(PHOTON_ECAPACITY, "chunk would pass max_tokens %lld", (long long)c->max_tokens);
   if (c->mode == PHOTON_HIERGEN && !c->wpre)
@@ -1165,9 +1301,10 @@ photon_status photon_consistency(photon_ctx* c, float* d_dist, void* d_ahat, voi
     return fail(PHOTON_ESTATE, "the diagnostic needs a HierGen context (RecGen never computes A_i)");
   if (c->tokens <= c->prompt_tokens) return fail(PHOTON_ESTATE, "no chunk decoded yet");
   const photon_config& cf = c->cfg;
-  const int R = (int)c->B * cf.chunk[1], d = cf.d_model;
+  const Levels lv = levels(&cf);
+  const int R = (int)c->B * lv.C[lv.L], d = cf.d_model;
   const size_t bytes = (size_t)R * d * elem_bytes(&cf);
-  const void* Ahat = c->ws + c->plan.Ahat.off;
+  const void* Ahat = c->ws + c->plan.Ahat[lv.L - 1].off;
   const void* A = c->ws + c->plan.AA.off;
   hipStream_t st = (hipStream_t)stream;
   HIP_TRY(launch_cosine_distance(cf.dtype, Ahat, A, R, d, d_dist, st));
@@ -1243,7 +1380,7 @@ photon_status photon_set_position(photon_ctx* c, int64_t tokens, void* stream) {
   if (!c) return fail(PHOTON_EINVAL, "ctx is NULL");
   if (!c->prefilled) return fail(PHOTON_ESTATE, "no prefill to rewind to");
   // a flat-baseline context counts tokens (steps per call), PHOTON top states
-  const int64_t S = c->vanilla ? c->vcfg.steps : (int64_t)c->cfg.chunk[0] * c->cfg.chunk[1];
+  const int64_t S = c->vanilla ? c->vcfg.steps : levels(&c->cfg).S();
   if ((tokens % S && tokens != c->prompt_tokens) || tokens < c->prompt_tokens || tokens > c->tokens)
     return fail(PHOTON_ESHAPE, "position %lld must be the prompt end or a multiple of %lld within [%lld, %lld]",
                 (long long)tokens, (long long)S, (long long)c->prompt_tokens, (long long)c->tokens);

@@ -30,14 +30,19 @@ class PhotonError(RuntimeError):
         self.status = status
 
 
+MAX_LEVELS = 4   # PHOTON_MAX_LEVELS
+
+
 class Config(ctypes.Structure):
-    _fields_ = [("n_levels", ctypes.c_int32), ("chunk", ctypes.c_int32 * 2),
+    _fields_ = [("n_levels", ctypes.c_int32), ("chunk", ctypes.c_int32 * MAX_LEVELS),
                 ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("mlp_mult", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_top", ctypes.c_int32), ("n_enc1", ctypes.c_int32),
                 ("n_dec1", ctypes.c_int32), ("n_dec0", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float),
-                ("rope_theta", ctypes.c_float)]
+                ("rope_theta", ctypes.c_float),
+                ("n_enc_hi", ctypes.c_int32 * (MAX_LEVELS - 2)),
+                ("n_dec_hi", ctypes.c_int32 * (MAX_LEVELS - 2))]
 
 
 class VanillaConfig_(ctypes.Structure):
@@ -159,10 +164,15 @@ def _check(status):
 def make_config(cfg):
     """photon_config from a photon_inputs.PhotonConfig."""
     c = Config()
-    c.n_levels = 2
-    c.chunk[0], c.chunk[1] = cfg.chunk
+    if len(cfg.chunk) > MAX_LEVELS:
+        raise ValueError(f"at most {MAX_LEVELS} levels")
+    c.n_levels = len(cfg.chunk)
+    for i, C in enumerate(cfg.chunk):
+        c.chunk[i] = C
     c.d_model, c.n_heads, c.mlp_mult, c.vocab = cfg.d_model, cfg.n_heads, cfg.mlp_mult, cfg.vocab
     c.n_top, c.n_enc1, c.n_dec1, c.n_dec0 = cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0
+    for i, (ne, nd) in enumerate(zip(cfg.n_enc_hi, cfg.n_dec_hi)):
+        c.n_enc_hi[i], c.n_dec_hi[i] = ne, nd
     c.dtype = BF16 if cfg.dtype == "bf16" else F32
     c.norm_eps, c.rope_theta = cfg.norm_eps, cfg.rope_theta
     return c
@@ -396,11 +406,11 @@ class Photon:
                                            _stream_handle(self.torch)))
 
     def consistency(self, copies=False):
-        """The Eq. 1 diagnostic of the last HierGen chunk: [B, C2] float32
-        (and, with copies, A-hat_i and A_i as [B, C2, d] storage-dtype
-        tensors)."""
+        """The Eq. 1 diagnostic of the last HierGen chunk: [B, C_L] float32
+        (and, with copies, A-hat_i and A_i as [B, C_L, d] storage-dtype
+        tensors), at the level under the top."""
         torch = self.torch
-        B, C2, d = self.batch, self.cfg.chunk[1], self.cfg.d_model
+        B, C2, d = self.batch, self.cfg.chunk[-1], self.cfg.d_model
         dist = torch.empty((B, C2), dtype=torch.float32, device=self.device)
         dt = torch.bfloat16 if self.cfg.dtype == "bf16" else torch.float32
         ah = torch.empty((B, C2, d), dtype=dt, device=self.device) if copies else None
@@ -453,7 +463,7 @@ class Photon:
         B, P = prompt.shape
         S = self.cfg.S
         if (P + new_tokens) % S:
-            raise ValueError("prompt + new tokens must end on a multiple of C1*C2")
+            raise ValueError("prompt + new tokens must end on a multiple of S")
         r = P % S
         chunks = (P + new_tokens) // S - P // S
         self.prefill(prompt, max_tokens or P + new_tokens, mode)

@@ -28,9 +28,15 @@
  *   - A photon_ctx is not thread safe; separate contexts are independent.
  *   - Token ids are int32 in [0, vocab).
  *
- * Shapes: L = 2 levels; chunk = {C1, C2}: C1 tokens form one level-1 state,
- * C2 level-1 states form one top state, so one top state covers S = C1*C2
- * tokens.  d = d_model, H = n_heads, hd = d / H, F = mlp_mult * d.
+ * Shapes: L levels (2 <= L <= PHOTON_MAX_LEVELS); chunk = {C1, ..., CL}:
+ * C_l states of level l-1 form one level-l state (level 0 = tokens, level L
+ * = the top), so a level-l state covers span(l) = C1*...*C_l tokens and one
+ * top state covers S = span(L) tokens (S = C1*C2 for two levels).  The
+ * explainer's module table gives a chunker and an encoder per level on the
+ * way up and a converter and a decoder per level on the way down, for any
+ * depth; its main setting is L = 2.  d = d_model, H = n_heads, hd = d / H,
+ * F = mlp_mult * d.  K1 = S / C1 is the number of level-1 states per chunk
+ * (C2 for two levels).
  */
 #ifndef PHOTON_H
 #define PHOTON_H
@@ -60,20 +66,27 @@ typedef enum { PHOTON_F32 = 0, PHOTON_BF16 = 1 } photon_dtype;
  * recursive-generation section). */
 typedef enum { PHOTON_RECGEN = 0, PHOTON_HIERGEN = 1 } photon_mode;
 
+#define PHOTON_MAX_LEVELS 4
+
 typedef struct {
-  int32_t n_levels;     /* must be 2 */
-  int32_t chunk[2];     /* C1, C2 */
+  int32_t n_levels;     /* L, 2 .. PHOTON_MAX_LEVELS */
+  int32_t chunk[PHOTON_MAX_LEVELS];  /* C1 .. CL, each 1 .. 16 (entries past
+                                        L are ignored) */
   int32_t d_model;
   int32_t n_heads;
   int32_t mlp_mult;     /* MLP width F = mlp_mult * d_model */
   int32_t vocab;
-  int32_t n_top;        /* top (level-2) encoder layers */
+  int32_t n_top;        /* top (level-L) encoder layers */
   int32_t n_enc1;       /* level-1 encoder layers (prefill / HierGen only) */
   int32_t n_dec1;       /* level-1 decoder layers */
   int32_t n_dec0;       /* token decoder layers */
   int32_t dtype;        /* photon_dtype: storage of weights, K/V, operands */
   float norm_eps;       /* RMSNorm epsilon */
   float rope_theta;     /* rotary base */
+  /* L > 2 only: layers of the level-l encoder (prefill / HierGen only) and
+   * of the level-l decoder at entry l - 2, for l = 2 .. L-1 */
+  int32_t n_enc_hi[PHOTON_MAX_LEVELS - 2];
+  int32_t n_dec_hi[PHOTON_MAX_LEVELS - 2];
 } photon_config;
 
 /* ------------------------------------------------------------------------
@@ -92,17 +105,21 @@ typedef struct {
   int64_t top_len;            /* ceil(tokens / S) top states per sequence */
   int64_t lower_len;          /* ceil(tokens / C1) level-1 states (HierGen) */
   uint64_t top_kv;            /* n_top*2*batch*top_len*d*elem bytes */
-  uint64_t lower_kv;          /* HierGen: n_enc1*2*batch*lower_len*d*elem; RecGen 0 */
-  uint64_t dec_kv;            /* n_dec0*2*batch*C2*C1*d*elem, independent of tokens */
+  uint64_t lower_kv;          /* HierGen: the sum over encoder levels l < L of
+                                 layers*2*batch*ceil(tokens/span(l))*d*elem;
+                                 RecGen 0 */
+  uint64_t dec_kv;            /* n_dec0*2*batch*S*d*elem (K1 groups of C1
+                                 slots per sequence), independent of tokens */
   uint64_t state;             /* h_{i-1}, positions, argmax keys, counters */
   uint64_t decode_scratch;    /* activations of one decode chunk */
   uint64_t workspace_total;   /* bytes the workspace must hold (256-aligned) */
   uint64_t weights_decode;    /* decode-resident weight blob */
   uint64_t weights_prefill_only; /* Chunker^1 + level-1 encoder blob */
   /* byte offsets of the regions inside the workspace; the top K/V region
-   * is [n_top][2 (K,V)][batch][H][top_len][hd], the level-1 region
-   * [n_enc1][2][batch][H][lower_len][hd], the decoder region
-   * [n_dec0][2][batch*C2][H][C1][hd]; h is [batch][d] at off_state. */
+   * is [n_top][2 (K,V)][batch][H][top_len][hd], the lower region holds
+   * level 1, 2, ... L-1 in turn, each [layers][2][batch][H][ceil(tokens /
+   * span(l))][hd] (256-byte aligned), the decoder region
+   * [n_dec0][2][batch*K1][H][C1][hd]; h is [batch][d] at off_state. */
   uint64_t off_top_kv, off_lower_kv, off_dec_kv, off_state, off_scratch;
 } photon_kv_report;
 
@@ -119,17 +136,18 @@ photon_status photon_prefill_scratch_bytes(const photon_config* cfg,
 
 /* ------------------------------------------------------------------------
  * Weight blobs (pure host).  Two device blobs: the decode blob (embedding,
- * Chunker^2, top encoder, Converter^2, level-1 decoder, Converter^1, token
- * decoder, output head) and the prefill-only blob (Chunker^1, level-1
- * encoder), which RecGen never touches after prefill (explainer, recursive-
- * generation section: only the decoder side must stay on the GPU).
+ * Chunker^L, top encoder, then Converter^l and the level-(l-1) decoder for
+ * l = L down to 1, output head) and the prefill-only blob (Chunker^l and the
+ * level-l encoder for l = 1 .. L-1), which RecGen never touches after
+ * prefill (explainer, recursive-generation section: only the decoder side
+ * must stay on the GPU).
  *
  * Tensors are the canonical ones: matrices W[out][in] (y = x W^T) stored in
  * the config dtype, row-major; norm gains float32.  Within a layer Wq, Wk, Wv
  * are adjacent so that [Wq;Wk;Wv] is one [3d][d] matrix.
- * Tensor names: "E", "W_ch1", "W_ch2", "W_cv2", "W_cv1", "W_out",
- * "<stack>.<l>.{g1,Wq,Wk,Wv,Wo,g2,W1,W2}", "<stack>.gf" for stack in
- * enc1, top, dec1, dec0.
+ * Tensor names: "E", "W_ch<l>" and "W_cv<l>" (l = 1 .. L), "W_out",
+ * "<stack>.<i>.{g1,Wq,Wk,Wv,Wo,g2,W1,W2}", "<stack>.gf" for stack in
+ * enc<l> (l = 1 .. L-1), top, dec<l> (l = 0 .. L-1).
  * ---------------------------------------------------------------------- */
 typedef struct {
   char name[32];
@@ -161,10 +179,13 @@ photon_status photon_close(photon_ctx* ctx);
 const char* photon_last_error(void);
 
 /* Prefill (explainer, module table and recursive-generation section):
- * embedding -> Chunker^1 -> level-1 encoder (causal) -> Chunker^2 -> top
- * encoder (causal), writing top K/V slots 0 .. n - 1 (n = prompt_len / S,
- * whole chunks) and the last top output h into the workspace.  RecGen keeps
- * no level-1 K/V; HierGen writes it into the workspace's level-1 region.
+ * embedding, then Chunker^l -> level-l encoder (causal) for l = 1 .. L-1,
+ * then Chunker^L -> top encoder (causal), writing top K/V slots 0 .. n - 1
+ * (n = prompt_len / S, whole chunks) and the last top output h into the
+ * workspace.  RecGen keeps no lower K/V; HierGen writes every lower level's
+ * into the workspace's lower region.  HierGen needs S / span(l) in
+ * {1, 2, 4} for every l < L (the queries of one encoder step per sequence;
+ * else PHOTON_EUNSUPPORTED).
  * A ragged prompt (prompt_len mod S = r > 0): only whole chunks form top
  * states; the r tail tokens open chunk n, whose decoders take them as given
  * tokens (the next photon_decode_chunk reports them as its first r tokens
@@ -185,15 +206,19 @@ photon_status photon_prefill(photon_ctx* ctx, int32_t mode, void* d_workspace,
                              int64_t max_tokens, void* stream);
 
 /* One decode chunk of S tokens per sequence (explainer, recursive-generation
- * section).  Converter^2 expands h_{i-1} into C2 conditioning vectors; the
- * level-1 decoder (attention confined to the chunk) gives A-hat_i; every
- * level-1 position is expanded by Converter^1 and the token decoder (in-chunk
- * K/V of C1 slots) into C1 greedy tokens; RecGen then feeds Chunker^2(A-hat_i)
- * to the top encoder, which appends slot i to the global K/V and attends
- * over slots 0..i to give h_i.  HierGen instead re-encodes the tokens through
- * Chunker^1 and one level-1 encoder step before the top step.
+ * section).  Converter^L expands h_{i-1} into C_L conditioning vectors; the
+ * level-(L-1) decoder (attention confined to the chunk) gives A-hat_i; for
+ * l = L-1 down to 2 every level-l vector is expanded by Converter^l and the
+ * level-(l-1) decoder over its own C_l positions; every level-1 position is
+ * expanded by Converter^1 and the token decoder (in-chunk K/V of C1 slots)
+ * into C1 greedy tokens; RecGen then feeds Chunker^L(A-hat_i) to the top
+ * encoder, which appends slot i to the global K/V and attends over slots
+ * 0..i to give h_i.  HierGen instead re-encodes the tokens through
+ * Chunker^l and one level-l encoder step for l = 1 .. L-1 before the top
+ * step.
  *   d_tokens  [batch][S] int32 out; token k*C1 + j is position j of level-1
- *             sub-chunk k; greedy argmax, lowest index on ties.
+ *             sub-chunk k (k < K1, in time order); greedy argmax, lowest
+ *             index on ties.
  *   d_logits  NULL, or [batch][S][vocab] float32 out (the logits behind
  *             every token).
  * PHOTON_ESTATE before a prefill; PHOTON_ECAPACITY when the chunk would pass
@@ -204,11 +229,12 @@ photon_status photon_decode_chunk(photon_ctx* ctx, int32_t* d_tokens,
 /* Consistency diagnostic: the recursive loss of the paper (explainer,
  * recursive-generation section: Eq. 1, a cosine distance that training may
  * add with weight alpha) measured on the chunk a HierGen context decoded
- * last.  d_dist [batch][C2] float32 out: 1 - cos(A-hat_i[k], A_i[k]) between
- * the level-1 decoder's reconstruction and the level-1 encoder's summary at
- * each level-1 position k, on the stored (post-norm, storage-dtype) values,
- * float32 sums.  d_ahat, d_a: NULL, or [batch][C2][d_model] storage-dtype
- * copies of A-hat_i and A_i.  PHOTON_ESTATE for a RecGen context (it never
+ * last.  d_dist [batch][C_L] float32 out: 1 - cos(A-hat_i[k], A_i[k]) between
+ * the level-(L-1) decoder's reconstruction and the level-(L-1) encoder's
+ * summary (the two values the top may read; level 1 for two levels) at each
+ * of the chunk's C_L positions, on the stored (post-norm, storage-dtype)
+ * values, float32 sums.  d_ahat, d_a: NULL, or [batch][C_L][d_model]
+ * storage-dtype copies of A-hat_i and A_i.  PHOTON_ESTATE for a RecGen context (it never
  * computes A_i) or before the first decoded chunk. */
 photon_status photon_consistency(photon_ctx* ctx, float* d_dist, void* d_ahat,
                                  void* d_a, void* stream);
@@ -363,7 +389,7 @@ typedef struct {
 } photon_sampling;
 
 /* Bytes of the sampling workspace of a context decoding `batch` sequences:
- * the logits of one token step ([batch*C2][vocab] float32) and the chunk's
+ * the logits of one token step ([batch*K1][vocab] float32) and the chunk's
  * log-likelihoods ([batch][S] float32).  Pure host. */
 photon_status photon_sampling_bytes(const photon_config* cfg, int32_t batch,
                                     uint64_t* bytes);

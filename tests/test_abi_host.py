@@ -103,7 +103,16 @@ def test_config_errors_are_reported():
     assert lib.photon_kv_bytes(ctypes.byref(c), 0, 16, 0, ctypes.byref(rep)) == P.ESHAPE
     assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 7, ctypes.byref(rep)) == P.EINVAL
     assert lib.photon_kv_bytes(None, 1, 16, 0, ctypes.byref(rep)) == P.EINVAL
-    c.n_levels = 3
+    for n in (1, 5):
+        c.n_levels = n
+        assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.EUNSUPPORTED
+    c.n_levels = 3                        # C3 = 0
+    assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.ESHAPE
+    c.chunk[2] = 2                        # level-2 stacks without layers
+    assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.ESHAPE
+    c.n_enc_hi[0] = c.n_dec_hi[0] = 1
+    assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.OK
+    c.chunk[2] = 17
     assert lib.photon_kv_bytes(ctypes.byref(c), 1, 16, 0, ctypes.byref(rep)) == P.EUNSUPPORTED
 
 
@@ -360,3 +369,68 @@ def test_consistency_needs_state():
     assert lib.photon_consistency(f.ctx, V(1 << 20), None, None, None) == P.ESTATE
     assert lib.photon_consistency(None, V(1 << 20), None, None, None) == P.EINVAL
     f.close()
+
+
+# ---------------- more than two levels ----------------
+L3 = pi.CONFIGS["tiny"].with_(chunk=(2, 3, 2), n_enc_hi=(1,), n_dec_hi=(2,))
+L4 = pi.CONFIGS["m150"].with_(chunk=(2, 2, 2, 2), n_enc_hi=(1, 2), n_dec_hi=(2, 1))
+
+
+@pytest.mark.parametrize("cfg", [L3, L4], ids=["tiny-2x3x2", "150m-2x2x2x2"])
+@pytest.mark.parametrize("mode", ["recgen", "hiergen"])
+def test_kv_bytes_closed_forms_deeper(cfg, mode):
+    for T in (cfg.S, 5 * cfg.S, 5 * cfg.S + 3):
+        r = P.kv_bytes(cfg, 3, T, mode)
+        o = O.kv_bytes(cfg, 3, T, mode)
+        assert r["top_len"] == -(-T // cfg.S)
+        assert (r["top_kv"], r["dec_kv"], r["lower_kv"]) == (o["top"], o["dec"], o["lower"])
+        assert r["lower_len"] == (-(-T // cfg.C1) if mode == "hiergen" else 0)
+
+
+@pytest.mark.parametrize("cfg", [L3, L4], ids=["tiny-2x3x2", "150m-2x2x2x2"])
+def test_weight_layout_deeper(cfg):
+    dec, pre, tensors = P.weight_layout(cfg)
+    shapes = dict(pi.weight_shapes(cfg))
+    assert sorted(t["name"] for t in tensors) == sorted(shapes)
+    for t in tensors:
+        assert t["rows"] * t["cols"] == int(np.prod(shapes[t["name"]]))
+    # the prefill-only blob holds every chunker and encoder below the top
+    pre_names = {t["name"] for t in tensors if t["blob"] == 1}
+    below = {f"W_ch{l}" for l in range(1, cfg.L)} | {n for n in shapes if n.startswith("enc")}
+    assert pre_names == below
+    # the decode blob runs in decode order: top chunker, top, then converter
+    # and decoder level by level downwards, the head
+    order = [t["name"] for t in tensors if t["blob"] == 0 and "." not in t["name"]]
+    L = cfg.L
+    assert order == ["E", f"W_ch{L}"] + [f"W_cv{l}" for l in range(L, 0, -1)] + ["W_out"]
+
+
+def test_hiergen_query_limit_is_checked_before_any_device_call():
+    # HierGen's level-l encoder step takes S/span(l) queries per sequence
+    # through the global attention (1, 2 or 4); RecGen has no such step
+    lib = P._lib
+    V = ctypes.c_void_p
+    cfg = pi.CONFIGS["tiny"].with_(chunk=(2, 2, 4), n_enc_hi=(1,), n_dec_hi=(1,))   # level 1: 8 queries
+    f = FakeCtx(cfg)
+    ws, sc, pr = V(4 << 20), V(64 << 20), V(128 << 20)
+    need = P.kv_bytes(cfg, 2, 64, "hiergen")["workspace_total"]
+    assert lib.photon_prefill(f.ctx, 1, ws, need, sc, 1 << 30, pr, 2, 32, 64, None) == P.EUNSUPPORTED
+    assert "queries" in lib.photon_last_error().decode()
+    top, toks = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    assert lib.photon_position(f.ctx, ctypes.byref(top), ctypes.byref(toks)) == P.OK
+    assert top.value == 0 and toks.value == 0        # nothing happened
+    f.close()
+
+
+def test_deeper_prompt_shape_errors():
+    out = ctypes.c_uint64()
+    c = P.make_config(L3)
+    lib = P._lib
+    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 11, 0, ctypes.byref(out)) == P.ESHAPE
+    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 12, 0, ctypes.byref(out)) == P.OK
+    assert lib.photon_prefill_scratch_bytes(ctypes.byref(c), 2, 23, 1, ctypes.byref(out)) == P.OK
+    sb = ctypes.c_uint64()
+    assert lib.photon_sampling_bytes(ctypes.byref(c), 3, ctypes.byref(sb)) == P.OK
+    # one token step's logits for every level-1 group, then the chunk's log-likelihoods
+    K1 = L3.S // L3.C1
+    assert sb.value >= 3 * K1 * L3.vocab * 4 + 3 * L3.S * 4
