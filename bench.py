@@ -5,7 +5,7 @@ A step is one decode chunk (one replay of the chunk's captured HIP graph):
 the whole hot path (Converter^2, level-1
 decoder, C1 token-decoder steps with the greedy head, Chunker^2 feedback and
 the top-encoder step over the global K/V) for every sequence of the batch,
-B * C1 * C2 tokens.  The workload is prefilled once (untimed); the timed
+B * S tokens (S = C1 * C2, or C1 * ... * CL with --chunk).  The workload is prefilled once (untimed); the timed
 steps decode chunk after chunk from the prompt end, rewinding to the prompt
 end (restore h, reset the position) whenever the workload's new_tokens are
 used up, so every step runs at the workload's real cache lengths.
@@ -195,6 +195,9 @@ def main():
     ap.add_argument("--prompt", type=int, default=None, help="override the workload's prompt length")
     ap.add_argument("--new-tokens", type=int, default=None, help="override the workload's generated tokens")
     ap.add_argument("--no-attn-standalone", action="store_true", help="skip the stand-alone attention figures")
+    ap.add_argument("--chunk", default=None, metavar="C1,C2[,C3[,C4]]",
+                    help="override the hierarchy's chunk sizes (2 to 4 levels); each level added above the "
+                         "second gets as many encoder and decoder layers as level 1")
     ap.add_argument("--sample", default=None, metavar="T,K",
                     help="sampling decode at temperature T with a top-K cut (K = 0: whole vocabulary) instead of "
                          "greedy; also times the multi-query aggregation of the batch in groups of 9")
@@ -223,6 +226,15 @@ def main():
         n = args.new_tokens or wl.new_tokens
         name = wl.name.split(" B")[0] + f" bf16 B{b} P{p} N{n}"
         wl = dataclasses.replace(wl, name=name + " (override)", batch=b, prompt=p, new_tokens=n)
+    if args.chunk:
+        import dataclasses
+        chunk = tuple(int(x) for x in args.chunk.split(","))
+        extra = len(chunk) - 2
+        c0 = wl.cfg
+        cfg_l = c0.with_(chunk=chunk, n_enc_hi=(c0.n_enc1,) * extra, n_dec_hi=(c0.n_dec1,) * extra)
+        if (wl.prompt % cfg_l.S) or (wl.new_tokens % cfg_l.S):
+            sys.exit(f"prompt and new tokens must be multiples of S = {cfg_l.S}")
+        wl = dataclasses.replace(wl, cfg=cfg_l, name=wl.name + " chunk " + "x".join(map(str, chunk)))
     cfg = wl.cfg
     K = args.steps if args.steps is not None else wl.chunks
     Wm = args.warmup if args.warmup is not None else wl.chunks
@@ -400,7 +412,9 @@ def main():
                    "new_tokens": wl.new_tokens, "d_model": cfg.d_model, "heads": cfg.n_heads,
                    "chunk": list(cfg.chunk),
                    **({"layers": mcfg.n_layers} if vanilla else
-                      {"layers_top_enc1_dec1_dec0": [cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0]}),
+                      {"layers_top_enc1_dec1_dec0": [cfg.n_top, cfg.n_enc1, cfg.n_dec1, cfg.n_dec0],
+                       **({"layers_enc_dec_above_level1": [list(cfg.n_enc_hi), list(cfg.n_dec_hi)]}
+                          if cfg.L > 2 else {})}),
                    "vocab": cfg.vocab, "tokens_per_step": B * S,
                    **({"sampling": {"temperature": sampling["temperature"], "top_k": sampling["top_k"]}}
                       if sampling else {})},
