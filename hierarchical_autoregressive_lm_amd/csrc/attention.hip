@@ -53,6 +53,62 @@ __device__ __forceinline__ int resolve_len(int L_host, const int* L_dev, int L_m
   return L_dev ? (*L_dev) * L_mul + L_add : L_host;
 }
 
+// Fused RoPE + K/V append: new row t of group g, head h, for lane c of its
+// 16-lane group (elements [c*CE, (c+1)*CE)).  Sums the QKV GEMM's slabs in
+// slab order; q and k turn by the rotate-half embedding at position pos(t)
+// (pairs (i, i + hd/2): lanes c and c ^ 8 hold partners, exchanged by a
+// shuffle, so all 16 lanes must be active); k and v are rounded to the
+// storage dtype (the values a cache read would give).  Returns pos(t).
+template <typename T, int HD>
+__device__ __forceinline__ int new_row(const AttnCall& a, int g, int t, int h, int c, float (&q)[HD / 16],
+                                       float (&k)[HD / 16], float (&v)[HD / 16]) {
+  constexpr int CE = HD / 16, half = HD / 2;
+  const float* p = a.qkv + ((int64_t)g * a.Q + t) * 3 * a.d + h * HD + c * CE;
+  float x[CE], y[CE];
+#pragma unroll
+  for (int e = 0; e < CE; ++e) { x[e] = 0.f; y[e] = 0.f; v[e] = 0.f; }
+  for (int sl = 0; sl < a.ksplit; ++sl) {
+    const float* ps = p + sl * a.pstride;
+#pragma unroll
+    for (int e = 0; e < CE; ++e) {
+      x[e] += ps[e];
+      y[e] += ps[a.d + e];
+      v[e] += ps[2 * a.d + e];
+    }
+  }
+  const int pos = a.pos_add + (a.pos_dev ? (*a.pos_dev) * a.pos_mul : 0) + t;
+  const float* rt = a.rope + ((int64_t)pos * half + (c & 7) * CE) * 2;
+#pragma unroll
+  for (int e = 0; e < CE; ++e) {
+    const float xp = __shfl_xor(x[e], 8, 64), yp = __shfl_xor(y[e], 8, 64);
+    const float cs = rt[2 * e], sn = rt[2 * e + 1];
+    if (c < 8) {
+      q[e] = x[e] * cs - xp * sn;
+      k[e] = St<T>::ld(St<T>::st(y[e] * cs - yp * sn));
+    } else {
+      q[e] = x[e] * cs + xp * sn;
+      k[e] = St<T>::ld(St<T>::st(y[e] * cs + yp * sn));
+    }
+    v[e] = St<T>::ld(St<T>::st(v[e]));
+  }
+  return pos;
+}
+
+// Store the lane's CE elements of a new key and value at cache slot pos.
+template <typename T, int HD>
+__device__ __forceinline__ void store_row(const AttnCall& a, int g, int h, int c, int pos, const float (&k)[HD / 16],
+                                          const float (&v)[HD / 16]) {
+  constexpr int CE = HD / 16;
+  const int64_t off = (int64_t)(a.seq0 + g) * a.seq_stride + ((int64_t)h * a.cap + pos) * HD + c * CE;
+  T* K = reinterpret_cast<T*>(const_cast<void*>(a.Kc)) + off;
+  T* V = reinterpret_cast<T*>(const_cast<void*>(a.Vc)) + off;
+#pragma unroll
+  for (int e = 0; e < CE; ++e) {
+    K[e] = St<T>::st(k[e]);
+    V[e] = St<T>::st(v[e]);
+  }
+}
+
 // ---------------------------------------------------------------- decode
 // Merge nsplit partial results (num[hd], max, sum) of one (g, h, t) query.
 template <typename T, int HD>
@@ -82,6 +138,20 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnCall a) {
   for (int e = threadIdx.x; e < HD; e += 64) combine_splits<T, HD>(a, g, h, t, e);
 }
 
+// One pass of a decode row slot: keys kb + r + SLOTS*u (u < U), clamped to
+// k1 - 1 (in bounds; the scores mask them), K and V rows for this lane.
+template <typename T, int CE, int U, int SLOTS, int HD>
+__device__ __forceinline__ void load_pass(Raw<T, CE, true> (&kr)[U], Raw<T, CE, true> (&vr)[U], const T* Kb,
+                                          const T* Vb, int kb, int r, int k1) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int key = kb + r + SLOTS * u;
+    key = key < k1 ? key : k1 - 1;
+    kr[u].load(Kb + (int64_t)key * HD);
+    vr[u].load(Vb + (int64_t)key * HD);
+  }
+}
+
 template <typename T, int HD, int Q, int U, int SLOTS = 16>
 __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, float scale) {
   constexpr int CE = HD / 16;
@@ -93,20 +163,51 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
   const int gh = blockIdx.x / nsplit;
   const int h = gh % a.H, g = gh / a.H;
   const int L = resolve_len(a.L_host, a.L_dev, a.L_mul, a.L_add);
-  int kps = (L + nsplit - 1) / nsplit;
+  // fused: keys 0 .. Lc-1 come from the cache, the Q new rows' keys Lc ..
+  // L-1 from registers (slot 0 of the last split folds them in below)
+  const bool fused = a.qkv != nullptr;
+  const int Lc = fused ? L - Q : L;
+  int kps = (Lc + nsplit - 1) / nsplit;
   kps = (kps + 15) & ~15;
   const int k0 = split * kps;
-  const int k1 = min(L, k0 + kps);
-
-  float qv[Q][CE];
-#pragma unroll
-  for (int t = 0; t < Q; ++t)
-#pragma unroll
-    for (int e = 0; e < CE; ++e)
-      qv[t][e] = a.q[(int64_t)(g * Q + t) * a.q_ld + h * HD + c * CE + e] * scale;
-
+  const int k1 = min(Lc, k0 + kps);
   const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
   const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
+
+  // fused: slot 0 forms the queries from the QKV slabs (one read of them
+  // per workgroup) and hands them to the other slots through LDS; with one
+  // query it also keeps the new row's k and v, which the last split's slot
+  // 0 stores and folds in after its pass
+  const bool owner = fused && r == 0 && split == nsplit - 1;
+  float qv[Q][CE], kn1[CE], vn1[CE];
+  if (fused) {
+    __shared__ float qs[Q][HD];
+    if (r == 0) {
+#pragma unroll
+      for (int t = 0; t < Q; ++t) {
+        float qn[CE], kn[CE], vn[CE];
+        const int pos = new_row<T, HD>(a, g, t, h, c, qn, kn, vn);
+#pragma unroll
+        for (int e = 0; e < CE; ++e) qs[t][c * CE + e] = qn[e] * scale;
+        if constexpr (Q == 1) {
+#pragma unroll
+          for (int e = 0; e < CE; ++e) { kn1[e] = kn[e]; vn1[e] = vn[e]; }
+          if (owner) store_row<T, HD>(a, g, h, c, pos, kn, vn);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+#pragma unroll
+      for (int e = 0; e < CE; ++e) qv[t][e] = qs[t][c * CE + e];
+  } else {
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+#pragma unroll
+      for (int e = 0; e < CE; ++e)
+        qv[t][e] = a.q[(int64_t)(g * Q + t) * a.q_ld + h * HD + c * CE + e] * scale;
+  }
 
   float m[Q], l[Q], o[Q][CE];
 #pragma unroll
@@ -121,13 +222,7 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
   // with a single rescale.
   for (int kb = k0; kb < k1; kb += SLOTS * U) {
     Raw<T, CE, true> kr[U], vr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int key = kb + r + SLOTS * u;
-      key = key < k1 ? key : k1 - 1;       // in-bounds; masked below
-      kr[u].load(Kb + (int64_t)key * HD);
-      vr[u].load(Vb + (int64_t)key * HD);
-    }
+    load_pass<T, CE, U, SLOTS, HD>(kr, vr, Kb, Vb, kb, r, k1);
     float kv[U][CE], vv[U][CE];
 #pragma unroll
     for (int u = 0; u < U; ++u) { kr[u].unpack(kv[u]); vr[u].unpack(vv[u]); }
@@ -162,6 +257,38 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
       }
       l[t] = l[t] * corr + ps;
       m[t] = mx;
+    }
+  }
+  if (owner) {
+    // the new rows' K/V (several queries: loaded again here, and stored)
+    // into the state of every query t >= tn as key Lc + tn
+    for (int tn = 0; tn < Q; ++tn) {
+      float kn[CE], vn[CE];
+      if constexpr (Q == 1) {
+#pragma unroll
+        for (int e = 0; e < CE; ++e) { kn[e] = kn1[e]; vn[e] = vn1[e]; }
+      } else {
+        float qd[CE];
+        const int pos = new_row<T, HD>(a, g, tn, h, c, qd, kn, vn);
+        store_row<T, HD>(a, g, h, c, pos, kn, vn);
+      }
+#pragma unroll
+      for (int t = 0; t < Q; ++t) {
+        if (t < tn) continue;
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) s = fmaf(qv[t][e], kn[e], s);
+        s += __shfl_xor(s, 8, 64);
+        s += __shfl_xor(s, 4, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 1, 64);
+        const float mx = fmaxf(m[t], s);
+        const float corr = expf(m[t] - mx), p = expf(s - mx);
+#pragma unroll
+        for (int e = 0; e < CE; ++e) o[t][e] = fmaf(p, vn[e], o[t][e] * corr);
+        l[t] = l[t] * corr + p;
+        m[t] = mx;
+      }
     }
   }
 
@@ -212,12 +339,14 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnCall a, float scale
   if (pair >= a.G * a.H) return;            // whole 16-lane groups exit together
   const int h = pair % a.H, g = pair / a.H;
   const int L = resolve_len(a.L_host, a.L_dev, a.L_mul, a.L_add);
+  const bool fused = a.qkv != nullptr;
+  const int Lc = fused ? L - a.Q : L;       // keys read from the cache
   const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
   const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
   R kr[MAXL], vr[MAXL];
 #pragma unroll
   for (int j = 0; j < MAXL; ++j) {
-    if (j < L) {
+    if (j < Lc) {
       kr[j].load(Kb + j * HD);
       vr[j].load(Vb + j * HD);
     } else {
@@ -228,12 +357,35 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnCall a, float scale
   float kv[MAXL][CE], vv[MAXL][CE];
 #pragma unroll
   for (int j = 0; j < MAXL; ++j) { kr[j].unpack(kv[j]); vr[j].unpack(vv[j]); }
+  float q1[CE];                             // the query of a one-row step
+  if (fused) {
+    // the new rows: keys Lc .. L-1 from registers, and into the cache
+    for (int t = 0; t < a.Q; ++t) {
+      float kn[CE], vn[CE];
+      const int pos = new_row<T, HD>(a, g, t, h, c, q1, kn, vn);
+      store_row<T, HD>(a, g, h, c, pos, kn, vn);
+#pragma unroll
+      for (int j = 0; j < MAXL; ++j)
+        if (j == Lc + t)
+#pragma unroll
+          for (int e = 0; e < CE; ++e) { kv[j][e] = kn[e]; vv[j][e] = vn[e]; }
+    }
+  }
   T* out = reinterpret_cast<T*>(a.out);
   for (int t = 0; t < a.Q; ++t) {
-    const float* qp = a.q + (int64_t)(g * a.Q + t) * a.q_ld + h * HD + c * CE;
     float q[CE];
+    if (fused) {
+      if (a.Q > 1) {                        // several rows: their queries again
+        float kn[CE], vn[CE];
+        (void)new_row<T, HD>(a, g, t, h, c, q1, kn, vn);
+      }
 #pragma unroll
-    for (int e = 0; e < CE; ++e) q[e] = qp[e] * scale;
+      for (int e = 0; e < CE; ++e) q[e] = q1[e] * scale;
+    } else {
+      const float* qp = a.q + (int64_t)(g * a.Q + t) * a.q_ld + h * HD + c * CE;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) q[e] = qp[e] * scale;
+    }
     const int last = L - a.Q + t;           // last visible key
     float s[MAXL];
     float mx = -INFINITY;

@@ -105,6 +105,16 @@ struct AttnCall {
   int L_host; const int* L_dev; int L_mul; int L_add;
   void* out; int64_t out_ld;      // storage dtype, same row/col map as q
   float* part; int nsplit;        // decode split-K partials
+  // Fused RoPE + K/V append (decode and chunk kernels, qkv != nullptr): the
+  // Q new rows of group g are rows g*Q + t of the QKV GEMM's ksplit slabs
+  // ([M][3d] fp32 each, q | k | v, pstride floats apart, summed in slab
+  // order); q and k are rotated at position pos(t) = pos_add + (pos_dev ?
+  // *pos_dev * pos_mul : 0) + t with the [pos][hd/2][2] (cos, sin) table
+  // `rope`, K and V rounded to the storage dtype and written to cache slot
+  // pos(t), which must be key L-Q+t; those keys are attended from
+  // registers, and `q` is not read.
+  const float* qkv; int ksplit; int64_t pstride; int d;
+  const float* rope; int pos_add; const int* pos_dev; int pos_mul;
 };
 // Long caches: split over keys, then combine.  part holds
 // G*H*Q*nsplit*(hd+2) floats when nsplit > 1.

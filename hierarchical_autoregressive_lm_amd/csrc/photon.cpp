@@ -263,15 +263,18 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.tail = cur.take((uint64_t)B * S * sizeof(int));   // a ragged prompt's tail tokens
   p.off_scratch = align_up(cur.pos);
   p.state_bytes = p.off_scratch - p.off_state;
-  // the top branch runs B rows, HierGen's re-encoding up to B*K1 (level 1);
-  // the decoders run up to B*K1 rows (the level-1 decoder, the token decoder)
-  const int64_t MA = hier ? B * K1 : B, MB = B * K1;
-  uint64_t partA = std::max(layer_part_bytes(c, B), part_bytes(dt, B, d, CL * d));
+  // Set A serves the top branch: the top (B rows), HierGen's re-encoding
+  // (up to B*K1 rows at level 1) and RecGen's decoders for the next chunk
+  // (up to B*K1 rows); set B the decoders and the token decoder (B*K1).
+  // The level-l stacks run B*per_chunk(l) rows (fewer rows may take more K
+  // slabs); the converters above level 1 and the chunkers store slabs too.
+  const int64_t MA = B * K1, MB = B * K1;
+  uint64_t stack_parts = layer_part_bytes(c, B);
+  for (int l = 1; l < L; ++l) stack_parts = std::max(stack_parts, layer_part_bytes(c, B * lv.per_chunk(l)));
+  for (int l = 2; l <= L; ++l) stack_parts = std::max(stack_parts, part_bytes(dt, B * lv.per_chunk(l), lv.C[l] * d, d));
+  uint64_t partA = std::max(stack_parts, part_bytes(dt, B, d, CL * d));
   if (hier)
-    for (int l = 1; l < L; ++l) {
-      const int64_t M = B * lv.per_chunk(l);
-      partA = std::max({partA, layer_part_bytes(c, M), part_bytes(dt, M, d, lv.C[l] * d)});
-    }
+    for (int l = 1; l < L; ++l) partA = std::max(partA, part_bytes(dt, B * lv.per_chunk(l), d, lv.C[l] * d));
   p.xA = cur.take((uint64_t)MA * d * 4);
   p.aA = cur.take((uint64_t)MA * d * eb);
   p.partA = cur.take(partA);
@@ -284,13 +287,7 @@ WsPlan plan_workspace(const photon_config* c, int64_t B, int64_t tokens, int mod
   p.apartA = cur.take((uint64_t)parts * (hd + 2) * 4);
   p.eA = cur.take(hier ? (uint64_t)B * S * d * eb : 0);
   p.AA = cur.take(hier ? (uint64_t)B * K1 * d * eb : 0);
-  // slabs of every decoder's layers (the level-l decoder runs B*per_chunk(l)
-  // rows; fewer rows may take more K slabs) and of the converters above
-  // level 1 (Converter^1 stores one slab)
-  uint64_t partB = 0;
-  for (int l = 1; l < L; ++l) partB = std::max(partB, layer_part_bytes(c, B * lv.per_chunk(l)));
-  for (int l = 2; l <= L; ++l)
-    partB = std::max(partB, part_bytes(dt, B * lv.per_chunk(l), lv.C[l] * d, d));
+  const uint64_t partB = stack_parts;
   p.xB = cur.take((uint64_t)MB * d * 4);
   p.aB = cur.take((uint64_t)MB * d * eb);
   p.partB = cur.take(partB);
@@ -539,6 +536,10 @@ struct photon_ctx {
   // given tokens; pending until that chunk is decoded
   int tail_r = 0;
   bool tail_pending = false;
+  // RecGen: the workspace's A-hat buffers hold the decoders' outputs for
+  // the next chunk (each chunk computes them for the one after it); false
+  // after a prefill or a rewind, when the next chunk computes them first
+  bool ahat_ready = false;
   unsigned char* ws = nullptr;
   WsPlan plan;
   Tracer tr;
@@ -760,15 +761,31 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
     unsigned char* kbase = r.kv.base + (r.kv.per_layer ? (int64_t)l * 2 * r.kv.plane_elems * eb : 0);
     void* Kc = kbase;
     void* Vc = kbase + r.kv.plane_elems * eb;
-    RopeKvCall rc{dt, b.part, ks, (int64_t)r.M * 3 * d, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
-                  r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
-    PH_TRY(traced(c, PHOTON_K_ROPE_KV, (double)r.M * d * (12.0 + 4 + 2 * eb), 6.0 * r.M * d, st, "rope_kv",
-                  [&] { return launch_rope_kv(rc, st); }));
+    // RoPE and the K/V append run inside the attention kernel (the new rows
+    // are the last Q keys of every group) for the chunk-confined decoders and
+    // for decode steps over caches of fewer than 1024 slots; a long cache's
+    // step (whose attention streams far more than the launch costs) and
+    // prefill give them a launch of their own, which keeps the forming of q
+    // off the long stream's start
+    const bool fuse = r.rows_per_seq == r.Q && (r.kind == ATT_CHUNK || (r.kind == ATT_DECODE && r.kv.cap < 1024));
+    if (!fuse) {
+      RopeKvCall rc{dt, b.part, ks, (int64_t)r.M * 3 * d, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
+                    r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
+      PH_TRY(traced(c, PHOTON_K_ROPE_KV, (double)r.M * d * (12.0 + 4 + 2 * eb), 6.0 * r.M * d, st, "rope_kv",
+                    [&] { return launch_rope_kv(rc, st); }));
+    }
     AttnCall ac{dt, r.G, r.Q, H, hd, b.q, d, Kc, Vc, r.kv.seq_stride, r.kv.cap, r.kv.seq0,
                 r.L_host, r.L_dev, r.L_mul, r.L_add, b.o, d, b.apart, r.nsplit};
-    // K and V of every visible key read once, q read, output written (the
-    // split partials are not counted)
-    const double abytes = (double)r.G * H * r.L_acct * hd * eb * 2 + (double)r.M * d * (4 + eb);
+    if (fuse) {
+      ac.qkv = b.part; ac.ksplit = ks; ac.pstride = (int64_t)r.M * 3 * d; ac.d = d;
+      ac.rope = r.rope; ac.pos_add = r.pos_add; ac.pos_dev = r.pos_dev; ac.pos_mul = r.pos_mul;
+    }
+    // K and V of every cached key read once, output written, and: q read
+    // (separate RoPE launch), or the new rows' q, k, v read and their K, V
+    // written (fused).  The split partials and the QKV GEMM's K slabs are
+    // not counted.
+    const double abytes = fuse ? (double)r.G * H * (r.L_acct - r.Q) * hd * eb * 2 + (double)r.M * d * (12 + 3 * eb)
+                               : (double)r.G * H * r.L_acct * hd * eb * 2 + (double)r.M * d * (4 + eb);
     const double aflops = 4.0 * r.G * H * r.Q * (double)r.L_acct * hd;
     if (r.kind == ATT_PREFILL)
       PH_TRY(traced(c, PHOTON_K_ATTN_PREFILL, abytes, aflops / 2, st, "attn_prefill",
@@ -1070,14 +1087,59 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   c->prompt_tokens = prompt_len;
   c->tail_r = tail_r;
   c->tail_pending = tail_r > 0;
+  c->ahat_ready = false;
   c->prefilled = true;
   return ok();
 }
 
-// Enqueue one decode chunk.  The decoders run on `st`; with RecGen and
-// st_top != st the top branch forks onto st_top (after A-hat exists) and
-// joins back before the chunk ends.  Everything reads positions from the
-// device counter, so the same sequence serves every chunk.
+// The chunk-confined decoders above the token decoder for the chunk after
+// top state h: Converter^L expands h into C_L conditioning vectors and the
+// level-(L-1) decoder gives A-hat (Ahat[L-1]); for l = L-1 .. 2 every level-l
+// vector is expanded by Converter^l and the level-(l-1) decoder over its own
+// C_l positions (attention confined to the group, positions 0 .. C_l-1, no
+// cache kept), down to the level-1 vectors (Ahat[1]).  Only h is read.
+photon_status enqueue_decoders(photon_ctx* c, const StackBufs& bufs, hipStream_t st) {
+  const photon_config& cf = c->cfg;
+  const Levels lv = levels(&cf);
+  const WsPlan& wp = c->plan;
+  unsigned char* ws = c->ws;
+  const int d = cf.d_model, H = cf.n_heads, hd = d / H, B = (int)c->B;
+  const float* rope = (const float*)(ws + wp.rope.off);
+  int ks = 1;
+  auto expand = [&](int l, const void* in, int M, void* out) -> photon_status {
+    const int C = lv.C[l];
+    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CONV, in, d, c->W_cv[l], M, C * d, d, bufs.part, &ks, st));
+    PH_TRY(stack_input(c, c->dec[l - 1], bufs.part, ks, M * C, bufs.x, bufs.a, st));
+    StackRun r{};
+    r.M = M * C; r.rows_per_seq = C; r.G = M;
+    r.kv = KvTarget{ws + wp.kv1tmp.off, (int64_t)M * H * C * hd, false, (int64_t)H * C * hd, C, 0};
+    r.pos_add = 0; r.rope = rope;
+    r.kind = ATT_CHUNK; r.Q = C; r.L_host = C; r.nsplit = 1; r.L_acct = C;
+    r.out = out; r.out_rows = M * C; r.in_stride = 1; r.in_off = 0;
+    return run_stack(c, c->dec[l - 1], bufs, r, st);
+  };
+  PH_TRY(expand(lv.L, ws + wp.h.off, B, ws + wp.Ahat[lv.L - 1].off));
+  for (int l = lv.L - 1; l >= 2; --l)
+    PH_TRY(expand(l, ws + wp.Ahat[l].off, (int)(B * lv.per_chunk(l)), ws + wp.Ahat[l - 1].off));
+  return ok();
+}
+
+// Enqueue one decode chunk.  The token decoder runs on `st`; with RecGen
+// and st_top != st the top branch forks onto st_top once the token branch
+// has its conditioning vectors, and joins back before the chunk ends.
+// Everything reads positions from the device counter, so the same sequence
+// serves every chunk.
+//
+// HierGen: the decoders of the chunk, the token steps, the bottom-up
+// re-encoding and the top step, in that order.  RecGen: the decoders above
+// the token decoder depend only on the previous top output, so each chunk's
+// top branch ends with them for the next chunk (feedback Chunker^L(A-hat_i),
+// top step i -> h_i, decoders -> A-hat_{i+1}), beside the token steps of
+// chunk i; the chunk after a prefill or a rewind runs them first
+// (`ahat_ready`, photon_decode_chunk_lp).  The results are those of the
+// sequential order: the two branches share no buffer (A-hat_i is consumed by
+// Converter^1 before the fork and by the feedback GEMM before the decoders
+// of the top branch overwrite it).
 photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipStream_t st_top, int given_r = 0) {
   const photon_config& cf = c->cfg;
   const Levels lv = levels(&cf);
@@ -1087,6 +1149,7 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
   const int dt = cf.dtype, d = cf.d_model, H = cf.n_heads, hd = d / H, V = cf.vocab;
   const int B = (int)c->B, MB = B * K1;
   const int eb = elem_bytes(&cf);
+  const bool recgen = c->mode == PHOTON_RECGEN;
   int* counter = (int*)(ws + wp.counter.off);
   const float* rope = (const float*)(ws + wp.rope.off);
   void* h = ws + wp.h.off;
@@ -1099,35 +1162,9 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
                ws + wp.oA.off, ws + wp.hidA.off, (float*)(ws + wp.apartA.off)};
   int ks = 1;
 
-  // Converter^l on M level-l rows -> C_l conditioning vectors each, then the
-  // level-(l-1) decoder over each group's C_l positions (attention confined
-  // to the group, positions 0 .. C_l-1, no cache kept) -> out [M*C_l][d]
-  auto expand = [&](int l, const void* in, int M, void* out) -> photon_status {
-    const int C = lv.C[l];
-    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CONV, in, d, c->W_cv[l], M, C * d, d, sb.part, &ks, st));
-    PH_TRY(stack_input(c, c->dec[l - 1], sb.part, ks, M * C, sb.x, sb.a, st));
-    StackRun r{};
-    r.M = M * C; r.rows_per_seq = C; r.G = M;
-    r.kv = KvTarget{ws + wp.kv1tmp.off, (int64_t)M * H * C * hd, false, (int64_t)H * C * hd, C, 0};
-    r.pos_add = 0; r.rope = rope;
-    r.kind = ATT_CHUNK; r.Q = C; r.L_host = C; r.nsplit = 1; r.L_acct = C;
-    r.out = out; r.out_rows = M * C; r.in_stride = 1; r.in_off = 0;
-    return run_stack(c, c->dec[l - 1], sb, r, st);
-  };
-  // Converter^L: h_{i-1} -> C_L conditioning vectors; the level-(L-1)
-  // decoder over them -> A-hat_i
-  PH_TRY(expand(L, h, B, Ahat_top));
-  const bool fork = c->mode == PHOTON_RECGEN && st_top != st;
-  if (fork) {
-    HIP_TRY(hipEventRecord(c->ev_fork, st));
-    HIP_TRY(hipStreamWaitEvent(st_top, c->ev_fork, 0));
-  }
-  // token branch: the decoders of the levels between (every level-l vector
-  // expanded on its own, l = L-1 .. 2), Converter^1 (all C1 conditioning
-  // vectors of every level-1 position), then C1 sequential token-decoder
-  // steps
-  for (int l = L - 1; l >= 2; --l)
-    PH_TRY(expand(l, ws + wp.Ahat[l].off, (int)(B * lv.per_chunk(l)), ws + wp.Ahat[l - 1].off));
+  if (!recgen) PH_TRY(enqueue_decoders(c, sb, st));
+  // Converter^1 (all C1 conditioning vectors of every level-1 position) and
+  // the first token step's input
   {
     GemmCall g{};
     g.dtype = dt; g.A = ws + wp.Ahat[1].off; g.lda = d; g.W = c->W_cv[1]; g.M = MB; g.N = C1 * d; g.K = d;
@@ -1139,6 +1176,12 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     e.R = MB; e.d = d; e.row_stride = 1; e.row_off = 0; e.eps = cf.norm_eps;
     PH_TRY(rows_epi(c, e, st));
   }
+  const bool fork = recgen && st_top != st;
+  if (fork) {
+    HIP_TRY(hipEventRecord(c->ev_fork, st));
+    HIP_TRY(hipStreamWaitEvent(st_top, c->ev_fork, 0));
+  }
+  // token branch: C1 sequential token-decoder steps
   for (int j = 0; j < C1; ++j) {
     StackRun r{};
     r.M = MB; r.rows_per_seq = 1; r.G = MB;
@@ -1178,7 +1221,7 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
   // top branch (RecGen: independent of the tokens, so it may run beside the
   // token branch on its own stream; its counter update closes it)
   const hipStream_t stt = fork ? st_top : st;
-  if (c->mode == PHOTON_RECGEN) {
+  if (recgen) {
     // feedback: u_i = Chunker^L(A-hat_i), nothing re-encoded
     PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, Ahat_top, (int64_t)CL * d, c->W_ch[L], B, d, CL * d, sa.part, &ks, stt));
     PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
@@ -1220,6 +1263,8 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     r.out = h; r.out_rows = B; r.in_stride = 1; r.in_off = 0;
     PH_TRY(run_stack(c, c->top, sa, r, stt));
   }
+  // RecGen: the next chunk's decoders from h_i, still in the top branch
+  if (recgen) PH_TRY(enqueue_decoders(c, sa, stt));
   // the position advances once both branches are done: the sampler of the
   // token branch reads it while the top branch runs
   if (fork) {
@@ -1253,6 +1298,16 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
   hipStream_t st = (hipStream_t)stream;
   const int B = (int)c->B;
   int* tok = (int*)(c->ws + c->plan.tok.off);
+  if (c->mode == PHOTON_RECGEN && !c->ahat_ready) {
+    // after a prefill or a rewind: this chunk's decoders from the current h
+    // (afterwards every chunk leaves them ready for the next one)
+    const WsPlan& wp = c->plan;
+    unsigned char* ws = c->ws;
+    const StackBufs sb{(float*)(ws + wp.xB.off), ws + wp.aB.off, (float*)(ws + wp.partB.off),
+                       (float*)(ws + wp.qB.off), ws + wp.oB.off, ws + wp.hidB.off, nullptr};
+    PH_TRY(enqueue_decoders(c, sb, st));
+    c->ahat_ready = true;
+  }
   if (c->tail_pending) {
     // the chunk a ragged prompt opened: its first tail_r tokens are given
     // (direct launches; the captured graph serves the whole chunks)
@@ -1390,6 +1445,7 @@ photon_status photon_set_position(photon_ctx* c, int64_t tokens, void* stream) {
   c->tokens = tokens;
   c->top_len = pos;
   c->tail_pending = !c->vanilla && c->tail_r > 0 && tokens == c->prompt_tokens;
+  c->ahat_ready = false;
   return ok();
 }
 

@@ -260,7 +260,11 @@ photon_status photon_set_position(photon_ctx* ctx, int64_t tokens,
  * every position from device memory, so the same graph serves every chunk)
  * and later calls replay it on the caller's stream; with RecGen the top
  * encoder step and the token decoder run as two parallel branches of the
- * graph.  Calls that ask for logits, and calls while tracing is on, launch
+ * graph.  RecGen's decoders above the token decoder read only the previous
+ * top output, so the top branch of chunk i also runs them for chunk i+1
+ * (from h_i) while chunk i's tokens are decoded; the first chunk after a
+ * prefill or a photon_set_position runs them first.  The results are those
+ * of the sequential order.  Calls that ask for logits, and calls while tracing is on, launch
  * the same kernels directly on the caller's stream instead.  enable = 0
  * turns graphs off for this context. */
 photon_status photon_use_graphs(photon_ctx* ctx, int32_t enable);
