@@ -117,3 +117,32 @@ def test_consistency_at_the_level_under_the_top():
     np.testing.assert_allclose(ah.cpu().numpy(), o["A_hat"], rtol=1e-4, atol=1e-5)
     np.testing.assert_allclose(a.cpu().numpy(), o["A"], rtol=1e-4, atol=1e-5)
     np.testing.assert_allclose(dist.cpu().numpy(), O.consistency(o["A_hat"], o["A"]), atol=1e-5)
+
+
+def test_graph_direct_and_rewind_three_levels():
+    # RecGen's top branch prepares the next chunk's decoders; after a rewind
+    # (or with direct launches) the first chunk prepares them itself: every
+    # order gives the same tokens and the same top K/V, bit for bit
+    import torch
+    from hierarchical_autoregressive_lm_amd.photon import Photon
+    cfg = small_cfg(chunk=(2, 3, 2), n_enc_hi=(1,), n_dec_hi=(1,))
+    W, pr = pi.gen_weights(cfg, 38), pi.gen_prompts(cfg, 3, 24, 38)
+    m = Photon(cfg, W)
+    prompt = torch.from_numpy(pr).cuda()
+    tg, _ = m.generate(prompt, 48)                        # graph replay
+    kv_g = m.top_kv().clone()
+    m.use_graphs(False)
+    td, _ = m.generate(prompt, 48)                        # direct launches
+    assert torch.equal(tg, td) and torch.equal(kv_g, m.top_kv())
+    m.use_graphs(True)
+    m.prefill(prompt, 24 + 48)
+    snap = m.state_snapshot()
+    a = torch.empty((3, cfg.S), dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    m.decode_chunk(a)
+    m.decode_chunk(b)
+    m.state_restore(snap, 24)                             # back to the prompt end
+    c = torch.empty_like(a)
+    m.decode_chunk(c)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c) and torch.equal(a, tg[:, :cfg.S]) and torch.equal(b, tg[:, cfg.S:2 * cfg.S])
