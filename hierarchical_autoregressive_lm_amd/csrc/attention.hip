@@ -173,6 +173,11 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
   const int k1 = min(Lc, k0 + kps);
   const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
   const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
+  // short caches (16 slots): the first pass's K/V loads go out before the
+  // queries are formed and stay in flight across the hand-over of q
+  constexpr bool kEarly = SLOTS == 16;
+  Raw<T, CE, true> kr[U], vr[U];
+  if (kEarly && k0 < k1) load_pass<T, CE, U, SLOTS, HD>(kr, vr, Kb, Vb, k0, r, k1);
 
   // fused: slot 0 forms the queries from the QKV slabs (one read of them
   // per workgroup) and hands them to the other slots through LDS; with one
@@ -196,7 +201,11 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
         }
       }
     }
-    __syncthreads();
+    // LDS-only fences: the barrier orders q's hand-over without waiting
+    // for the cache loads in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
     for (int t = 0; t < Q; ++t)
 #pragma unroll
@@ -221,8 +230,7 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
   // iteration, loaded together and folded into the slot's online softmax
   // with a single rescale.
   for (int kb = k0; kb < k1; kb += SLOTS * U) {
-    Raw<T, CE, true> kr[U], vr[U];
-    load_pass<T, CE, U, SLOTS, HD>(kr, vr, Kb, Vb, kb, r, k1);
+    if (!kEarly || kb != k0) load_pass<T, CE, U, SLOTS, HD>(kr, vr, Kb, Vb, kb, r, k1);
     float kv[U][CE], vv[U][CE];
 #pragma unroll
     for (int u = 0; u < U; ++u) { kr[u].unpack(kv[u]); vr[u].unpack(vv[u]); }
