@@ -21,6 +21,20 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Four consecutive outputs in the storage dtype, one store (8 bytes for
+// bf16; the column is a multiple of 4 and rows are 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    uint2 pk;
+    pk.x = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+    pk.y = (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16);
+    *reinterpret_cast<uint2*>(p) = pk;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+}
+
 // Row epilogue, one workgroup per output row i (input row r = i*row_stride
 // + row_off), one float4 column group per thread:
 //   x = resid[r] + sum_s P[s][r] + E[ids[r]]  (each term optional; slabs
@@ -66,10 +80,7 @@ __global__ __launch_bounds__(1024) void rows_epilogue_kernel(RowsEpi e) {
   if (act) {
     T* orow = reinterpret_cast<T*>(e.a_out) + (int64_t)i * e.a_ld;
     const float4 gg = *reinterpret_cast<const float4*>(e.g + c);
-    orow[c + 0] = St<T>::st(gg.x * (acc.x * inv));
-    orow[c + 1] = St<T>::st(gg.y * (acc.y * inv));
-    orow[c + 2] = St<T>::st(gg.z * (acc.z * inv));
-    orow[c + 3] = St<T>::st(gg.w * (acc.w * inv));
+    store4<T>(orow + c, gg.x * (acc.x * inv), gg.y * (acc.y * inv), gg.z * (acc.z * inv), gg.w * (acc.w * inv));
   }
 }
 
