@@ -93,7 +93,9 @@ def test_recgen_after_releasing_prefill_weights():
     ref_model, ref_t, _ = gpu_generate(cfg, W, pr, 32, logits=False)
     model = Photon(cfg, W)
     model.prefill(torch.from_numpy(pr).cuda(), 64)
+    blob = model.w_prefill
     model.release_prefill_weights()
+    blob.fill_(0xFF)                        # NaN bit patterns: decoding must not read them
     out = torch.empty((2, 2, cfg.S), dtype=torch.int32, device="cuda")
     model.decode_chunk(out[0])
     model.decode_chunk(out[1])
@@ -104,6 +106,26 @@ def test_recgen_after_releasing_prefill_weights():
         model.decode_chunk(out[0])          # capacity: 64 tokens reached
     with pytest.raises(PhotonError):
         model.prefill(torch.from_numpy(pr).cuda(), 64)
+
+
+def test_recgen_three_levels_never_reads_the_lower_encoders():
+    # the prefill-only blob (every chunker and encoder below the top) is
+    # overwritten after the prefill: RecGen's tokens do not change
+    import torch
+    from hierarchical_autoregressive_lm_amd.photon import Photon
+    cfg = small_cfg(chunk=(2, 3, 2), n_enc_hi=(1,), n_dec_hi=(1,))
+    W, pr = _inputs(cfg, 2, 24, 10)
+    ref_model, ref_t, _ = gpu_generate(cfg, W, pr, 24, logits=False)
+    model = Photon(cfg, W)
+    model.prefill(torch.from_numpy(pr).cuda(), 48)
+    blob = model.w_prefill
+    model.release_prefill_weights()
+    blob.fill_(0xFF)
+    out = torch.empty((2, 2, cfg.S), dtype=torch.int32, device="cuda")
+    model.decode_chunk(out[0])
+    model.decode_chunk(out[1])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.permute(1, 0, 2).reshape(2, 24).cpu().numpy(), ref_t)
 
 
 def test_full_size_150m_sampled_sequences():
