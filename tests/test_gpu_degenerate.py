@@ -1,0 +1,40 @@
+"""Degenerate hierarchy shapes on the GPU against the oracle (tiny fp32
+models, exact ids): chunks of one state at either level (the chunker and
+converter become square d x d maps), one-chunk prompts and generations, a
+batch of one, and a three-level model whose middle level has chunks of one.
+"""
+import pytest
+
+import photon_inputs as pi
+from parity import check_against_oracle, gpu_generate
+
+pytestmark = pytest.mark.gpu
+
+TINY = pi.CONFIGS["tiny"]
+
+CASES = [
+    # chunk, batch, prompt chunks, new chunks, mode
+    ((1, 4), 2, 3, 4, "recgen"),
+    ((4, 1), 2, 3, 4, "recgen"),
+    ((1, 1), 2, 5, 6, "recgen"),
+    ((1, 4), 2, 3, 4, "hiergen"),
+    ((4, 1), 2, 3, 4, "hiergen"),
+    ((1, 1), 1, 4, 4, "hiergen"),
+    ((4, 4), 1, 1, 1, "recgen"),        # one-chunk prompt and generation, batch of one
+    ((4, 4), 1, 1, 1, "hiergen"),
+    ((2, 1, 2), 2, 2, 3, "recgen"),     # a middle level with chunks of one
+    ((2, 1, 2), 2, 2, 3, "hiergen"),
+]
+
+
+@pytest.mark.parametrize("chunk,B,pc,nc,mode", CASES,
+                         ids=[f"{'x'.join(map(str, c))}-B{b}-{m}" for c, b, _, _, m in CASES])
+def test_degenerate_shapes_exact_ids(chunk, B, pc, nc, mode):
+    k = len(chunk) - 2
+    cfg = TINY.with_(chunk=chunk, n_enc_hi=(1,) * k, n_dec_hi=(1,) * k)
+    S = cfg.S
+    W, pr = pi.gen_weights(cfg, 41), pi.gen_prompts(cfg, B, pc * S, 41)
+    model, toks, lg = gpu_generate(cfg, W, pr, nc * S, mode)
+    r = check_against_oracle(cfg, W, pr, toks, lg, mode)
+    print(f"[degenerate] {chunk} B{B} {mode}: max_err={r['max_err']:.3g}", flush=True)
+    assert r["near_ties"] == 0
