@@ -289,13 +289,13 @@ constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 
 
 #define PH_LDS_SLOTS(X) X(0) X(1) X(2) X(3) X(4) X(5)
 
-template <int BM, int BN, int WM, int P, int EPI, int NKB>
-__global__ __launch_bounds__(256) void gemm_lds_kernel(GemmP p) {
-  constexpr int WN = 4 / WM, TM = BM / WM, TN = BN / WN, MF = TM / 16, NF = TN / 16;
+template <int BM, int BN, int WM, int P, int EPI, int NKB, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
+  constexpr int WN = NW / WM, TM = BM / WM, TN = BN / WN, MF = TM / 16, NF = TN / 16;
   constexpr int ROWS = BM + BN;             // A rows, then W rows; 128 B each
   constexpr int SLOT_U4 = ROWS * 8;         // 16-byte units per slot
-  constexpr int I = ROWS / 32;              // direct-load instructions per wave per stage
-  static_assert(ROWS % 32 == 0 && TM % 16 == 0 && TN % 16 == 0 && P >= 2 && P <= 6, "tile");
+  constexpr int I = ROWS / (8 * NW);        // direct-load instructions per wave per stage
+  static_assert(ROWS % (8 * NW) == 0 && TM % 16 == 0 && TN % 16 == 0 && P >= 2 && P <= 6, "tile");
   static_assert(EPI != EPI_ARGMAX || 2 * WN * BM * 4 <= ROWS * 128, "argmax partials fit a slot");
 #define PH_DECL(s) __shared__ __attribute__((aligned(16))) uint4 L##s[s < P ? SLOT_U4 : 1];
   PH_LDS_SLOTS(PH_DECL)
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmP p) {
       if ((lane >> 4) == 0) { bv[wn * BM + rl] = best; bi[wn * BM + rl] = bidx; }
     }
     __syncthreads();
-    for (int rl = tid; rl < BM; rl += 256) {
+    for (int rl = tid; rl < BM; rl += NW * 64) {
       const int row = m0 + rl;
       if (row >= p.M) continue;
       float best = bv[rl];
@@ -524,6 +524,7 @@ typedef void (*GemmKernel)(GemmP);
 struct Plan {
   int MB, NI, WK, m_tiles, n_tiles, ksplit;
   GemmKernel fn;   // tuned instantiation (fully unrolled k loop), or null
+  int threads = 256;
 };
 
 // Tuned tiles for the decode GEMMs of the PHOTON model shapes (d = 768 and
@@ -682,12 +683,21 @@ Plan plan_bf16(int M, int N, int K, int epi, bool allow_split) {
     return Plan{t->MB, t->NI, t->WK, (M + BM - 1) / BM, (N + BN - 1) / BN, t->ks, t->fn};
   }
   // prompt-sized GEMMs (many row tiles): the LDS-streaming kernel with a run
-  // time k loop, 128 rows x 256 features per workgroup (one wave row, four
-  // 64-feature columns), three stages; 1.4-1.7x the register tiles
-  if (M >= kBigM && (K / 64) % kBigP == 0 && K % 64 == 0 && (epi == EPI_STORE || epi == EPI_GELU)) {
-    GemmKernel fn = epi == EPI_STORE ? gemm_lds_kernel<128, 256, 1, kBigP, EPI_STORE, 0>
-                                     : gemm_lds_kernel<128, 256, 1, kBigP, EPI_GELU, 0>;
-    return Plan{0, 0, 0, (M + 127) / 128, (N + 255) / 256, 1, fn};
+  // time k loop and eight waves (two per SIMD, so one's LDS reads overlap
+  // the other's matrix products): 256 x 256 tiles (4 x 2 waves of 64 x 128,
+  // two 64 KB stages) for outputs at least 4096 wide, else 128 x 256 (2 x 4
+  // waves of 64 x 64, three stages); 1.1-1.4x the four-wave 128 x 256 tile
+  if (M >= kBigM && K % 64 == 0 && (epi == EPI_STORE || epi == EPI_GELU)) {
+    if (N >= 4096 && (K / 64) % 2 == 0) {
+      GemmKernel fn = epi == EPI_STORE ? gemm_lds_kernel<256, 256, 4, 2, EPI_STORE, 0, 8>
+                                       : gemm_lds_kernel<256, 256, 4, 2, EPI_GELU, 0, 8>;
+      return Plan{0, 0, 0, (M + 255) / 256, (N + 255) / 256, 1, fn, 512};
+    }
+    if ((K / 64) % kBigP == 0) {
+      GemmKernel fn = epi == EPI_STORE ? gemm_lds_kernel<128, 256, 2, kBigP, EPI_STORE, 0, 8>
+                                       : gemm_lds_kernel<128, 256, 2, kBigP, EPI_GELU, 0, 8>;
+      return Plan{0, 0, 0, (M + 127) / 128, (N + 255) / 256, 1, fn, 512};
+    }
   }
   Plan best{};
   const int MB0 = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : M <= 128 ? 8 : 16;
@@ -798,7 +808,7 @@ hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
           g.C, g.ldc, (bf16_t*)g.Cb, g.amax_val, g.amax_idx, pl.m_tiles, pl.n_tiles,
           pl.ksplit, (int64_t)g.M * g.ldc};
   if (pl.fn) {
-    PH_LAUNCH(pl.fn, pl.m_tiles * pl.n_tiles * pl.ksplit, 256, 0, st, p);
+    PH_LAUNCH(pl.fn, pl.m_tiles * pl.n_tiles * pl.ksplit, pl.threads, 0, st, p);
     return hipGetLastError();
   }
   switch (pl.MB) {
