@@ -581,44 +581,46 @@ struct Plan {
 // than every register-streaming tile above, same conditions (weights
 // rotated past the Infinity Cache).  Fields: M, N, K, epilogue, whether the
 // entry splits K into slabs, then rows x features per workgroup (BM, BN),
-// waves along M (WM; 4 / WM along N), ring depth P, K slabs, k-blocks per
-// workgroup; the comment gives the register kernel's time and this one's.
+// waves along M (WM; NW / WM along N), ring depth P, K slabs, k-blocks per
+// workgroup, waves per workgroup (NW: 4, or 8 for two per SIMD); the
+// comment gives the register kernel's time and this one's.
 #define PHOTON_GEMM_LDS_TUNED(X) \
-  X(32, 768, 768, EPI_STORE, 1, 32, 32, 2, 4, 4, 3) /* 3.8 -> 2.7 us */ \
-  X(32, 768, 3072, EPI_STORE, 1, 32, 32, 2, 6, 8, 6) /* 4.5 -> 3.2 us */ \
-  X(32, 2304, 768, EPI_STORE, 1, 32, 64, 1, 4, 4, 3) /* 3.8 -> 3.2 us */ \
-  X(32, 3072, 768, EPI_GELU, 0, 32, 32, 2, 6, 1, 12) /* 5.4 -> 3.9 us */ \
-  X(32, 3072, 768, EPI_STORE, 1, 32, 32, 2, 6, 2, 6) /* 4.2 -> 3.2 us */ \
-  X(64, 1536, 1536, EPI_STORE, 1, 32, 64, 1, 6, 4, 6) /* 4.9 -> 3.5 us */ \
-  X(64, 1536, 6144, EPI_STORE, 1, 64, 64, 2, 6, 8, 12) /* 10.0 -> 7.1 us */ \
-  X(64, 4608, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12) /* 7.8 -> 5.3 us */ \
-  X(64, 6144, 1536, EPI_GELU, 0, 64, 32, 2, 6, 1, 24) /* 12.9 -> 8.9 us */ \
-  X(64, 6144, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12) /* 9.9 -> 7.6 us */ \
-  X(64, 6144, 1536, EPI_STORE, 0, 64, 32, 2, 6, 1, 24) /* 10.9 -> 8.0 us */ \
-  X(64, 32000, 1536, EPI_ARGMAX, 0, 64, 128, 2, 4, 1, 24) /* 25.1 -> 22.8 us */ \
-  X(128, 768, 768, EPI_STORE, 1, 32, 32, 2, 6, 2, 6) /* 4.0 -> 3.1 us */ \
-  X(128, 768, 3072, EPI_STORE, 1, 64, 32, 2, 6, 4, 12) /* 6.1 -> 4.2 us */ \
-  X(128, 2304, 768, EPI_STORE, 1, 32, 32, 2, 4, 2, 6) /* 5.5 -> 4.0 us */ \
-  X(128, 3072, 768, EPI_GELU, 0, 32, 32, 2, 6, 1, 12) /* 7.8 -> 4.8 us */ \
-  X(128, 3072, 768, EPI_STORE, 1, 64, 32, 4, 6, 1, 12) /* 6.0 -> 4.1 us */ \
-  X(128, 3072, 768, EPI_STORE, 0, 32, 64, 2, 6, 1, 12) /* 7.1 -> 4.2 us */ \
-  X(128, 32000, 768, EPI_ARGMAX, 0, 128, 128, 2, 4, 1, 12) /* 20.4 -> 17.2 us */ \
-  X(256, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 4, 2, 12) /* 8.5 -> 5.2 us */ \
-  X(256, 1536, 3072, EPI_STORE, 1, 64, 64, 2, 6, 2, 24) /* 12.0 -> 7.0 us */ \
-  X(256, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 8, 12) /* 17.0 -> 12.9 us */ \
-  X(256, 3072, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24) /* 11.9 -> 7.0 us */ \
-  X(256, 4608, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24) /* 14.0 -> 9.7 us */ \
-  X(256, 6144, 1536, EPI_GELU, 0, 128, 64, 4, 4, 1, 24) /* 22.2 -> 17.1 us */ \
-  X(256, 6144, 1536, EPI_STORE, 1, 128, 128, 2, 4, 2, 12) /* 17.1 -> 13.3 us */ \
-  X(256, 6144, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24) /* 19.1 -> 13.8 us */ \
-  X(512, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24) /* 12.8 -> 6.9 us */ \
-  X(512, 1536, 3072, EPI_STORE, 1, 128, 64, 4, 4, 2, 24) /* 16.5 -> 10.2 us */ \
-  X(512, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 4, 24) /* 25.7 -> 18.9 us */ \
-  X(512, 3072, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24) /* 16.9 -> 9.9 us */ \
-  X(512, 3072, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24) /* 18.5 -> 10.1 us */ \
-  X(512, 4608, 1536, EPI_STORE, 1, 64, 64, 4, 3, 2, 12) /* 20.7 -> 15.0 us */ \
-  X(512, 6144, 1536, EPI_GELU, 0, 64, 64, 2, 3, 1, 24) /* 32.5 -> 23.5 us */ \
-  X(512, 32000, 1536, EPI_ARGMAX, 0, 128, 128, 2, 4, 1, 24) /* 83.0 -> 78.8 us */
+  X(32, 768, 768, EPI_STORE, 1, 32, 32, 2, 4, 4, 3, 4) /* 3.8 -> 2.7 us */ \
+  X(32, 768, 3072, EPI_STORE, 1, 32, 32, 2, 6, 8, 6, 4) /* 4.5 -> 3.2 us */ \
+  X(32, 2304, 768, EPI_STORE, 1, 32, 64, 1, 4, 4, 3, 4) /* 3.8 -> 3.2 us */ \
+  X(32, 3072, 768, EPI_GELU, 0, 32, 32, 2, 6, 1, 12, 4) /* 5.4 -> 3.9 us */ \
+  X(32, 3072, 768, EPI_STORE, 1, 32, 32, 2, 6, 2, 6, 4) /* 4.2 -> 3.2 us */ \
+  X(64, 1536, 1536, EPI_STORE, 1, 32, 64, 1, 6, 4, 6, 4) /* 4.9 -> 3.5 us */ \
+  X(64, 1536, 6144, EPI_STORE, 1, 64, 64, 2, 6, 8, 12, 4) /* 10.0 -> 7.1 us */ \
+  X(64, 4608, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12, 4) /* 7.8 -> 5.3 us */ \
+  X(64, 6144, 1536, EPI_GELU, 0, 64, 32, 2, 6, 1, 24, 4) /* 12.9 -> 8.9 us */ \
+  X(64, 6144, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12, 4) /* 9.9 -> 7.6 us */ \
+  X(64, 6144, 1536, EPI_STORE, 0, 64, 32, 2, 6, 1, 24, 4) /* 10.9 -> 8.0 us */ \
+  X(64, 32000, 1536, EPI_ARGMAX, 0, 64, 128, 2, 4, 1, 24, 4) /* 25.1 -> 22.8 us */ \
+  X(128, 768, 768, EPI_STORE, 1, 32, 32, 2, 6, 2, 6, 4) /* 4.0 -> 3.1 us */ \
+  X(128, 768, 3072, EPI_STORE, 1, 64, 32, 2, 6, 4, 12, 4) /* 6.1 -> 4.2 us */ \
+  X(128, 2304, 768, EPI_STORE, 1, 32, 32, 2, 4, 2, 6, 4) /* 5.5 -> 4.0 us */ \
+  X(128, 3072, 768, EPI_GELU, 0, 32, 32, 2, 6, 1, 12, 4) /* 7.8 -> 4.8 us */ \
+  X(128, 3072, 768, EPI_STORE, 1, 64, 32, 4, 6, 1, 12, 4) /* 6.0 -> 4.1 us */ \
+  X(128, 3072, 768, EPI_STORE, 0, 32, 64, 2, 6, 1, 12, 4) /* 7.1 -> 4.2 us */ \
+  X(128, 32000, 768, EPI_ARGMAX, 0, 128, 128, 4, 4, 1, 12, 8) /* 20.4 -> 17.2 us; 8 waves, later run: 15.1 -> 13.7 us */ \
+  X(256, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 4, 2, 12, 4) /* 8.5 -> 5.2 us */ \
+  X(256, 32000, 1536, EPI_ARGMAX, 0, 256, 128, 4, 3, 1, 24, 8) /* 8 waves against the register tile: 44.3 -> 32.0 us */ \
+  X(256, 1536, 3072, EPI_STORE, 1, 64, 64, 2, 6, 2, 24, 4) /* 12.0 -> 7.0 us */ \
+  X(256, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 8, 12, 4) /* 17.0 -> 12.9 us */ \
+  X(256, 3072, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24, 4) /* 11.9 -> 7.0 us */ \
+  X(256, 4608, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24, 4) /* 14.0 -> 9.7 us */ \
+  X(256, 6144, 1536, EPI_GELU, 0, 128, 64, 4, 4, 1, 24, 4) /* 22.2 -> 17.1 us */ \
+  X(256, 6144, 1536, EPI_STORE, 1, 128, 128, 2, 4, 2, 12, 4) /* 17.1 -> 13.3 us */ \
+  X(256, 6144, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24, 4) /* 19.1 -> 13.8 us */ \
+  X(512, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24, 4) /* 12.8 -> 6.9 us */ \
+  X(512, 1536, 3072, EPI_STORE, 1, 128, 64, 4, 4, 2, 24, 4) /* 16.5 -> 10.2 us */ \
+  X(512, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 4, 24, 4) /* 25.7 -> 18.9 us */ \
+  X(512, 3072, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24, 4) /* 16.9 -> 9.9 us */ \
+  X(512, 3072, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24, 4) /* 18.5 -> 10.1 us */ \
+  X(512, 4608, 1536, EPI_STORE, 1, 64, 64, 4, 3, 2, 12, 4) /* 20.7 -> 15.0 us */ \
+  X(512, 6144, 1536, EPI_GELU, 0, 64, 64, 2, 3, 1, 24, 4) /* 32.5 -> 23.5 us */ \
+  X(512, 32000, 1536, EPI_ARGMAX, 0, 256, 128, 4, 3, 1, 24, 8) /* 83.0 -> 78.8 us; 8 waves, later run: 73.9 -> 53.8 us */
 
 struct Tuned {
   int M, N, K, epi, split, MB, NI, WK, P, ks, nkb;
@@ -626,11 +628,11 @@ struct Tuned {
   GemmKernel fn;
 };
 struct TunedL {
-  int M, N, K, epi, split, BM, BN, WM, P, ks, nkb;
+  int M, N, K, epi, split, BM, BN, WM, P, ks, nkb, nw;
   GemmKernel fn;
 };
-#define PHOTON_LDS_ENTRY(M_, N_, K_, E_, S_, BM_, BN_, WM_, P_, KS_, NKB_) \
-  {M_, N_, K_, E_, S_, BM_, BN_, WM_, P_, KS_, NKB_, gemm_lds_kernel<BM_, BN_, WM_, P_, E_, NKB_>},
+#define PHOTON_LDS_ENTRY(M_, N_, K_, E_, S_, BM_, BN_, WM_, P_, KS_, NKB_, NW_) \
+  {M_, N_, K_, E_, S_, BM_, BN_, WM_, P_, KS_, NKB_, NW_, gemm_lds_kernel<BM_, BN_, WM_, P_, E_, NKB_, NW_>},
 const TunedL kTunedL[] = {PHOTON_GEMM_LDS_TUNED(PHOTON_LDS_ENTRY)};
 #undef PHOTON_LDS_ENTRY
 
@@ -677,7 +679,7 @@ int wk_of(int MB, int K) {
 // K into slabs (RAW partials, summed by the consumer).
 Plan plan_bf16(int M, int N, int K, int epi, bool allow_split) {
   if (const TunedL* t = find_tuned_lds(M, N, K, epi, allow_split))
-    return Plan{0, 0, 0, (M + t->BM - 1) / t->BM, (N + t->BN - 1) / t->BN, t->ks, t->fn};
+    return Plan{0, 0, 0, (M + t->BM - 1) / t->BM, (N + t->BN - 1) / t->BN, t->ks, t->fn, 64 * t->nw};
   if (const Tuned* t = find_tuned(M, N, K, epi, allow_split)) {
     const int BM = 16 * t->MB, BN = 16 * t->NI * (4 / t->WK);
     return Plan{t->MB, t->NI, t->WK, (M + BM - 1) / BM, (N + BN - 1) / BN, t->ks, t->fn};
