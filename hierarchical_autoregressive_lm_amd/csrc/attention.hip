@@ -15,8 +15,9 @@
 //    of the pair for hd/16 contiguous elements (non-temporal loads), so
 //    scores need one 16-lane reduction and the output is lane-local; 4 pairs
 //    per wave.
-//  * attn_prefill: causal attention over a whole prompt, fp32 FMA, 64
-//    queries per workgroup with K/V tiles of 64 keys staged in LDS.
+//  * attn_prefill: causal attention over a whole prompt with K/V tiles of
+//    64 keys staged in LDS: MFMA on bf16 caches (128 queries per
+//    workgroup), fp32 FMA on fp32 caches (64 queries per workgroup).
 // q is fp32 everywhere; K and V are read in the storage dtype; softmax and
 // accumulation are fp32; the output is rounded to the storage dtype.
 #include "common.h"
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnCall a, float sca
 // q and p are float32 in the rounding contract; each enters the products as
 // hi + lo, two bf16 terms (hi = bf16(x), lo = bf16(x - hi): 16 significant
 // bits), so every product is two MFMAs accumulating in float32.
-// A workgroup: 4 waves x NQ blocks of 16 queries of one (sequence, head);
+// A workgroup: NWV waves x NQ blocks of 16 queries of one (sequence, head);
 // K and V tiles of 64 keys staged in LDS (K row-major, V transposed),
 // double-buffered; query blocks run heaviest (last) first.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -533,17 +534,19 @@ __device__ __forceinline__ void split_hi_lo(float x, bf16_t& hi, bf16_t& lo) {
   lo = f2bf(x - bf2f(hi));
 }
 
-template <int HD, int NQ>
-__global__ __launch_bounds__(256, NQ == 1 ? 2 : 1) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
+template <int HD, int NQ, int NWV>
+__global__ __launch_bounds__(NWV * 64, (NQ == 1 && NWV <= 4) ? 2 : 1) void attn_prefill_mfma_kernel(AttnCall a,
+                                                                                                   float scale) {
+  constexpr int NT = NWV * 64;           // threads
   constexpr int TK = 64;                 // keys per tile
-  constexpr int BQ = 64 * NQ;            // queries per workgroup
+  constexpr int BQ = 16 * NQ * NWV;      // queries per workgroup
   constexpr int KS = HD / 32;            // k-steps of S^T
   constexpr int HB = HD / 16;            // 16-row blocks of O^T
   constexpr int KROW = HD + 8;           // padded K row (bf16)
   constexpr int VCOL = TK + 8;           // padded V^T row (bf16)
   constexpr int KCH = TK * HD / 8;       // 16-byte K chunks per tile
   constexpr int VCH = TK / 2 * HD / 8;   // (2 keys x 8 dims) V items per tile
-  constexpr int KPT = (KCH + 255) / 256, VPT = (VCH + 255) / 256;
+  constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TK][KROW];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][HD][VCOL];
 
@@ -595,7 +598,7 @@ __global__ __launch_bounds__(256, NQ == 1 ? 2 : 1) void attn_prefill_mfma_kernel
     const int k0 = t * TK;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + 256 * i;
+      const int ch = tid + NT * i;
       const int key = ch / (HD / 8), c8 = ch % (HD / 8);
       if (ch < KCH && k0 + key < T)
         kreg[i] = *reinterpret_cast<const uint4*>(Kb + (int64_t)(k0 + key) * HD + 8 * c8);
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(256, NQ == 1 ? 2 : 1) void attn_prefill_mfma_kernel
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int it = tid + 256 * i;
+      const int it = tid + NT * i;
       const int kp = it / (HD / 8), c8 = it % (HD / 8);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -619,13 +622,13 @@ __global__ __launch_bounds__(256, NQ == 1 ? 2 : 1) void attn_prefill_mfma_kernel
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + 256 * i;
+      const int ch = tid + NT * i;
       const int key = ch / (HD / 8), c8 = ch % (HD / 8);
       if (ch < KCH) *reinterpret_cast<uint4*>(&Ks[buf][key][8 * c8]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int it = tid + 256 * i;
+      const int it = tid + NT * i;
       const int kp = it / (HD / 8), c8 = it % (HD / 8);
       if (it < VCH) {
         const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
@@ -792,10 +795,12 @@ template <typename T, int HD>
 hipError_t prefill_hd(const AttnCall& a, hipStream_t st) {
   const float scale = 1.0f / sqrtf((float)HD);
   if constexpr (sizeof(T) == 2 && HD % 32 == 0) {
-    // bf16 caches: MFMA kernel, 64 queries per workgroup (16 per wave), two
-    // waves per SIMD so one's softmax overlaps the other's matrix products
-    const int nqb = (a.Q + 63) / 64;
-    PH_LAUNCH((attn_prefill_mfma_kernel<HD, 1>), a.G * a.H * nqb, 256, 0, st, a, scale);
+    // bf16 caches: MFMA kernel, 16 queries per wave, 8 waves (two per SIMD,
+    // so one's softmax overlaps the other's matrix products) sharing each
+    // staged K/V tile: half the LDS fills per query of 4 waves
+    constexpr int kWaves = 8;
+    const int nqb = (a.Q + 16 * kWaves - 1) / (16 * kWaves);
+    PH_LAUNCH((attn_prefill_mfma_kernel<HD, 1, kWaves>), a.G * a.H * nqb, 64 * kWaves, 0, st, a, scale);
   } else {
     const int nqb = (a.Q + 63) / 64;
     PH_LAUNCH((attn_prefill_kernel<T, HD>), a.G * a.H * nqb, 256, 0, st, a, scale);
