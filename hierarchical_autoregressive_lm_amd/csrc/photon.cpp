@@ -549,13 +549,27 @@ struct photon_ctx {
   photon_sampling samp{};
   unsigned char* sws = nullptr;
   uint64_t sws_bytes = 0;
-  // one decode chunk captured as a HIP graph, replayed for every chunk
+  // one decode chunk captured as HIP graphs, replayed for every chunk: each
+  // graph is one chain of kernels (the runtime replays a chain from packets
+  // it recorded at instantiation, a few tenths of a microsecond of host time
+  // per kernel, while a graph with parallel branches is submitted kernel by
+  // kernel at several microseconds each); RecGen's two branches are two
+  // graphs on two streams, ordered by events.  Slots: the chunk's prefix
+  // (or the whole chunk: HierGen, the flat baseline), the token branch, the
+  // top branch.
   bool use_graph = true;
-  hipGraphExec_t graph = nullptr;
+  hipGraphExec_t graph[3] = {nullptr, nullptr, nullptr};
   hipStream_t cap[2] = {nullptr, nullptr};
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  void drop_graphs() {
+    for (auto& g : graph)
+      if (g) {
+        (void)hipGraphExecDestroy(g);
+        g = nullptr;
+      }
+  }
   ~photon_ctx() {
-    if (graph) (void)hipGraphExecDestroy(graph);
+    drop_graphs();
     for (auto s : cap)
       if (s) (void)hipStreamDestroy(s);
     if (ev_fork) (void)hipEventDestroy(ev_fork);
@@ -1014,10 +1028,7 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
   unsigned char* ws = (unsigned char*)d_workspace;
   unsigned char* sc = (unsigned char*)d_scratch;
   c->prefilled = false;
-  if (c->graph) {
-    (void)hipGraphExecDestroy(c->graph);
-    c->graph = nullptr;
-  }
+  c->drop_graphs();
   c->ws = ws;
   c->plan = wp;
   c->mode = mode;
@@ -1140,7 +1151,13 @@ photon_status enqueue_decoders(photon_ctx* c, const StackBufs& bufs, hipStream_t
 // sequential order: the two branches share no buffer (A-hat_i is consumed by
 // Converter^1 before the fork and by the feedback GEMM before the decoders
 // of the top branch overwrite it).
-photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipStream_t st_top, int given_r = 0) {
+// `parts` selects what is enqueued: the prefix (HierGen's decoders, then
+// Converter^1 and the first token step's input), the token branch, the top
+// branch, the position update; the fork and join events only when all four
+// are (the graph replay orders its separately captured parts itself).
+enum { kPartPre = 1, kPartTok = 2, kPartTop = 4, kPartEnd = 8, kPartAll = 15 };
+photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipStream_t st_top, int given_r = 0,
+                            int parts = kPartAll) {
   const photon_config& cf = c->cfg;
   const Levels lv = levels(&cf);
   const int L = lv.L, C1 = lv.C[1], CL = lv.C[L], K1 = (int)lv.K1();
@@ -1162,10 +1179,10 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
                ws + wp.oA.off, ws + wp.hidA.off, (float*)(ws + wp.apartA.off)};
   int ks = 1;
 
-  if (!recgen) PH_TRY(enqueue_decoders(c, sb, st));
+  if ((parts & kPartPre) && !recgen) PH_TRY(enqueue_decoders(c, sb, st));
   // Converter^1 (all C1 conditioning vectors of every level-1 position) and
   // the first token step's input
-  {
+  if (parts & kPartPre) {
     GemmCall g{};
     g.dtype = dt; g.A = ws + wp.Ahat[1].off; g.lda = d; g.W = c->W_cv[1]; g.M = MB; g.N = C1 * d; g.K = d;
     g.epi = EPI_STORE; g.C = c0; g.ldc = (int64_t)C1 * d;
@@ -1176,13 +1193,13 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     e.R = MB; e.d = d; e.row_stride = 1; e.row_off = 0; e.eps = cf.norm_eps;
     PH_TRY(rows_epi(c, e, st));
   }
-  const bool fork = recgen && st_top != st;
+  const bool fork = recgen && st_top != st && parts == kPartAll;
   if (fork) {
     HIP_TRY(hipEventRecord(c->ev_fork, st));
     HIP_TRY(hipStreamWaitEvent(st_top, c->ev_fork, 0));
   }
   // token branch: C1 sequential token-decoder steps
-  for (int j = 0; j < C1; ++j) {
+  for (int j = 0; j < ((parts & kPartTok) ? C1 : 0); ++j) {
     StackRun r{};
     r.M = MB; r.rows_per_seq = 1; r.G = MB;
     r.kv = KvTarget{ws + wp.dec_kv.off, (int64_t)MB * H * C1 * hd, true, (int64_t)H * C1 * hd, C1, 0};
@@ -1221,7 +1238,9 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
   // top branch (RecGen: independent of the tokens, so it may run beside the
   // token branch on its own stream; its counter update closes it)
   const hipStream_t stt = fork ? st_top : st;
-  if (recgen) {
+  if (!(parts & kPartTop)) {
+    // not enqueued here
+  } else if (recgen) {
     // feedback: u_i = Chunker^L(A-hat_i), nothing re-encoded
     PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, Ahat_top, (int64_t)CL * d, c->W_ch[L], B, d, CL * d, sa.part, &ks, stt));
     PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
@@ -1252,7 +1271,7 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, in, (int64_t)CL * d, c->W_ch[L], B, d, CL * d, sa.part, &ks, stt));
     PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
   }
-  {
+  if (parts & kPartTop) {
     StackRun r{};
     r.M = B; r.rows_per_seq = 1; r.G = B;
     r.kv = KvTarget{ws + wp.top_kv.off, (int64_t)B * H * wp.top_cap * hd, true, (int64_t)H * wp.top_cap * hd,
@@ -1264,14 +1283,36 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     PH_TRY(run_stack(c, c->top, sa, r, stt));
   }
   // RecGen: the next chunk's decoders from h_i, still in the top branch
-  if (recgen) PH_TRY(enqueue_decoders(c, sa, stt));
+  if ((parts & kPartTop) && recgen) PH_TRY(enqueue_decoders(c, sa, stt));
   // the position advances once both branches are done: the sampler of the
   // token branch reads it while the top branch runs
   if (fork) {
     HIP_TRY(hipEventRecord(c->ev_join, st_top));
     HIP_TRY(hipStreamWaitEvent(st, c->ev_join, 0));
   }
-  HIP_TRY(launch_add_int(counter, 1, st));
+  if (parts & kPartEnd) HIP_TRY(launch_add_int(counter, 1, st));
+  return ok();
+}
+
+// Capture what `enqueue` puts on the context's capture stream as a graph
+// and instantiate it into *exec (left null on failure).
+extern "C++" template <class F>
+photon_status capture_graph(photon_ctx* c, hipGraphExec_t* exec, F&& enqueue) {
+  HIP_TRY(hipStreamBeginCapture(c->cap[0], hipStreamCaptureModeRelaxed));
+  const photon_status s = enqueue(c->cap[0]);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(c->cap[0], &g);
+  if (s != PHOTON_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return s;
+  }
+  if (e != hipSuccess) return fail(PHOTON_EHIP, "graph capture: %s", hipGetErrorString(e));
+  const hipError_t ie = hipGraphInstantiate(exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (ie != hipSuccess) {
+    *exec = nullptr;
+    return fail(PHOTON_EHIP, "graph instantiate: %s", hipGetErrorString(ie));
+  }
   return ok();
 }
 
@@ -1313,28 +1354,37 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
     // (direct launches; the captured graph serves the whole chunks)
     PH_TRY(enqueue_chunk(c, d_logits, st, st, c->tail_r));
   } else if (c->use_graph && !d_logits && c->tr.mask == 0) {
-    if (!c->graph) {
+    // RecGen: the prefix and the token branch on `st`, the top branch on a
+    // stream of the context, forked after the prefix and joined before the
+    // position update (the order enqueue_chunk's events give); HierGen: the
+    // whole chunk as one chain
+    const bool recgen = c->mode == PHOTON_RECGEN;
+    if (!c->graph[0]) {
       for (auto& cs : c->cap)
         if (!cs) HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
       if (!c->ev_fork) HIP_TRY(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming));
       if (!c->ev_join) HIP_TRY(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming));
-      HIP_TRY(hipStreamBeginCapture(c->cap[0], hipStreamCaptureModeRelaxed));
-      const photon_status s = enqueue_chunk(c, nullptr, c->cap[0], c->cap[1]);
-      hipGraph_t g = nullptr;
-      const hipError_t e = hipStreamEndCapture(c->cap[0], &g);
-      if (s != PHOTON_OK) {
-        if (g) (void)hipGraphDestroy(g);
-        return s;
-      }
-      if (e != hipSuccess) return fail(PHOTON_EHIP, "graph capture: %s", hipGetErrorString(e));
-      const hipError_t ie = hipGraphInstantiate(&c->graph, g, nullptr, nullptr, 0);
-      (void)hipGraphDestroy(g);
-      if (ie != hipSuccess) {
-        c->graph = nullptr;
-        return fail(PHOTON_EHIP, "graph instantiate: %s", hipGetErrorString(ie));
+      const int part[3] = {recgen ? (int)kPartPre : (int)kPartAll, kPartTok, kPartTop};
+      for (int i = 0; i < (recgen ? 3 : 1); ++i) {
+        const photon_status s = capture_graph(c, &c->graph[i], [&](hipStream_t cs) {
+          return enqueue_chunk(c, nullptr, cs, cs, 0, part[i]);
+        });
+        if (s != PHOTON_OK) {
+          c->drop_graphs();
+          return s;
+        }
       }
     }
-    HIP_TRY(hipGraphLaunch(c->graph, st));
+    HIP_TRY(hipGraphLaunch(c->graph[0], st));
+    if (recgen) {
+      HIP_TRY(hipEventRecord(c->ev_fork, st));
+      HIP_TRY(hipStreamWaitEvent(c->cap[1], c->ev_fork, 0));
+      HIP_TRY(hipGraphLaunch(c->graph[2], c->cap[1]));
+      HIP_TRY(hipEventRecord(c->ev_join, c->cap[1]));
+      HIP_TRY(hipGraphLaunch(c->graph[1], st));
+      HIP_TRY(hipStreamWaitEvent(st, c->ev_join, 0));
+      HIP_TRY(launch_add_int((int*)(c->ws + c->plan.counter.off), 1, st));
+    }
   } else {
     PH_TRY(enqueue_chunk(c, d_logits, st, st));
   }
@@ -1386,10 +1436,7 @@ photon_status photon_set_sampling(photon_ctx* c, const photon_sampling* sp, void
     if (!d_ws) return fail(PHOTON_EINVAL, "sampling workspace is NULL");
     if ((uintptr_t)d_ws % kAlign) return fail(PHOTON_EINVAL, "sampling workspace must be 256-byte aligned");
   }
-  if (c->graph) {
-    (void)hipGraphExecDestroy(c->graph);
-    c->graph = nullptr;
-  }
+  c->drop_graphs();
   c->sampling = sp != nullptr;
   c->samp = sp ? *sp : photon_sampling{};
   c->sws = sp ? (unsigned char*)d_ws : nullptr;
@@ -1719,10 +1766,7 @@ photon_status photon_vanilla_prefill(photon_ctx* c, void* d_workspace, uint64_t 
   unsigned char* ws = (unsigned char*)d_workspace;
   unsigned char* sc = (unsigned char*)d_scratch;
   c->prefilled = false;
-  if (c->graph) {
-    (void)hipGraphExecDestroy(c->graph);
-    c->graph = nullptr;
-  }
+  c->drop_graphs();
   c->ws = ws;
   c->vplan = wp;
   c->B = batch;
@@ -1773,25 +1817,11 @@ photon_status photon_vanilla_decode(photon_ctx* c, int32_t* d_tokens, float* d_l
   const int B = (int)c->B;
   int* tok = (int*)(c->ws + c->vplan.tok.off);
   if (c->use_graph && !d_logits && c->tr.mask == 0) {
-    if (!c->graph) {
+    if (!c->graph[0]) {
       if (!c->cap[0]) HIP_TRY(hipStreamCreateWithFlags(&c->cap[0], hipStreamNonBlocking));
-      HIP_TRY(hipStreamBeginCapture(c->cap[0], hipStreamCaptureModeRelaxed));
-      const photon_status s = enqueue_vanilla(c, nullptr, c->cap[0]);
-      hipGraph_t g = nullptr;
-      const hipError_t e = hipStreamEndCapture(c->cap[0], &g);
-      if (s != PHOTON_OK) {
-        if (g) (void)hipGraphDestroy(g);
-        return s;
-      }
-      if (e != hipSuccess) return fail(PHOTON_EHIP, "graph capture: %s", hipGetErrorString(e));
-      const hipError_t ie = hipGraphInstantiate(&c->graph, g, nullptr, nullptr, 0);
-      (void)hipGraphDestroy(g);
-      if (ie != hipSuccess) {
-        c->graph = nullptr;
-        return fail(PHOTON_EHIP, "graph instantiate: %s", hipGetErrorString(ie));
-      }
+      PH_TRY(capture_graph(c, &c->graph[0], [&](hipStream_t cs) { return enqueue_vanilla(c, nullptr, cs); }));
     }
-    HIP_TRY(hipGraphLaunch(c->graph, st));
+    HIP_TRY(hipGraphLaunch(c->graph[0], st));
   } else {
     PH_TRY(enqueue_vanilla(c, d_logits, st));
   }
