@@ -255,12 +255,16 @@ photon_status photon_position(const photon_ctx* ctx, int64_t* top_len,
 photon_status photon_set_position(photon_ctx* ctx, int64_t tokens,
                                   void* stream);
 
-/* Decode chunks run as one captured HIP graph by default: the first
+/* Decode chunks run as captured HIP graphs by default: the first
  * photon_decode_chunk after a prefill captures the chunk (its kernels read
- * every position from device memory, so the same graph serves every chunk)
- * and later calls replay it on the caller's stream; with RecGen the top
- * encoder step and the token decoder run as two parallel branches of the
- * graph.  RecGen's decoders above the token decoder read only the previous
+ * every position from device memory, so the same graphs serve every chunk)
+ * and later calls replay it.  Each graph is a single chain of kernels, which
+ * the runtime replays from packets recorded at instantiation.  HierGen: one
+ * graph on the caller's stream.  RecGen: the chunk's prefix and token
+ * decoder on the caller's stream, the top encoder step as a second graph on
+ * a stream of the context, forked after the prefix and joined before the
+ * position update through events, so the two run side by side and the
+ * caller's stream orders everything after the call.  RecGen's decoders above the token decoder read only the previous
  * top output, so the top branch of chunk i also runs them for chunk i+1
  * (from h_i) while chunk i's tokens are decoded; the first chunk after a
  * prefill or a photon_set_position runs them first.  The results are those
