@@ -583,7 +583,15 @@ struct Plan {
 // entry splits K into slabs, then rows x features per workgroup (BM, BN),
 // waves along M (WM; NW / WM along N), ring depth P, K slabs, k-blocks per
 // workgroup, waves per workgroup (NW: 4, or 8 for two per SIMD); the
-// comment gives the register kernel's time and this one's.
+// comment gives the register kernel's time and this one's (a second pair,
+// "8 waves, later run": the earlier 4-wave entry and this one, timed side by
+// side on one box).  Entries marked "wide" are 8-wave alternatives of a
+// 4-wave entry, taken when the caller asks for them (GemmCall::wide), with
+// the 4-wave entry's time and theirs, alone on one box: faster alone, they
+// speed up the decode chunk's critical path but slow its concurrent branch,
+// where they take more of each CU from the critical kernels (measured at 64
+// and 256 rows; at 128 rows they slowed the chunk in either branch, at 512
+// rows they sped it up in both).
 #define PHOTON_GEMM_LDS_TUNED(X) \
   X(32, 768, 768, EPI_STORE, 1, 32, 32, 2, 4, 4, 3, 4) /* 3.8 -> 2.7 us */ \
   X(32, 768, 3072, EPI_STORE, 1, 32, 32, 2, 6, 8, 6, 4) /* 4.5 -> 3.2 us */ \
@@ -591,8 +599,11 @@ struct Plan {
   X(32, 3072, 768, EPI_GELU, 0, 32, 32, 2, 6, 1, 12, 4) /* 5.4 -> 3.9 us */ \
   X(32, 3072, 768, EPI_STORE, 1, 32, 32, 2, 6, 2, 6, 4) /* 4.2 -> 3.2 us */ \
   X(64, 1536, 1536, EPI_STORE, 1, 32, 64, 1, 6, 4, 6, 4) /* 4.9 -> 3.5 us */ \
+  X(64, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 6, 4, 6, 8) /* wide: 4.7 -> 4.1 us */ \
   X(64, 1536, 6144, EPI_STORE, 1, 64, 64, 2, 6, 8, 12, 4) /* 10.0 -> 7.1 us */ \
+  X(64, 1536, 6144, EPI_STORE, 1, 64, 64, 2, 6, 8, 12, 8) /* wide: 8.6 -> 7.8 us */ \
   X(64, 4608, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12, 4) /* 7.8 -> 5.3 us */ \
+  X(64, 4608, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12, 8) /* wide: 7.8 -> 6.7 us */ \
   X(64, 6144, 1536, EPI_GELU, 0, 64, 32, 2, 6, 1, 24, 4) /* 12.9 -> 8.9 us */ \
   X(64, 6144, 1536, EPI_STORE, 1, 64, 64, 2, 6, 2, 12, 4) /* 9.9 -> 7.6 us */ \
   X(64, 6144, 1536, EPI_STORE, 0, 64, 32, 2, 6, 1, 24, 4) /* 10.9 -> 8.0 us */ \
@@ -605,21 +616,25 @@ struct Plan {
   X(128, 3072, 768, EPI_STORE, 0, 32, 64, 2, 6, 1, 12, 4) /* 7.1 -> 4.2 us */ \
   X(128, 32000, 768, EPI_ARGMAX, 0, 128, 128, 4, 4, 1, 12, 8) /* 20.4 -> 17.2 us; 8 waves, later run: 15.1 -> 13.7 us */ \
   X(256, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 4, 2, 12, 4) /* 8.5 -> 5.2 us */ \
+  X(256, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 4, 2, 12, 8) /* wide: 7.3 -> 5.2 us */ \
   X(256, 32000, 1536, EPI_ARGMAX, 0, 256, 128, 4, 3, 1, 24, 8) /* 8 waves against the register tile: 44.3 -> 32.0 us */ \
   X(256, 1536, 3072, EPI_STORE, 1, 64, 64, 2, 6, 2, 24, 4) /* 12.0 -> 7.0 us */ \
   X(256, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 8, 12, 4) /* 17.0 -> 12.9 us */ \
+  X(256, 1536, 6144, EPI_STORE, 1, 128, 128, 4, 4, 8, 12, 8) /* wide: 14.1 -> 13.0 us */ \
   X(256, 3072, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24, 4) /* 11.9 -> 7.0 us */ \
   X(256, 4608, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24, 4) /* 14.0 -> 9.7 us */ \
+  X(256, 4608, 1536, EPI_STORE, 1, 128, 128, 4, 4, 2, 12, 8) /* wide: 15.1 -> 12.1 us */ \
   X(256, 6144, 1536, EPI_GELU, 0, 128, 64, 4, 4, 1, 24, 4) /* 22.2 -> 17.1 us */ \
+  X(256, 6144, 1536, EPI_GELU, 0, 128, 64, 4, 4, 1, 24, 8) /* wide: 18.5 -> 15.0 us */ \
   X(256, 6144, 1536, EPI_STORE, 1, 128, 128, 2, 4, 2, 12, 4) /* 17.1 -> 13.3 us */ \
   X(256, 6144, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24, 4) /* 19.1 -> 13.8 us */ \
-  X(512, 1536, 1536, EPI_STORE, 1, 64, 64, 2, 6, 1, 24, 4) /* 12.8 -> 6.9 us */ \
+  X(512, 1536, 1536, EPI_STORE, 1, 128, 64, 4, 4, 2, 12, 8) /* 12.8 -> 6.9 us; 8 waves, later run: 10.3 -> 7.0 us */ \
   X(512, 1536, 3072, EPI_STORE, 1, 128, 64, 4, 4, 2, 24, 4) /* 16.5 -> 10.2 us */ \
-  X(512, 1536, 6144, EPI_STORE, 1, 128, 128, 2, 4, 4, 24, 4) /* 25.7 -> 18.9 us */ \
+  X(512, 1536, 6144, EPI_STORE, 1, 128, 128, 4, 4, 4, 24, 8) /* 25.7 -> 18.9 us; 8 waves, later run: 20.6 -> 19.3 us */ \
   X(512, 3072, 1536, EPI_STORE, 1, 128, 64, 4, 4, 1, 24, 4) /* 16.9 -> 9.9 us */ \
   X(512, 3072, 1536, EPI_STORE, 0, 128, 64, 4, 4, 1, 24, 4) /* 18.5 -> 10.1 us */ \
-  X(512, 4608, 1536, EPI_STORE, 1, 64, 64, 4, 3, 2, 12, 4) /* 20.7 -> 15.0 us */ \
-  X(512, 6144, 1536, EPI_GELU, 0, 64, 64, 2, 3, 1, 24, 4) /* 32.5 -> 23.5 us */ \
+  X(512, 4608, 1536, EPI_STORE, 1, 256, 128, 4, 3, 2, 12, 8) /* 20.7 -> 15.0 us; 8 waves, later run: 22.9 -> 17.8 us */ \
+  X(512, 6144, 1536, EPI_GELU, 0, 128, 128, 4, 4, 1, 24, 8) /* 32.5 -> 23.5 us; 8 waves, later run: 25.4 -> 21.2 us */ \
   X(512, 32000, 1536, EPI_ARGMAX, 0, 256, 128, 4, 3, 1, 24, 8) /* 83.0 -> 78.8 us; 8 waves, later run: 73.9 -> 53.8 us */
 
 struct Tuned {
@@ -636,12 +651,18 @@ struct TunedL {
 const TunedL kTunedL[] = {PHOTON_GEMM_LDS_TUNED(PHOTON_LDS_ENTRY)};
 #undef PHOTON_LDS_ENTRY
 
-const TunedL* find_tuned_lds(int M, int N, int K, int epi, bool allow_split) {
+const TunedL* find_tuned_lds(int M, int N, int K, int epi, bool allow_split, bool wide) {
   const TunedL* hit = nullptr;
+  int best = -1;
   for (const TunedL& t : kTunedL) {
     if (t.M != M || t.N != N || t.K != K || t.epi != epi) continue;
     if (t.split && !allow_split) continue;
-    if (!hit || (t.split && !hit->split)) hit = &t;
+    // slabs when the caller takes them, then the wave count it prefers
+    const int score = (t.split ? 2 : 0) + ((t.nw == 8) == wide ? 1 : 0);
+    if (score > best) {
+      best = score;
+      hit = &t;
+    }
   }
   return hit;
 }
@@ -677,8 +698,8 @@ int wk_of(int MB, int K) {
 // plan looks for enough workgroups to keep every CU streaming: the widest
 // column tile that still gives >= 256 workgroups, and otherwise a split of
 // K into slabs (RAW partials, summed by the consumer).
-Plan plan_bf16(int M, int N, int K, int epi, bool allow_split) {
-  if (const TunedL* t = find_tuned_lds(M, N, K, epi, allow_split))
+Plan plan_bf16(int M, int N, int K, int epi, bool allow_split, bool wide) {
+  if (const TunedL* t = find_tuned_lds(M, N, K, epi, allow_split, wide))
     return Plan{0, 0, 0, (M + t->BM - 1) / t->BM, (N + t->BN - 1) / t->BN, t->ks, t->fn, 64 * t->nw};
   if (const Tuned* t = find_tuned(M, N, K, epi, allow_split)) {
     const int BM = 16 * t->MB, BN = 16 * t->NI * (4 / t->WK);
@@ -784,12 +805,12 @@ int gemm_supported(int dtype, int M, int N, int K) {
 
 int gemm_argmax_tiles(int dtype, int M, int N, int K) {
   if (dtype == 0) return (N + 63) / 64;
-  return plan_bf16(M, N, K, EPI_ARGMAX, false).n_tiles;
+  return plan_bf16(M, N, K, EPI_ARGMAX, false, false).n_tiles;
 }
 
-int gemm_splits(int dtype, int M, int N, int K) {
+int gemm_splits(int dtype, int M, int N, int K, int wide) {
   if (dtype == 0) return 1;
-  return plan_bf16(M, N, K, EPI_STORE, true).ksplit;
+  return plan_bf16(M, N, K, EPI_STORE, true, wide != 0).ksplit;
 }
 
 hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
@@ -805,7 +826,7 @@ hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  const Plan pl = plan_bf16(g.M, g.N, g.K, g.epi, g.epi == EPI_STORE && g.allow_split);
+  const Plan pl = plan_bf16(g.M, g.N, g.K, g.epi, g.epi == EPI_STORE && g.allow_split, g.wide != 0);
   GemmP p{(const bf16_t*)g.A, g.lda, (const bf16_t*)g.W, g.M, g.N, g.K,
           g.C, g.ldc, (bf16_t*)g.Cb, g.amax_val, g.amax_idx, pl.m_tiles, pl.n_tiles,
           pl.ksplit, (int64_t)g.M * g.ldc};

@@ -43,6 +43,8 @@ enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_GELU = 2, EPI_ARGMAX = 3 };
 //   With allow_split (STORE only) K may be cut into gemm_splits() slabs; slab
 //   s then writes its raw partial sums to C + s*M*ldc and the consumer adds
 //   the slabs in order (deterministic).
+//   wide: prefer the 8-wave tiles where a shape has both (GEMMs on the
+//   critical path; the others leave more of each CU to concurrent work).
 struct GemmCall {
   int dtype;
   const void* A; int64_t lda;
@@ -53,10 +55,11 @@ struct GemmCall {
   void* Cb;
   float* amax_val; int* amax_idx;
   int allow_split;
+  int wide;
 };
 hipError_t launch_gemm(const GemmCall& g, hipStream_t st);
-// K slabs launch_gemm uses for a STORE GEMM with allow_split set.
-int gemm_splits(int dtype, int M, int N, int K);
+// K slabs launch_gemm uses for a STORE GEMM with allow_split (and wide) set.
+int gemm_splits(int dtype, int M, int N, int K, int wide);
 // Column tiles the ARGMAX epilogue produces for a GEMM of this shape.
 int gemm_argmax_tiles(int dtype, int M, int N, int K);
 // Host-side shape check: 0 when the GEMM kernels support (M, N, K).

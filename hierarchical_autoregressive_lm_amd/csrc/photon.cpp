@@ -217,9 +217,11 @@ struct Cursor {
   }
 };
 
-// bytes of the K-slab partials a STORE GEMM of this shape writes
+// bytes of the K-slab partials a STORE GEMM of this shape writes (with
+// either tile preference)
 uint64_t part_bytes(int dt, int64_t M, int64_t N, int64_t K) {
-  return (uint64_t)gemm_splits(dt, (int)M, (int)N, (int)K) * M * N * 4;
+  const int ks = std::max(gemm_splits(dt, (int)M, (int)N, (int)K, 0), gemm_splits(dt, (int)M, (int)N, (int)K, 1));
+  return (uint64_t)ks * M * N * 4;
 }
 
 // largest slab buffer any layer of a stack with M rows needs
@@ -558,6 +560,8 @@ struct photon_ctx {
   // (or the whole chunk: HierGen, the flat baseline), the token branch, the
   // top branch.
   bool use_graph = true;
+  // GEMMs enqueued meanwhile prefer their 8-wave tiles (WideGemms)
+  bool wide = false;
   hipGraphExec_t graph[3] = {nullptr, nullptr, nullptr};
   hipStream_t cap[2] = {nullptr, nullptr};
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -689,9 +693,22 @@ double gemm_bytes(const GemmCall& g) {
   return b;
 }
 
-photon_status run_gemm(photon_ctx* c, int cls, const GemmCall& g, hipStream_t st) {
+photon_status run_gemm(photon_ctx* c, int cls, GemmCall g, hipStream_t st) {
+  g.wide = c->wide;
   return traced(c, cls, gemm_bytes(g), 2.0 * g.M * g.N * g.K, st, "gemm", [&] { return launch_gemm(g, st); });
 }
+
+// While one is alive, the context's GEMMs prefer their 8-wave tiles: the
+// decode chunk's top stack and the decoders above the token decoder, its
+// critical path (the token decoder keeps the tiles that leave more of each
+// CU to the top branch running beside it).  Both modes set it on the same
+// GEMMs, so their top steps stay the same kernels.
+struct WideGemms {
+  photon_ctx* c;
+  bool prev;
+  explicit WideGemms(photon_ctx* c_) : c(c_), prev(c_->wide) { c->wide = true; }
+  ~WideGemms() { c->wide = prev; }
+};
 
 // Where a stack's K/V live.
 struct KvTarget {
@@ -746,7 +763,7 @@ photon_status gemm_slabs(photon_ctx* c, int cls, const void* A, int64_t lda, con
   GemmCall g{};
   g.dtype = c->cfg.dtype; g.A = A; g.lda = lda; g.W = W; g.M = M; g.N = N; g.K = K;
   g.epi = EPI_STORE; g.C = part; g.ldc = N; g.allow_split = 1;
-  *ks = gemm_splits(g.dtype, M, N, K);
+  *ks = gemm_splits(g.dtype, M, N, K, c->wide);
   return run_gemm(c, cls, g, st);
 }
 
@@ -1110,6 +1127,7 @@ photon_status photon_prefill(photon_ctx* c, int32_t mode, void* d_workspace, uin
 // C_l positions (attention confined to the group, positions 0 .. C_l-1, no
 // cache kept), down to the level-1 vectors (Ahat[1]).  Only h is read.
 photon_status enqueue_decoders(photon_ctx* c, const StackBufs& bufs, hipStream_t st) {
+  WideGemms wide(c);
   const photon_config& cf = c->cfg;
   const Levels lv = levels(&cf);
   const WsPlan& wp = c->plan;
@@ -1242,6 +1260,7 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     // not enqueued here
   } else if (recgen) {
     // feedback: u_i = Chunker^L(A-hat_i), nothing re-encoded
+    WideGemms wide(c);
     PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, Ahat_top, (int64_t)CL * d, c->W_ch[L], B, d, CL * d, sa.part, &ks, stt));
     PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
   } else {
@@ -1268,10 +1287,12 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
       PH_TRY(run_stack(c, c->enc[l], sa, r, stt));
       in = ws + wp.AA.off;
     }
+    WideGemms wide(c);
     PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_CHUNK, in, (int64_t)CL * d, c->W_ch[L], B, d, CL * d, sa.part, &ks, stt));
     PH_TRY(stack_input(c, c->top, sa.part, ks, B, sa.x, sa.a, stt));
   }
   if (parts & kPartTop) {
+    WideGemms wide(c);
     StackRun r{};
     r.M = B; r.rows_per_seq = 1; r.G = B;
     r.kv = KvTarget{ws + wp.top_kv.off, (int64_t)B * H * wp.top_cap * hd, true, (int64_t)H * wp.top_cap * hd,
