@@ -593,6 +593,10 @@ struct Plan {
 // and 256 rows; at 128 rows they slowed the chunk in either branch, at 512
 // rows they sped it up in both).
 #define PHOTON_GEMM_LDS_TUNED(X) \
+  X(16, 1536, 1536, EPI_STORE, 1, 32, 32, 2, 6, 4, 6, 4) /* 4.1 -> 3.1 us */ \
+  X(16, 1536, 6144, EPI_STORE, 1, 32, 64, 2, 6, 8, 12, 4) /* 7.7 -> 6.0 us */ \
+  X(16, 4608, 1536, EPI_STORE, 1, 32, 64, 2, 6, 2, 12, 4) /* 6.3 -> 5.6 us */ \
+  X(16, 6144, 1536, EPI_GELU, 0, 32, 32, 2, 6, 1, 24, 4) /* 8.2 -> 6.8 us */ \
   X(32, 768, 768, EPI_STORE, 1, 32, 32, 2, 4, 4, 3, 4) /* 3.8 -> 2.7 us */ \
   X(32, 768, 3072, EPI_STORE, 1, 32, 32, 2, 6, 8, 6, 4) /* 4.5 -> 3.2 us */ \
   X(32, 2304, 768, EPI_STORE, 1, 32, 64, 1, 4, 4, 3, 4) /* 3.8 -> 3.2 us */ \

@@ -6,7 +6,8 @@ request: the logits of the sampled rows come from a second, direct-launch
 run whose tokens must equal the graph run's).  The oracle then recomputes one
 sequence, teacher-forced with the GPU's tokens (see tests/parity.py).
 
-The photon-600m workload (P = 4096) runs by default; the long-context
+The photon-600m workload (P = 4096) runs by default, and the long-context
+workload's batch of 16 at a 512-token prompt; the long-context
 (P = 32768) and 2x2 (B = 256, P = 8192) workloads need several minutes of
 oracle time per sequence and run when PHOTON_FULLSIZE=1.
 """
@@ -22,30 +23,40 @@ pytestmark = pytest.mark.gpu
 LONG = os.environ.get("PHOTON_FULLSIZE") == "1"
 
 
-def run_full(idx, row, mode="recgen"):
+def run_full(idx, row, mode="recgen", prompt_len=None, new_tokens=None):
     import torch
     from hierarchical_autoregressive_lm_amd.photon import Photon
     wl = pi.get(idx)
+    P = prompt_len or wl.prompt
+    N = new_tokens or wl.new_tokens
     W = pi.gen_weights(wl.cfg, wl.seed)
-    pr = pi.gen_prompts(wl.cfg, wl.batch, wl.prompt, wl.seed)
+    pr = pi.gen_prompts(wl.cfg, wl.batch, P, wl.seed)
     model = Photon(wl.cfg, W)
     prompt = torch.from_numpy(pr).cuda()
-    toks_g, _ = model.generate(prompt, wl.new_tokens, mode=mode, logits=False)
-    toks_e, lg = model.generate(prompt, wl.new_tokens, mode=mode, logits=True)
+    toks_g, _ = model.generate(prompt, N, mode=mode, logits=False)
+    toks_e, lg = model.generate(prompt, N, mode=mode, logits=True)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(toks_g.cpu().numpy(), toks_e.cpu().numpy())
-    assert model.position() == (wl.max_tokens // wl.cfg.S, wl.max_tokens)
+    assert model.position() == ((P + N) // wl.cfg.S, P + N)
     t = toks_e[row:row + 1].cpu().numpy()
     l = lg[row:row + 1].cpu().numpy()
     del lg, model
     r = check_against_oracle(wl.cfg, W, pr[row:row + 1], t, l, mode,
                              log=lambda msg: print(f"[oracle] {msg}", flush=True))
-    print(f"[parity] {wl.name} {mode} row {row}: max_err={r['max_err']:.3g} "
+    print(f"[parity] {wl.name} (P {P}, N {N}) {mode} row {row}: max_err={r['max_err']:.3g} "
           f"noise_max={r['noise_max']:.3g} near_ties={r['near_ties']}/{r['tokens']}", flush=True)
 
 
 def test_photon600m_last_sequence():
     run_full(3, pi.get(3).batch - 1)
+
+
+@pytest.mark.parametrize("mode", ["recgen", "hiergen"])
+def test_photon600m_sixteen_sequences_short_prompt(mode):
+    # the long-context workload's batch of 16 (its top stack's 16-row GEMM
+    # tiles, 64-row token and upper decoders) at a prompt the oracle
+    # finishes in seconds
+    run_full(4, 5, mode, prompt_len=512, new_tokens=64)
 
 
 @pytest.mark.skipif(not LONG, reason="several minutes of oracle time; set PHOTON_FULLSIZE=1")
