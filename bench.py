@@ -42,8 +42,11 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sam
     """The oracle as it stands, RecGen decode phase only (perf_counter),
     prefill and weight setup untimed.  seqs = 0: one sequence is decoded
     first to size the sample, then as many sequences (up to the batch) as
-    fill about target_s seconds; when the whole batch takes less, its decode
-    is repeated from the same prefill state until target_s is filled."""
+    fill about target_s seconds at that rate, or the whole batch when that
+    rate puts it under 2 * target_s (a batch decodes faster per sequence
+    than one sequence alone); when the whole batch takes less than
+    target_s / 2, its decode is repeated from the same prefill state until
+    target_s is filled."""
     from threadpoolctl import threadpool_limits
     import photon_inputs as pi
     from oracle import photon_oracle as O
@@ -63,7 +66,8 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sam
         reps = 1
         if seqs <= 0:
             t1 = decode(prefill(m, prompt[:1]))
-            seqs = max(1, min(wl.batch, round(target_s / t1)))
+            fit = target_s / t1
+            seqs = wl.batch if fit >= wl.batch / 2 else max(1, min(wl.batch, round(fit)))
             if seqs == 1:
                 return wl.new_tokens / t1, t1, 1, 1
         st0 = prefill(m, prompt[:seqs])
