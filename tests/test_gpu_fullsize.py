@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import photon_inputs as pi
-from parity import check_against_oracle
+from parity import check_against_oracle, gpu_generate
 
 pytestmark = pytest.mark.gpu
 LONG = os.environ.get("PHOTON_FULLSIZE") == "1"
@@ -57,6 +57,24 @@ def test_photon600m_sixteen_sequences_short_prompt(mode):
     # tiles, 64-row token and upper decoders) at a prompt the oracle
     # finishes in seconds
     run_full(4, 5, mode, prompt_len=512, new_tokens=64)
+
+
+def test_photon600m_theorem_a6_bitwise():
+    # Theorem A.6 at the 600M shape with its batch of 64: with W_ch^2 = 0 the
+    # top encoder's input depends on neither A-hat nor A, so RecGen and
+    # HierGen give the same tokens, logits and top K/V bit for bit.  At this
+    # shape the top stack (64 rows) and the decoders above the token decoder
+    # (256 rows) run on their 8-wave tiles, which both modes must pick alike.
+    wl = pi.get(3)
+    W = pi.gen_weights(wl.cfg, wl.seed, zero=("W_ch2",))
+    pr = pi.gen_prompts(wl.cfg, wl.batch, 64, wl.seed)
+    m1, t1, l1 = gpu_generate(wl.cfg, W, pr, 32, "recgen")
+    kv1 = m1.top_kv().clone()
+    del m1
+    m2, t2, l2 = gpu_generate(wl.cfg, W, pr, 32, "hiergen")
+    assert bool((kv1 == m2.top_kv()).all())
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(l1, l2)
 
 
 @pytest.mark.skipif(not LONG, reason="several minutes of oracle time; set PHOTON_FULLSIZE=1")
