@@ -406,7 +406,7 @@ photon_status photon_sampling_bytes(const photon_config* cfg, int32_t batch,
  * memory of >= photon_sampling_bytes(cfg, batch) bytes, 256-byte aligned,
  * valid while sampling; a decode chunk with a larger batch than it holds
  * returns PHOTON_ECAPACITY.  Takes effect at the next decode chunk (the
- * captured graph is rebuilt).  PHOTON_ESTATE on a flat-baseline context. */
+ * captured graphs are rebuilt).  PHOTON_ESTATE on a flat-baseline context. */
 photon_status photon_set_sampling(photon_ctx* ctx, const photon_sampling* s,
                                   void* d_ws, uint64_t ws_bytes);
 /* photon_decode_chunk plus d_logprobs: NULL, or [batch][S] float32 out, the
