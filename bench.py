@@ -10,14 +10,18 @@ steps decode chunk after chunk from the prompt end, rewinding to the prompt
 end (restore h, reset the position) whenever the workload's new_tokens are
 used up, so every step runs at the workload's real cache lengths.
 
+The default workload is the largest one that fits one GPU: the 600M shape
+with 2x2 chunks, 256 sequences, 8192-token prompts and 512 new tokens.
+
 Prints one JSON line: decode tok/s (value), TPM = tok/s per GiB of resident
 decode weights + top K/V + decoder K/V + state, the whole path's fraction of
 the HBM roofline (algorithmic bytes per chunk at 8 TB/s), the achieved
 bandwidth of the kernel class that moves the most bytes (events recorded by
 every kernel dispatch, in a traced pass over the same steps right after the
-timed ones) against 8 TB/s and against a measured plain copy, per-class
-figures, and the CPU oracle timed on a bounded sample
-of the same workload.
+timed ones) against 8 TB/s and against a measured plain copy, the two
+attention kernels' own fractions, per-class figures, decode tok/s and TPM of
+every other workload (one timed pass each), and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 import argparse
 import json
@@ -78,6 +82,83 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sam
             reps = max(1, round(target_s / dt))
             dt += sum(decode(copy(st0)) for _ in range(reps - 1))
     return reps * seqs * wl.new_tokens / dt, dt, seqs, reps
+
+
+def cpu_baseline_injected(wl, W, threads, mode="recgen", target_s=15.0, sampling=None):
+    """The oracle as it stands, decode phase only (perf_counter), on the
+    fixed sample of sequences {0, B-1}, starting at the prompt end from the
+    seeded decode state the parity tests inject
+    (photon_inputs.gen_decode_state): the top K/V over the prompt's top
+    states, the last top output, and for HierGen the level-1 K/V.  The
+    oracle's prefill of even two sequences of the long prompts takes it many
+    minutes, and the decode work does not depend on the state's values.
+    Chunks are decoded in order until about target_s seconds are filled or
+    the workload's chunks are used up, and then again from the same state.
+    Returns (tok/s, seconds, sequences, chunks decoded)."""
+    from threadpoolctl import threadpool_limits
+    import photon_inputs as pi
+    from oracle import photon_oracle as O
+
+    rows = sorted({0, wl.batch - 1})
+    n = wl.prompt // wl.cfg.S
+    with threadpool_limits(limits=threads):
+        m = O.Model(wl.cfg, W)
+        seqs = [pi.gen_decode_state(wl.cfg, r, n, mode, wl.seed) for r in rows]
+        dt, done = 0.0, 0
+        while dt < target_s:
+            st = O.state_from_arrays(m, seqs)
+            for _ in range(wl.chunks):
+                t0 = time.perf_counter()
+                O.decode_chunk(m, st, mode, sampling=sampling)
+                dt += time.perf_counter() - t0
+                done += 1
+                if dt >= target_s:
+                    break
+    return len(rows) * wl.cfg.S * done / dt, dt, rows, done
+
+
+def per_config_lines(P, torch, skip, mode):
+    """Decode tok/s and TPM of every workload but `skip`: the workload's
+    seeded weights and prompts, prefill, one untimed pass over its chunks,
+    then one timed pass (graph replay, the headline's method)."""
+    import photon_inputs as pi
+    out = {}
+    for idx in sorted(pi.WORKLOADS):
+        if idx == skip:
+            continue
+        wl = pi.get(idx)
+        log(f"per-config line: {wl.name}")
+        W = pi.gen_weights(wl.cfg, wl.seed)
+        model = P.Photon(wl.cfg, W)
+        del W
+        model.prefill(torch.from_numpy(pi.gen_prompts(wl.cfg, wl.batch, wl.prompt, wl.seed)).cuda(),
+                      wl.max_tokens, mode)
+        if mode == "recgen":
+            model.release_prefill_weights()
+        snap = model.state_snapshot()
+        tok = torch.empty((wl.batch, wl.cfg.S), dtype=torch.int32, device="cuda")
+        for timed in (False, True):
+            model.state_restore(snap, wl.prompt)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(wl.chunks):
+                model.decode_chunk(tok)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+        rep = model.report(wl.batch, wl.max_tokens, mode)
+        resident = rep["weights_decode"] + rep["top_kv"] + rep["dec_kv"] + rep["state"]
+        if mode == "hiergen":
+            resident += rep["weights_prefill_only"] + rep["lower_kv"]
+        kv = rep["top_kv"] + rep["dec_kv"] + rep["lower_kv"]
+        tok_s = wl.batch * wl.new_tokens / dt
+        out[wl.name] = {"tok_s": round(tok_s, 1), "ms_per_step": round(dt / wl.chunks * 1e3, 4),
+                        "steps": wl.chunks, "dtype": "bf16" if wl.cfg.dtype == "bf16" else "f32",
+                        "tpm": round(tok_s / (resident / 2 ** 30), 1), "resident_gib": round(resident / 2 ** 30, 4),
+                        "tpm_kv_only": round(tok_s / (kv / 2 ** 30), 1)}
+        model.close()
+        del model, snap, tok
+        torch.cuda.empty_cache()
+    return out
 
 
 def host_info():
@@ -189,12 +270,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed decode chunks (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed decode chunks (default: the workload's)")
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: photon-150m B32 P1024 N256)")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1..5 (default 5: photon-600m-2x2 B256 P8192 N512, the largest single-GPU workload)")
     ap.add_argument("--mode", default="recgen", choices=["recgen", "hiergen", "vanilla"],
                     help="PHOTON RecGen / HierGen, or the flat Transformer baseline matched to the workload's "
                          "shape (same width, heads, vocabulary; as many layers as the PHOTON stacks)")
     ap.add_argument("--cpu-seqs", type=int, default=0,
-                    help="sequences in the oracle's timed sample (0: sized for ~15 s; -1: skip)")
+                    help="-1: skip the oracle baseline.  PHOTON modes time sequences {0, B-1} from an injected "
+                         "state; the flat baseline: 0 sizes its sample for ~15 s, N > 0 takes N sequences")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the decode tok/s and TPM lines of the other workloads")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (stress runs)")
     ap.add_argument("--prompt", type=int, default=None, help="override the workload's prompt length")
     ap.add_argument("--new-tokens", type=int, default=None, help="override the workload's generated tokens")
@@ -377,27 +462,52 @@ def main():
                "us": round(e0.elapsed_time(e1) * 1e3 / 20, 2)}
 
     attn = None
+    model.close()
+    del model, snap
+    torch.cuda.empty_cache()
     if not args.no_attn_standalone and not vanilla:
         log("stand-alone attention")
-        model.close()
-        del model
-        torch.cuda.empty_cache()
         attn = attn_standalone(P, torch, wl, wl.max_tokens // S, rep["top_len"])
+
+    per_config = None
+    if not args.no_per_config and not vanilla and not (args.chunk or args.batch or args.prompt or args.new_tokens):
+        per_config = per_config_lines(P, torch, args.workload, args.mode)
 
     cpu = None
     if args.cpu_seqs >= 0:
-        threads = min(16, len(os.sched_getaffinity(0)))
-        log(f"oracle baseline, {threads} threads")
-        cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads, vanilla=vanilla,
-                                         sampling=sampling)
+        # the oracle's BLAS threads: the host's CPU share for this GPU where
+        # the environment states it (OMP_NUM_THREADS), else every core this
+        # process may run on
+        visible = len(os.sched_getaffinity(0))
+        threads = min(visible, int(os.environ.get("OMP_NUM_THREADS") or visible))
+        log(f"oracle baseline, {threads} threads ({visible} visible)")
         prec = "float64" if cfg.dtype == "f32" else "float64 with the bf16 rounding contract"
-        rep_txt = f", decoded {reps} times from the same prefill" if reps > 1 else ""
-        what = "flat-baseline" if vanilla else ("sampled " if sampling else "") + "RecGen"
         cpu_model, blas = host_info()
-        cpu = {"value": round(cv, 2), "unit": "tok/s", "cores": threads, "kind": "oracle",
-               "cpu_model": cpu_model, "blas": blas,
-               "sample": f"{what} decode phase of {ns} of {B} sequences, all {wl.chunks} chunks{rep_txt} "
-                         f"({reps * ns * wl.new_tokens} tokens, {cdt:.1f} s), numpy {prec}"}
+        if vanilla:
+            cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads, vanilla=True)
+            rep_txt = f", decoded {reps} times from the same prefill" if reps > 1 else ""
+            sample = (f"flat-baseline decode phase of {ns} of {B} sequences, all {wl.chunks} chunks{rep_txt} "
+                      f"({reps * ns * wl.new_tokens} tokens, {cdt:.1f} s), numpy {prec}")
+        else:
+            cv, cdt, rows, done = cpu_baseline_injected(wl, W, threads, args.mode, sampling=sampling)
+            what = ("sampled " if sampling else "") + ("HierGen" if args.mode == "hiergen" else "RecGen")
+            sample = (f"{what} decode phase of sequences {rows} of {B}, {done} chunks from the prompt end "
+                      f"({len(rows) * S * done} tokens, {cdt:.1f} s) from the seeded decode state the parity "
+                      f"tests inject (decode work does not depend on its values), numpy {prec}")
+        cpu = {"value": round(cv, 2), "unit": "tok/s", "cores": threads, "visible_cores": visible,
+               "kind": "oracle", "cpu_model": cpu_model, "blas": blas, "sample": sample}
+
+    attn_roof = None
+    if per_class:
+        attn_roof = {}
+        for k in ("attn_top", "attn_chunk"):
+            if k in per_class:
+                v = per_class[k]
+                gbs = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+                attn_roof[k] = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "launches_per_step": v["launches"] // K,
+                                "avg_us": round(v["ms"] * 1e3 / v["launches"], 2),
+                                "bytes_per_launch": round(v["bytes"] / v["launches"])}
 
     out = {
         "metric": METRIC,
@@ -429,6 +539,7 @@ def main():
         "tpm_kv_only": round(tok_s / kv_gib, 1),
         "path_roofline": path_roof,
         "roofline": roofline,
+        "attention_roofline": attn_roof,
         "kernels": {k: {"launches_per_step": v["launches"] // K,
                         "us_per_step": round(v["ms"] * 1e3 / K, 2),
                         "GB_s": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1),
@@ -440,6 +551,7 @@ def main():
         "prefill": prefill,
         "aggregate": agg,
         "attn_standalone": attn,
+        "per_config": per_config,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -169,6 +169,9 @@ __global__ __launch_bounds__(1024) void argmax_next_kernel(ArgmaxNext c) {
   best = bvs[0]; bi = bis[0];
   for (int i = 1; i < nw; ++i)
     if (bvs[i] > best || (bvs[i] == best && bis[i] < bi)) { best = bvs[i]; bi = bis[i]; }
+  // a row with no ordered maximum (every logit NaN) leaves the initial id:
+  // take 0, so the token and the embedding row read below stay in range
+  if ((unsigned)bi >= (unsigned)c.V) bi = 0;
   {
     const int b = m / c.C2, p = (m % c.C2) * c.C1 + c.j;
     if (p < c.given_r) bi = c.given[(int64_t)b * c.C1 * c.C2 + p];   // block-uniform

@@ -150,6 +150,7 @@ struct ArgmaxNext {
   const float* c0; int64_t c0_ld; const void* E;
   float* x; void* a; const float* g; int d; float eps;
   const int* given; int given_r;
+  int V;   // vocabulary: a reduced id outside [0, V) (all-NaN row) becomes 0
 };
 hipError_t launch_argmax_next(int dtype, const ArgmaxNext& c, hipStream_t st);
 // out[r] = 1 - cos(a[r], e[r]) for R rows of d storage-dtype elements.

@@ -1247,7 +1247,7 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
     const bool next = j + 1 < C1;
     ArgmaxNext an{g.amax_val, g.amax_idx, c->sampling ? 1 : wp.head_tiles, MB, C1, K1, j, tok,
                   c0, (int64_t)C1 * d, c->E, next ? sb.x : nullptr, sb.a, c->dec[0].layers[0].g1, d, cf.norm_eps,
-                  (const int*)(ws + wp.tail.off), given_r};
+                  (const int*)(ws + wp.tail.off), given_r, V};
     // the next step's input (conditioning row + embedding in, stream and its
     // norm out); the token ids are counted with the head
     const double nb = next ? (double)MB * d * (8 + 2 * eb) : 0;
@@ -1655,7 +1655,7 @@ photon_status enqueue_vanilla(photon_ctx* c, float* d_logits, hipStream_t st) {
     PH_TRY(run_gemm(c, PHOTON_K_GEMM_HEAD, g, st));
     // token j of every sequence, then its embedding and norm as the stack input
     ArgmaxNext an{g.amax_val, g.amax_idx, wp.head_tiles, B, steps, 1, j, tok,
-                  nullptr, 0, c->E, b.x, b.a, c->vlayers.layers[0].g1, d, cf.norm_eps};
+                  nullptr, 0, c->E, b.x, b.a, c->vlayers.layers[0].g1, d, cf.norm_eps, nullptr, 0, V};
     PH_TRY(traced(c, PHOTON_K_ARGMAX, (double)B * d * (4 + 2 * eb), 0, st, "argmax_next",
                   [&] { return launch_argmax_next(dt, an, st); }));
     StackRun r{};

@@ -496,6 +496,21 @@ class Photon:
         raw = self.workspace[rep["off_top_kv"]:rep["off_top_kv"] + rep["top_kv"]]
         return raw.view(dt)[:n].view(cfg.n_top, 2, self.batch, cfg.n_heads, rep["top_len"], cfg.head_dim)
 
+    def lower_kv(self):
+        """HierGen's level-1 encoder K/V as a tensor [n_enc1, 2, B, H, lower_cap, hd]
+        (storage dtype); the first region of the lower-level K/V."""
+        torch = self.torch
+        rep = self.report_
+        cfg = self.cfg
+        if not rep["lower_kv"]:
+            raise ValueError("no lower-level K/V is kept (RecGen)")
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        eb = 2 if cfg.dtype == "bf16" else 4
+        cap = rep["lower_len"]
+        n = cfg.n_enc1 * 2 * self.batch * cfg.n_heads * cap * cfg.head_dim
+        raw = self.workspace[rep["off_lower_kv"]:rep["off_lower_kv"] + n * eb]
+        return raw.view(dt).view(cfg.n_enc1, 2, self.batch, cfg.n_heads, cap, cfg.head_dim)
+
     def h_state(self):
         torch = self.torch
         cfg = self.cfg

@@ -272,6 +272,29 @@ class State:
                      None if self.tail is None else self.tail.copy())
 
 
+def state_from_arrays(model, seqs):
+    """A State built from given cache contents instead of a prefill: seqs is
+    a list (one entry per sequence, in batch order) of dicts with top_k,
+    top_v [n_top, n, H, hd], h [d] and, to keep the lower encoders' caches
+    (HierGen), low_k, low_v {l: [layers_l, n_l, H, hd]} -- the layout of
+    photon_inputs.gen_decode_state.  The values are taken as they are (no
+    rounding); the state sits at top position n (a prompt of n*S tokens)."""
+    dt = model.dt
+    n = seqs[0]["top_k"].shape[1]
+
+    def cache(pick):
+        layers = pick(seqs[0], "k").shape[0]
+        return [{"k": np.stack([pick(s, "k")[i] for s in seqs]).astype(dt),
+                 "v": np.stack([pick(s, "v")[i] for s in seqs]).astype(dt)} for i in range(layers)]
+
+    top = cache(lambda s, kv: s["top_" + kv])
+    h = np.stack([s["h"] for s in seqs]).astype(dt)
+    lower = None
+    if "low_k" in seqs[0]:
+        lower = {l: cache(lambda s, kv, l=l: s["low_" + kv][l]) for l in range(1, model.cfg.L)}
+    return State(top, h, n, lower)
+
+
 def prefill(model, prompt, mode="recgen", log=None):
     """Bottom-up pass over the prompt [modules], [recgen].
 

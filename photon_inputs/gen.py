@@ -97,3 +97,37 @@ def gen_weights(cfg, seed, zero=()):
 def gen_prompts(cfg, batch, prompt, seed):
     rng = np.random.default_rng([seed, 1])
     return rng.integers(0, cfg.vocab, size=(batch, prompt), dtype=np.int32)
+
+
+def gen_decode_state(cfg, seq, n_top_states, mode="recgen", seed=0):
+    """Seeded stand-in for the decode state one sequence holds after a
+    prefill of n_top_states top states (a prompt of n_top_states * S
+    tokens), for tests that inject the same state into both sides.
+
+    Stream ``default_rng([seed, 2, seq])``, so a sequence's values do not
+    depend on which other sequences are drawn.  Returns a dict:
+      top_k, top_v: [n_top, n_top_states, H, hd], one entry per top layer;
+      h:            [d], the last top output;
+      low_k, low_v: (HierGen only) {l: [layers_l, n_l, H, hd]} for every
+                    encoder level l = 1 .. L-1, n_l = n_top_states * S / span(l).
+    Cached keys and values are N(0, (0.02 sqrt(d))^2): the spread of a
+    projection of a unit-RMS row by N(0, 0.02^2) weights.  h is N(0, 1), the
+    spread of a normalized row with unit gains.  bf16 models get bf16-exact
+    values (round to nearest even), like every stored cache entry."""
+    rng = np.random.default_rng([seed, 2, seq])
+    H, hd, d = cfg.n_heads, cfg.head_dim, cfg.d_model
+    sd = np.float32(0.02 * np.sqrt(d))
+    cast = _bf16_values if cfg.dtype == "bf16" else (lambda a: a)
+
+    def kv(layers, n):
+        return [cast(rng.standard_normal((layers, n, H, hd), dtype=np.float32) * sd) for _ in range(2)]
+
+    out = {}
+    out["top_k"], out["top_v"] = kv(cfg.n_top, n_top_states)
+    out["h"] = cast(rng.standard_normal(d, dtype=np.float32))
+    if mode == "hiergen":
+        out["low_k"], out["low_v"] = {}, {}
+        for l in range(1, cfg.L):
+            n_l = n_top_states * cfg.S // cfg.span(l)
+            out["low_k"][l], out["low_v"][l] = kv(cfg.enc_layers(l), n_l)
+    return out

@@ -16,7 +16,9 @@ photon-600m 2x2: B = 256, P = 8192).
       outputs are kept in OUTDIR/<case>.oracle.npz with the tokens they were
       forced with, and reused while a later GPU dump emits the same tokens.
 
-Same cases as tests/test_gpu_fullsize.py behind PHOTON_FULLSIZE=1.
+These are free-running drift reports under the widened bar of tests/parity.py;
+the stated bar is checked per chunk from an injected state in
+tests/test_gpu_injected.py.
 """
 import os
 import sys

@@ -4,16 +4,23 @@ ABI, run the oracle teacher-forced with the GPU's tokens, compare.
 Tolerances (logits): fp32 models |dlogit| <= 1e-4 * max(1, max|oracle row|)
 and identical greedy ids.
 
-bf16 models: the rounding contract (bf16 operands and K/V, fp32 accumulate)
-has an intrinsic noise: two valid implementations that differ only in
-accumulation precision flip some bf16 roundings by one ulp, and RecGen's top
-stream, a recurrence over chunks, carries those flips forward.  The noise is
-measured by running the oracle's own code in float32 beside the float64
-reference.  The bar is |dlogit| <= max(3e-2, 1.5 x that noise), both for the
-largest and (with 1.5x) the mean deviation.  Greedy ids must be identical,
-except where the reference's margin between its argmax and the GPU's id is
-within twice the tolerance (near ties: both ids are correct under rounding
-differences); those positions are counted and reported.
+bf16 models, free-running generations (compare): the rounding contract
+(bf16 operands and K/V, fp32 accumulate) has an intrinsic noise: two valid
+implementations that differ only in accumulation precision flip some bf16
+roundings by one ulp, and RecGen's top stream, a recurrence over chunks,
+carries those flips forward.  The noise is measured by running the oracle's
+own code in float32 beside the float64 reference.  The drift bar is
+|dlogit| <= max(3e-2, 1.5 x that noise), both for the largest and (with
+1.5x) the mean deviation.  Greedy ids must be identical, except where the
+reference's margin between its argmax and the GPU's id is within twice the
+tolerance (near ties: both ids are correct under rounding differences);
+those positions are counted and reported.  This drift bar departs from the
+stated 3e-2: it was adopted after a free-running photon-150m generation of
+16 chunks measured 0.0515 against it.
+
+Injected states (compare_stated): one or two chunks decoded from the same
+seeded state on both sides are held to the stated bar itself, 3e-2 absolute
+with near ties of margin <= 6e-2.
 """
 import numpy as np
 
@@ -146,3 +153,59 @@ def small_cfg(**kw):
                 n_enc1=1, n_dec1=2, n_dec0=2, dtype="bf16")
     base.update(kw)
     return pi.PhotonConfig(**base)
+
+
+# --------------------------------------------------------------------------
+# injected decode states: one or two chunks from the same seeded state on
+# both sides, judged at the stated bar
+# --------------------------------------------------------------------------
+def inject_state(model, seq, st):
+    """Overwrite sequence ``seq``'s decode state in the GPU workspace with
+    ``st`` (photon_inputs.gen_decode_state): its top K/V over the first n
+    slots of every top layer, its h, and (HierGen) its level-1 K/V."""
+    import torch
+    dt = torch.bfloat16 if model.cfg.dtype == "bf16" else torch.float32
+
+    def put(view, arr):
+        # arr [layers, n, H, hd] -> view [layers, H, cap, hd] (first n slots)
+        n = arr.shape[1]
+        view[:, :, :n, :].copy_(torch.from_numpy(np.ascontiguousarray(arr.transpose(0, 2, 1, 3))).to(dt))
+
+    kv = model.top_kv()
+    put(kv[:, 0, seq], st["top_k"])
+    put(kv[:, 1, seq], st["top_v"])
+    model.h_state()[seq].copy_(torch.from_numpy(st["h"]).to(dt))
+    if "low_k" in st:
+        low = model.lower_kv()
+        put(low[:, 0, seq], st["low_k"][1])
+        put(low[:, 1, seq], st["low_v"][1])
+
+
+def oracle_state(model, states):
+    """The oracle's State for the sequences of ``states`` (a list of
+    gen_decode_state dicts) as one batch, in the oracle's float type."""
+    return O.state_from_arrays(model, states)
+
+
+def compare_stated(cfg, toks, lg, ot, ol):
+    """The stated bar, with no allowance for drift: bf16 max |dlogit| <=
+    3e-2 absolute (fp32: 1e-4 relative to the row's largest logit, ids
+    identical); greedy ids identical except where the oracle's margin
+    between its own argmax and the GPU's id is <= 2 * 3e-2 (logits within
+    the tolerance either way can swap such a pair).  Returns a report."""
+    dev = np.abs(lg.astype(np.float64) - ol)
+    if cfg.dtype == "f32":
+        err = (dev.max(-1) / np.maximum(1.0, np.abs(ol).max(-1))).max()
+        assert err <= TOL_F32, f"fp32 logits differ: {err:.3g}"
+        assert (ot == toks).all(), "fp32 greedy ids differ"
+        return {"max_err": float(err), "mean_err": float(dev.mean()), "near_ties": 0, "tokens": int(toks.size),
+                "max_tie_gap": 0.0}
+    err = float(dev.max())
+    assert err <= TOL_BF16, f"bf16 logits differ: {err:.4g} > {TOL_BF16}"
+    diff = ot != toks
+    gap = np.take_along_axis(ol, ot[..., None].astype(np.int64), -1)[..., 0] - \
+        np.take_along_axis(ol, toks[..., None].astype(np.int64), -1)[..., 0]
+    worst = float(gap[diff].max()) if diff.any() else 0.0
+    assert worst <= 2 * TOL_BF16, f"ids differ beyond a near tie: margin {worst:.4g} > {2 * TOL_BF16}"
+    return {"max_err": err, "mean_err": float(dev.mean()), "near_ties": int(diff.sum()), "tokens": int(toks.size),
+            "max_tie_gap": worst}

@@ -1,18 +1,21 @@
-"""GPU parity at the full 600M-shaped workloads, on sampled sequences.
+"""Free-running drift reports at the 600M shape, on sampled sequences.
 
 The GPU runs the whole batch at the full prompt and generation length in the
 launch configuration the benchmark times (captured HIP graphs, no logits
 request: the logits of the sampled rows come from a second, direct-launch
 run whose tokens must equal the graph run's).  The oracle then recomputes one
-sequence, teacher-forced with the GPU's tokens (see tests/parity.py).
+sequence from its own prefill, teacher-forced with the GPU's tokens, and the
+two are compared over every generated chunk under the drift bar of
+tests/parity.py (max(3e-2, 1.5 x the oracle's own float32-vs-float64
+spread)): over 16 to 32 chunks RecGen's top stream, a recurrence, carries
+one-ulp rounding differences forward, so these are drift reports, not the
+stated bar.  The stated 3e-2 bar is checked per chunk from an injected state
+at every full-size workload in tests/test_gpu_injected.py.
 
-The photon-600m workload (P = 4096) runs by default, and the long-context
-workload's batch of 16 at a 512-token prompt; the long-context
-(P = 32768) and 2x2 (B = 256, P = 8192) workloads need several minutes of
-oracle time per sequence and run when PHOTON_FULLSIZE=1.
+The long-context (P = 32768) and 2x2 (B = 256, P = 8192) free-running rows
+need many minutes of oracle prefill per sequence; tests/fullsize_offline.py
+runs them in two halves (GPU dump, then the CPU check).
 """
-import os
-
 import numpy as np
 import pytest
 
@@ -20,7 +23,6 @@ import photon_inputs as pi
 from parity import check_against_oracle, gpu_generate
 
 pytestmark = pytest.mark.gpu
-LONG = os.environ.get("PHOTON_FULLSIZE") == "1"
 
 
 def run_full(idx, row, mode="recgen", prompt_len=None, new_tokens=None):
@@ -75,18 +77,3 @@ def test_photon600m_theorem_a6_bitwise():
     assert bool((kv1 == m2.top_kv()).all())
     np.testing.assert_array_equal(t1, t2)
     np.testing.assert_array_equal(l1, l2)
-
-
-@pytest.mark.skipif(not LONG, reason="several minutes of oracle time; set PHOTON_FULLSIZE=1")
-def test_photon600m_long_context_first_sequence():
-    run_full(4, 0)
-
-
-@pytest.mark.skipif(not LONG, reason="several minutes of oracle time; set PHOTON_FULLSIZE=1")
-def test_photon600m_long_context_hiergen():
-    run_full(4, 7, mode="hiergen")
-
-
-@pytest.mark.skipif(not LONG, reason="several minutes of oracle time; set PHOTON_FULLSIZE=1")
-def test_photon600m_2x2_multiquery_sequence():
-    run_full(5, 137)

@@ -110,6 +110,74 @@ def test_decoder_cache_independent_of_context():
         assert O.kv_bytes(cfg, 4, 1024, "hiergen")["lower"] > 0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layers", [(1, 2), (3, 1)], ids=["dec1<dec0", "dec1>dec0"])
+def test_dec_bytes_equal_the_cache_the_token_decoder_builds(dtype, layers):
+    # the TPM denominator's decoder term against the in-chunk caches the
+    # token decoder really fills (every empty_cache the chunk creates for it,
+    # measured after the chunk), with n_dec1 != n_dec0 so that counting the
+    # wrong decoder's layers fails
+    n_dec1, n_dec0 = layers
+    cfg = tiny(dtype, n_dec1=n_dec1, n_dec0=n_dec0)
+    m = make(cfg)
+    st = O.prefill(m, prompts(cfg, 3, 32))
+    made = []
+    orig = m.empty_cache
+
+    def spy(n_layers, B):
+        c = orig(n_layers, B)
+        made.append(c)
+        return c
+
+    m.empty_cache = spy
+    O.decode_chunk(m, st)
+    b = 2 if dtype == "bf16" else 4
+    dec_caches = [c for c in made if len(c) == cfg.n_dec0 and c[0]["k"].shape[0] == 3 * cfg.S // cfg.C1]
+    assert len(dec_caches) == 1
+    built = sum(e["k"].size + e["v"].size for e in dec_caches[0]) * b
+    assert built == O.kv_bytes(cfg, 3, 32 + cfg.S)["dec"] == O.kv_bytes(cfg, 3, 4096)["dec"]
+
+
+def test_state_from_arrays_decodes_like_the_prefilled_state():
+    # an injected state laid out as photon_inputs.gen_decode_state lays it
+    # out ([layers, n, H, hd] per sequence) and filled with a real
+    # prefill's caches decodes exactly like that prefill's own state
+    for mode in ("recgen", "hiergen"):
+        cfg = tiny()
+        m = make(cfg)
+        st = O.prefill(m, prompts(cfg, 2, 48), mode)
+        seqs = []
+        for b in range(2):
+            e = {"top_k": np.stack([c["k"][b] for c in st.top]), "top_v": np.stack([c["v"][b] for c in st.top]),
+                 "h": st.h[b]}
+            if mode == "hiergen":
+                e["low_k"] = {1: np.stack([c["k"][b] for c in st.lower[1]])}
+                e["low_v"] = {1: np.stack([c["v"][b] for c in st.lower[1]])}
+            seqs.append(e)
+        inj = O.state_from_arrays(m, seqs)
+        assert inj.top_len == st.top_len == 48 // cfg.S
+        for _ in range(2):
+            a, b_ = O.decode_chunk(m, st, mode), O.decode_chunk(m, inj, mode)
+            np.testing.assert_array_equal(a["tokens"], b_["tokens"])
+            np.testing.assert_array_equal(a["logits"], b_["logits"])
+            np.testing.assert_array_equal(a["h"], b_["h"])
+
+
+def test_injected_state_shapes_and_spread():
+    # the seeded stand-in has the shapes of a prefilled state, bf16-exact
+    # values for bf16 models and the stated spreads
+    cfg = pi.CONFIGS["m150"]
+    st = pi.gen_decode_state(cfg, 3, 64, "hiergen", seed=1)
+    assert st["top_k"].shape == (cfg.n_top, 64, cfg.n_heads, cfg.head_dim)
+    assert st["low_v"][1].shape == (cfg.n_enc1, 64 * cfg.C2, cfg.n_heads, cfg.head_dim)
+    for a in (st["top_k"], st["h"], st["low_k"][1]):
+        assert (O.round_bf16(a.astype(np.float64)) == a).all()
+    assert abs(st["top_v"].std() / (0.02 * np.sqrt(cfg.d_model)) - 1) < 0.01
+    assert abs(st["h"].std() - 1) < 0.1
+    again = pi.gen_decode_state(cfg, 3, 64, "recgen", seed=1)
+    np.testing.assert_array_equal(again["top_k"], st["top_k"])
+
+
 # ---------------- incremental == full recompute ----------------
 @pytest.mark.parametrize("P,N", [(16, 16), (32, 48), (64, 32)])
 def test_recgen_top_incremental_equals_full(P, N):
