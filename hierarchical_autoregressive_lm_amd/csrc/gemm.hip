@@ -271,7 +271,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmP p) {
 // the MFMA fragment reads spread over the banks.  Every wave issues its
 // share of a stage's loads; before computing on stage kb it waits until at
 // most the loads of the stages after kb are in flight (an explicit vmcnt)
-// and meets the others at a barrier, which also frees the slot the next
+// and its own LDS reads of the previous stage are done (lgkmcnt(0)), then
+// meets the others at a barrier, which thereby frees the slot the next
 // stage is loaded into.  Each ring slot is an LDS object of its own: the
 // compiler then tells the slots apart and inserts no wait of its own.  The
 // k loop is unrolled at compile time (NKB k-blocks per workgroup), so every
@@ -284,8 +285,14 @@ __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I..
   (f(std::integral_constant<int, I>{}), ...);
 }
 
-// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt not waited on
-constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0), expcnt not waited on.  The
+// lgkmcnt(0) matters: the barrier after it is what lets the other waves
+// refill the slot this wave read last, and the compiler issues those LDS
+// reads early but waits for them only where the products use them, which
+// may be after the barrier; without the wait a refill that lands quickly
+// (an L2 hit) can overwrite a slot before a wave held back on a busy CU
+// has read it.
+constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (0 << 8) | (((n >> 4) & 3) << 14); }
 
 #define PH_LDS_SLOTS(X) X(0) X(1) X(2) X(3) X(4) X(5)
 
@@ -442,7 +449,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
   } else {
     // greedy head: optional logits, then the per-row first maximum of the
     // tile; the partials go through ring slot 0 once every wave is done
-    __builtin_amdgcn_s_barrier();
+    // reading it (a full barrier: each wave's LDS reads complete first)
+    __syncthreads();
     float* bv = reinterpret_cast<float*>(L0);
     int* bi = reinterpret_cast<int*>(L0) + WN * BM;
 #pragma unroll
