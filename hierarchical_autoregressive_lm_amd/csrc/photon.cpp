@@ -18,6 +18,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1622,6 +1623,62 @@ photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q, co
                                                    : launch_attn_prefill(a, st);
   if (e != hipSuccess) return fail(PHOTON_EHIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------- attention without allocation
+// The split partials of photon_attention_noalloc live in this file-scope
+// device array: every GPU the library runs on holds its own copy, for as
+// long as the process lives.  Host code never passes `scratch` itself (on
+// the host it is a stand-in, not a device address): each device's address
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and kernels receive that pointer.
+namespace {
+constexpr uint64_t kNoallocScratchBytes = PHOTON_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use).
+photon_status noalloc_scratch(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PHOTON_EUNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PHOTON_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+photon_status photon_attention_noalloc(int32_t kind, int32_t dtype, const float* d_q, const void* d_k,
+                                       const void* d_v, void* d_out, int32_t groups, int32_t heads,
+                                       int32_t head_dim, int32_t queries, int32_t keys, int32_t cap, void* stream) {
+  PH_TRY(check_attention(kind, groups, heads, head_dim, queries, cap));
+  int ns = 1;
+  const uint64_t need = attention_part_bytes(kind, groups, heads, head_dim, queries, cap, &ns);
+  if (need > kNoallocScratchBytes)
+    return fail(PHOTON_ECAPACITY, "split partials need %llu bytes; the built-in scratch holds %llu",
+                (unsigned long long)need, (unsigned long long)kNoallocScratchBytes);
+  void* p = nullptr;
+  PH_TRY(noalloc_scratch(&p));
+  // every split writes its whole partial before the combine reads it, so
+  // nothing left by an earlier call needs clearing
+  return photon_attention(kind, dtype, d_q, d_k, d_v, d_out, groups, heads, head_dim, queries, keys, cap, p,
+                          kNoallocScratchBytes, stream);
 }
 
 }  // extern "C"

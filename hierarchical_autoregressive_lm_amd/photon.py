@@ -99,7 +99,7 @@ EXPORTS = ["photon_kv_bytes", "photon_prefill_scratch_bytes",
            "photon_last_error", "photon_prefill", "photon_decode_chunk",
            "photon_position", "photon_set_position", "photon_use_graphs",
            "photon_trace_enable", "photon_trace_read",
-           "photon_attention_scratch_bytes", "photon_attention",
+           "photon_attention_scratch_bytes", "photon_attention", "photon_attention_noalloc",
            "photon_vanilla_kv_bytes", "photon_vanilla_prefill_scratch_bytes",
            "photon_vanilla_weight_layout", "photon_vanilla_weight_tensor",
            "photon_vanilla_open", "photon_vanilla_prefill", "photon_vanilla_decode",
@@ -132,6 +132,7 @@ def _load():
         "photon_trace_read": [V, P(TraceStat)],
         "photon_attention_scratch_bytes": [i32, i32, i32, i32, i32, i32, P(u64)],
         "photon_attention": [i32, i32, V, V, V, V, i32, i32, i32, i32, i32, i32, V, u64, V],
+        "photon_attention_noalloc": [i32, i32, V, V, V, V, i32, i32, i32, i32, i32, i32, V],
         "photon_vanilla_kv_bytes": [P(VanillaConfig_), i32, i64, P(KvReport)],
         "photon_vanilla_prefill_scratch_bytes": [P(VanillaConfig_), i32, i32, P(u64)],
         "photon_vanilla_weight_layout": [P(VanillaConfig_), P(u64), P(i32)],
@@ -305,6 +306,25 @@ class Attention:
                                      ctypes.c_void_p(self.scratch_ptr), self.scratch_bytes,
                                      _stream_handle(torch)))
         return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # PHOTON_NOALLOC_SCRATCH_BYTES
+
+
+def attention_noalloc(kind, q, K, V, out, keys, queries=1):
+    """photon_attention_noalloc on torch tensors laid out as for Attention
+    (q [G*Q, H*hd] float32, K and V [G, H, cap, hd], out like q in K's
+    dtype); the split partials live in the library's built-in device array."""
+    G, H, cap, hd = K.shape
+    dt = BF16 if K.dtype == torch.bfloat16 else F32
+    assert q.dtype == torch.float32 and tuple(q.shape) == (G * queries, H * hd) and q.is_contiguous()
+    assert K.shape == V.shape and K.dtype == V.dtype and K.is_contiguous() and V.is_contiguous()
+    assert out.dtype == K.dtype and tuple(out.shape) == (G * queries, H * hd) and out.is_contiguous()
+    _check(_lib.photon_attention_noalloc(_ATTN[kind], dt, ctypes.c_void_p(q.data_ptr()),
+                                         ctypes.c_void_p(K.data_ptr()), ctypes.c_void_p(V.data_ptr()),
+                                         ctypes.c_void_p(out.data_ptr()), G, H, hd, queries, keys, cap,
+                                         _stream_handle(torch)))
+    return out
 
 
 class Photon:

@@ -369,6 +369,27 @@ photon_status photon_attention(int32_t kind, int32_t dtype, const float* d_q,
                                void* d_scratch, uint64_t scratch_bytes,
                                void* stream);
 
+/* photon_attention for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, same arguments and limits, with the split
+ * partials in a built-in device array of PHOTON_NOALLOC_SCRATCH_BYTES
+ * (8 MiB) per GPU, held until the process ends.  It calls no
+ * allocator.  A launch whose partials
+ * (photon_attention_scratch_bytes) exceed that size is rejected with
+ * PHOTON_ECAPACITY before anything is enqueued (within the limits above a
+ * launch needs at most 3.6 MB, so this only guards later changes of the
+ * split rule).  Nothing in the array needs clearing: every split writes its
+ * whole partial before the combine reads it.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and may return wrong results; serialize them. */
+photon_status photon_attention_noalloc(int32_t kind, int32_t dtype,
+                                       const float* d_q, const void* d_k,
+                                       const void* d_v, void* d_out,
+                                       int32_t groups, int32_t heads,
+                                       int32_t head_dim, int32_t queries,
+                                       int32_t keys, int32_t cap, void* stream);
+#define PHOTON_NOALLOC_SCRATCH_BYTES (8ull << 20)
+
 /* ------------------------------------------------------------------------
  * Sampling decode and multi-query aggregation (explainer, the paragraph on
  * recovering quality: several slightly varied queries are run and bound by
