@@ -220,6 +220,43 @@ def measured_traffic(wl, cls):
     return None, None, None
 
 
+def measured_counters(wl):
+    """MFMA use and DRAM traffic of the workload's kernels from the committed
+    rocprofv3 counter summary (profiles/counters_photon600m.json), while the
+    kernels' sources still hash to it: the time-weighted MFMA busy fraction
+    and executed TFLOP/s of the prompt GEMMs (M >= 2048 rows), the prompt
+    attention and the decode GEMMs, and the top attention's DRAM reads per
+    launch.  None when the workload was not profiled or a source changed."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters_photon600m.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"] or wl.name not in rec["workloads"]:
+        return None
+    ks = rec["workloads"][wl.name]
+
+    def group(pred):
+        sel = {k: v for k, v in ks.items() if pred(k)}
+        t = sum(v["avg_us"] * v["dispatches"] for v in sel.values())
+        if not t:
+            return None
+        return {"mfma_busy": round(sum(v["mfma_busy"] * v["avg_us"] * v["dispatches"] for v in sel.values()) / t, 4),
+                "mfma_tflop_s_executed": round(sum(v["mfma_tflop_s"] * v["avg_us"] * v["dispatches"]
+                                                   for v in sel.values()) / t, 1),
+                "kernels": len(sel)}
+    prompt = lambda k: k.startswith("gemm_lds_kernel<128, 256,") or k.startswith("gemm_lds_kernel<256, 256,")
+    top = [v for k, v in ks.items() if k.startswith("attn_decode_kernel")]
+    return {"source": "profiles/counters_photon600m.json",
+            "prompt_gemm": group(prompt),
+            "prompt_attention": group(lambda k: k.startswith("attn_prefill_mfma")),
+            "decode_gemm": group(lambda k: k.startswith("gemm_") and not prompt(k)),
+            "attn_top_dram_read_bytes": top[0]["dram_read_bytes"] if top else None}
+
+
 def attn_standalone(P, torch, wl, top_len, top_cap):
     """photon_attention alone, K/V rotated over copies larger than the
     Infinity Cache: the chunk kernel at the token decoder's shape (one query
@@ -352,6 +389,7 @@ def main():
         fl = sum(pre_cls[n]["flops"] for n in names if n in pre_cls)
         return {"ms": round(ms, 3), "tflop": round(fl / 1e12, 3),
                 "tflop_s": round(fl / (ms * 1e-3) / 1e12, 1) if ms else None}
+    counters = measured_counters(wl)
     prefill = {"seconds": round(pre_s, 4), "tok_s": round(B * wl.prompt / pre_s, 1),
                "tflop": round(pre_flops / 1e12, 3), "tflop_s": round(pre_flops / pre_s / 1e12, 1),
                "attention": tf(["attn_prefill"]),
@@ -551,6 +589,7 @@ def main():
         "prefill": prefill,
         "aggregate": agg,
         "attn_standalone": attn,
+        "counters": counters,
         "per_config": per_config,
         "cpu_baseline": cpu,
     }
