@@ -24,9 +24,27 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-sanitized variant for the CPU tests of the C ABI: AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (each -fsanitize= behind
+# -Xarch_host; the device code is built as usual).
+SAN_BUILD = os.path.join(BUILD, "hostsan")
+SAN_OUT = os.path.join(SAN_BUILD, "libphoton_hostsan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime():
+    """The clang AddressSanitizer runtime the sanitized build links against
+    (a process that loads the library preloads it)."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang", "*",
+                                         "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def _compile(src, flags=FLAGS, build=BUILD):
+    obj = os.path.join(build, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -46,6 +64,23 @@ def build(verbose=False):
     if verbose:
         print(f"built {OUT}")
     return OUT
+
+
+def build_hostsan(verbose=False):
+    """The host-sanitized library (SAN_OUT), for CPU tests only."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", *SAN_FLAGS]
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, flags, SAN_BUILD), SOURCES))
+    tmp = SAN_OUT + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libsan", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_OUT)
+    if verbose:
+        print(f"built {SAN_OUT}")
+    return SAN_OUT
 
 
 if __name__ == "__main__":

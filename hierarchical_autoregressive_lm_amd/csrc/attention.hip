@@ -523,233 +523,264 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnCall a, float sca
 // q and p are float32 in the rounding contract; each enters the products as
 // hi + lo, two bf16 terms (hi = bf16(x), lo = bf16(x - hi): 16 significant
 // bits), so every product is two MFMAs accumulating in float32.
-// A workgroup: NWV waves x NQ blocks of 16 queries of one (sequence, head);
-// K and V tiles of 64 keys staged in LDS (K row-major, V transposed),
-// double-buffered; query blocks run heaviest (last) first.
+// A workgroup: NWV waves x 16 queries of one (sequence, head); K and V
+// tiles of 64 keys staged in LDS, double-buffered; query blocks run
+// heaviest (last) first.
+//
+// LDS layout: both tiles are rows of 128 bytes, eight 16-byte chunks, with
+// the chunk index XOR-ed by (row / 2) % 8, so that the 16 rows x 16 bytes
+// one fragment read touches fall in distinct banks (measured on gfx950: 4
+// cycles per 64-lane 16-byte read, no bank conflict; rows of 64 or 208 bytes
+// took 8, and the V^T rows of 144 bytes read in 8-byte halves 16).
+//   K: row = key, chunk = 8 dimensions; dims 64r .. 64r+63 in region r
+//      (HD/64 rounded up regions of 64 rows).  Filled by direct global->LDS
+//      loads (lane l of a load writes slot base + l, so each lane fetches the
+//      chunk its slot holds); rows past the prompt repeat its last key (their
+//      scores are masked) and unused chunks of a region repeat chunk 0.
+//   V^T: row = dimension, chunk q = 4s + j holds the 8 keys of k-step s that
+//      lane group j multiplies: 32s+4j .. +3, then 32s+16+4j .. +3.  Each
+//      thread loads 8 dimensions of 4 consecutive keys (zero past the
+//      prompt), transposes them in registers and stores 8 half-chunks.
+// Tile t+1's K loads go out at the start of tile t and land in LDS by
+// themselves; its V rows load once tile t's scores are formed (they would
+// otherwise hold registers through the score products) and are stored at
+// the end of the tile; one barrier per tile.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void attn_lds_t;
+typedef __attribute__((address_space(1))) const void attn_glb_t;
 
 __device__ __forceinline__ void split_hi_lo(float x, bf16_t& hi, bf16_t& lo) {
   hi = f2bf(x);
   lo = f2bf(x - bf2f(hi));
 }
 
-template <int HD, int NQ, int NWV>
-__global__ __launch_bounds__(NWV * 64, (NQ == 1 && NWV <= 4) ? 2 : 1) void attn_prefill_mfma_kernel(AttnCall a,
-                                                                                                   float scale) {
+// 16-byte slot of (row, chunk) in a tile of 128-byte rows
+__device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
+
+template <int HD, int NWV>
+__global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
   constexpr int NT = NWV * 64;           // threads
   constexpr int TK = 64;                 // keys per tile
-  constexpr int BQ = 16 * NQ * NWV;      // queries per workgroup
+  constexpr int BQ = 16 * NWV;           // queries per workgroup
   constexpr int KS = HD / 32;            // k-steps of S^T
   constexpr int HB = HD / 16;            // 16-row blocks of O^T
-  constexpr int KROW = HD + 8;           // padded K row (bf16)
-  constexpr int VCOL = TK + 8;           // padded V^T row (bf16)
-  constexpr int KCH = TK * HD / 8;       // 16-byte K chunks per tile
-  constexpr int VCH = TK / 2 * HD / 8;   // (2 keys x 8 dims) V items per tile
-  constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][TK][KROW];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][HD][VCOL];
+  constexpr int KR = (HD + 63) / 64;     // K regions of 64 dims
+  constexpr int KSLOTS = KR * TK * 8;    // 16-byte K slots per tile
+  static_assert(KSLOTS % (64 * NWV) == 0, "K tile fills whole direct loads per wave");
+  constexpr int KI = KSLOTS / (64 * NWV);    // direct loads per wave per tile
+  constexpr int VIT = (TK / 4) * (HD / 8);   // (4 keys x 8 dims) V items per tile
+  constexpr int VPT = (VIT + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) uint4 Ks[2][KSLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 Vt[2][HD * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, j = lane >> 4;
   const int T = a.Q;                     // queries = keys = prompt rows
   const int nqb = (T + BQ - 1) / BQ;
-  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);     // heaviest first
-  const int gh = blockIdx.x / nqb;
+  // consecutive workgroups go to different XCDs: give each XCD a contiguous
+  // run of (sequence, head, query block) tiles, so that the query blocks of
+  // one (sequence, head), which all stream its K/V, share one L2
+  const int total = (int)gridDim.x;
+  const int bid = (total % 8 == 0) ? (int)(blockIdx.x % 8) * (total / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int qb = nqb - 1 - bid % nqb;    // heaviest first
+  const int gh = bid / nqb;
   const int h = gh % a.H, g = gh / a.H;
-  const int q0 = qb * BQ + wave * 16 * NQ;
+  const int q0 = qb * BQ + wave * 16;
   // scores in base-2 units: q carries log2(e), the softmax uses exp2
   const float scale2 = scale * 1.44269504088896341f;
   const bf16_t* Kb = reinterpret_cast<const bf16_t*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
   const bf16_t* Vb = reinterpret_cast<const bf16_t*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
 
-  // Q^T fragments (B operand): lane holds query q0 + 16n + c, dims 32ks + 8j .. +8
-  bf16x8_t qhi[NQ][KS], qlo[NQ][KS];
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) {
-    const int qi = q0 + 16 * n + c;
+  // Q^T fragments (B operand): lane holds query q0 + c, dims 32ks + 8j .. +8
+  bf16x8_t qhi[KS], qlo[KS];
+  {
+    const int qi = q0 + c;
     const float* qp = a.q + (int64_t)(g * a.Q + (qi < T ? qi : T - 1)) * a.q_ld + h * HD + 8 * j;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16_t hb[8], lb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) split_hi_lo(qi < T ? qp[32 * ks + e] * scale2 : 0.f, hb[e], lb[e]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        qhi[n][ks][e] = __builtin_bit_cast(__bf16, hb[e]);
-        qlo[n][ks][e] = __builtin_bit_cast(__bf16, lb[e]);
+        bf16_t hb, lb;
+        split_hi_lo(qi < T ? qp[32 * ks + e] * scale2 : 0.f, hb, lb);
+        qhi[ks][e] = __builtin_bit_cast(__bf16, hb);
+        qlo[ks][e] = __builtin_bit_cast(__bf16, lb);
       }
     }
   }
-  f32x4_t o[NQ][HB];
-  float m[NQ], l[NQ];
+  f32x4_t o[HB];
+  float m = -INFINITY, l = 0.f;
 #pragma unroll
-  for (int n = 0; n < NQ; ++n) {
-    m[n] = -INFINITY; l[n] = 0.f;
-#pragma unroll
-    for (int b = 0; b < HB; ++b) o[n][b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int b = 0; b < HB; ++b) o[b] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   const int kend = min(T, qb * BQ + BQ);  // keys any query of the block sees
   const int ntiles = (kend + TK - 1) / TK;
-  uint4 kreg[KPT];
-  uint4 vreg[VPT][2];
-  auto load_tile = [&](int t) {
+  // this lane's fragment slots (uint4 index inside a tile): K for the two
+  // halves (k-steps 2r, 2r+1) of a region's row, V^T for the two k-steps
+  const int kfr0 = lds_slot(c, j), kfr1 = lds_slot(c, 4 + j);
+  const int vfr0 = lds_slot(c, j), vfr1 = lds_slot(c, 4 + j);
+  uint4 vreg[VPT][4];
+  // direct K loads: lane l of load i fills slot (wave*KI + i)*64 + l and
+  // fetches the (key, dim chunk) that slot holds
+  auto issue_k = [&](int t, uint4* Kdst) {
     const int k0 = t * TK;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + NT * i;
-      const int key = ch / (HD / 8), c8 = ch % (HD / 8);
-      if (ch < KCH && k0 + key < T)
-        kreg[i] = *reinterpret_cast<const uint4*>(Kb + (int64_t)(k0 + key) * HD + 8 * c8);
-      else
-        kreg[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < KI; ++i) {
+      const int slot = (wave * KI + i) * 64 + lane;
+      const int key = (slot % (TK * 8)) / 8;
+      const int c8 = 8 * (slot / (TK * 8)) + ((slot & 7) ^ ((key >> 1) & 7));
+      const int row = k0 + key < T ? k0 + key : T - 1;
+      const bf16_t* src = Kb + (int64_t)row * HD + 8 * (c8 < HD / 8 ? c8 : 0);
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)src, (attn_lds_t*)(Kdst + (wave * KI + i) * 64), 16, 0, 0);
     }
+  };
+  auto load_v = [&](int t) {
+    const int k0 = t * TK;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
+      // 16 consecutive threads take the 16 groups of 4 keys of one block of
+      // 8 dims (their half-chunk stores then hit distinct banks)
       const int it = tid + NT * i;
-      const int kp = it / (HD / 8), c8 = it % (HD / 8);
+      const int db = it / (TK / 4), g4 = it % (TK / 4);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int key = k0 + 2 * kp + u;
-        if (it < VCH && key < T)
-          vreg[i][u] = *reinterpret_cast<const uint4*>(Vb + (int64_t)key * HD + 8 * c8);
+      for (int u = 0; u < 4; ++u) {
+        const int key = k0 + 4 * g4 + u;
+        if (it < VIT && key < T)
+          vreg[i][u] = *reinterpret_cast<const uint4*>(Vb + (int64_t)key * HD + 8 * db);
         else
           vreg[i][u] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + NT * i;
-      const int key = ch / (HD / 8), c8 = ch % (HD / 8);
-      if (ch < KCH) *reinterpret_cast<uint4*>(&Ks[buf][key][8 * c8]) = kreg[i];
-    }
+  auto store_v = [&](uint4* Vdst) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int it = tid + NT * i;
-      const int kp = it / (HD / 8), c8 = it % (HD / 8);
-      if (it < VCH) {
+      if (it < VIT) {
+        const int db = it / (TK / 4), g4 = it % (TK / 4);
+        // keys 4g4 .. 4g4+3 of the tile: k-step s, lane group jj, half hh
+        const int s = g4 >> 3, jj = g4 & 3, hh = (g4 >> 2) & 1;
         const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
         const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
+        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
+        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
+        uint2* row = reinterpret_cast<uint2*>(Vdst);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          // dims 8c8 + 2w and 8c8 + 2w + 1 of keys 2kp and 2kp + 1
-          const uint32_t lo = (v0[w] & 0xffffu) | (v1[w] << 16);
-          const uint32_t hi = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
-          *reinterpret_cast<uint32_t*>(&Vt[buf][8 * c8 + 2 * w][2 * kp]) = lo;
-          *reinterpret_cast<uint32_t*>(&Vt[buf][8 * c8 + 2 * w + 1][2 * kp]) = hi;
+          // dims 8db + 2w (low halves) and 8db + 2w + 1 (high halves) of the 4 keys
+          const uint2 ev = make_uint2((v0[w] & 0xffffu) | (v1[w] << 16), (v2[w] & 0xffffu) | (v3[w] << 16));
+          const uint2 od = make_uint2((v0[w] >> 16) | (v1[w] & 0xffff0000u), (v2[w] >> 16) | (v3[w] & 0xffff0000u));
+          row[lds_slot(8 * db + 2 * w, 4 * s + jj) * 2 + hh] = ev;
+          row[lds_slot(8 * db + 2 * w + 1, 4 * s + jj) * 2 + hh] = od;
         }
       }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+  // one tile: products on buffer BUF while tile t+1 loads into the other
+  auto step = [&](int BUF, int t) {
+    const uint4* Kc = Ks[BUF];
+    const uint4* Vc = Vt[BUF];
+    const bool more = t + 1 < ntiles;
+    if (more) issue_k(t + 1, Ks[BUF ^ 1]);
     const int k0 = t * TK;
-    // S^T for 4 blocks of 16 keys x NQ blocks of 16 queries
-    f32x4_t sc[4][NQ];
+    // S^T for 4 blocks of 16 keys x 16 queries
+    f32x4_t sc[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) sc[kb][n] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][16 * kb + c][32 * ks + 8 * j]);
-#pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-          sc[kb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qhi[n][ks], sc[kb][n], 0, 0, 0);
-          sc[kb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[n][ks], sc[kb][n], 0, 0, 0);
-        }
+        const bf16x8_t kf = __builtin_bit_cast(
+            bf16x8_t, Kc[(ks >> 1) * TK * 8 + kb * 16 * 8 + ((ks & 1) ? kfr1 : kfr0)]);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qhi[ks], sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[ks], sc[kb], 0, 0, 0);
       }
+    // the next tile's V rows load while the softmax and the P V products
+    // run (their registers are free again by then)
+    if (more) load_v(t + 1);
     // online softmax per query; p in place of the scores.  Only a tile that
     // reaches past this wave's first query or past the prompt needs masking.
     const bool masked = k0 + TK - 1 > q0 || k0 + TK > T;
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      const int qi = q0 + 16 * n + c;
-      float mx = m[n];
+    {
+      const int qi = q0 + c;
+      float mx = m;
       if (masked) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = k0 + 16 * kb + 4 * j + r;
-            if (key > qi || key >= T) sc[kb][n][r] = -INFINITY;
+            if (key > qi || key >= T) sc[kb][r] = -INFINITY;
           }
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][n][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // a query sees key 0 in the first tile, so mx is finite from then on
-      const float corr = __builtin_amdgcn_exp2f(m[n] - mx);
+      const float corr = __builtin_amdgcn_exp2f(m - mx);
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sc[kb][n][r] - mx);
-          sc[kb][n][r] = p;
+          const float p = __builtin_amdgcn_exp2f(sc[kb][r] - mx);
+          sc[kb][r] = p;
           ps += p;
         }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
-      l[n] = l[n] * corr + ps;
-      m[n] = mx;
+      l = l * corr + ps;
+      m = mx;
 #pragma unroll
-      for (int b = 0; b < HB; ++b) o[n][b] *= corr;
+      for (int b = 0; b < HB; ++b) o[b] *= corr;
     }
     // O^T += V^T P^T, two k-steps of 32 keys
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      bf16x8_t phi[NQ], plo[NQ];
+    for (int s = 0; s < 2; ++s) {
+      bf16x8_t phi, plo;
 #pragma unroll
-      for (int n = 0; n < NQ; ++n)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16_t hb, lb;
-          split_hi_lo(sc[2 * ps + (e >> 2)][n][e & 3], hb, lb);
-          phi[n][e] = __builtin_bit_cast(__bf16, hb);
-          plo[n][e] = __builtin_bit_cast(__bf16, lb);
-        }
+      for (int e = 0; e < 8; ++e) {
+        bf16_t hb, lb;
+        split_hi_lo(sc[2 * s + (e >> 2)][e & 3], hb, lb);
+        phi[e] = __builtin_bit_cast(__bf16, hb);
+        plo[e] = __builtin_bit_cast(__bf16, lb);
+      }
 #pragma unroll
       for (int b = 0; b < HB; ++b) {
-        const uint2 v0 = *reinterpret_cast<const uint2*>(&Vt[buf][16 * b + c][32 * ps + 4 * j]);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(&Vt[buf][16 * b + c][32 * ps + 16 + 4 * j]);
-        const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vv);
-#pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-          o[n][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[n], o[n][b], 0, 0, 0);
-          o[n][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[n], o[n][b], 0, 0, 0);
-        }
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, Vc[b * 16 * 8 + (s ? vfr1 : vfr0)]);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[b], 0, 0, 0);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[b], 0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    // the next tile's V^T goes to the other buffer (free since the last
+    // barrier); its direct K loads have landed for this wave, then for all
+    if (more) store_v(Vt[BUF ^ 1]);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
-  // lane holds O^T[dims 16b + 4j + r][query 16n + c]
+  };
+
+  issue_k(0, Ks[0]);
+  load_v(0);
+  store_v(Vt[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) step(t & 1, t);
+
+  // lane holds O^T[dims 16b + 4j + r][query c]
   bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) {
-    const int qi = q0 + 16 * n + c;
-    if (qi >= T) continue;
-    const float inv = 1.f / l[n];
+  const int qi = q0 + c;
+  if (qi < T) {
+    const float inv = 1.f / l;
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
       uint2 pk;
-      pk.x = (uint32_t)f2bf(o[n][b][0] * inv) | ((uint32_t)f2bf(o[n][b][1] * inv) << 16);
-      pk.y = (uint32_t)f2bf(o[n][b][2] * inv) | ((uint32_t)f2bf(o[n][b][3] * inv) << 16);
+      pk.x = (uint32_t)f2bf(o[b][0] * inv) | ((uint32_t)f2bf(o[b][1] * inv) << 16);
+      pk.y = (uint32_t)f2bf(o[b][2] * inv) | ((uint32_t)f2bf(o[b][3] * inv) << 16);
       *reinterpret_cast<uint2*>(out + (int64_t)(g * a.Q + qi) * a.out_ld + h * HD + 16 * b + 4 * j) = pk;
     }
   }
@@ -800,7 +831,7 @@ hipError_t prefill_hd(const AttnCall& a, hipStream_t st) {
     // staged K/V tile: half the LDS fills per query of 4 waves
     constexpr int kWaves = 8;
     const int nqb = (a.Q + 16 * kWaves - 1) / (16 * kWaves);
-    PH_LAUNCH((attn_prefill_mfma_kernel<HD, 1, kWaves>), a.G * a.H * nqb, 64 * kWaves, 0, st, a, scale);
+    PH_LAUNCH((attn_prefill_mfma_kernel<HD, kWaves>), a.G * a.H * nqb, 64 * kWaves, 0, st, a, scale);
   } else {
     const int nqb = (a.Q + 63) / 64;
     PH_LAUNCH((attn_prefill_kernel<T, HD>), a.G * a.H * nqb, 256, 0, st, a, scale);

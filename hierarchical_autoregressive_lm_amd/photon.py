@@ -14,7 +14,9 @@ import numpy as np
 import torch  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libphoton.so")
+# PHOTON_LIB selects another build of the same library (the host-sanitized
+# one that the CPU tests load)
+LIB_PATH = os.environ.get("PHOTON_LIB") or os.path.join(_PKG, "libphoton.so")
 
 OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
