@@ -117,14 +117,15 @@ def cpu_baseline_injected(wl, W, threads, mode="recgen", target_s=15.0, sampling
     return len(rows) * wl.cfg.S * done / dt, dt, rows, done
 
 
-def per_config_lines(P, torch, skip, mode):
-    """Decode tok/s and TPM of every workload but `skip`: the workload's
-    seeded weights and prompts, prefill, one untimed pass over its chunks,
-    then one timed pass (graph replay, the headline's method)."""
+def per_config_lines(P, torch, skip, mode, only=None, trace=False):
+    """Decode tok/s and TPM of every workload but `skip` (or of workload
+    `only`): the workload's seeded weights and prompts, prefill, one untimed
+    pass over its chunks, then one timed pass (graph replay, the headline's
+    method)."""
     import photon_inputs as pi
     out = {}
     for idx in sorted(pi.WORKLOADS):
-        if idx == skip:
+        if idx == skip or (only is not None and idx != only):
             continue
         wl = pi.get(idx)
         log(f"per-config line: {wl.name}")
@@ -145,6 +146,21 @@ def per_config_lines(P, torch, skip, mode):
                 model.decode_chunk(tok)
             torch.cuda.synchronize()
             dt = time.perf_counter() - t0
+        path = None
+        if trace:
+            # the same pass again, every dispatch traced: algorithmic bytes
+            # per chunk, so the line carries its own HBM-roofline fraction
+            model.state_restore(snap, wl.prompt)
+            model.trace_enable(None)
+            for _ in range(wl.chunks):
+                model.decode_chunk(tok)
+            torch.cuda.synchronize()
+            cls = model.trace_read()
+            model.trace_enable([])
+            chunk_bytes = sum(v["bytes"] for v in cls.values()) / wl.chunks
+            roof = wl.batch * wl.cfg.S / (chunk_bytes / (HBM_PEAK_GBS * 1e9))
+            path = {"algorithmic_bytes_per_step": round(chunk_bytes), "roofline_tok_s": round(roof, 1),
+                    "frac": round(wl.batch * wl.new_tokens / dt / roof, 4)}
         rep = model.report(wl.batch, wl.max_tokens, mode)
         resident = rep["weights_decode"] + rep["top_kv"] + rep["dec_kv"] + rep["state"]
         if mode == "hiergen":
@@ -154,7 +170,8 @@ def per_config_lines(P, torch, skip, mode):
         out[wl.name] = {"tok_s": round(tok_s, 1), "ms_per_step": round(dt / wl.chunks * 1e3, 4),
                         "steps": wl.chunks, "dtype": "bf16" if wl.cfg.dtype == "bf16" else "f32",
                         "tpm": round(tok_s / (resident / 2 ** 30), 1), "resident_gib": round(resident / 2 ** 30, 4),
-                        "tpm_kv_only": round(tok_s / (kv / 2 ** 30), 1)}
+                        "tpm_kv_only": round(tok_s / (kv / 2 ** 30), 1),
+                        **({"path_roofline": path} if path else {})}
         model.close()
         del model, snap, tok
         torch.cuda.empty_cache()
@@ -510,6 +527,15 @@ def main():
     per_config = None
     if not args.no_per_config and not vanilla and not (args.chunk or args.batch or args.prompt or args.new_tokens):
         per_config = per_config_lines(P, torch, args.workload, args.mode)
+    versus = None
+    if vanilla and not (args.chunk or args.batch or args.prompt or args.new_tokens):
+        # PHOTON RecGen on the same workload (same batch, prompt and new
+        # tokens; one timed pass of its chunks) for the TPM ratio
+        ph = per_config_lines(P, torch, None, "recgen", only=args.workload, trace=True)[wl.name]
+        versus = {"photon_recgen": ph,
+                  "tpm_ratio": round(ph["tpm"] / (tok_s / gib), 1),
+                  "tpm_kv_only_ratio": round(ph["tpm_kv_only"] / (tok_s / kv_gib), 1),
+                  "tok_s_ratio": round(ph["tok_s"] / tok_s, 2)}
 
     cpu = None
     if args.cpu_seqs >= 0:
@@ -590,6 +616,7 @@ def main():
         "aggregate": agg,
         "attn_standalone": attn,
         "counters": counters,
+        "versus_photon": versus,
         "per_config": per_config,
         "cpu_baseline": cpu,
     }
