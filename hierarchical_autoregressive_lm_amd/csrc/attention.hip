@@ -58,7 +58,7 @@ __device__ __forceinline__ int resolve_len(int L_host, const int* L_dev, int L_m
 // 16-lane group (elements [c*CE, (c+1)*CE)).  Sums the QKV GEMM's slabs in
 // slab order; q and k turn by the rotate-half embedding at position pos(t)
 // (pairs (i, i + hd/2): lanes c and c ^ 8 hold partners, exchanged by a
-// shuffle, so all 16 lanes must be active); k and v are rounded to the
+// DPP move inside the 16-lane row, so all 16 lanes must be active); k and v are rounded to the
 // storage dtype (the values a cache read would give).  Returns pos(t).
 template <typename T, int HD>
 __device__ __forceinline__ int new_row(const AttnCall& a, int g, int t, int h, int c, float (&q)[HD / 16],
@@ -81,7 +81,7 @@ __device__ __forceinline__ int new_row(const AttnCall& a, int g, int t, int h, i
   const float* rt = a.rope + ((int64_t)pos * half + (c & 7) * CE) * 2;
 #pragma unroll
   for (int e = 0; e < CE; ++e) {
-    const float xp = __shfl_xor(x[e], 8, 64), yp = __shfl_xor(y[e], 8, 64);
+    const float xp = row16_swap8(x[e]), yp = row16_swap8(y[e]);
     const float cs = rt[2 * e], sn = rt[2 * e + 1];
     if (c < 8) {
       q[e] = x[e] * cs - xp * sn;
@@ -244,10 +244,7 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < CE; ++e) s = fmaf(qv[t][e], kv[u][e], s);
-        s += __shfl_xor(s, 8, 64);
-        s += __shfl_xor(s, 4, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 1, 64);
+        s = row16_sum(s);
         const int key = kb + r + SLOTS * u;
         sc[u] = (key < k1 && key <= L - Q + t) ? s : -INFINITY;
         mx = fmaxf(mx, sc[u]);
@@ -287,10 +284,7 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < CE; ++e) s = fmaf(qv[t][e], kn[e], s);
-        s += __shfl_xor(s, 8, 64);
-        s += __shfl_xor(s, 4, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 1, 64);
+        s = row16_sum(s);
         const float mx = fmaxf(m[t], s);
         const float corr = expf(m[t] - mx), p = expf(s - mx);
 #pragma unroll
@@ -403,10 +397,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnCall a, float scale
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < CE; ++e) d = fmaf(q[e], kv[j][e], d);
-      d += __shfl_xor(d, 8, 64);
-      d += __shfl_xor(d, 4, 64);
-      d += __shfl_xor(d, 2, 64);
-      d += __shfl_xor(d, 1, 64);
+      d = row16_sum(d);
       s[j] = d;
       if (j <= last) mx = fmaxf(mx, d);
     }

@@ -31,6 +31,29 @@ template <> struct St<bf16_t> {
   static __device__ __forceinline__ bf16_t st(float f) { return f2bf(f); }
 };
 
+// DPP moves inside 16-lane rows (lanes 16k .. 16k+15): a VALU operand
+// modifier, so no trip through the LDS crossbar that a shuffle takes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a row, every lane receiving the total: pairs
+// inside each quad (quad_perm 1,0,3,2), the two pairs of a quad (2,3,0,1),
+// the two quads of each half row (row_half_mirror), the two half rows
+// (row_mirror).  At each step both lanes of a pair add the same two values,
+// so the 16 results are bit-identical.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// The value of lane c ^ 8 of the same 16-lane row (row_ror by 8).
+__device__ __forceinline__ float row16_swap8(float v) { return dpp_mov<0x128>(v); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -1316,6 +1316,17 @@ photon_status enqueue_chunk(photon_ctx* c, float* d_logits, hipStream_t st, hipS
   return ok();
 }
 
+// The chunk's token ids (and, when sampling, the log-likelihoods of the
+// drawn tokens) into the caller's buffers, on stream st.
+static photon_status copy_chunk_outputs(photon_ctx* c, int32_t* d_tokens, float* d_logprobs, hipStream_t st) {
+  const int B = (int)c->B, S = (int)levels(&c->cfg).S();
+  HIP_TRY(hipMemcpyAsync(d_tokens, c->ws + c->plan.tok.off, (size_t)B * S * sizeof(int), hipMemcpyDeviceToDevice, st));
+  if (d_logprobs)
+    HIP_TRY(hipMemcpyAsync(d_logprobs, c->sws + sampling_lp_off(c->cfg, B), (size_t)B * S * sizeof(float),
+                           hipMemcpyDeviceToDevice, st));
+  return ok();
+}
+
 // Capture what `enqueue` puts on the context's capture stream as a graph
 // and instantiate it into *exec (left null on failure).
 extern "C++" template <class F>
@@ -1360,7 +1371,6 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
                 (unsigned long long)c->sws_bytes, (long long)c->B, (unsigned long long)sampling_bytes(cf, c->B));
   hipStream_t st = (hipStream_t)stream;
   const int B = (int)c->B;
-  int* tok = (int*)(c->ws + c->plan.tok.off);
   if (c->mode == PHOTON_RECGEN && !c->ahat_ready) {
     // after a prefill or a rewind: this chunk's decoders from the current h
     // (afterwards every chunk leaves them ready for the next one)
@@ -1404,16 +1414,18 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
       HIP_TRY(hipGraphLaunch(c->graph[2], c->cap[1]));
       HIP_TRY(hipEventRecord(c->ev_join, c->cap[1]));
       HIP_TRY(hipGraphLaunch(c->graph[1], st));
+      // the token branch alone writes the chunk's tokens (and the sampler's
+      // log-likelihoods): their copies overlap the top branch's tail
+      PH_TRY(copy_chunk_outputs(c, d_tokens, d_logprobs, st));
       HIP_TRY(hipStreamWaitEvent(st, c->ev_join, 0));
       HIP_TRY(launch_add_int((int*)(c->ws + c->plan.counter.off), 1, st));
+    } else {
+      PH_TRY(copy_chunk_outputs(c, d_tokens, d_logprobs, st));
     }
   } else {
     PH_TRY(enqueue_chunk(c, d_logits, st, st));
+    PH_TRY(copy_chunk_outputs(c, d_tokens, d_logprobs, st));
   }
-  HIP_TRY(hipMemcpyAsync(d_tokens, tok, (size_t)B * S * sizeof(int), hipMemcpyDeviceToDevice, st));
-  if (d_logprobs)
-    HIP_TRY(hipMemcpyAsync(d_logprobs, c->sws + sampling_lp_off(cf, B), (size_t)B * S * sizeof(float),
-                           hipMemcpyDeviceToDevice, st));
   c->top_len += 1;
   c->tokens = c->top_len * S;
   c->tail_pending = false;
