@@ -675,7 +675,11 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
     const bool more = t + 1 < ntiles;
     if (more) issue_k(t + 1, Ks[BUF ^ 1]);
     const int k0 = t * TK;
-    // S^T for 4 blocks of 16 keys x 16 queries
+    // S^T for 4 blocks of 16 keys x 16 queries.  The matrix-product runs
+    // raise the wave's issue priority: of the two waves sharing a SIMD, the
+    // one with products to issue goes first while the other runs its
+    // softmax (1-2 % at 4096-8192 keys)
+    __builtin_amdgcn_s_setprio(1);
     f32x4_t sc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sc[kb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -690,6 +694,7 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
       }
     // the next tile's V rows load while the softmax and the P V products
     // run (their registers are free again by then)
+    __builtin_amdgcn_s_setprio(0);
     if (more) load_v(t + 1);
     // online softmax per query; p in place of the scores.  Only a tile that
     // reaches past this wave's first query or past the prompt needs masking.
@@ -731,6 +736,7 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
       for (int b = 0; b < HB; ++b) o[b] *= corr;
     }
     // O^T += V^T P^T, two k-steps of 32 keys
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8_t phi, plo;
@@ -750,6 +756,7 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
     }
     // the next tile's V^T goes to the other buffer (free since the last
     // barrier); its direct K loads have landed for this wave, then for all
+    __builtin_amdgcn_s_setprio(0);
     if (more) store_v(Vt[BUF ^ 1]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

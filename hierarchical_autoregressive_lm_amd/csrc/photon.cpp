@@ -1385,6 +1385,7 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
     // the chunk a ragged prompt opened: its first tail_r tokens are given
     // (direct launches; the captured graphs serve the whole chunks)
     PH_TRY(enqueue_chunk(c, d_logits, st, st, c->tail_r));
+    PH_TRY(copy_chunk_outputs(c, d_tokens, d_logprobs, st));
   } else if (c->use_graph && !d_logits && c->tr.mask == 0) {
     // RecGen: the prefix and the token branch on `st`, the top branch on a
     // stream of the context, forked after the prefix and joined before the
