@@ -138,32 +138,57 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
   const bool vec = (c.ld % 4 == 0) && (reinterpret_cast<uintptr_t>(c.logits) % 16 == 0);
   BlockRed red{redf, redn, 0};
 
-  // ids 4*(tid + kThreads*q) + w
-  float x[Q][4];
+  // ids 4*(tid + kThreads*q) + w.  Up to 8 groups of 4 stay in registers;
+  // past 32768 ids the other groups go to LDS, one float4 per thread and
+  // group (consecutive threads, consecutive 16 bytes), and every pass visits
+  // them in a rolled loop, so that a 1024-thread block keeps within its 128
+  // registers per lane instead of spilling.
+  constexpr int QR = Q <= 8 ? Q : 8, QL = Q - QR;
+  __shared__ float4 xl[QL > 0 ? QL : 1][QL > 0 ? kThreads : 1];
+  float xr[QR][4];
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const int base = 4 * (tid + kThreads * q);
+    float4 v;
     if (vec && base + 3 < V) {
-      const float4 v = *reinterpret_cast<const float4*>(row + base);
-      x[q][0] = v.x; x[q][1] = v.y; x[q][2] = v.z; x[q][3] = v.w;
+      v = *reinterpret_cast<const float4*>(row + base);
     } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) x[q][w] = base + w < V ? row[base + w] : -INFINITY;
+      v.x = base < V ? row[base] : -INFINITY;
+      v.y = base + 1 < V ? row[base + 1] : -INFINITY;
+      v.z = base + 2 < V ? row[base + 2] : -INFINITY;
+      v.w = base + 3 < V ? row[base + 3] : -INFINITY;
+    }
+    if (q < QR) {
+      xr[q < QR ? q : 0][0] = v.x; xr[q < QR ? q : 0][1] = v.y;
+      xr[q < QR ? q : 0][2] = v.z; xr[q < QR ? q : 0][3] = v.w;
+    } else {
+      xl[q < QR ? 0 : q - QR][tid] = v;   // read back by this thread only
     }
   }
+  // f(q, x) for every group q of this thread, x its 4 values in id order
+  auto each = [&](auto&& f) {
+#pragma unroll
+    for (int q = 0; q < QR; ++q) f(q, xr[q]);
+#pragma unroll 1
+    for (int q = QR; q < Q; ++q) {
+      const float4 v = xl[q - QR][tid];
+      const float x[4] = {v.x, v.y, v.z, v.w};
+      f(q, x);
+    }
+  };
 
   // log-sum-exp of the row (the model's distribution, temperature 1)
   float m = -INFINITY;
+  each([&](int, const float* x) {
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) m = fmaxf(m, x[q][w]);
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, x[w]);
+  });
   m = red.max(m, wave, lane);
   float s = 0.f;
+  each([&](int, const float* x) {
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) s += __expf(x[q][w] - m);   // padding: exp(-inf) = 0
+    for (int w = 0; w < 4; ++w) s += __expf(x[w] - m);   // padding: exp(-inf) = 0
+  });
   s = red.sum(s, wave, lane);
   const float lse = m + logf(s);
 
@@ -188,28 +213,28 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
         continue;
       }
       int n1 = 0, n2 = 0, n3 = 0;
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
+      each([&](int q, const float* x) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t key = 4 * (tid + kThreads * q) + w < V ? order_key(x[q][w]) : 0u;
+          const uint32_t key = 4 * (tid + kThreads * q) + w < V ? order_key(x[w]) : 0u;
           n1 += key >= c1;
           n2 += key >= c2;
           n3 += key >= c3;
         }
+      });
       red.count3(n1, n2, n3, wave, lane);
       band_step(n1, n2, n3, c1, c2, c3, k, t, nt, nu);
     }
     if (b >= 0) {
       // list the band's keys (nt - nu <= kCap of them)
       const uint64_t top = (uint64_t)t + (4ull << b);
-#pragma unroll
-      for (int q = 0; q < Q; ++q)
+      each([&](int q, const float* x) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t key = order_key(x[q][w]);
+          const uint32_t key = order_key(x[w]);
           if (4 * (tid + kThreads * q) + w < V && key >= t && (uint64_t)key < top) cand[atomicAdd(&n_list[0], 1)] = key;
         }
+      });
       __syncthreads();
       const int n = n_list[0];
       const uint32_t mine = tid < n ? cand[tid] : 0u;
@@ -256,25 +281,24 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleCall c) {
   const float inv_t = 1.0f / c.temperature;
   float best = -INFINITY, bx = 0.f;
   int bi = 0x7fffffff;
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
+  each([&](int q, const float* x) {
     const int base = 4 * (tid + kThreads * q);
-    if (base >= V) continue;
+    if (base >= V) return;
     bool any = false;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) any |= base + w < V && (!cut || order_key(x[q][w]) >= t);
-    if (!any) continue;
+    for (int w = 0; w < 4; ++w) any |= base + w < V && (!cut || order_key(x[w]) >= t);
+    if (!any) return;
     const uint4 rw = philox4x32_10(make_uint4((uint32_t)(base / 4), (uint32_t)pos, (uint32_t)seq, 0u), c.k0, c.k1);
     const uint32_t word[4] = {rw.x, rw.y, rw.z, rw.w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int v = base + w;
-      if (v >= V || (cut && order_key(x[q][w]) < t)) continue;
+      if (v >= V || (cut && order_key(x[w]) < t)) continue;
       const float u = ((float)(word[w] >> 9) + 0.5f) * 0x1p-23f;
-      const float sc = x[q][w] * inv_t - __logf(-logf(u));
-      if (sc > best) { best = sc; bi = v; bx = x[q][w]; }
+      const float sc = x[w] * inv_t - __logf(-logf(u));
+      if (sc > best) { best = sc; bi = v; bx = x[w]; }
     }
-  }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float os = __shfl_xor(best, o, 64), ox = __shfl_xor(bx, o, 64);
