@@ -42,7 +42,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sampling=None):
+def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sampling=None, compute="f64"):
     """The oracle as it stands, RecGen decode phase only (perf_counter),
     prefill and weight setup untimed.  seqs = 0: one sequence is decoded
     first to size the sample, then as many sequences (up to the batch) as
@@ -66,7 +66,7 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sam
 
     prefill = O.vanilla_prefill if vanilla else O.prefill
     with threadpool_limits(limits=threads):
-        m = O.Model(pi.vanilla_of(wl.cfg) if vanilla else wl.cfg, W)
+        m = O.Model(pi.vanilla_of(wl.cfg) if vanilla else wl.cfg, W, compute=compute)
         reps = 1
         if seqs <= 0:
             t1 = decode(prefill(m, prompt[:1]))
@@ -84,7 +84,7 @@ def cpu_baseline(wl, W, prompt, seqs, threads, target_s=15.0, vanilla=False, sam
     return reps * seqs * wl.new_tokens / dt, dt, seqs, reps
 
 
-def cpu_baseline_injected(wl, W, threads, mode="recgen", target_s=15.0, sampling=None):
+def cpu_baseline_injected(wl, W, threads, mode="recgen", target_s=15.0, sampling=None, compute="f64"):
     """The oracle as it stands, decode phase only (perf_counter), on the
     fixed sample of sequences {0, B-1}, starting at the prompt end from the
     seeded decode state the parity tests inject
@@ -102,7 +102,7 @@ def cpu_baseline_injected(wl, W, threads, mode="recgen", target_s=15.0, sampling
     rows = sorted({0, wl.batch - 1})
     n = wl.prompt // wl.cfg.S
     with threadpool_limits(limits=threads):
-        m = O.Model(wl.cfg, W)
+        m = O.Model(wl.cfg, W, compute=compute)
         seqs = [pi.gen_decode_state(wl.cfg, r, n, mode, wl.seed) for r in rows]
         dt, done = 0.0, 0
         while dt < target_s:
@@ -545,15 +545,18 @@ def main():
         visible = len(os.sched_getaffinity(0))
         threads = min(visible, int(os.environ.get("OMP_NUM_THREADS") or visible))
         log(f"oracle baseline, {threads} threads ({visible} visible)")
-        prec = "float64" if cfg.dtype == "f32" else "float64 with the bf16 rounding contract"
+        # bf16 models: the oracle's float32 arithmetic (its second
+        # implementation of the rounding contract); fp32 models: float64
+        compute = "f64" if cfg.dtype == "f32" else "f32"
+        prec = "float64" if cfg.dtype == "f32" else "float32 arithmetic with the bf16 rounding contract"
         cpu_model, blas = host_info()
         if vanilla:
-            cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads, vanilla=True)
+            cv, cdt, ns, reps = cpu_baseline(wl, W, prompt, args.cpu_seqs, threads, vanilla=True, compute=compute)
             rep_txt = f", decoded {reps} times from the same prefill" if reps > 1 else ""
             sample = (f"flat-baseline decode phase of {ns} of {B} sequences, all {wl.chunks} chunks{rep_txt} "
                       f"({reps * ns * wl.new_tokens} tokens, {cdt:.1f} s), numpy {prec}")
         else:
-            cv, cdt, rows, done = cpu_baseline_injected(wl, W, threads, args.mode, sampling=sampling)
+            cv, cdt, rows, done = cpu_baseline_injected(wl, W, threads, args.mode, sampling=sampling, compute=compute)
             what = ("sampled " if sampling else "") + ("HierGen" if args.mode == "hiergen" else "RecGen")
             sample = (f"{what} decode phase of sequences {rows} of {B}, {done} chunks from the prompt end "
                       f"({len(rows) * S * done} tokens, {cdt:.1f} s) from the seeded decode state the parity "
