@@ -1370,7 +1370,6 @@ photon_status photon_decode_chunk_lp(photon_ctx* c, int32_t* d_tokens, float* d_
     return fail(PHOTON_ECAPACITY, "sampling workspace holds %llu bytes, batch %lld needs %llu",
                 (unsigned long long)c->sws_bytes, (long long)c->B, (unsigned long long)sampling_bytes(cf, c->B));
   hipStream_t st = (hipStream_t)stream;
-  const int B = (int)c->B;
   if (c->mode == PHOTON_RECGEN && !c->ahat_ready) {
     // after a prefill or a rewind: this chunk's decoders from the current h
     // (afterwards every chunk leaves them ready for the next one)
