@@ -121,7 +121,8 @@ def per_config_lines(P, torch, skip, mode, only=None, trace=False):
     """Decode tok/s and TPM of every workload but `skip` (or of workload
     `only`): the workload's seeded weights and prompts, prefill, one untimed
     pass over its chunks, then one timed pass (graph replay, the headline's
-    method)."""
+    method); with `trace`, a third pass with every dispatch traced gives the
+    line its path-roofline fraction and the top attention's in place."""
     import photon_inputs as pi
     out = {}
     for idx in sorted(pi.WORKLOADS):
@@ -161,6 +162,13 @@ def per_config_lines(P, torch, skip, mode, only=None, trace=False):
             roof = wl.batch * wl.cfg.S / (chunk_bytes / (HBM_PEAK_GBS * 1e9))
             path = {"algorithmic_bytes_per_step": round(chunk_bytes), "roofline_tok_s": round(roof, 1),
                     "frac": round(wl.batch * wl.new_tokens / dt / roof, 4)}
+            if "attn_top" in cls:
+                # the top attention in place (the other branch beside it)
+                v = cls["attn_top"]
+                gbs = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+                path["attn_top"] = {"frac": round(gbs / HBM_PEAK_GBS, 4), "GB_s": round(gbs, 1),
+                                    "avg_us": round(v["ms"] * 1e3 / v["launches"], 2),
+                                    "bytes_per_launch": round(v["bytes"] / v["launches"])}
         rep = model.report(wl.batch, wl.max_tokens, mode)
         resident = rep["weights_decode"] + rep["top_kv"] + rep["dec_kv"] + rep["state"]
         if mode == "hiergen":
@@ -526,7 +534,7 @@ def main():
 
     per_config = None
     if not args.no_per_config and not vanilla and not (args.chunk or args.batch or args.prompt or args.new_tokens):
-        per_config = per_config_lines(P, torch, args.workload, args.mode)
+        per_config = per_config_lines(P, torch, args.workload, args.mode, trace=not args.no_trace)
     versus = None
     if vanilla and not (args.chunk or args.batch or args.prompt or args.new_tokens):
         # PHOTON RecGen on the same workload (same batch, prompt and new
