@@ -583,22 +583,12 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
   const bf16_t* Kb = reinterpret_cast<const bf16_t*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
   const bf16_t* Vb = reinterpret_cast<const bf16_t*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD;
 
-  // Q^T fragments (B operand): lane holds query q0 + c, dims 32ks + 8j .. +8
+  // Q^T fragments (B operand): lane holds query q0 + c, dims 32ks + 8j .. +8,
+  // read as two 16-byte loads per k-step where q's rows allow it (the 8
+  // scalar loads a k-step otherwise takes touch each 128-byte line of the
+  // row 8 times, and this prologue then cost about a sixth of a 2048-key
+  // prompt's workgroup time)
   bf16x8_t qhi[KS], qlo[KS];
-  {
-    const int qi = q0 + c;
-    const float* qp = a.q + (int64_t)(g * a.Q + (qi < T ? qi : T - 1)) * a.q_ld + h * HD + 8 * j;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16_t hb, lb;
-        split_hi_lo(qi < T ? qp[32 * ks + e] * scale2 : 0.f, hb, lb);
-        qhi[ks][e] = __builtin_bit_cast(__bf16, hb);
-        qlo[ks][e] = __builtin_bit_cast(__bf16, lb);
-      }
-    }
-  }
   f32x4_t o[HB];
   float m = -INFINITY, l = 0.f;
 #pragma unroll
@@ -762,8 +752,35 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
     __syncthreads();
   };
 
+  // the first tile's K and V go out before the queries are formed, so the
+  // two prologue latencies overlap
   issue_k(0, Ks[0]);
   load_v(0);
+  {
+    const int qi = q0 + c;
+    const float* qp = a.q + (int64_t)(g * a.Q + (qi < T ? qi : T - 1)) * a.q_ld + h * HD + 8 * j;
+    const bool vec = ((reinterpret_cast<uintptr_t>(a.q) | ((uintptr_t)a.q_ld * sizeof(float))) & 15) == 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float x[8];
+      if (vec) {
+        const float4 v0 = *reinterpret_cast<const float4*>(qp + 32 * ks);
+        const float4 v1 = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
+        x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+        x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = qp[32 * ks + e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16_t hb, lb;
+        split_hi_lo(qi < T ? x[e] * scale2 : 0.f, hb, lb);
+        qhi[ks][e] = __builtin_bit_cast(__bf16, hb);
+        qlo[ks][e] = __builtin_bit_cast(__bf16, lb);
+      }
+    }
+  }
   store_v(Vt[0]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
