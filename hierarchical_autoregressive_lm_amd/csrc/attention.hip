@@ -153,7 +153,7 @@ __device__ __forceinline__ void load_pass(Raw<T, CE, true> (&kr)[U], Raw<T, CE, 
   }
 }
 
-template <typename T, int HD, int Q, int U, int SLOTS = 16>
+template <typename T, int HD, int Q, int U, int SLOTS = 16, bool EARLY = SLOTS == 16>
 __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, float scale) {
   constexpr int CE = HD / 16;
   constexpr int NT = SLOTS * 16;
@@ -174,9 +174,10 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
   const int k1 = min(Lc, k0 + kps);
   const T* Kb = reinterpret_cast<const T*>(a.Kc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
   const T* Vb = reinterpret_cast<const T*>(a.Vc) + (int64_t)(a.seq0 + g) * a.seq_stride + (int64_t)h * a.cap * HD + c * CE;
-  // short caches (16 slots): the first pass's K/V loads go out before the
-  // queries are formed and stay in flight across the hand-over of q
-  constexpr bool kEarly = SLOTS == 16;
+  // EARLY (short caches, and long ones that form q inside): the first
+  // pass's K/V loads go out before the queries are formed and stay in
+  // flight across the hand-over of q
+  constexpr bool kEarly = EARLY;
   Raw<T, CE, true> kr[U], vr[U];
   if (kEarly && k0 < k1) load_pass<T, CE, U, SLOTS, HD>(kr, vr, Kb, Vb, k0, r, k1);
 
@@ -809,8 +810,13 @@ hipError_t decode_hd(const AttnCall& a, hipStream_t st) {
     case 1:
       // long caches: 32 row slots x 8 keys in flight per workgroup; short
       // ones: 16 slots x 6 keys, so that the last pass over the keys is not
-      // nearly empty and more workgroups share the chip
-      if (a.cap >= 1024)
+      // nearly empty and more workgroups share the chip.  A long cache's
+      // step that forms q inside (one round of workgroups) takes 6 keys per
+      // slot with the first pass issued early: 8 keys plus the early pass
+      // need 148 registers, one workgroup per CU instead of two
+      if (a.cap >= 1024 && a.qkv)
+        PH_LAUNCH((attn_decode_kernel<T, HD, 1, 6, 32, true>), grid, dim3(512), 0, st, a, scale);
+      else if (a.cap >= 1024)
         PH_LAUNCH((attn_decode_kernel<T, HD, 1, 8, 32>), grid, dim3(512), 0, st, a, scale);
       else
         PH_LAUNCH((attn_decode_kernel<T, HD, 1, 6>), grid, block, 0, st, a, scale);
@@ -886,6 +892,15 @@ hipError_t dispatch_prefill(const AttnCall& a, hipStream_t st) {
 }
 
 }  // namespace
+
+bool attn_decode_rope_inside(int G, int H, int cap, int nsplit) {
+  // the forming of q (counter -> RoPE table -> QKV slabs) sits before every
+  // workgroup's first scores: paid once by a launch whose workgroups are all
+  // resident at once (short caches: 4 per CU; long: 2 per CU of 512
+  // threads), once per round by a longer one, where a launch of its own is
+  // cheaper
+  return cap < 1024 || (int64_t)G * H * nsplit <= 2 * 256;
+}
 
 int attn_decode_splits(int G, int H, int cap, int Q) {
   const int pairs = G * H;

@@ -204,5 +204,10 @@ hipError_t launch_aggregate(const AggregateCall& c, hipStream_t st);
 // queries each over a cache of `cap` slots (plan-time, so one plan serves
 // every length <= cap).
 int attn_decode_splits(int G, int H, int cap, int Q);
+// Whether a decode step's attention should form q and append the new K/V
+// rows itself (AttnCall::qkv) rather than take them from a RoPE launch of
+// their own: caches under 1024 slots, and longer ones whose G*H*nsplit
+// workgroups are all resident at once.
+bool attn_decode_rope_inside(int G, int H, int cap, int nsplit);
 
 }  // namespace photon

@@ -795,11 +795,13 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
     void* Vc = kbase + r.kv.plane_elems * eb;
     // RoPE and the K/V append run inside the attention kernel (the new rows
     // are the last Q keys of every group) for the chunk-confined decoders and
-    // for decode steps over caches of fewer than 1024 slots; a long cache's
-    // step (whose attention streams far more than the launch costs) and
-    // prefill give them a launch of their own, which keeps the forming of q
-    // off the long stream's start
-    const bool fuse = r.rows_per_seq == r.Q && (r.kind == ATT_CHUNK || (r.kind == ATT_DECODE && r.kv.cap < 1024));
+    // for decode steps over caches of fewer than 1024 slots or whose
+    // workgroups are all resident at once; a longer launch over a long cache
+    // (where every round of workgroups would wait for its q) and prefill
+    // give them a launch of their own
+    const bool fuse = r.rows_per_seq == r.Q &&
+                      (r.kind == ATT_CHUNK ||
+                       (r.kind == ATT_DECODE && attn_decode_rope_inside(r.G, H, (int)r.kv.cap, r.nsplit)));
     if (!fuse) {
       RopeKvCall rc{dt, b.part, ks, (int64_t)r.M * 3 * d, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
                     r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
