@@ -60,15 +60,47 @@ __device__ __forceinline__ int resolve_len(int L_host, const int* L_dev, int L_m
 // (pairs (i, i + hd/2): lanes c and c ^ 8 hold partners, exchanged by a
 // DPP move inside the 16-lane row, so all 16 lanes must be active); k and v are rounded to the
 // storage dtype (the values a cache read would give).  Returns pos(t).
-template <typename T, int HD>
+// AHEAD (decode kernels, whose register peak lies in the key loop): every
+// load goes out before the first sum waits (the table entries, then the
+// slabs two at a time, summed in slab order all the same), so forming q
+// costs one round trip instead of one per slab plus the table's.  The chunk
+// kernel keeps the loads in step with the sums (the extra values in flight
+// would cost it occupancy).
+template <typename T, int HD, bool AHEAD = false>
 __device__ __forceinline__ int new_row(const AttnCall& a, int g, int t, int h, int c, float (&q)[HD / 16],
                                        float (&k)[HD / 16], float (&v)[HD / 16]) {
   constexpr int CE = HD / 16, half = HD / 2;
   const float* p = a.qkv + ((int64_t)g * a.Q + t) * 3 * a.d + h * HD + c * CE;
+  const int pos = a.pos_add + (a.pos_dev ? (*a.pos_dev) * a.pos_mul : 0) + t;
+  const float* rt = a.rope + ((int64_t)pos * half + (c & 7) * CE) * 2;
+  float cs[CE], sn[CE];
+  if constexpr (AHEAD) {
+#pragma unroll
+    for (int e = 0; e < CE; ++e) { cs[e] = rt[2 * e]; sn[e] = rt[2 * e + 1]; }
+  }
   float x[CE], y[CE];
 #pragma unroll
   for (int e = 0; e < CE; ++e) { x[e] = 0.f; y[e] = 0.f; v[e] = 0.f; }
-  for (int sl = 0; sl < a.ksplit; ++sl) {
+  int sl = 0;
+  if constexpr (AHEAD) {
+    for (; sl + 1 < a.ksplit; sl += 2) {
+      const float* p0 = p + sl * a.pstride;
+      const float* p1 = p0 + a.pstride;
+      float x0[CE], y0[CE], v0[CE], x1[CE], y1[CE], v1[CE];
+#pragma unroll
+      for (int e = 0; e < CE; ++e) {
+        x0[e] = p0[e]; y0[e] = p0[a.d + e]; v0[e] = p0[2 * a.d + e];
+        x1[e] = p1[e]; y1[e] = p1[a.d + e]; v1[e] = p1[2 * a.d + e];
+      }
+#pragma unroll
+      for (int e = 0; e < CE; ++e) {
+        x[e] = (x[e] + x0[e]) + x1[e];
+        y[e] = (y[e] + y0[e]) + y1[e];
+        v[e] = (v[e] + v0[e]) + v1[e];
+      }
+    }
+  }
+  for (; sl < a.ksplit; ++sl) {
     const float* ps = p + sl * a.pstride;
 #pragma unroll
     for (int e = 0; e < CE; ++e) {
@@ -77,18 +109,19 @@ __device__ __forceinline__ int new_row(const AttnCall& a, int g, int t, int h, i
       v[e] += ps[2 * a.d + e];
     }
   }
-  const int pos = a.pos_add + (a.pos_dev ? (*a.pos_dev) * a.pos_mul : 0) + t;
-  const float* rt = a.rope + ((int64_t)pos * half + (c & 7) * CE) * 2;
+  if constexpr (!AHEAD) {
+#pragma unroll
+    for (int e = 0; e < CE; ++e) { cs[e] = rt[2 * e]; sn[e] = rt[2 * e + 1]; }
+  }
 #pragma unroll
   for (int e = 0; e < CE; ++e) {
     const float xp = row16_swap8(x[e]), yp = row16_swap8(y[e]);
-    const float cs = rt[2 * e], sn = rt[2 * e + 1];
     if (c < 8) {
-      q[e] = x[e] * cs - xp * sn;
-      k[e] = St<T>::ld(St<T>::st(y[e] * cs - yp * sn));
+      q[e] = x[e] * cs[e] - xp * sn[e];
+      k[e] = St<T>::ld(St<T>::st(y[e] * cs[e] - yp * sn[e]));
     } else {
-      q[e] = x[e] * cs + xp * sn;
-      k[e] = St<T>::ld(St<T>::st(y[e] * cs + yp * sn));
+      q[e] = x[e] * cs[e] + xp * sn[e];
+      k[e] = St<T>::ld(St<T>::st(y[e] * cs[e] + yp * sn[e]));
     }
     v[e] = St<T>::ld(St<T>::st(v[e]));
   }
@@ -193,7 +226,7 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
 #pragma unroll
       for (int t = 0; t < Q; ++t) {
         float qn[CE], kn[CE], vn[CE];
-        const int pos = new_row<T, HD>(a, g, t, h, c, qn, kn, vn);
+        const int pos = new_row<T, HD, true>(a, g, t, h, c, qn, kn, vn);
 #pragma unroll
         for (int e = 0; e < CE; ++e) qs[t][c * CE + e] = qn[e] * scale;
         if constexpr (Q == 1) {
@@ -276,7 +309,7 @@ __global__ __launch_bounds__(SLOTS * 16) void attn_decode_kernel(AttnCall a, flo
         for (int e = 0; e < CE; ++e) { kn[e] = kn1[e]; vn[e] = vn1[e]; }
       } else {
         float qd[CE];
-        const int pos = new_row<T, HD>(a, g, tn, h, c, qd, kn, vn);
+        const int pos = new_row<T, HD, true>(a, g, tn, h, c, qd, kn, vn);
         store_row<T, HD>(a, g, h, c, pos, kn, vn);
       }
 #pragma unroll
