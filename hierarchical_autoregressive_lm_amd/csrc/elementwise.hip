@@ -21,6 +21,20 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// The same for a kernel that sums once: one barrier, ordering only LDS (the
+// row's global stores before it need not complete first).
+__device__ __forceinline__ float block_sum_once(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
 // Four consecutive outputs in the storage dtype, one store (8 bytes for
 // bf16; the column is a multiple of 4 and rows are 16-byte aligned).
 template <typename T>
@@ -52,6 +66,14 @@ __global__ __launch_bounds__(1024) void rows_epilogue_kernel(RowsEpi e) {
     if (e.resid) acc = *reinterpret_cast<const float4*>(e.resid + r * d + c);
     const float* pp = e.P + r * e.ldp + c;
     int s = 0;
+    if (e.ksplit >= 8) {                  // eight slabs in flight, added in order
+      float4 p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = *reinterpret_cast<const float4*>(pp + k * e.pstride);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { acc.x += p[k].x; acc.y += p[k].y; acc.z += p[k].z; acc.w += p[k].w; }
+      s = 8;
+    }
     for (; s + 4 <= e.ksplit; s += 4) {   // four slabs in flight, added in order
       const float4 p0 = *reinterpret_cast<const float4*>(pp + (s + 0) * e.pstride);
       const float4 p1 = *reinterpret_cast<const float4*>(pp + (s + 1) * e.pstride);
@@ -71,13 +93,18 @@ __global__ __launch_bounds__(1024) void rows_epilogue_kernel(RowsEpi e) {
       acc.x += St<T>::ld(erow[c]); acc.y += St<T>::ld(erow[c + 1]);
       acc.z += St<T>::ld(erow[c + 2]); acc.w += St<T>::ld(erow[c + 3]);
     }
-    if (e.x_out) *reinterpret_cast<float4*>(e.x_out + r * d + c) = acc;
   }
-  if (!e.a_out) return;                   // uniform across the block
+  // both stores after the row's sum: a store still in flight would hold
+  // the reduction up (the wait before it counts stores too)
+  if (!e.a_out) {                         // uniform across the block
+    if (act && e.x_out) *reinterpret_cast<float4*>(e.x_out + r * d + c) = acc;
+    return;
+  }
   float ss = act ? acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w : 0.f;
-  ss = block_sum(ss, red);
+  ss = block_sum_once(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + e.eps);
   if (act) {
+    if (e.x_out) *reinterpret_cast<float4*>(e.x_out + r * d + c) = acc;
     T* orow = reinterpret_cast<T*>(e.a_out) + (int64_t)i * e.a_ld;
     const float4 gg = *reinterpret_cast<const float4*>(e.g + c);
     store4<T>(orow + c, gg.x * (acc.x * inv), gg.y * (acc.y * inv), gg.z * (acc.z * inv), gg.w * (acc.w * inv));
