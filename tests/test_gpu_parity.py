@@ -37,6 +37,19 @@ def test_tiny_f32_long_prompt_split_attention():
     _report("tiny-f32 P=4800", r)
 
 
+def test_tiny_f32_long_cache_split_attention_rope_inside():
+    # 1100 top states, a cache of 1103 slots (past the 1024 from which the
+    # long-cache kernel runs): two sequences of two heads give 4 (sequence,
+    # head) pairs, so the top step splits its keys over 5 workgroups per
+    # pair, all resident at once, and that launch forms q, appends the new
+    # K/V row and folds it in itself (last split), then the splits combine
+    cfg = pi.CONFIGS["tiny"]
+    W, pr = _inputs(cfg, 2, 16 * 1100, 23)
+    model, toks, lg = gpu_generate(cfg, W, pr, 48)
+    r = check_against_oracle(cfg, W, pr, toks, lg)
+    _report("tiny-f32 P=17600", r)
+
+
 @pytest.mark.parametrize("mode", ["recgen", "hiergen"])
 def test_small_bf16_ragged_batch(mode):
     cfg = small_cfg()
