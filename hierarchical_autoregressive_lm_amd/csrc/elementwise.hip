@@ -9,20 +9,10 @@
 namespace photon {
 namespace {
 
-// Block-wide sum for the row kernels (blockDim.x a multiple of 64, <= 1024).
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();                      // red may still be read by a previous call
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int i = 0; i < nw; ++i) t += red[i];
-  return t;
-}
 
-// The same for a kernel that sums once: one barrier, ordering only LDS (the
-// row's global stores before it need not complete first).
+// Block-wide sum for the row kernels (blockDim.x a multiple of 64, <= 1024),
+// once per kernel (red is not reused): one barrier, ordering only LDS, so
+// no global access before it has to complete first.
 __device__ __forceinline__ float block_sum_once(float v, float* red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -214,12 +204,12 @@ __global__ __launch_bounds__(1024) void argmax_next_kernel(ArgmaxNext c) {
     const T* erow = reinterpret_cast<const T*>(c.E) + (int64_t)bi * d;
     acc.x += St<T>::ld(erow[col]); acc.y += St<T>::ld(erow[col + 1]);
     acc.z += St<T>::ld(erow[col + 2]); acc.w += St<T>::ld(erow[col + 3]);
-    *reinterpret_cast<float4*>(c.x + (int64_t)m * d + col) = acc;
   }
   float ss = act ? acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w : 0.f;
-  ss = block_sum(ss, red);
+  ss = block_sum_once(ss, red);           // the stores after it (see rows_epilogue_kernel)
   const float inv = 1.0f / sqrtf(ss / (float)d + c.eps);
   if (act) {
+    *reinterpret_cast<float4*>(c.x + (int64_t)m * d + col) = acc;
     T* orow = reinterpret_cast<T*>(c.a) + (int64_t)m * d;
     const float4 gg = *reinterpret_cast<const float4*>(c.g + col);
     orow[col + 0] = St<T>::st(gg.x * (acc.x * inv));
