@@ -419,6 +419,7 @@ def main():
                "tflop": round(pre_flops / 1e12, 3), "tflop_s": round(pre_flops / pre_s / 1e12, 1),
                "attention": tf(["attn_prefill"]),
                "gemm": tf(["gemm_qkv", "gemm_o", "gemm_up", "gemm_down", "gemm_chunk"]),
+               "by_class": {n: tf([n]) for n in sorted(pre_cls)},
                "mfma_peak_tflop_s": MFMA_BF16_PEAK_TFLOPS}
     log(f"prefill {pre_s:.3f} s ({prefill['tflop_s']} TFLOP/s)")
     if args.mode == "recgen":

@@ -148,6 +148,21 @@ __global__ __launch_bounds__(256) void embed_gather_kernel(const int* ids, int64
   out[idx] = E[clamp_id(ids[(r / L) * ld + r % L], V) * d + e];
 }
 
+// The same, 16 bytes per thread (rows of d storage elements, d * sizeof(T)
+// a multiple of 16, E and out 16-byte aligned).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_gather16_kernel(const int* ids, int64_t n, int L, int64_t ld,
+                                                             const T* E, int d, int V, T* out) {
+  constexpr int PER = 16 / sizeof(T);
+  const int dv = d / PER;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n * dv) return;
+  const int64_t r = idx / dv;
+  const int e = (int)(idx % dv) * PER;
+  *reinterpret_cast<uint4*>(out + r * d + e) =
+      *reinterpret_cast<const uint4*>(E + clamp_id(ids[(r / L) * ld + r % L], V) * d + e);
+}
+
 __global__ __launch_bounds__(256) void copy_ids_kernel(int* dst, int64_t dst_ld, const int* src, int64_t src_ld,
                                                        int rows, int cols, int V) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -283,6 +298,17 @@ hipError_t launch_embed_gather_rows(int dtype, const int* ids, int64_t rows, int
                                     int V, void* out, hipStream_t st) {
   const int64_t n = rows * L;
   if (n <= 0) return hipSuccess;
+  const int eb = dtype ? 2 : 4;
+  if ((d * eb) % 16 == 0 && (uintptr_t)E % 16 == 0 && (uintptr_t)out % 16 == 0) {
+    const int64_t nv = n * (d * eb / 16);
+    if (dtype)
+      PH_LAUNCH((embed_gather16_kernel<bf16_t>), blocks(nv), 256, 0, st, ids, n, L, ld, (const bf16_t*)E, d, V,
+                (bf16_t*)out);
+    else
+      PH_LAUNCH((embed_gather16_kernel<float>), blocks(nv), 256, 0, st, ids, n, L, ld, (const float*)E, d, V,
+                (float*)out);
+    return hipGetLastError();
+  }
   if (dtype)
     PH_LAUNCH((embed_gather_kernel<bf16_t>), blocks(n * d), 256, 0, st, ids, n, L, ld, (const bf16_t*)E, d, V,
               (bf16_t*)out);

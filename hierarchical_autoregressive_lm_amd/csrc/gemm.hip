@@ -32,6 +32,10 @@ struct GemmP {
   float* av; int* ai;
   int m_tiles, n_tiles;
   int ksplit; int64_t pstride;   // k slabs; elements between RAW slabs
+  // EPI_ROPE (prompt QKV projection): rotated q to q (fp32 [M][d]), rotated
+  // k and v rounded to bf16 into the cache planes Kc / Vc
+  float* q; bf16_t* Kc; bf16_t* Vc; const float* rope;
+  int64_t seq_stride; int cap, rows_per_seq, seq0, pos_add, d;
 };
 
 template <int MB, int NI, int WK, int P, int EPI, int NKB, bool NTW>
@@ -421,7 +425,65 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
 
   // epilogue: each lane holds features 4*(lane>>4)..+3 of row (lane&15)
   const int fl = (lane >> 4) * 4;
-  if constexpr (EPI != EPI_ARGMAX) {
+  if constexpr (EPI == EPI_ROPE) {
+    // A wave's TN columns are one head of q, k or v (TN = head size, the
+    // tile starts on a head), so the rotate-half partner of feature c < TN/2,
+    // c + TN/2, sits in the same lane, fragment j + NF/2.  Row r of the
+    // product is new row t = r % rows_per_seq of sequence r / rows_per_seq,
+    // at position pos_add + t; its K and V go to cache slot pos.
+    static_assert(NF % 2 == 0, "rotation partners are half a head apart");
+    constexpr int HALF = TN / 2;
+    const int col0 = n0 + wn * TN;
+    const int part = col0 / p.d;                 // 0 q, 1 k, 2 v (uniform per wave)
+    const int h = (col0 - part * p.d) / TN;
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int row = m0 + wm * TM + i * 16 + (lane & 15);
+      if (row >= p.M) continue;
+      const int sq = row / p.rows_per_seq, t = row - sq * p.rows_per_seq;
+      const int pos = p.pos_add + t;
+      const int64_t slot = (int64_t)(p.seq0 + sq) * p.seq_stride + ((int64_t)h * p.cap + pos) * TN;
+      if (part == 2) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const f32x4 v = acc[i][j];
+          uint2 pk;
+          pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+          pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          *reinterpret_cast<uint2*>(p.Vc + slot + j * 16 + fl) = pk;
+        }
+        continue;
+      }
+      const float* rp = p.rope + (int64_t)pos * TN;   // (cos, sin) of features 0 .. HALF-1
+#pragma unroll
+      for (int j = 0; j < NF / 2; ++j) {
+        const int cc = j * 16 + fl;
+        const float4 r0 = *reinterpret_cast<const float4*>(rp + 2 * cc);
+        const float4 r1 = *reinterpret_cast<const float4*>(rp + 2 * cc + 4);
+        const float cs[4] = {r0.x, r0.z, r1.x, r1.z}, sn[4] = {r0.y, r0.w, r1.y, r1.w};
+        const f32x4 a = acc[i][j], b = acc[i][j + NF / 2];
+        float lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = a[e] * cs[e] - b[e] * sn[e];
+          hi[e] = b[e] * cs[e] + a[e] * sn[e];
+        }
+        if (part == 0) {
+          float* q = p.q + (int64_t)row * p.d + h * TN + cc;
+          *reinterpret_cast<float4*>(q) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+          *reinterpret_cast<float4*>(q + HALF) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+        } else {
+          uint2 pl, ph;
+          pl.x = (uint32_t)f2bf(lo[0]) | ((uint32_t)f2bf(lo[1]) << 16);
+          pl.y = (uint32_t)f2bf(lo[2]) | ((uint32_t)f2bf(lo[3]) << 16);
+          ph.x = (uint32_t)f2bf(hi[0]) | ((uint32_t)f2bf(hi[1]) << 16);
+          ph.y = (uint32_t)f2bf(hi[2]) | ((uint32_t)f2bf(hi[3]) << 16);
+          *reinterpret_cast<uint2*>(p.Kc + slot + cc) = pl;
+          *reinterpret_cast<uint2*>(p.Kc + slot + cc + HALF) = ph;
+        }
+      }
+    }
+  } else if constexpr (EPI != EPI_ARGMAX) {
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int row = m0 + wm * TM + i * 16 + (lane & 15);
@@ -832,6 +894,47 @@ int gemm_argmax_tiles(int dtype, int M, int N, int K) {
 int gemm_splits(int dtype, int M, int N, int K, int wide) {
   if (dtype == 0) return 1;
   return plan_bf16(M, N, K, EPI_STORE, true, wide != 0).ksplit;
+}
+
+// Prompt QKV projection with RoPE and the K/V append in its epilogue: 256-row
+// tiles two heads wide (8 waves, 4 along M; each wave's columns are one head),
+// three ring stages where two fit the LDS, else two.
+namespace {
+GemmKernel qkv_rope_kernel(int hd, int K, int* stages) {
+  GemmKernel fn = nullptr;
+  int P = 0;
+  if (hd == 64) { fn = gemm_lds_kernel<256, 128, 4, 3, EPI_ROPE, 0, 8>; P = 3; }
+  if (hd == 96) { fn = gemm_lds_kernel<256, 192, 4, 2, EPI_ROPE, 0, 8>; P = 2; }
+  if (hd == 128) { fn = gemm_lds_kernel<256, 256, 4, 2, EPI_ROPE, 0, 8>; P = 2; }
+  if (!fn || K % 64 || (K / 64) % P) return nullptr;
+  if (stages) *stages = P;
+  return fn;
+}
+bool aligned(const void* ptr, int bytes) { return ((uintptr_t)ptr % bytes) == 0; }
+}  // namespace
+
+int gemm_qkv_rope_supported(const GemmCall& g, const RopeKvCall& rc) {
+  if (g.dtype != 1 || rc.dtype != 1 || g.M < kBigM || rc.M != g.M || rc.pos_dev) return 0;
+  if (!qkv_rope_kernel(rc.hd, g.K, nullptr) || rc.d != rc.H * rc.hd || g.N != 3 * rc.d || (3 * rc.H) % 2) return 0;
+  if (g.lda % 8 || !aligned(g.A, 16) || !aligned(g.W, 16) || !aligned(rc.q_out, 16) || !aligned(rc.Kc, 8) ||
+      !aligned(rc.Vc, 8) || !aligned(rc.rope, 16) || rc.seq_stride % 4 || rc.rows_per_seq < 1)
+    return 0;
+  return 1;
+}
+
+hipError_t launch_gemm_qkv_rope(const GemmCall& g, const RopeKvCall& rc, hipStream_t st) {
+  if (!gemm_qkv_rope_supported(g, rc)) return hipErrorInvalidValue;
+  GemmKernel fn = qkv_rope_kernel(rc.hd, g.K, nullptr);
+  const int BN = 2 * rc.hd;
+  GemmP p{};
+  p.A = (const bf16_t*)g.A; p.lda = g.lda; p.W = (const bf16_t*)g.W;
+  p.M = g.M; p.N = g.N; p.K = g.K;
+  p.m_tiles = (g.M + 255) / 256; p.n_tiles = g.N / BN; p.ksplit = 1;
+  p.q = rc.q_out; p.Kc = (bf16_t*)rc.Kc; p.Vc = (bf16_t*)rc.Vc; p.rope = rc.rope;
+  p.seq_stride = rc.seq_stride; p.cap = rc.cap; p.rows_per_seq = rc.rows_per_seq; p.seq0 = rc.seq0;
+  p.pos_add = rc.pos_add; p.d = rc.d;
+  PH_LAUNCH(fn, p.m_tiles * p.n_tiles, 512, 0, st, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmCall& g, hipStream_t st) {

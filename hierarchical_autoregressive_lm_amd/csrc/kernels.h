@@ -32,7 +32,7 @@ inline LaunchEvents& launch_events() {
     }                                                                                                  \
   } while (0)
 
-enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_GELU = 2, EPI_ARGMAX = 3 };
+enum Epi { EPI_STORE = 0, EPI_ADD = 1, EPI_GELU = 2, EPI_ARGMAX = 3, EPI_ROPE = 4 };
 
 // C[M,N] = A[M,K] W[N,K]^T with a fused epilogue:
 //   STORE : C (fp32, row stride ldc) = acc
@@ -97,6 +97,16 @@ struct RopeKvCall {
   const float* rope;       // [max_pos][hd/2][2] (cos, sin)
 };
 hipError_t launch_rope_kv(const RopeKvCall& c, hipStream_t st);
+
+// Prompt QKV projection fused with launch_rope_kv's work: the GEMM g (A the
+// normalized rows, W = Wqkv, N = 3d, no K slabs) writes rotated q to
+// rc.q_out and rotated k and v, rounded to bf16, to the cache planes, with
+// rc's row, sequence and position map (rc.qkv and rc.ksplit unused).  Only
+// for bf16 prompt-sized GEMMs (M >= 2048) with head size 64, 96 or 128, an
+// even number of heads in 3d, host positions (pos_dev null) and aligned
+// buffers; gemm_qkv_rope_supported says whether a call qualifies.
+int gemm_qkv_rope_supported(const GemmCall& g, const RopeKvCall& rc);
+hipError_t launch_gemm_qkv_rope(const GemmCall& g, const RopeKvCall& rc, hipStream_t st);
 
 // Attention of Q new queries per sequence over a K/V cache.  Query t of
 // sequence g sees keys 0 .. L - Q + t, L = L_host or *L_dev*L_mul + L_add.

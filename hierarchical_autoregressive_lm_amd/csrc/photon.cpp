@@ -789,10 +789,25 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
   for (int l = 0; l < L; ++l) {
     const LayerW& w = sw.layers[l];
     int ks = 1;
-    PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_QKV, b.a, d, w.Wqkv, r.M, 3 * d, d, b.part, &ks, st));
     unsigned char* kbase = r.kv.base + (r.kv.per_layer ? (int64_t)l * 2 * r.kv.plane_elems * eb : 0);
     void* Kc = kbase;
     void* Vc = kbase + r.kv.plane_elems * eb;
+    // a prompt's QKV projection rotates q and k and appends K/V in its own
+    // epilogue where the kernel supports the shape; otherwise the product's
+    // K slabs go to a RoPE + append launch (or into the attention, below)
+    GemmCall gq{};
+    gq.dtype = dt; gq.A = b.a; gq.lda = d; gq.W = w.Wqkv; gq.M = r.M; gq.N = 3 * d; gq.K = d;
+    RopeKvCall rq{dt, nullptr, 1, 0, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
+                  r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
+    const bool qkv_rope = r.kind == ATT_PREFILL && gemm_qkv_rope_supported(gq, rq);
+    if (qkv_rope) {
+      // W and the operand rows read once, q (fp32) and K, V written once
+      const double qb = (double)gq.N * d * eb + (double)r.M * d * eb + (double)r.M * d * (4 + 2.0 * eb);
+      PH_TRY(traced(c, PHOTON_K_GEMM_QKV, qb, 2.0 * r.M * gq.N * d, st, "gemm",
+                    [&] { return launch_gemm_qkv_rope(gq, rq, st); }));
+    } else {
+      PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_QKV, b.a, d, w.Wqkv, r.M, 3 * d, d, b.part, &ks, st));
+    }
     // RoPE and the K/V append run inside the attention kernel (the new rows
     // are the last Q keys of every group) for the chunk-confined decoders and
     // for decode steps over caches of fewer than 1024 slots or whose
@@ -802,7 +817,7 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
     const bool fuse = r.rows_per_seq == r.Q &&
                       (r.kind == ATT_CHUNK ||
                        (r.kind == ATT_DECODE && attn_decode_rope_inside(r.G, H, (int)r.kv.cap, r.nsplit)));
-    if (!fuse) {
+    if (!fuse && !qkv_rope) {
       RopeKvCall rc{dt, b.part, ks, (int64_t)r.M * 3 * d, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
                     r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
       PH_TRY(traced(c, PHOTON_K_ROPE_KV, (double)r.M * d * (12.0 + 4 + 2 * eb), 6.0 * r.M * d, st, "rope_kv",
