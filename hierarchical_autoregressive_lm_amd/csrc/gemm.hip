@@ -300,7 +300,7 @@ constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (0 << 8) | (((n >> 4
 
 #define PH_LDS_SLOTS(X) X(0) X(1) X(2) X(3) X(4) X(5)
 
-template <int BM, int BN, int WM, int P, int EPI, int NKB, int NW = 4>
+template <int BM, int BN, int WM, int P, int EPI, int NKB, int NW = 4, bool PERSIST = false>
 __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
   constexpr int WN = NW / WM, TM = BM / WM, TN = BN / WN, MF = TM / 16, NF = TN / 16;
   constexpr int ROWS = BM + BN;             // A rows, then W rows; 128 B each
@@ -308,6 +308,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
   constexpr int I = ROWS / (8 * NW);        // direct-load instructions per wave per stage
   static_assert(ROWS % (8 * NW) == 0 && TM % 16 == 0 && TN % 16 == 0 && P >= 2 && P <= 6, "tile");
   static_assert(EPI != EPI_ARGMAX || 2 * WN * BM * 4 <= ROWS * 128, "argmax partials fit a slot");
+  static_assert(!PERSIST || (NKB == 0 && (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_ROPE)),
+                "persistent workgroups: run-time k loop, epilogues that store only");
+  static_assert(!PERSIST || (P - 2) * I + MF * NF <= 63, "waits fit the counter");
 #define PH_DECL(s) __shared__ __attribute__((aligned(16))) uint4 L##s[s < P ? SLOT_U4 : 1];
   PH_LDS_SLOTS(PH_DECL)
 #undef PH_DECL
@@ -315,20 +318,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
   const int wm = wave / WN, wn = wave % WN;
 
   const int total = p.m_tiles * p.n_tiles;
-  const int ks = blockIdx.x % p.ksplit;
-  const int bid = blockIdx.x / p.ksplit;
-  const int tile = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
-  // row tiles in groups of 1024 rows, the row tile fastest inside a group:
-  // while an XCD walks a group's columns its A tiles stay in L2 and each W
-  // column slab serves the whole group (prompt-sized GEMMs, whose A
-  // outgrows the Infinity Cache: 5-17 % faster than walking every row tile
-  // per column; groups of 512 or 2048 rows measured slower); at most 1024
-  // rows (every decode shape) this is the plain row-fastest order
-  constexpr int GR = 1024 / BM;
-  const int grp = tile / (GR * p.n_tiles), base = grp * GR;
-  const int gs = min(GR, p.m_tiles - base), r = tile - grp * GR * p.n_tiles;
-  const int mt = base + r % gs, nt = r / gs;
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int ks = PERSIST ? 0 : blockIdx.x % p.ksplit;
+  // XCD-aware tile order: consecutive workgroups land on different XCDs, so
+  // each XCD takes a contiguous run of tiles.  Inside the run, row tiles in
+  // groups of 1024 rows, the row tile fastest inside a group: while an XCD
+  // walks a group's columns its A tiles stay in L2 and each W column slab
+  // serves the whole group (prompt-sized GEMMs, whose A outgrows the
+  // Infinity Cache: 5-17 % faster than walking every row tile per column;
+  // groups of 512 or 2048 rows measured slower); at most 1024 rows (every
+  // decode shape) this is the plain row-fastest order.  Persistent
+  // workgroups take virtual tiles v, v + gridDim.x, ... (gridDim.x a
+  // multiple of 8, so every one stays on its XCD's run).
+  auto tile_of = [&](int v, int& tm0, int& tn0) {
+    const int tile = (total % 8 == 0) ? (v % 8) * (total / 8) + v / 8 : v;
+    constexpr int GR = 1024 / BM;
+    const int grp = tile / (GR * p.n_tiles), base = grp * GR;
+    const int gs = min(GR, p.m_tiles - base), r = tile - grp * GR * p.n_tiles;
+    tm0 = (base + r % gs) * BM;
+    tn0 = (r / gs) * BN;
+  };
+  int vt = PERSIST ? (int)blockIdx.x : (int)blockIdx.x / p.ksplit;
+  int m0, n0;
+  tile_of(vt, m0, n0);
   const int K = p.K;
   // k-blocks of this workgroup's slab: compile-time (fully unrolled loop) or,
   // with NKB = 0, K / 64 / ksplit at run time, a multiple of P
@@ -338,13 +349,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
   // the source row of this lane in each of its load instructions (rows past
   // M or N are clamped: their results are never stored)
   const bf16_t* src[I];
+  auto set_src = [&](int tm0, int tn0) {
 #pragma unroll
-  for (int q = 0; q < I; ++q) {
-    const int row = (wave * I + q) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ (row & 7);
-    if (row < BM) src[q] = p.A + (int64_t)min(m0 + row, p.M - 1) * p.lda + chunk * 8;
-    else src[q] = p.W + (int64_t)min(n0 + row - BM, p.N - 1) * K + chunk * 8;
-  }
+    for (int q = 0; q < I; ++q) {
+      const int row = (wave * I + q) * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ (row & 7);
+      if (row < BM) src[q] = p.A + (int64_t)min(tm0 + row, p.M - 1) * p.lda + chunk * 8;
+      else src[q] = p.W + (int64_t)min(tn0 + row - BM, p.N - 1) * K + chunk * 8;
+    }
+  };
+  set_src(m0, n0);
   auto issue = [&](auto sc, int kb) {
     constexpr int s = decltype(sc)::value;
     uint4* Ls = s == 0 ? L0 : s == 1 ? L1 : s == 2 ? L2 : s == 3 ? L3 : s == 4 ? L4 : L5;
@@ -384,6 +398,96 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
     }
   };
 
+  // the tile's results (every epilogue but the greedy head's): each lane
+  // holds features 4*(lane>>4)..+3 of row (lane&15) of each fragment
+  const int fl = (lane >> 4) * 4;
+  auto store_tile = [&](int m0, int n0) {
+    if constexpr (EPI == EPI_ROPE) {
+      // A wave's TN columns are one head of q, k or v (TN = head size, the
+      // tile starts on a head), so the rotate-half partner of feature c < TN/2,
+      // c + TN/2, sits in the same lane, fragment j + NF/2.  Row r of the
+      // product is new row t = r % rows_per_seq of sequence r / rows_per_seq,
+      // at position pos_add + t; its K and V go to cache slot pos.
+      static_assert(NF % 2 == 0, "rotation partners are half a head apart");
+      constexpr int HALF = TN / 2;
+      const int col0 = n0 + wn * TN;
+      const int part = col0 / p.d;                 // 0 q, 1 k, 2 v (uniform per wave)
+      const int h = (col0 - part * p.d) / TN;
+  #pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int row = m0 + wm * TM + i * 16 + (lane & 15);
+        if (row >= p.M) continue;
+        const int sq = row / p.rows_per_seq, t = row - sq * p.rows_per_seq;
+        const int pos = p.pos_add + t;
+        const int64_t slot = (int64_t)(p.seq0 + sq) * p.seq_stride + ((int64_t)h * p.cap + pos) * TN;
+        if (part == 2) {
+  #pragma unroll
+          for (int j = 0; j < NF; ++j) {
+            const f32x4 v = acc[i][j];
+            uint2 pk;
+            pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+            pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            *reinterpret_cast<uint2*>(p.Vc + slot + j * 16 + fl) = pk;
+          }
+          continue;
+        }
+        const float* rp = p.rope + (int64_t)pos * TN;   // (cos, sin) of features 0 .. HALF-1
+  #pragma unroll
+        for (int j = 0; j < NF / 2; ++j) {
+          const int cc = j * 16 + fl;
+          const float4 r0 = *reinterpret_cast<const float4*>(rp + 2 * cc);
+          const float4 r1 = *reinterpret_cast<const float4*>(rp + 2 * cc + 4);
+          const float cs[4] = {r0.x, r0.z, r1.x, r1.z}, sn[4] = {r0.y, r0.w, r1.y, r1.w};
+          const f32x4 a = acc[i][j], b = acc[i][j + NF / 2];
+          float lo[4], hi[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = a[e] * cs[e] - b[e] * sn[e];
+            hi[e] = b[e] * cs[e] + a[e] * sn[e];
+          }
+          if (part == 0) {
+            float* q = p.q + (int64_t)row * p.d + h * TN + cc;
+            *reinterpret_cast<float4*>(q) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<float4*>(q + HALF) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+          } else {
+            uint2 pl, ph;
+            pl.x = (uint32_t)f2bf(lo[0]) | ((uint32_t)f2bf(lo[1]) << 16);
+            pl.y = (uint32_t)f2bf(lo[2]) | ((uint32_t)f2bf(lo[3]) << 16);
+            ph.x = (uint32_t)f2bf(hi[0]) | ((uint32_t)f2bf(hi[1]) << 16);
+            ph.y = (uint32_t)f2bf(hi[2]) | ((uint32_t)f2bf(hi[3]) << 16);
+            *reinterpret_cast<uint2*>(p.Kc + slot + cc) = pl;
+            *reinterpret_cast<uint2*>(p.Kc + slot + cc + HALF) = ph;
+          }
+        }
+      }
+    } else if constexpr (EPI != EPI_ARGMAX) {
+  #pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int row = m0 + wm * TM + i * 16 + (lane & 15);
+        if (row >= p.M) continue;
+  #pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const int f = n0 + wn * TN + j * 16 + fl;
+          if (f >= p.N) continue;
+          const f32x4 v = acc[i][j];
+          if constexpr (EPI == EPI_STORE) {
+            *reinterpret_cast<float4*>(p.C + ks * p.pstride + (int64_t)row * p.ldc + f) = make_float4(v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EPI_ADD) {
+            float4* o = reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f);
+            float4 c = *o;
+            c.x += v[0]; c.y += v[1]; c.z += v[2]; c.w += v[3];
+            *o = c;
+          } else {   // GELU, rounded to bf16
+            uint2 pk;
+            pk.x = (uint32_t)f2bf(gelu_f(v[0])) | ((uint32_t)f2bf(gelu_f(v[1])) << 16);
+            pk.y = (uint32_t)f2bf(gelu_f(v[2])) | ((uint32_t)f2bf(gelu_f(v[3])) << 16);
+            *reinterpret_cast<uint2*>(p.Cb + (int64_t)row * p.ldc + f) = pk;
+          }
+        }
+      }
+    }
+  };
+
   if constexpr (NKB > 0) {
     static_for([&](auto sc) {
       constexpr int s = decltype(sc)::value;
@@ -397,7 +501,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
       if constexpr (kb + P - 1 < NKB) issue(std::integral_constant<int, (kb + P - 1) % P>{}, kb0 + kb + P - 1);
       compute(std::integral_constant<int, kb % P>{});
     }, std::make_integer_sequence<int, NKB>{});
-  } else {
+  } else if constexpr (!PERSIST) {
     // run-time loop over groups of P stages (slot s of a group is stage
     // kb + s, so slots stay compile-time constants); in every group but the
     // last each stage issues its successor P - 1 stages ahead, so P - 2
@@ -421,93 +525,76 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
       if constexpr (s == 0) issue(std::integral_constant<int, P - 1>{}, kb0 + kb + P - 1);
       compute(sc);
     }, std::make_integer_sequence<int, P>{});
+  } else {
+    // Persistent workgroups (prompt-sized GEMMs): one workgroup per CU walks
+    // its tiles with the same run-time k loop.  At the last stage of a tile,
+    // once the barrier has freed slots 0 .. P-2, the next tile's first P-1
+    // stages are issued, so they load while the last products and the
+    // epilogue run and the epilogue's stores drain under the next tile's
+    // first stages (a synchronised store burst from every CU at once would
+    // otherwise leave the matrix cores idle).  The vector memory counter
+    // retires in issue order, so a wait for a prefetched stage also counts
+    // the E stores issued after it: while those stages are consumed the
+    // wait allows E more, which holds only when the tile stored all of its
+    // E results (a full tile); after a partial one the plain wait is used.
+    // (A direct-to-LDS load under a branch makes the compiler wait for every
+    // load before the next LDS read, so the tile's first stage also waits
+    // for those stores in places: with two ring stages, whose waits drain
+    // the ring anyway, this costs nothing, and only the two-stage QKV tile
+    // of 96-wide heads runs persistent: 10 % faster at the 600M prompts,
+    // where three-stage tiles measured 15-30 % slower.)
+    constexpr int E = MF * NF;                  // stores per wave of a full tile
+    static_for([&](auto sc) { issue(sc, decltype(sc)::value); }, std::make_integer_sequence<int, P - 1>{});
+    bool behind = false;   // the previous tile's E stores sit behind the prefetched stages
+    const int ngroups = nkb / P;
+    for (;;) {
+      const int cm0 = m0, cn0 = n0;
+      const int vn = vt + (int)gridDim.x;
+      const bool more = vn < total;
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int g = 0; g < ngroups; ++g) {
+        const int kb = g * P;
+        const bool last = g + 1 == ngroups;
+        const bool extra = behind && g == 0;
+        static_for([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          constexpr int mid = P - 2;                                      // later stages issued before the wait
+          constexpr int fin = (P - 2 < P - 1 - s) ? P - 2 : P - 1 - s;   // the same in the last group
+          if (extra && s < P - 1) {
+            if (last) __builtin_amdgcn_s_waitcnt(vm_wait(fin * I + E));
+            else __builtin_amdgcn_s_waitcnt(vm_wait(mid * I + E));
+          } else {
+            if (last) __builtin_amdgcn_s_waitcnt(vm_wait(fin * I));
+            else __builtin_amdgcn_s_waitcnt(vm_wait(mid * I));
+          }
+          __builtin_amdgcn_s_barrier();
+          if (!last) {
+            issue(std::integral_constant<int, (s + P - 1) % P>{}, kb + s + P - 1);
+          } else {
+            if constexpr (s == 0) issue(std::integral_constant<int, P - 1>{}, kb + P - 1);
+            if constexpr (s == P - 1) {
+              if (more) {
+                tile_of(vn, m0, n0);
+                set_src(m0, n0);
+                static_for([&](auto nc) { issue(nc, decltype(nc)::value); }, std::make_integer_sequence<int, P - 1>{});
+              }
+            }
+          }
+          compute(sc);
+        }, std::make_integer_sequence<int, P>{});
+      }
+      store_tile(cm0, cn0);
+      if (!more) break;
+      vt = vn;
+      behind = cm0 + BM <= p.M;
+    }
   }
 
-  // epilogue: each lane holds features 4*(lane>>4)..+3 of row (lane&15)
-  const int fl = (lane >> 4) * 4;
-  if constexpr (EPI == EPI_ROPE) {
-    // A wave's TN columns are one head of q, k or v (TN = head size, the
-    // tile starts on a head), so the rotate-half partner of feature c < TN/2,
-    // c + TN/2, sits in the same lane, fragment j + NF/2.  Row r of the
-    // product is new row t = r % rows_per_seq of sequence r / rows_per_seq,
-    // at position pos_add + t; its K and V go to cache slot pos.
-    static_assert(NF % 2 == 0, "rotation partners are half a head apart");
-    constexpr int HALF = TN / 2;
-    const int col0 = n0 + wn * TN;
-    const int part = col0 / p.d;                 // 0 q, 1 k, 2 v (uniform per wave)
-    const int h = (col0 - part * p.d) / TN;
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int row = m0 + wm * TM + i * 16 + (lane & 15);
-      if (row >= p.M) continue;
-      const int sq = row / p.rows_per_seq, t = row - sq * p.rows_per_seq;
-      const int pos = p.pos_add + t;
-      const int64_t slot = (int64_t)(p.seq0 + sq) * p.seq_stride + ((int64_t)h * p.cap + pos) * TN;
-      if (part == 2) {
-#pragma unroll
-        for (int j = 0; j < NF; ++j) {
-          const f32x4 v = acc[i][j];
-          uint2 pk;
-          pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-          pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-          *reinterpret_cast<uint2*>(p.Vc + slot + j * 16 + fl) = pk;
-        }
-        continue;
-      }
-      const float* rp = p.rope + (int64_t)pos * TN;   // (cos, sin) of features 0 .. HALF-1
-#pragma unroll
-      for (int j = 0; j < NF / 2; ++j) {
-        const int cc = j * 16 + fl;
-        const float4 r0 = *reinterpret_cast<const float4*>(rp + 2 * cc);
-        const float4 r1 = *reinterpret_cast<const float4*>(rp + 2 * cc + 4);
-        const float cs[4] = {r0.x, r0.z, r1.x, r1.z}, sn[4] = {r0.y, r0.w, r1.y, r1.w};
-        const f32x4 a = acc[i][j], b = acc[i][j + NF / 2];
-        float lo[4], hi[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = a[e] * cs[e] - b[e] * sn[e];
-          hi[e] = b[e] * cs[e] + a[e] * sn[e];
-        }
-        if (part == 0) {
-          float* q = p.q + (int64_t)row * p.d + h * TN + cc;
-          *reinterpret_cast<float4*>(q) = make_float4(lo[0], lo[1], lo[2], lo[3]);
-          *reinterpret_cast<float4*>(q + HALF) = make_float4(hi[0], hi[1], hi[2], hi[3]);
-        } else {
-          uint2 pl, ph;
-          pl.x = (uint32_t)f2bf(lo[0]) | ((uint32_t)f2bf(lo[1]) << 16);
-          pl.y = (uint32_t)f2bf(lo[2]) | ((uint32_t)f2bf(lo[3]) << 16);
-          ph.x = (uint32_t)f2bf(hi[0]) | ((uint32_t)f2bf(hi[1]) << 16);
-          ph.y = (uint32_t)f2bf(hi[2]) | ((uint32_t)f2bf(hi[3]) << 16);
-          *reinterpret_cast<uint2*>(p.Kc + slot + cc) = pl;
-          *reinterpret_cast<uint2*>(p.Kc + slot + cc + HALF) = ph;
-        }
-      }
-    }
-  } else if constexpr (EPI != EPI_ARGMAX) {
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int row = m0 + wm * TM + i * 16 + (lane & 15);
-      if (row >= p.M) continue;
-#pragma unroll
-      for (int j = 0; j < NF; ++j) {
-        const int f = n0 + wn * TN + j * 16 + fl;
-        if (f >= p.N) continue;
-        const f32x4 v = acc[i][j];
-        if constexpr (EPI == EPI_STORE) {
-          *reinterpret_cast<float4*>(p.C + ks * p.pstride + (int64_t)row * p.ldc + f) = make_float4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_ADD) {
-          float4* o = reinterpret_cast<float4*>(p.C + (int64_t)row * p.ldc + f);
-          float4 c = *o;
-          c.x += v[0]; c.y += v[1]; c.z += v[2]; c.w += v[3];
-          *o = c;
-        } else {   // GELU, rounded to bf16
-          uint2 pk;
-          pk.x = (uint32_t)f2bf(gelu_f(v[0])) | ((uint32_t)f2bf(gelu_f(v[1])) << 16);
-          pk.y = (uint32_t)f2bf(gelu_f(v[2])) | ((uint32_t)f2bf(gelu_f(v[3])) << 16);
-          *reinterpret_cast<uint2*>(p.Cb + (int64_t)row * p.ldc + f) = pk;
-        }
-      }
-    }
+  if constexpr (EPI != EPI_ARGMAX) {
+    if constexpr (!PERSIST) store_tile(m0, n0);
   } else {
     // greedy head: optional logits, then the per-row first maximum of the
     // tile; the partials go through ring slot 0 once every wave is done
@@ -549,8 +636,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
 #pragma unroll
       for (int w = 1; w < WN; ++w)
         if (bv[w * BM + rl] > best) { best = bv[w * BM + rl]; bidx = bi[w * BM + rl]; }
-      p.av[(int64_t)nt * p.M + row] = best;
-      p.ai[(int64_t)nt * p.M + row] = bidx;
+      p.av[(int64_t)(n0 / BN) * p.M + row] = best;
+      p.ai[(int64_t)(n0 / BN) * p.M + row] = bidx;
     }
   }
 }
@@ -605,6 +692,26 @@ struct Plan {
   GemmKernel fn;   // tuned instantiation (fully unrolled k loop), or null
   int threads = 256;
 };
+
+// Compute units of the current device (one persistent workgroup each).
+int cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!counts[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
+// Workgroups of a persistent launch over `total` tiles: one per CU, a
+// multiple of 8 so that each stays on its XCD's run of tiles.
+int persist_grid(int total) {
+  const int g = cu_count() / 8 * 8;
+  return total <= g || g < 8 ? total : g;
+}
 
 // Tuned tiles for the decode GEMMs of the PHOTON model shapes (d = 768 and
 // 1536, MLP 4d, vocab 32000, rows B or B*C2 from 16 to 512), measured on
@@ -898,16 +1005,18 @@ int gemm_splits(int dtype, int M, int N, int K, int wide) {
 
 // Prompt QKV projection with RoPE and the K/V append in its epilogue: 256-row
 // tiles two heads wide (8 waves, 4 along M; each wave's columns are one head),
-// three ring stages where two fit the LDS, else two.
+// three ring stages where two fit the LDS, else two; persistent workgroups
+// for the two-stage tile of 96-wide heads.
 namespace {
-GemmKernel qkv_rope_kernel(int hd, int K, int* stages) {
+GemmKernel qkv_rope_kernel(int hd, int K, bool* persist) {
   GemmKernel fn = nullptr;
   int P = 0;
+  bool pst = false;
   if (hd == 64) { fn = gemm_lds_kernel<256, 128, 4, 3, EPI_ROPE, 0, 8>; P = 3; }
-  if (hd == 96) { fn = gemm_lds_kernel<256, 192, 4, 2, EPI_ROPE, 0, 8>; P = 2; }
+  if (hd == 96) { fn = gemm_lds_kernel<256, 192, 4, 2, EPI_ROPE, 0, 8, true>; P = 2; pst = true; }
   if (hd == 128) { fn = gemm_lds_kernel<256, 256, 4, 2, EPI_ROPE, 0, 8>; P = 2; }
   if (!fn || K % 64 || (K / 64) % P) return nullptr;
-  if (stages) *stages = P;
+  if (persist) *persist = pst;
   return fn;
 }
 bool aligned(const void* ptr, int bytes) { return ((uintptr_t)ptr % bytes) == 0; }
@@ -924,7 +1033,8 @@ int gemm_qkv_rope_supported(const GemmCall& g, const RopeKvCall& rc) {
 
 hipError_t launch_gemm_qkv_rope(const GemmCall& g, const RopeKvCall& rc, hipStream_t st) {
   if (!gemm_qkv_rope_supported(g, rc)) return hipErrorInvalidValue;
-  GemmKernel fn = qkv_rope_kernel(rc.hd, g.K, nullptr);
+  bool pst = false;
+  GemmKernel fn = qkv_rope_kernel(rc.hd, g.K, &pst);
   const int BN = 2 * rc.hd;
   GemmP p{};
   p.A = (const bf16_t*)g.A; p.lda = g.lda; p.W = (const bf16_t*)g.W;
@@ -933,7 +1043,7 @@ hipError_t launch_gemm_qkv_rope(const GemmCall& g, const RopeKvCall& rc, hipStre
   p.q = rc.q_out; p.Kc = (bf16_t*)rc.Kc; p.Vc = (bf16_t*)rc.Vc; p.rope = rc.rope;
   p.seq_stride = rc.seq_stride; p.cap = rc.cap; p.rows_per_seq = rc.rows_per_seq; p.seq0 = rc.seq0;
   p.pos_add = rc.pos_add; p.d = rc.d;
-  PH_LAUNCH(fn, p.m_tiles * p.n_tiles, 512, 0, st, p);
+  PH_LAUNCH(fn, pst ? persist_grid(p.m_tiles * p.n_tiles) : p.m_tiles * p.n_tiles, 512, 0, st, p);
   return hipGetLastError();
 }
 
