@@ -273,7 +273,9 @@ def measured_counters(wl):
                 "mfma_tflop_s_executed": round(sum(v["mfma_tflop_s"] * v["avg_us"] * v["dispatches"]
                                                    for v in sel.values()) / t, 1),
                 "kernels": len(sel)}
-    prompt = lambda k: k.startswith("gemm_lds_kernel<128, 256,") or k.startswith("gemm_lds_kernel<256, 256,")
+    # prompt-sized GEMMs: the LDS-streaming kernel with a run-time k loop
+    # (template argument NKB, the sixth, is 0)
+    prompt = lambda k: k.startswith("gemm_lds_kernel<") and k[len("gemm_lds_kernel<"):].split(",")[5].strip() == "0"
     top = [v for k, v in ks.items() if k.startswith("attn_decode_kernel")]
     return {"source": "profiles/counters_photon600m.json",
             "prompt_gemm": group(prompt),
