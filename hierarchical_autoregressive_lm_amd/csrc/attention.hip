@@ -708,9 +708,12 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sc[kb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int kb = 0; kb < 4; ++kb) {
+        // k-step outer, key block inner: consecutive products go to the
+        // four independent accumulators (each one's order of terms, and so
+        // its bits, as with the key block outer)
         const bf16x8_t kf = __builtin_bit_cast(
             bf16x8_t, Kc[(ks >> 1) * TK * 8 + kb * 16 * 8 + ((ks & 1) ? kfr1 : kfr0)]);
         sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qhi[ks], sc[kb], 0, 0, 0);
@@ -754,10 +757,15 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
         }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
+      // the output rescale is skipped when no query of the wave has a new
+      // maximum (corr = 1 for all of them, so nothing changes)
+      const bool grew = __builtin_amdgcn_ballot_w64(mx != m) != 0;
       l = l * corr + ps;
       m = mx;
+      if (grew) {
 #pragma unroll
-      for (int b = 0; b < HB; ++b) o[b] *= corr;
+        for (int b = 0; b < HB; ++b) o[b] *= corr;
+      }
     }
     // O^T += V^T P^T, two k-steps of 32 keys
     __builtin_amdgcn_s_setprio(1);
