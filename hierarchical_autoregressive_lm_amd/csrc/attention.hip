@@ -584,7 +584,7 @@ __device__ __forceinline__ void split_hi_lo(float x, bf16_t& hi, bf16_t& lo) {
 __device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 template <int HD, int NWV>
-__global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
+__global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
   constexpr int NT = NWV * 64;           // threads
   constexpr int TK = 64;                 // keys per tile
   constexpr int BQ = 16 * NWV;           // queries per workgroup
@@ -779,11 +779,17 @@ __global__ __launch_bounds__(NWV * 64, HD <= 64 ? 4 : 2) void attn_prefill_mfma_
         phi[e] = __builtin_bit_cast(__bf16, hb);
         plo[e] = __builtin_bit_cast(__bf16, lb);
       }
+      // two row blocks at a time: both V fragment reads in flight, the hi
+      // products of both, then the lo products (per accumulator the same
+      // order of terms)
 #pragma unroll
-      for (int b = 0; b < HB; ++b) {
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, Vc[b * 16 * 8 + (s ? vfr1 : vfr0)]);
-        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[b], 0, 0, 0);
-        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[b], 0, 0, 0);
+      for (int b = 0; b < HB; b += 2) {
+        const bf16x8_t v0 = __builtin_bit_cast(bf16x8_t, Vc[b * 16 * 8 + (s ? vfr1 : vfr0)]);
+        const bf16x8_t v1 = __builtin_bit_cast(bf16x8_t, Vc[(b + 1) * 16 * 8 + (s ? vfr1 : vfr0)]);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, phi, o[b], 0, 0, 0);
+        o[b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, phi, o[b + 1], 0, 0, 0);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, plo, o[b], 0, 0, 0);
+        o[b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, plo, o[b + 1], 0, 0, 0);
       }
     }
     // the next tile's V^T goes to the other buffer (free since the last
