@@ -580,6 +580,29 @@ __device__ __forceinline__ void split_hi_lo(float x, bf16_t& hi, bf16_t& lo) {
   lo = f2bf(x - bf2f(hi));
 }
 
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 with gfx950's lane swaps
+// (VALU, no trip through the LDS crossbar): with the same value as both
+// operands, v_permlane16_swap leaves lane l's value and its l ^ 16 partner's
+// in the two results (in some order), v_permlane32_swap likewise for l ^ 32.
+// Each step combines the pair with a commutative operation, so every lane
+// gets the same bits as a shuffle-based xor reduction.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 16-byte slot of (row, chunk) in a tile of 128-byte rows
 __device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
@@ -742,8 +765,7 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = xor32_max(xor16_max(mx));
       // a query sees key 0 in the first tile, so mx is finite from then on
       const float corr = __builtin_amdgcn_exp2f(m - mx);
       float ps = 0.f;
@@ -755,8 +777,7 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
           sc[kb][r] = p;
           ps += p;
         }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      ps = xor32_sum(xor16_sum(ps));
       // the output rescale is skipped when no query of the wave has a new
       // maximum (corr = 1 for all of them, so nothing changes)
       const bool grew = __builtin_amdgcn_ballot_w64(mx != m) != 0;
