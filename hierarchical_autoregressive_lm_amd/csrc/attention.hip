@@ -562,14 +562,16 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnCall a, float sca
 //      loads (lane l of a load writes slot base + l, so each lane fetches the
 //      chunk its slot holds); rows past the prompt repeat its last key (their
 //      scores are masked) and unused chunks of a region repeat chunk 0.
-//   V^T: row = dimension, chunk q = 4s + j holds the 8 keys of k-step s that
-//      lane group j multiplies: 32s+4j .. +3, then 32s+16+4j .. +3.  Each
-//      thread loads 8 dimensions of 4 consecutive keys (zero past the
-//      prompt), transposes them in registers and stores 8 half-chunks.
-// Tile t+1's K loads go out at the start of tile t and land in LDS by
-// themselves; its V rows load once tile t's scores are formed (they would
-// otherwise hold registers through the score products) and are stored at
-// the end of the tile; one barrier per tile.
+//   V: row = key, like K (regions of 64 dims, direct global->LDS loads), with
+//      chunk c of row r at position c ^ 2(r mod 4).  The P V products read it
+//      with gfx950's transposing LDS reads (ds_read_b64_tr_b16): in each group
+//      of 16 lanes, lanes 4a .. 4a+3 name 16 consecutive dims of one key row
+//      a and lane i receives dim i of the four rows, so two such reads give a
+//      lane the 8 keys of its V^T fragment (keys 32s+4j .. +3, then
+//      32s+16+4j .. +3, the order of its probabilities).  The swizzle puts the
+//      two chunks each of a group's four rows at eight distinct positions.
+// Tile t+1's K and V loads go out at the start of tile t and land in LDS by
+// themselves; one barrier per tile.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void attn_lds_t;
@@ -603,8 +605,12 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 16-byte slot of (row, chunk) in a tile of 128-byte rows
+// 16-byte slot of (row, chunk) in a tile of 128-byte rows: K, and V
 __device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
+__device__ __forceinline__ int vlds_pos(int row, int chunk) { return chunk ^ (2 * (row & 3)); }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 template <int HD, int NWV>
 __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_kernel(AttnCall a, float scale) {
@@ -616,11 +622,9 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
   constexpr int KR = (HD + 63) / 64;     // K regions of 64 dims
   constexpr int KSLOTS = KR * TK * 8;    // 16-byte K slots per tile
   static_assert(KSLOTS % (64 * NWV) == 0, "K tile fills whole direct loads per wave");
-  constexpr int KI = KSLOTS / (64 * NWV);    // direct loads per wave per tile
-  constexpr int VIT = (TK / 4) * (HD / 8);   // (4 keys x 8 dims) V items per tile
-  constexpr int VPT = (VIT + NT - 1) / NT;
+  constexpr int KI = KSLOTS / (64 * NWV);    // direct loads per wave per tile (K, and V)
   __shared__ __attribute__((aligned(16))) uint4 Ks[2][KSLOTS];
-  __shared__ __attribute__((aligned(16))) uint4 Vt[2][HD * 8];
+  __shared__ __attribute__((aligned(16))) uint4 Vs[2][KSLOTS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, j = lane >> 4;
@@ -656,8 +660,9 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
   // this lane's fragment slots (uint4 index inside a tile): K for the two
   // halves (k-steps 2r, 2r+1) of a region's row, V^T for the two k-steps
   const int kfr0 = lds_slot(c, j), kfr1 = lds_slot(c, 4 + j);
-  const int vfr0 = lds_slot(c, j), vfr1 = lds_slot(c, 4 + j);
-  uint4 vreg[VPT][4];
+  // this lane's part of the transposing V reads: key row 4j + (c >> 2) of a
+  // 16-key block, dims 4(c & 3) .. +3 of a 16-dim block (half of a chunk)
+  const int vrow = 4 * j + (c >> 2), vsub = c & 3;
   // direct K loads: lane l of load i fills slot (wave*KI + i)*64 + l and
   // fetches the (key, dim chunk) that slot holds
   auto issue_k = [&](int t, uint4* Kdst) {
@@ -672,55 +677,41 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
       __builtin_amdgcn_global_load_lds((attn_glb_t*)src, (attn_lds_t*)(Kdst + (wave * KI + i) * 64), 16, 0, 0);
     }
   };
-  auto load_v = [&](int t) {
+  // direct V loads: the same slots as K, each holding chunk c of its row at
+  // position vlds_pos(row, c)
+  auto issue_v = [&](int t, uint4* Vdst) {
     const int k0 = t * TK;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      // 16 consecutive threads take the 16 groups of 4 keys of one block of
-      // 8 dims (their half-chunk stores then hit distinct banks)
-      const int it = tid + NT * i;
-      const int db = it / (TK / 4), g4 = it % (TK / 4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int key = k0 + 4 * g4 + u;
-        if (it < VIT && key < T)
-          vreg[i][u] = *reinterpret_cast<const uint4*>(Vb + (int64_t)key * HD + 8 * db);
-        else
-          vreg[i][u] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < KI; ++i) {
+      const int slot = (wave * KI + i) * 64 + lane;
+      const int key = (slot % (TK * 8)) / 8;
+      const int c8 = 8 * (slot / (TK * 8)) + vlds_pos(key, slot & 7);
+      const int row = k0 + key < T ? k0 + key : T - 1;
+      const bf16_t* src = Vb + (int64_t)row * HD + 8 * (c8 < HD / 8 ? c8 : 0);
+      __builtin_amdgcn_global_load_lds((attn_glb_t*)src, (attn_lds_t*)(Vdst + (wave * KI + i) * 64), 16, 0, 0);
     }
   };
-  auto store_v = [&](uint4* Vdst) {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int it = tid + NT * i;
-      if (it < VIT) {
-        const int db = it / (TK / 4), g4 = it % (TK / 4);
-        // keys 4g4 .. 4g4+3 of the tile: k-step s, lane group jj, half hh
-        const int s = g4 >> 3, jj = g4 & 3, hh = (g4 >> 2) & 1;
-        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-        uint2* row = reinterpret_cast<uint2*>(Vdst);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // dims 8db + 2w (low halves) and 8db + 2w + 1 (high halves) of the 4 keys
-          const uint2 ev = make_uint2((v0[w] & 0xffffu) | (v1[w] << 16), (v2[w] & 0xffffu) | (v3[w] << 16));
-          const uint2 od = make_uint2((v0[w] >> 16) | (v1[w] & 0xffff0000u), (v2[w] >> 16) | (v3[w] & 0xffff0000u));
-          row[lds_slot(8 * db + 2 * w, 4 * s + jj) * 2 + hh] = ev;
-          row[lds_slot(8 * db + 2 * w + 1, 4 * s + jj) * 2 + hh] = od;
-        }
-      }
-    }
+  // V^T fragment of dims 16b .. 16b+15 and k-step s (8 keys per lane)
+  auto v_frag = [&](const uint4* Vc, int s, int b) {
+    const int cc = 2 * (b & 3) + (vsub >> 1);
+    const uint4* base = Vc + (b >> 2) * TK * 8;
+    const int r0 = 32 * s + vrow, r1 = r0 + 16;
+    const char* p0 = reinterpret_cast<const char*>(base + r0 * 8 + vlds_pos(r0, cc)) + 8 * (vsub & 1);
+    const char* p1 = reinterpret_cast<const char*>(base + r1 * 8 + vlds_pos(r1, cc)) + 8 * (vsub & 1);
+    const v4i16_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p0);
+    const v4i16_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p1);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   // one tile: products on buffer BUF while tile t+1 loads into the other
   auto step = [&](int BUF, int t) {
     const uint4* Kc = Ks[BUF];
-    const uint4* Vc = Vt[BUF];
+    const uint4* Vc = Vs[BUF];
     const bool more = t + 1 < ntiles;
-    if (more) issue_k(t + 1, Ks[BUF ^ 1]);
+    if (more) {
+      issue_k(t + 1, Ks[BUF ^ 1]);
+      issue_v(t + 1, Vs[BUF ^ 1]);
+    }
     const int k0 = t * TK;
     // S^T for 4 blocks of 16 keys x 16 queries.  The matrix-product runs
     // raise the wave's issue priority: of the two waves sharing a SIMD, the
@@ -742,10 +733,7 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
         sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qhi[ks], sc[kb], 0, 0, 0);
         sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[ks], sc[kb], 0, 0, 0);
       }
-    // the next tile's V rows load while the softmax and the P V products
-    // run (their registers are free again by then)
     __builtin_amdgcn_s_setprio(0);
-    if (more) load_v(t + 1);
     // online softmax per query; p in place of the scores.  Only a tile that
     // reaches past this wave's first query or past the prompt needs masking.
     const bool masked = k0 + TK - 1 > q0 || k0 + TK > T;
@@ -805,18 +793,17 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
       // order of terms)
 #pragma unroll
       for (int b = 0; b < HB; b += 2) {
-        const bf16x8_t v0 = __builtin_bit_cast(bf16x8_t, Vc[b * 16 * 8 + (s ? vfr1 : vfr0)]);
-        const bf16x8_t v1 = __builtin_bit_cast(bf16x8_t, Vc[(b + 1) * 16 * 8 + (s ? vfr1 : vfr0)]);
+        const bf16x8_t v0 = v_frag(Vc, s, b);
+        const bf16x8_t v1 = v_frag(Vc, s, b + 1);
         o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, phi, o[b], 0, 0, 0);
         o[b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, phi, o[b + 1], 0, 0, 0);
         o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, plo, o[b], 0, 0, 0);
         o[b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, plo, o[b + 1], 0, 0, 0);
       }
     }
-    // the next tile's V^T goes to the other buffer (free since the last
-    // barrier); its direct K loads have landed for this wave, then for all
+    // the next tile's direct K and V loads have landed for this wave, then
+    // (the barrier) for all
     __builtin_amdgcn_s_setprio(0);
-    if (more) store_v(Vt[BUF ^ 1]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -824,7 +811,7 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
   // the first tile's K and V go out before the queries are formed, so the
   // two prologue latencies overlap
   issue_k(0, Ks[0]);
-  load_v(0);
+  issue_v(0, Vs[0]);
   {
     const int qi = q0 + c;
     const float* qp = a.q + (int64_t)(g * a.Q + (qi < T ? qi : T - 1)) * a.q_ld + h * HD + 8 * j;
@@ -850,7 +837,6 @@ __global__ __launch_bounds__(NWV * 64, HD <= 96 ? 4 : 2) void attn_prefill_mfma_
       }
     }
   }
-  store_v(Vt[0]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) step(t & 1, t);
