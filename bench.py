@@ -422,6 +422,9 @@ def main():
                "attention": tf(["attn_prefill"]),
                "gemm": tf(["gemm_qkv", "gemm_o", "gemm_up", "gemm_down", "gemm_chunk"]),
                "by_class": {n: tf([n]) for n in sorted(pre_cls)},
+               "note": "bf16 prompts: gemm_qkv includes the RoPE rotation and the K/V cache append in its "
+                       "epilogue (no rope_kv launch); attention flops are the causal half, counted once "
+                       "although q and p each enter the products as two bf16 terms",
                "mfma_peak_tflop_s": MFMA_BF16_PEAK_TFLOPS}
     log(f"prefill {pre_s:.3f} s ({prefill['tflop_s']} TFLOP/s)")
     if args.mode == "recgen":
