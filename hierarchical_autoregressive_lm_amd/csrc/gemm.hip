@@ -36,6 +36,7 @@ struct GemmP {
   // k and v rounded to bf16 into the cache planes Kc / Vc
   float* q; bf16_t* Kc; bf16_t* Vc; const float* rope;
   int64_t seq_stride; int cap, rows_per_seq, seq0, pos_add, d;
+  const int* pos_dev; int pos_mul;   // positions also advance with a device counter (decode)
 };
 
 template <int MB, int NI, int WK, int P, int EPI, int NKB, bool NTW>
@@ -413,12 +414,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_lds_kernel(GemmP p) {
       const int col0 = n0 + wn * TN;
       const int part = col0 / p.d;                 // 0 q, 1 k, 2 v (uniform per wave)
       const int h = (col0 - part * p.d) / TN;
+      const int pos0 = p.pos_add + (p.pos_dev ? *p.pos_dev * p.pos_mul : 0);
   #pragma unroll
       for (int i = 0; i < MF; ++i) {
         const int row = m0 + wm * TM + i * 16 + (lane & 15);
         if (row >= p.M) continue;
         const int sq = row / p.rows_per_seq, t = row - sq * p.rows_per_seq;
-        const int pos = p.pos_add + t;
+        const int pos = pos0 + t;
         const int64_t slot = (int64_t)(p.seq0 + sq) * p.seq_stride + ((int64_t)h * p.cap + pos) * TN;
         if (part == 2) {
   #pragma unroll
@@ -1003,28 +1005,40 @@ int gemm_splits(int dtype, int M, int N, int K, int wide) {
   return plan_bf16(M, N, K, EPI_STORE, true, wide != 0).ksplit;
 }
 
-// Prompt QKV projection with RoPE and the K/V append in its epilogue: 256-row
-// tiles two heads wide (8 waves, 4 along M; each wave's columns are one head),
-// three ring stages where two fit the LDS, else two; persistent workgroups
-// for the two-stage tile of 96-wide heads.
+// QKV projection with RoPE and the K/V append in its epilogue.  Prompts:
+// 256-row tiles two heads wide (8 waves, 4 along M; each wave's columns are
+// one head), three ring stages where two fit the LDS, else two; persistent
+// workgroups for the two-stage tile of 96-wide heads.  Decode steps of 64-512
+// rows: 64-row tiles (below).
 namespace {
-GemmKernel qkv_rope_kernel(int hd, int K, bool* persist) {
+GemmKernel qkv_rope_kernel(int hd, int K, int M, bool* persist, int* rows, int* threads) {
   GemmKernel fn = nullptr;
-  int P = 0;
+  int P = 0, BM = 256, NT = 512;
   bool pst = false;
-  if (hd == 64) { fn = gemm_lds_kernel<256, 128, 4, 3, EPI_ROPE, 0, 8>; P = 3; }
-  if (hd == 96) { fn = gemm_lds_kernel<256, 192, 4, 2, EPI_ROPE, 0, 8, true>; P = 2; pst = true; }
-  if (hd == 128) { fn = gemm_lds_kernel<256, 256, 4, 2, EPI_ROPE, 0, 8>; P = 2; }
+  if (M >= kBigM) {
+    if (hd == 64) { fn = gemm_lds_kernel<256, 128, 4, 3, EPI_ROPE, 0, 8>; P = 3; }
+    if (hd == 96) { fn = gemm_lds_kernel<256, 192, 4, 2, EPI_ROPE, 0, 8, true>; P = 2; pst = true; }
+    if (hd == 128) { fn = gemm_lds_kernel<256, 256, 4, 2, EPI_ROPE, 0, 8>; P = 2; }
+  } else if (M >= 64 && M <= 512) {
+    // decode steps of 64-512 rows: 64-row tiles of 4 waves (2 x 2, 32 rows x
+    // one head each), four ring stages; M/64 x 3H/2 workgroups
+    BM = 64;
+    NT = 256;
+    if (hd == 64) { fn = gemm_lds_kernel<64, 128, 2, 4, EPI_ROPE, 0, 4>; P = 4; }
+    if (hd == 96) { fn = gemm_lds_kernel<64, 192, 2, 4, EPI_ROPE, 0, 4>; P = 4; }
+  }
   if (!fn || K % 64 || (K / 64) % P) return nullptr;
   if (persist) *persist = pst;
+  if (rows) *rows = BM;
+  if (threads) *threads = NT;   // 64 x the tile's waves (its launch bound)
   return fn;
 }
 bool aligned(const void* ptr, int bytes) { return ((uintptr_t)ptr % bytes) == 0; }
 }  // namespace
 
 int gemm_qkv_rope_supported(const GemmCall& g, const RopeKvCall& rc) {
-  if (g.dtype != 1 || rc.dtype != 1 || g.M < kBigM || rc.M != g.M || rc.pos_dev) return 0;
-  if (!qkv_rope_kernel(rc.hd, g.K, nullptr) || rc.d != rc.H * rc.hd || g.N != 3 * rc.d || (3 * rc.H) % 2) return 0;
+  if (g.dtype != 1 || rc.dtype != 1 || rc.M != g.M) return 0;
+  if (!qkv_rope_kernel(rc.hd, g.K, g.M, nullptr, nullptr, nullptr) || rc.d != rc.H * rc.hd || g.N != 3 * rc.d || (3 * rc.H) % 2) return 0;
   if (g.lda % 8 || !aligned(g.A, 16) || !aligned(g.W, 16) || !aligned(rc.q_out, 16) || !aligned(rc.Kc, 8) ||
       !aligned(rc.Vc, 8) || !aligned(rc.rope, 16) || rc.seq_stride % 4 || rc.rows_per_seq < 1)
     return 0;
@@ -1034,16 +1048,17 @@ int gemm_qkv_rope_supported(const GemmCall& g, const RopeKvCall& rc) {
 hipError_t launch_gemm_qkv_rope(const GemmCall& g, const RopeKvCall& rc, hipStream_t st) {
   if (!gemm_qkv_rope_supported(g, rc)) return hipErrorInvalidValue;
   bool pst = false;
-  GemmKernel fn = qkv_rope_kernel(rc.hd, g.K, &pst);
+  int BM = 256, NT = 512;
+  GemmKernel fn = qkv_rope_kernel(rc.hd, g.K, g.M, &pst, &BM, &NT);
   const int BN = 2 * rc.hd;
   GemmP p{};
   p.A = (const bf16_t*)g.A; p.lda = g.lda; p.W = (const bf16_t*)g.W;
   p.M = g.M; p.N = g.N; p.K = g.K;
-  p.m_tiles = (g.M + 255) / 256; p.n_tiles = g.N / BN; p.ksplit = 1;
+  p.m_tiles = (g.M + BM - 1) / BM; p.n_tiles = g.N / BN; p.ksplit = 1;
   p.q = rc.q_out; p.Kc = (bf16_t*)rc.Kc; p.Vc = (bf16_t*)rc.Vc; p.rope = rc.rope;
   p.seq_stride = rc.seq_stride; p.cap = rc.cap; p.rows_per_seq = rc.rows_per_seq; p.seq0 = rc.seq0;
-  p.pos_add = rc.pos_add; p.d = rc.d;
-  PH_LAUNCH(fn, pst ? persist_grid(p.m_tiles * p.n_tiles) : p.m_tiles * p.n_tiles, 512, 0, st, p);
+  p.pos_add = rc.pos_add; p.d = rc.d; p.pos_dev = rc.pos_dev; p.pos_mul = rc.pos_mul;
+  PH_LAUNCH(fn, pst ? persist_grid(p.m_tiles * p.n_tiles) : p.m_tiles * p.n_tiles, NT, 0, st, p);
   return hipGetLastError();
 }
 

@@ -98,13 +98,14 @@ struct RopeKvCall {
 };
 hipError_t launch_rope_kv(const RopeKvCall& c, hipStream_t st);
 
-// Prompt QKV projection fused with launch_rope_kv's work: the GEMM g (A the
+// QKV projection fused with launch_rope_kv's work: the GEMM g (A the
 // normalized rows, W = Wqkv, N = 3d, no K slabs) writes rotated q to
 // rc.q_out and rotated k and v, rounded to bf16, to the cache planes, with
-// rc's row, sequence and position map (rc.qkv and rc.ksplit unused).  Only
-// for bf16 prompt-sized GEMMs (M >= 2048) with head size 64, 96 or 128, an
-// even number of heads in 3d, host positions (pos_dev null) and aligned
-// buffers; gemm_qkv_rope_supported says whether a call qualifies.
+// rc's row, sequence and position map, the device counter included
+// (rc.qkv and rc.ksplit unused).  bf16 only, for prompt-sized GEMMs (M >=
+// 2048; head size 64, 96 or 128) and decode steps of 64-512 rows (head
+// size 64 or 96), an even number of heads in 3d and aligned buffers;
+// gemm_qkv_rope_supported says whether a call qualifies.
 int gemm_qkv_rope_supported(const GemmCall& g, const RopeKvCall& rc);
 hipError_t launch_gemm_qkv_rope(const GemmCall& g, const RopeKvCall& rc, hipStream_t st);
 

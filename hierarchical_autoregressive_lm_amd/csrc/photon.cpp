@@ -792,14 +792,21 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
     unsigned char* kbase = r.kv.base + (r.kv.per_layer ? (int64_t)l * 2 * r.kv.plane_elems * eb : 0);
     void* Kc = kbase;
     void* Vc = kbase + r.kv.plane_elems * eb;
-    // a prompt's QKV projection rotates q and k and appends K/V in its own
-    // epilogue where the kernel supports the shape; otherwise the product's
-    // K slabs go to a RoPE + append launch (or into the attention, below)
+    // RoPE and the K/V append run inside the attention kernel (the new rows
+    // are the last Q keys of every group) for the chunk-confined decoders and
+    // for decode steps over caches of fewer than 1024 slots or whose
+    // workgroups are all resident at once; otherwise the QKV projection
+    // rotates q and k and appends K/V in its own epilogue where the kernel
+    // supports the shape (prompts, decode steps of 64-512 rows), and else its
+    // K slabs go to a RoPE + append launch of their own
+    const bool fuse = r.rows_per_seq == r.Q &&
+                      (r.kind == ATT_CHUNK ||
+                       (r.kind == ATT_DECODE && attn_decode_rope_inside(r.G, H, (int)r.kv.cap, r.nsplit)));
     GemmCall gq{};
     gq.dtype = dt; gq.A = b.a; gq.lda = d; gq.W = w.Wqkv; gq.M = r.M; gq.N = 3 * d; gq.K = d;
     RopeKvCall rq{dt, nullptr, 1, 0, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
                   r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
-    const bool qkv_rope = r.kind == ATT_PREFILL && gemm_qkv_rope_supported(gq, rq);
+    const bool qkv_rope = !fuse && r.kind != ATT_CHUNK && gemm_qkv_rope_supported(gq, rq);
     if (qkv_rope) {
       // W and the operand rows read once, q (fp32) and K, V written once
       const double qb = (double)gq.N * d * eb + (double)r.M * d * eb + (double)r.M * d * (4 + 2.0 * eb);
@@ -808,15 +815,6 @@ photon_status run_stack(photon_ctx* c, const StackW& sw, const StackBufs& b, con
     } else {
       PH_TRY(gemm_slabs(c, PHOTON_K_GEMM_QKV, b.a, d, w.Wqkv, r.M, 3 * d, d, b.part, &ks, st));
     }
-    // RoPE and the K/V append run inside the attention kernel (the new rows
-    // are the last Q keys of every group) for the chunk-confined decoders and
-    // for decode steps over caches of fewer than 1024 slots or whose
-    // workgroups are all resident at once; a longer launch over a long cache
-    // (where every round of workgroups would wait for its q) and prefill
-    // give them a launch of their own
-    const bool fuse = r.rows_per_seq == r.Q &&
-                      (r.kind == ATT_CHUNK ||
-                       (r.kind == ATT_DECODE && attn_decode_rope_inside(r.G, H, (int)r.kv.cap, r.nsplit)));
     if (!fuse && !qkv_rope) {
       RopeKvCall rc{dt, b.part, ks, (int64_t)r.M * 3 * d, r.M, d, H, hd, b.q, Kc, Vc, r.kv.seq_stride, r.kv.cap,
                     r.rows_per_seq, r.kv.seq0, r.pos_add, r.pos_dev, r.pos_mul, r.rope};
